@@ -1,0 +1,15 @@
+"""Reference (oracle) implementation of paged-KV attention: TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of ``bench.py`` may
+import or run anything in this package.  The library's product path never touches it, and this
+package imports nothing from the library or its Python binding.
+
+* ``oracle.attention`` - numpy float64 definition: explicit block-table gather, then masked
+  softmax attention per q-head; pool append (scatter) and block copy as plain integer indexing.
+* ``oracle.brute``     - pure-Python brute force for tiny inputs (``math.fsum``, log-sum-exp
+  normalisation, element-wise scatter by the storage formula) used to pin ``oracle.attention``.
+
+Every function is pinned by a ``-m "not gpu"`` test against something other than itself
+(brute force, closed forms, invariants).  Nothing here is "parity unpinned".
+"""
+from . import attention, brute  # noqa: F401
