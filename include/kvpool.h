@@ -1,0 +1,159 @@
+/*
+ * kvpool.h - C ABI of the paged-KV attention library for MI355X (gfx950).
+ *
+ * What the library computes: attention of new query tokens against keys and values held in
+ * a block-paged KV pool that all sequences share.  The pool is sized once and each request
+ * owns a list of fixed-size token blocks; blocks of a shared prefix are shared rather than
+ * copied (sparkinfer server README, "Request isolation & continuous batching" and
+ * "Automatic prefix cache"; NInfer serving doc, "Execution behavior").  One call covers
+ *   - single-token decode for a batch of sequences (NInfer serving doc, "Execution behavior"),
+ *   - verification of 1 + k draft tokens, causal among themselves (sparkinfer server README,
+ *     "Serve Qwen3.8 with DSpark"; NInfer serving doc, "Server options", --spec/--draft-tokens),
+ *   - prefix-reuse prefill, where only the uncached suffix is computed against the cached
+ *     prefix (sparkinfer server README, "Automatic prefix cache").
+ * For sequence s with L = ctx_lens[s] keys and T = q_lens[s] query tokens, query row i sits at
+ * position L - T + i and attends to keys 0 .. L - T + i.  q-head h reads KV head
+ * h / (num_q_heads / num_kv_heads) (GQA).  Softmax runs in fp32 with the caller's scale.
+ *
+ * Conventions shared by every entry point
+ *   - Ownership: the caller owns every device buffer (pool storage, q, out, metadata,
+ *     workspace).  The library allocates no device memory and keeps no pointer beyond
+ *     kvpool_create's storage pointers.
+ *   - Asynchrony: work is enqueued on `stream` (a hipStream_t; NULL = the null stream) with no
+ *     host synchronisation, so calls can be captured in a HIP graph.  Faults inside kernels
+ *     surface at the caller's next synchronisation.
+ *   - Errors: a non-zero return enqueues no work; kvpool_last_error() then describes it.  The
+ *     library never falls back silently to another method: unsupported shapes are rejected
+ *     (compare the pages' rule that requested features are refused rather than silently
+ *     degraded, sparkinfer server README, "Serve Qwen3.8 with DSpark").
+ *   - Metadata checks: scalar arguments are always checked on the host.  Device metadata
+ *     (block tables, lengths, block ids) is trusted unless the environment variable
+ *     KVPOOL_VALIDATE=1 is set, in which case it is copied to the host (synchronising the
+ *     stream) and every violation returns KV_ERANGE.  Without validation, kernels clamp ids and
+ *     lengths into range so that bad metadata gives wrong values, never an out-of-bounds access.
+ *   - Determinism: no float atomics.  The split of a sequence's keys depends only on that
+ *     sequence's own length, so a sequence's output is bitwise independent of the rest of the
+ *     batch and of where its blocks sit in the pool (the pages' decode path has no float
+ *     atomics and a deterministic mode is batch-invariant: sparkinfer server README,
+ *     "Determinism").
+ *
+ * Pool storage layout (K and V are separate buffers of identical size).  Element type: fp32
+ * or bf16; X = 16 bytes / element size (4 for fp32, 8 for bf16).  For layer l, block b,
+ * KV head h, in-block token t (0 .. block_size-1) and dim d (0 .. head_dim-1):
+ *   tile  = ((l * num_blocks + b) * num_kv_heads + h) * (block_size / 16) + t / 16
+ *   K at element  tile * 16 * head_dim + ((d / X) * 16 + t % 16) * X + d % X
+ *   V at element  tile * 16 * head_dim + d * 16 + t % 16
+ * Every 16-token slice of a block is a contiguous tile of 16*head_dim elements: K as 16-byte
+ * dim chunks (chunk-major, 16 tokens per chunk) and V transposed (dims-major).  One tile is
+ * 4 KiB for bf16 at head_dim 128, so each tile is one coalesced read, and it can be copied
+ * to LDS verbatim in the order the matrix cores consume it.
+ */
+#ifndef KVPOOL_H
+#define KVPOOL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#if defined(__GNUC__)
+#define KVPOOL_API __attribute__((visibility("default")))
+#else
+#define KVPOOL_API
+#endif
+
+typedef struct kvpool kvpool_t; /* opaque; immutable after creation, so thread-safe to share */
+
+typedef enum {
+  KV_OK = 0,
+  KV_EINVAL = -1,        /* null handle/pointer, bad scalar argument, misaligned buffer   */
+  KV_ERANGE = -2,        /* metadata out of range (only reported with KVPOOL_VALIDATE=1)   */
+  KV_EUNSUPPORTED = -3,  /* head_dim, block_size, dtype or GQA ratio the kernels don't have */
+  KV_EDEVICE = -4,       /* a HIP runtime call failed                                       */
+  KV_ENOMEM = -5         /* workspace smaller than kvattn_workspace_size() asks for         */
+} kv_status;
+
+typedef enum { KV_F32 = 0, KV_BF16 = 1 } kv_dtype;
+
+/* Bytes of ONE of the two storage buffers (K or V) for this geometry, written to *bytes.
+ * Supported: block_size in {16, 64}, head_dim in {64, 128}, dtype KV_F32 or KV_BF16. */
+KVPOOL_API int kvpool_storage_bytes(int32_t num_layers, int32_t num_blocks, int32_t block_size,
+                                    int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
+                                    size_t *bytes);
+
+/* Wraps caller-owned device storage as a pool (the block pool sized once for the whole
+ * context, sparkinfer server README, "Serve Qwen3.8 with DSpark"; NInfer serving doc,
+ * "Execution behavior").  k_storage and v_storage: device pointers, 16-byte aligned, each of
+ * kvpool_storage_bytes() bytes, laid out as described above.  The handle records the current
+ * HIP device.  *out receives the handle (host memory, freed by kvpool_destroy). */
+KVPOOL_API int kvpool_create(kvpool_t **out, int32_t num_layers, int32_t num_blocks,
+                             int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+                             int32_t dtype, void *k_storage, void *v_storage);
+
+/* Frees the handle only, never the storage.  NULL is accepted. */
+KVPOOL_API int kvpool_destroy(kvpool_t *pool);
+
+/* Writes the K/V rows of each sequence's new tokens into its blocks: row i of sequence s
+ * (rows packed in sequence order, q_lens[s] rows each) goes to position ctx_lens[s] - q_lens[s]
+ * + i, i.e. block block_tables[s * max_blocks_per_seq + pos / block_size], slot
+ * pos % block_size.  This is how only the uncached suffix enters the pool on a prefix hit
+ * (sparkinfer server README, "Automatic prefix cache").  Bit copy; every other slot keeps its
+ * bits.
+ *   k_new, v_new   device, [total_q][num_kv_heads][head_dim] of the pool dtype, row-major
+ *   block_tables   device int32 [num_seqs][max_blocks_per_seq]
+ *   ctx_lens       device int32 [num_seqs], length after the append (counts the new tokens)
+ *   q_lens         device int32 [num_seqs], new tokens per sequence; sum == total_q
+ *   max_q_len      host upper bound of q_lens (sizes the grid)
+ * Blocks written here must not be shared with another live sequence (copy them first with
+ * kvpool_copy_blocks). */
+KVPOOL_API int kvpool_append(kvpool_t *pool, int32_t layer, const void *k_new,
+                             const void *v_new, const int32_t *block_tables,
+                             int32_t max_blocks_per_seq, const int32_t *ctx_lens,
+                             const int32_t *q_lens, int32_t num_seqs, int32_t total_q,
+                             int32_t max_q_len, void *stream);
+
+/* pool[dst[i]] <- pool[src[i]] for i < n, every layer, K and V: the copy-on-write step for a
+ * shared prefix block that a sequence is about to write (blocks are shared, not copied, until
+ * they diverge: sparkinfer server README, "Automatic prefix cache").  src, dst: device int32
+ * [n].  dst ids must be distinct and disjoint from src ids (then the result does not depend on
+ * order; KV_ERANGE under validation otherwise).  Bit copy. */
+KVPOOL_API int kvpool_copy_blocks(kvpool_t *pool, const int32_t *src, const int32_t *dst,
+                                  int32_t n, void *stream);
+
+/* Workspace bytes kvattn_forward needs for these bounds (written to *bytes; may be 0). */
+KVPOOL_API int kvattn_workspace_size(const kvpool_t *pool, int32_t num_q_heads,
+                                     int32_t num_seqs, int32_t total_q, int32_t max_ctx_len,
+                                     int32_t max_q_len, size_t *bytes);
+
+/* Attention of every sequence's q_lens[s] query rows against its ctx_lens[s] keys (the new
+ * tokens' K/V must already be appended).
+ *   q    device, [total_q][num_q_heads][head_dim], pool dtype, rows packed in sequence order
+ *   out  device, same shape and dtype as q; each element is written exactly once, rounded to
+ *        nearest-even from the fp32 result
+ *   scale            softmax scale applied to q.k (e.g. 1/sqrt(head_dim))
+ *   block_tables     device int32 [num_seqs][max_blocks_per_seq]
+ *   ctx_lens, q_lens device int32 [num_seqs]; 0 <= q_lens[s] <= ctx_lens[s]
+ *                    <= max_blocks_per_seq * block_size; q_lens[s] == 0 produces no rows
+ *   max_ctx_len, max_q_len  host upper bounds of ctx_lens / q_lens (size the grid)
+ *   workspace        device scratch of at least kvattn_workspace_size() bytes, 256-byte
+ *                    aligned; contents on entry don't matter
+ * num_q_heads must be a multiple of the pool's num_kv_heads with at most 16 q-heads per KV
+ * head. */
+KVPOOL_API int kvattn_forward(kvpool_t *pool, int32_t layer, const void *q, void *out,
+                              int32_t num_q_heads, float scale, const int32_t *block_tables,
+                              int32_t max_blocks_per_seq, const int32_t *ctx_lens,
+                              const int32_t *q_lens, int32_t num_seqs, int32_t total_q,
+                              int32_t max_ctx_len, int32_t max_q_len, void *workspace,
+                              size_t workspace_bytes, void *stream);
+
+/* Message for the last non-OK return on this thread ("" if none).  Valid until the next call
+ * on the same thread. */
+KVPOOL_API const char *kvpool_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVPOOL_H */

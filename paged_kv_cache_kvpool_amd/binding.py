@@ -1,0 +1,210 @@
+"""ctypes binding of libkvpool.so: one Python function per C entry point, same names.
+
+Argument marshalling only: torch tensors supply device pointers (``data_ptr()``) and the HIP
+stream defaults to torch's current stream.  Every step of the computation runs in the
+library's HIP kernels; there is no other code path.  If the library is not built, loading
+fails with an error (build it with ``python -m paged_kv_cache_kvpool_amd.build``).
+
+torch is imported before the library is loaded so that both use the same HIP runtime
+(libamdhip64.so.7 is resolved to the copy torch already loaded).
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvpool.so")
+
+KV_OK, KV_EINVAL, KV_ERANGE, KV_EUNSUPPORTED, KV_EDEVICE, KV_ENOMEM = 0, -1, -2, -3, -4, -5
+KV_F32, KV_BF16 = 0, 1
+STATUS_NAMES = {0: "KV_OK", -1: "KV_EINVAL", -2: "KV_ERANGE", -3: "KV_EUNSUPPORTED",
+                -4: "KV_EDEVICE", -5: "KV_ENOMEM"}
+
+_i32, _f32, _sz, _vp = ctypes.c_int32, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
+
+# name -> (restype, argtypes); mirrors include/kvpool.h
+SIGNATURES = {
+    "kvpool_storage_bytes": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_sz)]),
+    "kvpool_create": (_i32, [ctypes.POINTER(_vp), _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp]),
+    "kvpool_destroy": (_i32, [_vp]),
+    "kvpool_append": (_i32, [_vp, _i32, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _vp]),
+    "kvpool_copy_blocks": (_i32, [_vp, _vp, _vp, _i32, _vp]),
+    "kvattn_workspace_size": (_i32, [_vp, _i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_sz)]),
+    "kvattn_forward": (_i32, [_vp, _i32, _vp, _vp, _i32, _f32, _vp, _i32, _vp, _vp, _i32, _i32,
+                              _i32, _i32, _vp, _sz, _vp]),
+    "kvpool_last_error": (ctypes.c_char_p, []),
+}
+
+
+class KVPoolError(RuntimeError):
+    def __init__(self, code: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(code, code)}: {message}")
+        self.code = code
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m paged_kv_cache_kvpool_amd.build`")
+        cdll = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in SIGNATURES.items():
+            fn = getattr(cdll, name)
+            fn.restype, fn.argtypes = res, args
+        _lib = cdll
+    return _lib
+
+
+def _check(rc: int) -> None:
+    if rc != KV_OK:
+        raise KVPoolError(rc, kvpool_last_error())
+
+
+def _ptr(x) -> Optional[int]:
+    if x is None:
+        return None
+    if isinstance(x, torch.Tensor):
+        return x.data_ptr()
+    return int(x)
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream
+    return int(stream)
+
+
+def kvpool_last_error() -> str:
+    return lib().kvpool_last_error().decode()
+
+
+def kvpool_storage_bytes(num_layers, num_blocks, block_size, num_kv_heads, head_dim, dtype) -> int:
+    out = _sz(0)
+    _check(lib().kvpool_storage_bytes(num_layers, num_blocks, block_size, num_kv_heads, head_dim,
+                                      dtype, ctypes.byref(out)))
+    return out.value
+
+
+def kvpool_create(num_layers, num_blocks, block_size, num_kv_heads, head_dim, dtype, k_storage,
+                  v_storage) -> int:
+    h = _vp(0)
+    _check(lib().kvpool_create(ctypes.byref(h), num_layers, num_blocks, block_size, num_kv_heads,
+                               head_dim, dtype, _ptr(k_storage), _ptr(v_storage)))
+    return h.value
+
+
+def kvpool_destroy(handle) -> None:
+    _check(lib().kvpool_destroy(handle))
+
+
+def kvpool_append(handle, layer, k_new, v_new, block_tables, max_blocks_per_seq, ctx_lens,
+                  q_lens, num_seqs, total_q, max_q_len, stream=None) -> None:
+    _check(lib().kvpool_append(handle, layer, _ptr(k_new), _ptr(v_new), _ptr(block_tables),
+                               max_blocks_per_seq, _ptr(ctx_lens), _ptr(q_lens), num_seqs,
+                               total_q, max_q_len, _stream(stream)))
+
+
+def kvpool_copy_blocks(handle, src, dst, n, stream=None) -> None:
+    _check(lib().kvpool_copy_blocks(handle, _ptr(src), _ptr(dst), n, _stream(stream)))
+
+
+def kvattn_workspace_size(handle, num_q_heads, num_seqs, total_q, max_ctx_len, max_q_len) -> int:
+    out = _sz(0)
+    _check(lib().kvattn_workspace_size(handle, num_q_heads, num_seqs, total_q, max_ctx_len,
+                                       max_q_len, ctypes.byref(out)))
+    return out.value
+
+
+def kvattn_forward(handle, layer, q, out, num_q_heads, scale, block_tables, max_blocks_per_seq,
+                   ctx_lens, q_lens, num_seqs, total_q, max_ctx_len, max_q_len, workspace,
+                   workspace_bytes, stream=None) -> None:
+    _check(lib().kvattn_forward(handle, layer, _ptr(q), _ptr(out), num_q_heads, float(scale),
+                                _ptr(block_tables), max_blocks_per_seq, _ptr(ctx_lens),
+                                _ptr(q_lens), num_seqs, total_q, max_ctx_len, max_q_len,
+                                _ptr(workspace), workspace_bytes, _stream(stream)))
+
+
+# ---------------------------------------------------------------------------------------------
+# Convenience wrapper: owns torch storage for one pool and sizes the workspace.
+# ---------------------------------------------------------------------------------------------
+
+_TORCH_DTYPE = {KV_F32: torch.float32, KV_BF16: torch.bfloat16}
+
+
+class PagedKVPool:
+    """A pool whose K/V storage is a pair of torch tensors on one device.
+
+    ``k_storage`` / ``v_storage`` are flat tensors of the pool dtype (see include/kvpool.h for
+    the element order).  Metadata arguments are int32 device tensors.
+    """
+
+    def __init__(self, num_layers, num_blocks, block_size, num_kv_heads, head_dim, dtype,
+                 device="cuda", k_storage=None, v_storage=None):
+        self.num_layers, self.num_blocks, self.block_size = num_layers, num_blocks, block_size
+        self.num_kv_heads, self.head_dim, self.dtype = num_kv_heads, head_dim, dtype
+        nbytes = kvpool_storage_bytes(num_layers, num_blocks, block_size, num_kv_heads, head_dim,
+                                      dtype)
+        tdt = _TORCH_DTYPE[dtype]
+        n = nbytes // torch.empty((), dtype=tdt).element_size()
+        self.k_storage = torch.empty(n, dtype=tdt, device=device) if k_storage is None else k_storage
+        self.v_storage = torch.empty(n, dtype=tdt, device=device) if v_storage is None else v_storage
+        assert self.k_storage.numel() == n and self.v_storage.numel() == n
+        with torch.cuda.device(self.k_storage.device):
+            self.handle = kvpool_create(num_layers, num_blocks, block_size, num_kv_heads,
+                                        head_dim, dtype, self.k_storage, self.v_storage)
+        self._ws = None
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h and _lib is not None:
+            _lib.kvpool_destroy(h)
+            self.handle = None
+
+    @property
+    def torch_dtype(self):
+        return _TORCH_DTYPE[self.dtype]
+
+    def block_storage(self, which="k"):
+        """[num_layers, num_blocks, Hkv*block_size*head_dim] view of K or V storage."""
+        t = self.k_storage if which == "k" else self.v_storage
+        return t.view(self.num_layers, self.num_blocks, -1)
+
+    def append(self, layer, k_new, v_new, block_tables, ctx_lens, q_lens, max_q_len=None,
+               stream=None):
+        max_q_len = int(q_lens.max().item()) if max_q_len is None else max_q_len
+        kvpool_append(self.handle, layer, k_new, v_new, block_tables, block_tables.shape[1],
+                      ctx_lens, q_lens, ctx_lens.shape[0], k_new.shape[0], max_q_len, stream)
+
+    def copy_blocks(self, src, dst, stream=None):
+        kvpool_copy_blocks(self.handle, src, dst, src.shape[0], stream)
+
+    def workspace(self, num_q_heads, num_seqs, total_q, max_ctx_len, max_q_len):
+        need = kvattn_workspace_size(self.handle, num_q_heads, num_seqs, total_q, max_ctx_len,
+                                     max_q_len)
+        if need and (self._ws is None or self._ws.numel() < need):
+            self._ws = torch.empty(need, dtype=torch.uint8, device=self.k_storage.device)
+        return self._ws, need
+
+    def forward(self, layer, q, block_tables, ctx_lens, q_lens, scale=None, max_ctx_len=None,
+                max_q_len=None, out=None, stream=None):
+        total_q, hq, d = q.shape
+        scale = 1.0 / math.sqrt(d) if scale is None else scale
+        max_ctx_len = int(ctx_lens.max().item()) if max_ctx_len is None else max_ctx_len
+        max_q_len = int(q_lens.max().item()) if max_q_len is None else max_q_len
+        out = torch.empty_like(q) if out is None else out
+        ws, need = self.workspace(hq, ctx_lens.shape[0], total_q, max_ctx_len, max_q_len)
+        kvattn_forward(self.handle, layer, q, out, hq, scale, block_tables, block_tables.shape[1],
+                       ctx_lens, q_lens, ctx_lens.shape[0], total_q, max_ctx_len, max_q_len,
+                       ws, need, stream)
+        return out

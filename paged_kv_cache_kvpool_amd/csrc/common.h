@@ -1,0 +1,146 @@
+// Device helpers shared by the gfx950 kernels: bf16 bit handling, wave64 cross-lane
+// reductions, pool tile addressing and the kernel argument block.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kvp {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int TILE = 16;        // tokens per layout tile
+constexpr int WAVE = 64;
+constexpr float LOG2E = 1.4426950408889634f;
+
+// ---- bf16 <-> fp32 --------------------------------------------------------------------
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> nearest-even bf16, result in the low 16 bits (finite and inf inputs; NaN stays NaN).
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;  // quiet NaN
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+// fp32 value of the nearest-even bf16 of f.
+__device__ __forceinline__ float round_to_bf16(float f) {
+  return __uint_as_float(f32_to_bf16_bits(f) << 16);
+}
+// Two floats that are already exact bf16 values -> packed pair (lo in bits 0..15).
+__device__ __forceinline__ uint32_t pack_exact_bf16(float lo, float hi) {
+  return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
+}
+
+// ---- wave64 cross-lane ----------------------------------------------------------------
+// DPP controls (within a row of 16 lanes): quad_perm xor1 / xor2, row_ror 4 / 8.
+constexpr int DPP_XOR1 = 0xB1, DPP_XOR2 = 0x4E, DPP_ROR4 = 0x124, DPP_ROR8 = 0x128;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Lane-pair views used for butterflies across rows: op(x[l], x[l ^ 16]) and op(x[l], x[l ^ 32]).
+__device__ __forceinline__ void swap16(float x, float& a, float& b) {
+  auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void swap32(float x, float& a, float& b) {
+  auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+
+// Reductions over the 4 rows of the wave (lanes l, l^16, l^32, l^48), result in every lane.
+__device__ __forceinline__ float xrow_sum(float x) {
+  float a, b;
+  swap32(x, a, b);
+  x = a + b;
+  swap16(x, a, b);
+  return a + b;
+}
+__device__ __forceinline__ float xrow_max(float x) {
+  float a, b;
+  swap32(x, a, b);
+  x = fmaxf(a, b);
+  swap16(x, a, b);
+  return fmaxf(a, b);
+}
+// Reductions within each row of 16 lanes, result in every lane of the row.
+__device__ __forceinline__ float row_sum(float x) {
+  x += dpp<DPP_ROR8>(x);
+  x += dpp<DPP_ROR4>(x);
+  x += dpp<DPP_XOR2>(x);
+  x += dpp<DPP_XOR1>(x);
+  return x;
+}
+__device__ __forceinline__ float row_max(float x) {
+  x = fmaxf(x, dpp<DPP_ROR8>(x));
+  x = fmaxf(x, dpp<DPP_ROR4>(x));
+  x = fmaxf(x, dpp<DPP_XOR2>(x));
+  x = fmaxf(x, dpp<DPP_XOR1>(x));
+  return x;
+}
+
+// Sum of v[0 .. n) over the wave, every lane gets it (n small: a few thousand at most).
+__device__ __forceinline__ int wave_prefix_total(const int32_t* v, int n) {
+  int lane = threadIdx.x & (WAVE - 1);
+  int acc = 0;
+  for (int i = lane; i < n; i += WAVE) acc += max(0, v[i]);
+  float f = (float)acc;  // exact: totals stay far below 2^24
+  f = row_sum(f);
+  f = xrow_sum(f);
+  return (int)f;
+}
+
+// exp2 that maps -inf to 0 without a branch (hardware v_exp_f32 already does).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---- kernel arguments -------------------------------------------------------------------
+struct AttnArgs {
+  const void* q;            // [total_q][Hq][D]
+  void* out;                // [total_q][Hq][D]
+  const void* k_layer;      // pool K storage of the selected layer
+  const void* v_layer;
+  const int32_t* block_tables;
+  const int32_t* ctx_lens;
+  const int32_t* q_lens;
+  float* part_o;            // [total_q][Hq][max_splits][D]   (split mode)
+  float* part_ml;           // [total_q][Hq][max_splits][2]   (split mode: max, sum)
+  int32_t num_seqs, total_q, num_q_heads, num_kv_heads, group, block_size, num_blocks;
+  int32_t max_blocks_per_seq;
+  int32_t split_tokens;     // keys per split (split mode) ; ignored otherwise
+  int32_t max_splits;       // splits per row slot in the workspace (split mode)
+  int32_t row_tiles;        // row tiles per (sequence, kv head)
+  int32_t split_mode;       // 1: write partials for the reduce kernel; 0: write `out`
+  float scale_log2;         // softmax scale * log2(e)
+};
+
+// Clamped per-sequence lengths (bad metadata must never index out of bounds).
+__device__ __forceinline__ void seq_lens(const AttnArgs& a, int s, int& L, int& T) {
+  int cap = a.max_blocks_per_seq * a.block_size;
+  L = min(max(a.ctx_lens[s], 0), cap);
+  T = min(max(a.q_lens[s], 0), L);
+}
+
+// Element offset of the 16-token tile holding logical position `pos` of sequence s for KV head
+// h, within one layer.  Block ids outside [0, num_blocks) are clamped to 0.
+__device__ __forceinline__ size_t tile_offset(const int32_t* table_row, int pos, int h,
+                                              int block_size, int num_blocks, int num_kv_heads,
+                                              int head_dim) {
+  int bi = pos / block_size;
+  int blk = table_row[bi];
+  blk = ((unsigned)blk < (unsigned)num_blocks) ? blk : 0;
+  int sub = (pos % block_size) / TILE;
+  size_t tile = ((size_t)blk * num_kv_heads + h) * (size_t)(block_size / TILE) + sub;
+  return tile * (size_t)(TILE * head_dim);
+}
+
+}  // namespace kvp

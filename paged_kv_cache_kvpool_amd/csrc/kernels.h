@@ -1,0 +1,50 @@
+// Launchers of the gfx950 kernels, called by the C ABI layer (kvpool.cpp).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace kvp {
+
+struct AppendArgs {
+  void* k_layer;
+  void* v_layer;
+  const void* k_new;
+  const void* v_new;
+  const int32_t* block_tables;
+  const int32_t* ctx_lens;
+  const int32_t* q_lens;
+  int32_t num_seqs, total_q, num_kv_heads, head_dim, block_size, num_blocks;
+  int32_t max_blocks_per_seq;
+};
+
+struct CopyArgs {
+  void* k;
+  void* v;
+  const int32_t* src;
+  const int32_t* dst;
+  int32_t num_blocks;
+  size_t block_bytes;  // one block of one layer: Hkv * block_size * head_dim * elt
+};
+
+hipError_t launch_append(const AppendArgs& a, int elt_bytes, int max_q_len, hipStream_t st);
+hipError_t launch_copy_blocks(const CopyArgs& a, int n, int num_layers, hipStream_t st);
+
+// Split-K attention on the matrix cores (bf16): one wave per (row tile of <= 32 rows, split,
+// KV head, sequence).  Used for decode and verification, and for any call without splits.
+hipError_t launch_attn_split_mfma(const AttnArgs& a, int head_dim, int rows_per_tile,
+                                  int grid_x, hipStream_t st);
+// Vector-ALU attention (fp32 and bf16), one wave per (row tile of <= 8 rows, split, KV head,
+// sequence).
+hipError_t launch_attn_vec(const AttnArgs& a, int elt_bytes, int head_dim, int rows_per_tile,
+                           int grid_x, hipStream_t st);
+// Prefill attention on the matrix cores (bf16): 4 waves x 32 rows share LDS-staged K/V tiles.
+hipError_t launch_attn_prefill_mfma(const AttnArgs& a, int head_dim, int grid_x,
+                                    hipStream_t st);
+// Cross-split merge of the partials written in split mode.
+hipError_t launch_attn_reduce(const AttnArgs& a, int elt_bytes, int head_dim, int max_q_len,
+                              hipStream_t st);
+
+}  // namespace kvp

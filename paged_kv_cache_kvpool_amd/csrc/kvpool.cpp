@@ -1,0 +1,403 @@
+// C ABI of the paged-KV attention library: handle, argument checks, optional metadata
+// validation, split planning and kernel dispatch.  Declared in include/kvpool.h.
+#include "../../include/kvpool.h"
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "kernels.h"
+
+struct kvpool {
+  int32_t num_layers, num_blocks, block_size, num_kv_heads, head_dim, dtype;
+  void* k;
+  void* v;
+  size_t layer_elems;  // elements of one layer of K (or V)
+  int device;
+};
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+int ok() {
+  g_err.clear();
+  return KV_OK;
+}
+
+int elt_bytes(int32_t dtype) { return dtype == KV_F32 ? 4 : 2; }
+
+bool env_flag(const char* name) {
+  const char* v = getenv(name);
+  return v && *v && strcmp(v, "0") != 0;
+}
+
+// Keys per split in split mode.  A fixed count (never derived from the batch) keeps each
+// sequence's reduction order a function of its own length only.
+int split_tokens() {
+  const char* v = getenv("KVATTN_SPLIT_TOKENS");
+  int s = v ? atoi(v) : 256;
+  s = std::max(32, std::min(s, 1 << 20));
+  return (s + 31) / 32 * 32;
+}
+
+// Split mode serves decode and verification (few query rows per KV head): the context is cut
+// into splits so that even one sequence fills the GPU.  Longer query blocks (prefill) carry
+// enough rows to fill it without splitting.
+constexpr int kSplitRowsMax = 128;
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int check_geometry(int32_t num_layers, int32_t num_blocks, int32_t block_size,
+                   int32_t num_kv_heads, int32_t head_dim, int32_t dtype) {
+  if (num_layers <= 0 || num_blocks <= 0 || num_kv_heads <= 0)
+    return fail(KV_EINVAL, "num_layers, num_blocks and num_kv_heads must be positive");
+  if (block_size != 16 && block_size != 64)
+    return fail(KV_EUNSUPPORTED, "block_size %d not supported (16 or 64)", block_size);
+  if (head_dim != 64 && head_dim != 128)
+    return fail(KV_EUNSUPPORTED, "head_dim %d not supported (64 or 128)", head_dim);
+  if (dtype != KV_F32 && dtype != KV_BF16)
+    return fail(KV_EUNSUPPORTED, "dtype %d not supported (KV_F32 or KV_BF16)", dtype);
+  return KV_OK;
+}
+
+hipError_t current_device_matches(const kvpool* p) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  return dev == p->device ? hipSuccess : hipErrorInvalidDevice;
+}
+
+struct HostMeta {
+  std::vector<int32_t> tables, ctx, ql;
+};
+
+int fetch_meta(const int32_t* tables, int32_t max_blocks, const int32_t* ctx, const int32_t* ql,
+               int32_t num_seqs, hipStream_t st, HostMeta& m) {
+  m.tables.resize((size_t)num_seqs * max_blocks);
+  m.ctx.resize(num_seqs);
+  m.ql.resize(num_seqs);
+  hipError_t e = hipMemcpyAsync(m.tables.data(), tables, m.tables.size() * 4,
+                                hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(m.ctx.data(), ctx, (size_t)num_seqs * 4, hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess)
+    e = hipMemcpyAsync(m.ql.data(), ql, (size_t)num_seqs * 4, hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return fail(KV_EDEVICE, "metadata copy failed: %s", hipGetErrorString(e));
+  return KV_OK;
+}
+
+int validate_meta(const kvpool* p, const HostMeta& m, int32_t max_blocks, int32_t num_seqs,
+                  int32_t total_q, int32_t max_ctx_len, int32_t max_q_len) {
+  long long sum_q = 0;
+  for (int s = 0; s < num_seqs; ++s) {
+    const int L = m.ctx[s], T = m.ql[s];
+    if (T < 0 || L < T) return fail(KV_ERANGE, "seq %d: need 0 <= q_len (%d) <= ctx_len (%d)", s, T, L);
+    if ((long long)L > (long long)max_blocks * p->block_size)
+      return fail(KV_ERANGE, "seq %d: ctx_len %d exceeds max_blocks_per_seq*block_size", s, L);
+    if (L > max_ctx_len) return fail(KV_ERANGE, "seq %d: ctx_len %d > max_ctx_len %d", s, L, max_ctx_len);
+    if (T > max_q_len) return fail(KV_ERANGE, "seq %d: q_len %d > max_q_len %d", s, T, max_q_len);
+    const int nb = (L + p->block_size - 1) / p->block_size;
+    for (int b = 0; b < nb; ++b) {
+      const int id = m.tables[(size_t)s * max_blocks + b];
+      if (id < 0 || id >= p->num_blocks)
+        return fail(KV_ERANGE, "seq %d: block table entry %d = %d outside [0, %d)", s, b, id, p->num_blocks);
+    }
+    sum_q += T;
+  }
+  if (sum_q != total_q) return fail(KV_ERANGE, "sum of q_lens (%lld) != total_q (%d)", sum_q, total_q);
+  return KV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kvpool_storage_bytes(int32_t num_layers, int32_t num_blocks, int32_t block_size,
+                         int32_t num_kv_heads, int32_t head_dim, int32_t dtype, size_t* bytes) {
+  if (!bytes) return fail(KV_EINVAL, "bytes is NULL");
+  int rc = check_geometry(num_layers, num_blocks, block_size, num_kv_heads, head_dim, dtype);
+  if (rc) return rc;
+  *bytes = (size_t)num_layers * num_blocks * num_kv_heads * block_size * head_dim * elt_bytes(dtype);
+  return ok();
+}
+
+int kvpool_create(kvpool_t** out, int32_t num_layers, int32_t num_blocks, int32_t block_size,
+                  int32_t num_kv_heads, int32_t head_dim, int32_t dtype, void* k_storage,
+                  void* v_storage) {
+  if (!out) return fail(KV_EINVAL, "out is NULL");
+  *out = nullptr;
+  int rc = check_geometry(num_layers, num_blocks, block_size, num_kv_heads, head_dim, dtype);
+  if (rc) return rc;
+  if (!k_storage || !v_storage) return fail(KV_EINVAL, "storage pointers must not be NULL");
+  if (!aligned16(k_storage) || !aligned16(v_storage))
+    return fail(KV_EINVAL, "storage pointers must be 16-byte aligned");
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(KV_EDEVICE, "hipGetDevice: %s", hipGetErrorString(e));
+  kvpool* p = new (std::nothrow) kvpool;
+  if (!p) return fail(KV_EINVAL, "out of host memory");
+  p->num_layers = num_layers;
+  p->num_blocks = num_blocks;
+  p->block_size = block_size;
+  p->num_kv_heads = num_kv_heads;
+  p->head_dim = head_dim;
+  p->dtype = dtype;
+  p->k = k_storage;
+  p->v = v_storage;
+  p->layer_elems = (size_t)num_blocks * num_kv_heads * block_size * head_dim;
+  p->device = dev;
+  *out = p;
+  return ok();
+}
+
+int kvpool_destroy(kvpool_t* pool) {
+  delete pool;
+  return ok();
+}
+
+int kvpool_append(kvpool_t* pool, int32_t layer, const void* k_new, const void* v_new,
+                  const int32_t* block_tables, int32_t max_blocks_per_seq,
+                  const int32_t* ctx_lens, const int32_t* q_lens, int32_t num_seqs,
+                  int32_t total_q, int32_t max_q_len, void* stream) {
+  if (!pool) return fail(KV_EINVAL, "pool is NULL");
+  if (layer < 0 || layer >= pool->num_layers) return fail(KV_EINVAL, "layer %d out of range", layer);
+  if (num_seqs < 0 || total_q < 0 || max_q_len < 0 || max_blocks_per_seq < 0)
+    return fail(KV_EINVAL, "negative size argument");
+  if (num_seqs > 65535) return fail(KV_EUNSUPPORTED, "num_seqs %d > 65535", num_seqs);
+  if (num_seqs == 0 || total_q == 0 || max_q_len == 0) return ok();
+  if (!k_new || !v_new || !block_tables || !ctx_lens || !q_lens)
+    return fail(KV_EINVAL, "NULL device pointer");
+  if (!aligned16(k_new) || !aligned16(v_new)) return fail(KV_EINVAL, "k_new/v_new must be 16-byte aligned");
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (current_device_matches(pool) != hipSuccess)
+    return fail(KV_EINVAL, "current HIP device is not the pool's device %d", pool->device);
+  if (env_flag("KVPOOL_VALIDATE")) {
+    HostMeta m;
+    int rc = fetch_meta(block_tables, max_blocks_per_seq, ctx_lens, q_lens, num_seqs, st, m);
+    if (rc) return rc;
+    rc = validate_meta(pool, m, max_blocks_per_seq, num_seqs, total_q, INT32_MAX, max_q_len);
+    if (rc) return rc;
+    // Blocks being written must belong to exactly one sequence of this call.
+    std::vector<int> owner(pool->num_blocks, -1);
+    for (int s = 0; s < num_seqs; ++s) {
+      const int nb = (m.ctx[s] + pool->block_size - 1) / pool->block_size;
+      for (int b = 0; b < nb; ++b) {
+        const int id = m.tables[(size_t)s * max_blocks_per_seq + b];
+        if (owner[id] >= 0 && owner[id] != s) {
+          const int first_new = (m.ctx[s] - m.ql[s]) / pool->block_size;
+          if (b >= first_new) return fail(KV_ERANGE, "seq %d writes block %d shared with seq %d", s, id, owner[id]);
+        }
+        owner[id] = s;
+      }
+    }
+  }
+  kvp::AppendArgs a;
+  const size_t lo = (size_t)layer * pool->layer_elems * elt_bytes(pool->dtype);
+  a.k_layer = static_cast<char*>(pool->k) + lo;
+  a.v_layer = static_cast<char*>(pool->v) + lo;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.block_tables = block_tables;
+  a.ctx_lens = ctx_lens;
+  a.q_lens = q_lens;
+  a.num_seqs = num_seqs;
+  a.total_q = total_q;
+  a.num_kv_heads = pool->num_kv_heads;
+  a.head_dim = pool->head_dim;
+  a.block_size = pool->block_size;
+  a.num_blocks = pool->num_blocks;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  hipError_t e = kvp::launch_append(a, elt_bytes(pool->dtype), max_q_len, st);
+  if (e != hipSuccess) return fail(KV_EDEVICE, "append launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int kvpool_copy_blocks(kvpool_t* pool, const int32_t* src, const int32_t* dst, int32_t n,
+                       void* stream) {
+  if (!pool) return fail(KV_EINVAL, "pool is NULL");
+  if (n < 0) return fail(KV_EINVAL, "n must be >= 0");
+  if (n == 0) return ok();
+  if (!src || !dst) return fail(KV_EINVAL, "NULL device pointer");
+  if (n > INT32_MAX / 2) return fail(KV_EINVAL, "n too large");
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (current_device_matches(pool) != hipSuccess)
+    return fail(KV_EINVAL, "current HIP device is not the pool's device %d", pool->device);
+  if (env_flag("KVPOOL_VALIDATE")) {
+    std::vector<int32_t> hs(n), hd(n);
+    hipError_t e = hipMemcpyAsync(hs.data(), src, (size_t)n * 4, hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipMemcpyAsync(hd.data(), dst, (size_t)n * 4, hipMemcpyDeviceToHost, st);
+    if (e == hipSuccess) e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return fail(KV_EDEVICE, "metadata copy failed: %s", hipGetErrorString(e));
+    std::vector<char> is_src(pool->num_blocks, 0), is_dst(pool->num_blocks, 0);
+    for (int i = 0; i < n; ++i) {
+      if (hs[i] < 0 || hs[i] >= pool->num_blocks || hd[i] < 0 || hd[i] >= pool->num_blocks)
+        return fail(KV_ERANGE, "copy pair %d (%d -> %d) outside [0, %d)", i, hs[i], hd[i], pool->num_blocks);
+      is_src[hs[i]] = 1;
+    }
+    for (int i = 0; i < n; ++i) {
+      if (is_dst[hd[i]]) return fail(KV_ERANGE, "dst block %d appears twice", hd[i]);
+      if (is_src[hd[i]]) return fail(KV_ERANGE, "dst block %d is also a src block", hd[i]);
+      is_dst[hd[i]] = 1;
+    }
+  }
+  kvp::CopyArgs a;
+  a.k = pool->k;
+  a.v = pool->v;
+  a.src = src;
+  a.dst = dst;
+  a.num_blocks = pool->num_blocks;
+  a.block_bytes = (size_t)pool->num_kv_heads * pool->block_size * pool->head_dim * elt_bytes(pool->dtype);
+  hipError_t e = kvp::launch_copy_blocks(a, n, pool->num_layers, st);
+  if (e != hipSuccess) return fail(KV_EDEVICE, "copy launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+namespace {
+
+struct Plan {
+  bool split_mode;
+  int split;
+  int max_splits;
+  size_t bytes;
+};
+
+Plan make_plan(const kvpool* p, int32_t num_q_heads, int32_t total_q, int32_t max_ctx_len,
+               int32_t max_q_len) {
+  Plan pl{};
+  const int G = num_q_heads / p->num_kv_heads;
+  pl.split_mode = (long long)max_q_len * G <= kSplitRowsMax;
+  pl.split = split_tokens();
+  pl.max_splits = pl.split_mode ? std::max(1, (max_ctx_len + pl.split - 1) / pl.split) : 1;
+  if (pl.split_mode) {
+    const size_t slots = (size_t)total_q * num_q_heads * pl.max_splits;
+    const size_t o_bytes = (slots * p->head_dim * 4 + 255) / 256 * 256;
+    pl.bytes = o_bytes + slots * 2 * 4;
+  }
+  return pl;
+}
+
+}  // namespace
+
+int kvattn_workspace_size(const kvpool_t* pool, int32_t num_q_heads, int32_t num_seqs,
+                          int32_t total_q, int32_t max_ctx_len, int32_t max_q_len,
+                          size_t* bytes) {
+  if (!pool || !bytes) return fail(KV_EINVAL, "pool or bytes is NULL");
+  if (num_q_heads <= 0 || num_q_heads % pool->num_kv_heads)
+    return fail(KV_EINVAL, "num_q_heads must be a positive multiple of num_kv_heads");
+  if (num_seqs < 0 || total_q < 0 || max_ctx_len < 0 || max_q_len < 0)
+    return fail(KV_EINVAL, "negative size argument");
+  *bytes = make_plan(pool, num_q_heads, total_q, max_ctx_len, max_q_len).bytes;
+  return ok();
+}
+
+int kvattn_forward(kvpool_t* pool, int32_t layer, const void* q, void* out, int32_t num_q_heads,
+                   float scale, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                   const int32_t* ctx_lens, const int32_t* q_lens, int32_t num_seqs,
+                   int32_t total_q, int32_t max_ctx_len, int32_t max_q_len, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  if (!pool) return fail(KV_EINVAL, "pool is NULL");
+  if (layer < 0 || layer >= pool->num_layers) return fail(KV_EINVAL, "layer %d out of range", layer);
+  if (num_q_heads <= 0 || num_q_heads % pool->num_kv_heads)
+    return fail(KV_EINVAL, "num_q_heads %d must be a positive multiple of num_kv_heads %d",
+                num_q_heads, pool->num_kv_heads);
+  const int G = num_q_heads / pool->num_kv_heads;
+  if (G > 16) return fail(KV_EUNSUPPORTED, "%d q-heads per KV head (at most 16)", G);
+  if (num_seqs < 0 || total_q < 0 || max_ctx_len < 0 || max_q_len < 0 || max_blocks_per_seq < 0)
+    return fail(KV_EINVAL, "negative size argument");
+  if (num_seqs > 65535) return fail(KV_EUNSUPPORTED, "num_seqs %d > 65535", num_seqs);
+  if (!(scale == scale) || scale == INFINITY || scale == -INFINITY) return fail(KV_EINVAL, "scale must be finite");
+  if (num_seqs == 0 || total_q == 0 || max_q_len == 0 || max_ctx_len == 0) return ok();
+  if (max_q_len > max_ctx_len) return fail(KV_EINVAL, "max_q_len > max_ctx_len");
+  if (!q || !out || !block_tables || !ctx_lens || !q_lens)
+    return fail(KV_EINVAL, "NULL device pointer");
+  if (!aligned16(q) || !aligned16(out)) return fail(KV_EINVAL, "q and out must be 16-byte aligned");
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  if (current_device_matches(pool) != hipSuccess)
+    return fail(KV_EINVAL, "current HIP device is not the pool's device %d", pool->device);
+  const Plan pl = make_plan(pool, num_q_heads, total_q, max_ctx_len, max_q_len);
+  if (pl.bytes) {
+    if (!workspace) return fail(KV_ENOMEM, "workspace of %zu bytes required", pl.bytes);
+    if (workspace_bytes < pl.bytes)
+      return fail(KV_ENOMEM, "workspace has %zu bytes, %zu required", workspace_bytes, pl.bytes);
+    if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+      return fail(KV_EINVAL, "workspace must be 256-byte aligned");
+  }
+  if (env_flag("KVPOOL_VALIDATE")) {
+    HostMeta m;
+    int rc = fetch_meta(block_tables, max_blocks_per_seq, ctx_lens, q_lens, num_seqs, st, m);
+    if (rc) return rc;
+    rc = validate_meta(pool, m, max_blocks_per_seq, num_seqs, total_q, max_ctx_len, max_q_len);
+    if (rc) return rc;
+  }
+
+  kvp::AttnArgs a;
+  const size_t lo = (size_t)layer * pool->layer_elems * elt_bytes(pool->dtype);
+  a.q = q;
+  a.out = out;
+  a.k_layer = static_cast<const char*>(pool->k) + lo;
+  a.v_layer = static_cast<const char*>(pool->v) + lo;
+  a.block_tables = block_tables;
+  a.ctx_lens = ctx_lens;
+  a.q_lens = q_lens;
+  const size_t slots = (size_t)total_q * num_q_heads * pl.max_splits;
+  a.part_o = static_cast<float*>(workspace);
+  a.part_ml = pl.bytes ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                                  (slots * pool->head_dim * 4 + 255) / 256 * 256)
+                       : nullptr;
+  a.num_seqs = num_seqs;
+  a.total_q = total_q;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = pool->num_kv_heads;
+  a.group = G;
+  a.block_size = pool->block_size;
+  a.num_blocks = pool->num_blocks;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  a.split_tokens = pl.split;
+  a.max_splits = pl.max_splits;
+  a.split_mode = pl.split_mode ? 1 : 0;
+  a.scale_log2 = scale * kvp::LOG2E;
+
+  const int rows = max_q_len * G;
+  const int eb = elt_bytes(pool->dtype);
+  hipError_t e;
+  if (pool->dtype == KV_F32 || (pl.split_mode && max_q_len == 1 && env_flag("KVATTN_DECODE_VEC"))) {
+    // Rows per wave: the template instance just large enough (1, 2, 4, 5 or 8).
+    const int r8 = std::min(rows, 8);
+    const int rpt = r8 <= 1 ? 1 : r8 <= 2 ? 2 : r8 <= 4 ? 4 : r8 <= 5 ? 5 : 8;
+    a.row_tiles = (rows + rpt - 1) / rpt;
+    e = kvp::launch_attn_vec(a, eb, pool->head_dim, rpt, a.row_tiles * pl.max_splits, st);
+  } else {
+    const int rpt = rows <= 16 ? 16 : 32;
+    a.row_tiles = (rows + rpt - 1) / rpt;
+    e = kvp::launch_attn_split_mfma(a, pool->head_dim, rpt, a.row_tiles * pl.max_splits, st);
+  }
+  if (e != hipSuccess) return fail(KV_EDEVICE, "attention launch: %s", hipGetErrorString(e));
+  if (pl.split_mode) {
+    e = kvp::launch_attn_reduce(a, eb, pool->head_dim, max_q_len, st);
+    if (e != hipSuccess) return fail(KV_EDEVICE, "reduce launch: %s", hipGetErrorString(e));
+  }
+  return ok();
+}
+
+const char* kvpool_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"

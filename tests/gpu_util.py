@@ -1,0 +1,115 @@
+"""Helpers for the GPU parity tests: put a seeded workload on the device, run the library
+through its C ABI, and run the oracle on the same input bits."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from oracle import attention as ora
+from paged_kv_cache_kvpool_amd import binding as kb
+from paged_kv_cache_kvpool_amd import workloads as wl
+
+TOL = {wl.BF16: dict(max_abs=2e-2, rel_l2=5e-3), wl.F32: dict(max_abs=1e-5, rel_l2=1e-5)}
+
+
+def to_torch(arr: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
+    if dtype == wl.BF16:
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).to(device)
+
+
+def to_numpy(t: torch.Tensor, dtype: str) -> np.ndarray:
+    t = t.detach().cpu()
+    if dtype == wl.BF16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def out_f64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+class DeviceCase:
+    """A workload materialised on the GPU (pool, q, metadata) plus its host copy."""
+
+    def __init__(self, w: wl.Workload, device="cuda"):
+        self.w = w
+        dt = kb.KV_BF16 if w.dtype == wl.BF16 else kb.KV_F32
+        self.pool = kb.PagedKVPool(w.num_layers, w.num_blocks, w.block_size, w.num_kv_heads,
+                                   w.head_dim, dt, device=device)
+        kview, vview = self.pool.block_storage("k"), self.pool.block_storage("v")
+        if w.k_pool is not None:
+            kview.copy_(to_torch(w.k_pool, w.dtype, device).view(kview.shape))
+            vview.copy_(to_torch(w.v_pool, w.dtype, device).view(vview.shape))
+        else:
+            g = torch.Generator(device=device)
+            g.manual_seed(int(w.pool_seed))
+            tdt = self.pool.torch_dtype
+            for view in (kview, vview):
+                for layer in range(w.num_layers):
+                    view[layer].copy_(torch.randn(view[layer].shape, generator=g, device=device,
+                                                  dtype=torch.float32).to(tdt))
+                if w.referenced is not None:
+                    dead = torch.from_numpy(~w.referenced).to(device)
+                    view[:, dead] = float("nan")
+        self.q = to_torch(w.q, w.dtype, device)
+        self.tables = torch.from_numpy(w.block_tables).to(device)
+        self.ctx = torch.from_numpy(w.ctx_lens).to(device)
+        self.ql = torch.from_numpy(w.q_lens).to(device)
+        self.k_new = None if w.k_new is None else to_torch(w.k_new, w.dtype, device)
+        self.v_new = None if w.v_new is None else to_torch(w.v_new, w.dtype, device)
+
+    # -- library --------------------------------------------------------------------------
+    def append(self):
+        if self.k_new is not None:
+            self.pool.append(self.w.layer, self.k_new, self.v_new, self.tables, self.ctx, self.ql,
+                             max_q_len=int(self.w.q_lens.max()))
+
+    def forward(self, q=None, out=None):
+        w = self.w
+        return self.pool.forward(w.layer, self.q if q is None else q, self.tables, self.ctx,
+                                 self.ql, scale=w.scale, max_ctx_len=int(w.ctx_lens.max()),
+                                 max_q_len=int(w.q_lens.max()), out=out)
+
+    # -- host copies for the oracle ---------------------------------------------------------
+    def host_pools(self):
+        w = self.w
+        k = to_numpy(self.pool.block_storage("k"), w.dtype)
+        v = to_numpy(self.pool.block_storage("v"), w.dtype)
+        return k, v
+
+    def oracle(self, k_pool=None, v_pool=None, seqs=None):
+        """Oracle output.  Pools default to the workload's own pre-append pool with the new rows
+        appended by the oracle (never the device's pool)."""
+        w = self.w
+        if k_pool is None:
+            if w.k_pool is None:
+                raise ValueError("pool drawn on the device: pass the pre-append host pool")
+            k_pool, v_pool = w.k_pool, w.v_pool
+        if w.k_new is not None:
+            k_pool, v_pool = ora.append(k_pool, v_pool, w.layer, w.k_new, w.v_new, w.block_tables,
+                                        w.ctx_lens, w.q_lens, num_kv_heads=w.num_kv_heads,
+                                        block_size=w.block_size, head_dim=w.head_dim,
+                                        dtype=w.dtype)
+        return ora.paged_attention(w.q, k_pool, v_pool, w.layer, w.block_tables, w.ctx_lens,
+                                   w.q_lens, scale=w.scale, num_kv_heads=w.num_kv_heads,
+                                   block_size=w.block_size, head_dim=w.head_dim, dtype=w.dtype,
+                                   seqs=seqs)
+
+
+def errors(gpu: np.ndarray, ref: np.ndarray):
+    mask = ~np.isnan(ref)
+    d = gpu[mask] - ref[mask]
+    max_abs = float(np.max(np.abs(d))) if d.size else 0.0
+    rel_l2 = float(np.linalg.norm(d) / max(np.linalg.norm(ref[mask]), 1e-300)) if d.size else 0.0
+    return max_abs, rel_l2
+
+
+def assert_close(gpu: np.ndarray, ref: np.ndarray, dtype: str, what=""):
+    assert gpu.shape == ref.shape
+    assert np.all(np.isfinite(gpu[~np.isnan(ref)])), f"{what}: non-finite output"
+    max_abs, rel_l2 = errors(gpu, ref)
+    tol = TOL[dtype]
+    assert max_abs <= tol["max_abs"] and rel_l2 <= tol["rel_l2"], \
+        f"{what}: max_abs={max_abs:.3e} rel_l2={rel_l2:.3e} (tol {tol})"
+    return max_abs, rel_l2

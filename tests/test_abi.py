@@ -1,0 +1,73 @@
+"""The C-ABI library loads and exports every entry point include/kvpool.h declares; host-side
+argument checks answer without touching a GPU (CPU only)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from paged_kv_cache_kvpool_amd import binding as kb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvpool.h")
+
+if not os.path.exists(kb.LIB_PATH):  # pragma: no cover
+    pytest.skip("libkvpool.so not built (run __graft_entry__.build())", allow_module_level=True)
+
+
+def declared():
+    text = open(HEADER).read()
+    return re.findall(r"KVPOOL_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)
+
+
+def test_header_declares_the_abi():
+    names = declared()
+    assert set(names) == set(kb.SIGNATURES), names
+
+
+def test_every_declared_symbol_is_exported():
+    lib = kb.lib()
+    for name in declared():
+        assert hasattr(lib, name), name
+        assert ctypes.cast(getattr(lib, name), ctypes.c_void_p).value
+
+
+def test_storage_bytes():
+    assert kb.kvpool_storage_bytes(2, 10, 16, 8, 128, kb.KV_BF16) == 2 * 10 * 16 * 8 * 128 * 2
+    assert kb.kvpool_storage_bytes(1, 3, 64, 1, 64, kb.KV_F32) == 3 * 64 * 64 * 4
+
+
+@pytest.mark.parametrize("args,code", [
+    ((1, 4, 32, 1, 128, kb.KV_BF16), kb.KV_EUNSUPPORTED),   # block size
+    ((1, 4, 16, 1, 96, kb.KV_BF16), kb.KV_EUNSUPPORTED),    # head dim
+    ((1, 4, 16, 1, 128, 7), kb.KV_EUNSUPPORTED),            # dtype
+    ((0, 4, 16, 1, 128, kb.KV_BF16), kb.KV_EINVAL),         # layers
+    ((1, 4, 16, 0, 128, kb.KV_BF16), kb.KV_EINVAL),         # kv heads
+])
+def test_storage_bytes_rejects(args, code):
+    with pytest.raises(kb.KVPoolError) as e:
+        kb.kvpool_storage_bytes(*args)
+    assert e.value.code == code
+    assert kb.kvpool_last_error()
+
+
+def test_create_rejects_before_any_device_call():
+    lib = kb.lib()
+    assert lib.kvpool_create(None, 1, 4, 16, 1, 128, kb.KV_BF16, 16, 16) == kb.KV_EINVAL
+    h = ctypes.c_void_p(0)
+    assert lib.kvpool_create(ctypes.byref(h), 1, 4, 16, 1, 128, kb.KV_BF16, None, 16) == kb.KV_EINVAL
+    assert lib.kvpool_create(ctypes.byref(h), 1, 4, 16, 1, 128, kb.KV_BF16, 8, 16) == kb.KV_EINVAL
+    assert lib.kvpool_create(ctypes.byref(h), 1, 4, 48, 1, 128, kb.KV_BF16, 16, 16) == kb.KV_EUNSUPPORTED
+    assert h.value is None
+
+
+def test_null_handles():
+    lib = kb.lib()
+    assert lib.kvpool_destroy(None) == kb.KV_OK
+    assert lib.kvattn_forward(None, 0, None, None, 8, 1.0, None, 1, None, None, 1, 1, 1, 1,
+                              None, 0, None) == kb.KV_EINVAL
+    assert lib.kvpool_append(None, 0, None, None, None, 1, None, None, 1, 1, 1, None) == kb.KV_EINVAL
+    assert lib.kvpool_copy_blocks(None, None, None, 1, None) == kb.KV_EINVAL
+    sz = ctypes.c_size_t(0)
+    assert lib.kvattn_workspace_size(None, 8, 1, 1, 1, 1, ctypes.byref(sz)) == kb.KV_EINVAL
+    assert "NULL" in kb.kvpool_last_error()
