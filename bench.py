@@ -1,0 +1,325 @@
+"""Benchmark of the paged-KV attention hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+One step is one pass of the hot path over one batch: append the new tokens' K/V into their
+pool blocks (kvpool_append), then attention against the paged pool (kvattn_forward: the split
+attention kernel or the prefill kernel, plus the cross-split reduce in split mode).  Inputs are
+resident in HBM before the timed region.  Between steps a 1 GiB scratch read evicts the 256 MB
+MALL and the L2s so every step reads its KV from HBM; that read is outside the per-step device
+timings.  (A scratch *write* would leave dirty lines that the step itself must write back.)
+
+Prints ONE JSON line.  ``value`` is the whole step's algorithmic throughput: HBM GB/s for the
+decode and verify workloads (K+V of every attended token once per KV head, plus Q, O, block
+tables and the appended rows), TFLOP/s for prefill (4*D per unmasked (query, key) pair per
+q-head).  ``roofline`` reports the dominant kernel alone, timed with HIP events recorded by the
+library around each of its launches on the launch stream; ``cpu_baseline`` times the float64
+oracle on a bounded sample of the same workload on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "decode attention achieved HBM GB/s + KV tokens/s; prefill MFMA TFLOP/s"
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+FLUSH_BYTES = 1 << 30
+
+WORKLOADS = {
+    "batched_gqa_decode": dict(kind="hbm", desc="32 seqs x 1 token, ctx U[1024,8192], 32/8 heads, D=128, bf16, B=16"),
+    "tiny_decode": dict(kind="latency", desc="1 seq x 1 token, ctx 256 (16 of 32 blocks), 1/1 heads, D=64, fp32"),
+    "spec_verify_32k": dict(kind="hbm", desc="1 seq, 1+3 tokens causal, ctx 32768+4, 40/8 heads, D=128, bf16"),
+    "spec_verify_128k": dict(kind="hbm", desc="1 seq, 1+3 tokens causal, ctx 131072+4, 40/8 heads, D=128, bf16"),
+    "prefix_prefill": dict(kind="mfma", desc="4 seqs x (4096 cached + 512 new causal), 40/8 heads, D=128, bf16"),
+    "long_decode": dict(kind="hbm", desc="2 seqs x 1 token at 262144 and 131072, 40/8 heads, D=128, bf16, pool 24576 blocks"),
+}
+
+
+def make_workload(name):
+    from paged_kv_cache_kvpool_amd import workloads as wl
+    if name == "batched_gqa_decode":
+        return wl.batched_gqa_decode(host_pool=False)
+    if name == "tiny_decode":
+        return wl.tiny_decode()
+    if name == "spec_verify_32k":
+        return wl.spec_verify(cached=32768, host_pool=False)
+    if name == "spec_verify_128k":
+        return wl.spec_verify(cached=131072, host_pool=False)
+    if name == "prefix_prefill":
+        return wl.prefix_prefill(host_pool=False)
+    if name == "long_decode":
+        return wl.long_decode(host_pool=False)
+    raise SystemExit(f"unknown workload {name}")
+
+
+def algorithmic(w):
+    """Per-step algorithmic bytes and flops (and attended KV tokens), from the definition."""
+    eb = w.elt_bytes
+    d, hq, hkv = w.head_dim, w.num_q_heads, w.num_kv_heads
+    kv_tokens = int(w.ctx_lens.astype(np.int64).sum())
+    kv_bytes = kv_tokens * hkv * d * 2 * eb
+    qo_bytes = 2 * w.total_q * hq * d * eb
+    table_bytes = int(sum((int(c) + w.block_size - 1) // w.block_size for c in w.ctx_lens)) * 4
+    append_bytes = 2 * 2 * w.total_q * hkv * d * eb if w.k_new is not None else 0
+    pairs = 0
+    for L, T in zip(w.ctx_lens.astype(np.int64), w.q_lens.astype(np.int64)):
+        pairs += T * (L - T) + T * (T + 1) // 2   # row i sees L - T + i + 1 keys
+    flops = 4 * d * hq * int(pairs)
+    return dict(kv_tokens=kv_tokens, kv_bytes=kv_bytes, attn_bytes=kv_bytes + qo_bytes + table_bytes,
+                append_bytes=append_bytes, step_bytes=kv_bytes + qo_bytes + table_bytes + append_bytes,
+                flops=flops, pairs=int(pairs))
+
+
+def kernel_sha(path):
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def load_traffic(workload, kernel):
+    """Per-launch HBM bytes from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary, or None
+    when it is missing or was taken on a different kernel source."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(p) as f:
+            t = json.load(f)[workload]
+    except (OSError, KeyError, ValueError):
+        return None
+    src = os.path.join(ROOT, "paged_kv_cache_kvpool_amd", "csrc", t.get("source", ""))
+    if t.get("kernel") != kernel or not os.path.exists(src) or kernel_sha(src) != t.get("source_sha"):
+        return None
+    return t.get("bytes_per_launch")
+
+
+def cpu_baseline(w, dev, kind, budget_s=15.0):
+    """The float64 oracle (as it stands) on a bounded sample: whole sequences, in order, until
+    about budget_s of CPU work; scaled to the metric's unit."""
+    from oracle import attention as ora
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    k_pool, v_pool = dev.pre_append_host()
+    if w.k_new is not None:
+        k_pool, v_pool = ora.append(k_pool, v_pool, w.layer, w.k_new, w.v_new, w.block_tables,
+                                    w.ctx_lens, w.q_lens, num_kv_heads=w.num_kv_heads,
+                                    block_size=w.block_size, head_dim=w.head_dim, dtype=w.dtype)
+    n_done, t_used, b_done, f_done, tok_done = 0, 0.0, 0, 0, 0
+    for s in range(w.num_seqs):
+        t0 = time.perf_counter()
+        ora.paged_attention(w.q, k_pool, v_pool, w.layer, w.block_tables, w.ctx_lens, w.q_lens,
+                            scale=w.scale, num_kv_heads=w.num_kv_heads, block_size=w.block_size,
+                            head_dim=w.head_dim, dtype=w.dtype, seqs=[s])
+        t_used += time.perf_counter() - t0
+        L, T = int(w.ctx_lens[s]), int(w.q_lens[s])
+        n_done += 1
+        tok_done += L
+        b_done += (L * w.num_kv_heads * w.head_dim * 2 * w.elt_bytes
+                   + 2 * T * w.num_q_heads * w.head_dim * w.elt_bytes)
+        f_done += 4 * w.head_dim * w.num_q_heads * (T * (L - T) + T * (T + 1) // 2)
+        if t_used >= budget_s:
+            break
+    sample = (f"{n_done} of {w.num_seqs} sequences ({tok_done} KV tokens, "
+              f"{t_used:.1f} s of oracle time)")
+    if kind == "mfma":
+        return dict(value=f_done / t_used / 1e12, unit="TFLOP/s", cores=threads, kind="oracle",
+                    sample=sample)
+    return dict(value=b_done / t_used / 1e9, unit="GB/s", cores=threads, kind="oracle",
+                sample=sample)
+
+
+class Device:
+    """The workload on cuda:0 through the library's binding."""
+
+    def __init__(self, w):
+        import torch
+        from paged_kv_cache_kvpool_amd import binding as kb
+        from paged_kv_cache_kvpool_amd import workloads as wl
+        self.w = w
+        self.torch = torch
+        dt = kb.KV_BF16 if w.dtype == wl.BF16 else kb.KV_F32
+        self.pool = kb.PagedKVPool(w.num_layers, w.num_blocks, w.block_size, w.num_kv_heads,
+                                   w.head_dim, dt, device="cuda")
+        tdt = self.pool.torch_dtype
+
+        def dev(a):
+            if a is None:
+                return None
+            if w.dtype == wl.BF16:
+                return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+            return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+        kv, vv = self.pool.block_storage("k"), self.pool.block_storage("v")
+        if w.k_pool is not None:
+            kv.copy_(dev(w.k_pool).view(kv.shape))
+            vv.copy_(dev(w.v_pool).view(vv.shape))
+        else:
+            g = torch.Generator(device="cuda")
+            g.manual_seed(int(w.pool_seed))
+            for view in (kv, vv):
+                for layer in range(w.num_layers):
+                    view[layer].copy_(torch.randn(view[layer].shape, generator=g, device="cuda",
+                                                  dtype=torch.float32).to(tdt))
+                view[:, torch.from_numpy(~w.referenced).cuda()] = float("nan")
+        self._pre = None
+        self.q = dev(w.q)
+        self.k_new, self.v_new = dev(w.k_new), dev(w.v_new)
+        self.tables = torch.from_numpy(w.block_tables).cuda()
+        self.ctx = torch.from_numpy(w.ctx_lens).cuda()
+        self.ql = torch.from_numpy(w.q_lens).cuda()
+        self.out = torch.empty_like(self.q)
+        self.max_ctx, self.max_q = int(w.ctx_lens.max()), int(w.q_lens.max())
+        self.pool.workspace(w.num_q_heads, w.num_seqs, w.total_q, self.max_ctx, self.max_q)
+
+    def pre_append_host(self):
+        """Host copy of the pool as drawn (taken before the first append)."""
+        return self._pre
+
+    def snapshot_pre_append(self, need):
+        if not need:
+            return
+        from paged_kv_cache_kvpool_amd import workloads as wl
+        torch = self.torch
+        out = []
+        for which in ("k", "v"):
+            t = self.pool.block_storage(which).cpu()
+            out.append(t.view(torch.int16).numpy().view(np.uint16) if self.w.dtype == wl.BF16 else t.numpy())
+        self._pre = tuple(out)
+
+    def step(self):
+        w = self.w
+        if self.k_new is not None:
+            self.pool.append(w.layer, self.k_new, self.v_new, self.tables, self.ctx, self.ql,
+                             max_q_len=self.max_q)
+        self.pool.forward(w.layer, self.q, self.tables, self.ctx, self.ql, scale=w.scale,
+                          max_ctx_len=self.max_ctx, max_q_len=self.max_q, out=self.out)
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="batched_gqa_decode", choices=sorted(WORKLOADS))
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--flush", default="read", choices=["read", "write", "none"],
+                    help="evict MALL and L2 between steps by reading (default) or writing 1 GiB")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from paged_kv_cache_kvpool_amd import binding as kb
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    wname = args.workload
+    info = WORKLOADS[wname]
+    t_setup = time.perf_counter()
+    w = make_workload(wname)
+    alg = algorithmic(w)
+    dev = Device(w)
+    want_cpu = not args.no_cpu_baseline
+    dev.snapshot_pre_append(want_cpu)
+    scratch = torch.zeros(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t_setup
+
+    for _ in range(args.warmup):
+        dev.step()
+    torch.cuda.synchronize()
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    kb.kvpool_profile(True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    flush_f32 = scratch.view(torch.float32)
+    for k in range(args.steps):
+        if args.flush == "read":
+            flush_f32.sum()        # reads 1 GiB: evicts with clean lines only
+        elif args.flush == "write":
+            scratch.fill_(k & 0xFF)  # leaves dirty lines that later reads must write back
+        starts[k].record()
+        dev.step()
+        ends[k].record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kb.kvpool_profile(False)
+    step_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    ktimes = kb.kernel_times()
+    ms = float(np.mean(step_ms))
+
+    attn_kernels = [k for k in ("attn_prefill_mfma", "attn_split_mfma", "attn_vec") if k in ktimes]
+    dom = attn_kernels[0]
+    launches, total = ktimes[dom]
+    dom_ms = total / launches
+    kind = info["kind"]
+    dom_bytes = alg["kv_bytes"] + w.total_q * w.num_q_heads * w.head_dim * w.elt_bytes + \
+        int(sum((int(c) + w.block_size - 1) // w.block_size for c in w.ctx_lens)) * 4
+    if kind == "mfma":
+        achieved = alg["flops"] / (dom_ms * 1e-3) / 1e12
+        roof = dict(bound="mfma", achieved=achieved, peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                    frac=achieved / MFMA_BF16_PEAK_TFLOPS)
+        value, unit = alg["flops"] / (ms * 1e-3) / 1e12, "TFLOP/s"
+    else:
+        achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+        roof = dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
+                    frac=achieved / HBM_PEAK_GBS)
+        value, unit = alg["step_bytes"] / (ms * 1e-3) / 1e9, "GB/s"
+    src = {"attn_split_mfma": "attn_split_mfma.hip", "attn_vec": "attn_vec.hip",
+           "attn_prefill_mfma": "attn_prefill_mfma.hip"}[dom]
+    roof["kernel"] = dom
+    roof["kernel_ms"] = dom_ms
+    roof["traffic"] = load_traffic(wname, dom)
+
+    cpu = None
+    if want_cpu:
+        cpu = cpu_baseline(w, dev, kind)
+
+    line = {
+        "metric": METRIC,
+        "value": value,
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": wname, "desc": info["desc"], "kv_tokens": alg["kv_tokens"],
+                   "num_seqs": w.num_seqs, "total_q": w.total_q, "block_size": w.block_size,
+                   "head_dim": w.head_dim, "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
+                   "mall_flush": args.flush},
+        "kv_tokens_per_s": alg["kv_tokens"] / (ms * 1e-3),
+        "step_ms_p10_p50_p90": [float(np.percentile(step_ms, p)) for p in (10, 50, 90)],
+        "kernel_ms_per_launch": {k: v[1] / v[0] for k, v in ktimes.items()},
+        "algorithmic": {"step_bytes": alg["step_bytes"], "dominant_kernel_bytes": dom_bytes,
+                        "flops": alg["flops"]},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "wall_s_timed_region": wall,
+        "setup_s": setup_s,
+        "kernel_source_sha": kernel_sha(os.path.join(ROOT, "paged_kv_cache_kvpool_amd", "csrc", src)),
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

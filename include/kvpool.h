@@ -148,6 +148,19 @@ KVPOOL_API int kvattn_forward(kvpool_t *pool, int32_t layer, const void *q, void
                               int32_t max_ctx_len, int32_t max_q_len, void *workspace,
                               size_t workspace_bytes, void *stream);
 
+/* Opt-in per-kernel timing for measurement.  With enable != 0, every kernel launch made by this
+ * library (any pool, any thread) is bracketed by a pair of HIP events recorded on the launch's
+ * stream, and earlier records are dropped; with enable == 0 recording stops (records are kept).
+ * It measures without changing what is computed, like the per-phase timings the pages' servers
+ * log (NInfer serving doc, "Structured request log").  Costs a few microseconds per launch. */
+KVPOOL_API int kvpool_profile(int32_t enable);
+
+/* Totals for kernel `index` (0, 1, ... in a fixed order) since the last kvpool_profile(1): its
+ * name (static string), the number of recorded launches and the summed event time in
+ * milliseconds.  Waits for the recorded events to complete.  KV_ERANGE past the last kernel. */
+KVPOOL_API int kvpool_profile_kernel(int32_t index, const char **name, int32_t *launches,
+                                     double *total_ms);
+
 /* Message for the last non-OK return on this thread ("" if none).  Valid until the next call
  * on the same thread. */
 KVPOOL_API const char *kvpool_last_error(void);

@@ -37,6 +37,9 @@ SIGNATURES = {
     "kvattn_forward": (_i32, [_vp, _i32, _vp, _vp, _i32, _f32, _vp, _i32, _vp, _vp, _i32, _i32,
                               _i32, _i32, _vp, _sz, _vp]),
     "kvpool_last_error": (ctypes.c_char_p, []),
+    "kvpool_profile": (_i32, [_i32]),
+    "kvpool_profile_kernel": (_i32, [_i32, ctypes.POINTER(ctypes.c_char_p),
+                                     ctypes.POINTER(_i32), ctypes.POINTER(ctypes.c_double)]),
 }
 
 
@@ -87,6 +90,32 @@ def _stream(stream) -> Optional[int]:
 
 def kvpool_last_error() -> str:
     return lib().kvpool_last_error().decode()
+
+
+def kvpool_profile(enable: bool) -> None:
+    _check(lib().kvpool_profile(1 if enable else 0))
+
+
+def kvpool_profile_kernel(index: int):
+    """(name, launches, total_ms) for one kernel, or None past the last kernel index."""
+    name, n, ms = ctypes.c_char_p(), _i32(0), ctypes.c_double(0.0)
+    rc = lib().kvpool_profile_kernel(index, ctypes.byref(name), ctypes.byref(n), ctypes.byref(ms))
+    if rc == KV_ERANGE:
+        return None
+    _check(rc)
+    return name.value.decode(), n.value, ms.value
+
+
+def kernel_times() -> dict:
+    """{kernel name: (launches, total_ms)} for every kernel launched since kvpool_profile(True)."""
+    out, i = {}, 0
+    while True:
+        r = kvpool_profile_kernel(i)
+        if r is None:
+            return out
+        if r[1]:
+            out[r[0]] = (r[1], r[2])
+        i += 1
 
 
 def kvpool_storage_bytes(num_layers, num_blocks, block_size, num_kv_heads, head_dim, dtype) -> int:

@@ -58,10 +58,11 @@ __global__ __launch_bounds__(64) void attn_vec_kernel(AttnArgs a) {
   const int r0 = rt * ROWS;
   if (r0 >= rows) return;
   const int p_last = L - T + (min(r0 + ROWS, rows) - 1) / G;
+  const int split = seq_split(a, L);
   int kb = 0, ke = min(L, p_last + 1);
   if (a.split_mode) {
-    kb = sp * a.split_tokens;
-    ke = min(ke, kb + a.split_tokens);
+    kb = sp * split;
+    ke = min(ke, kb + split);
   }
   if (kb >= ke) return;
   const int q_start = wave_prefix_total(a.q_lens, s);
@@ -195,7 +196,8 @@ __global__ __launch_bounds__(64) void attn_vec_kernel(AttnArgs a) {
       o[r][j] = v;
     }
     if (prow[r] < kb) continue;
-    if (a.split_mode) {
+    // Rows whose keys all lie in split 0 are finished here (the reduce skips them).
+    if (a.split_mode && prow[r] >= split) {
       const size_t slot = rh[r] * a.max_splits + sp;
       if (lane == 0) {
         a.part_ml[2 * slot] = m_run[r];

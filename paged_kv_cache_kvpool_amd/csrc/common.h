@@ -91,9 +91,10 @@ __device__ __forceinline__ float row_max(float x) {
 
 // Sum of v[0 .. n) over the wave, every lane gets it (n small: a few thousand at most).
 __device__ __forceinline__ int wave_prefix_total(const int32_t* v, int n) {
-  int lane = threadIdx.x & (WAVE - 1);
+  const int lane = threadIdx.x & (WAVE - 1);
   int acc = 0;
-  for (int i = lane; i < n; i += WAVE) acc += max(0, v[i]);
+  for (int base = 0; base < n; base += WAVE)  // uniform trip count
+    acc += (base + lane < n) ? max(0, v[base + lane]) : 0;
   float f = (float)acc;  // exact: totals stay far below 2^24
   f = row_sum(f);
   f = xrow_sum(f);
@@ -115,13 +116,26 @@ struct AttnArgs {
   float* part_o;            // [total_q][Hq][max_splits][D]   (split mode)
   float* part_ml;           // [total_q][Hq][max_splits][2]   (split mode: max, sum)
   int32_t num_seqs, total_q, num_q_heads, num_kv_heads, group, block_size, num_blocks;
+  int32_t block_shift;      // log2(block_size)
   int32_t max_blocks_per_seq;
-  int32_t split_tokens;     // keys per split (split mode) ; ignored otherwise
+  int32_t split_tokens;     // split mode: keys per split if > 0, else the per-length rule
   int32_t max_splits;       // splits per row slot in the workspace (split mode)
   int32_t row_tiles;        // row tiles per (sequence, kv head)
   int32_t split_mode;       // 1: write partials for the reduce kernel; 0: write `out`
   float scale_log2;         // softmax scale * log2(e)
 };
+
+// Keys per split of a sequence with L keys (split mode): a fixed count if the caller set one,
+// else the smallest power of two >= floor(L/128) within [256, 2048] (at most ~128 splits per
+// sequence up to 262144 keys).  It depends on the sequence's own length only, so its reduction
+// order does too.
+__device__ __forceinline__ int seq_split(const AttnArgs& a, int L) {
+  if (a.split_tokens > 0) return a.split_tokens;
+  const int t = L >> 7;
+  int sp = 256;
+  while (sp < t && sp < 2048) sp <<= 1;
+  return sp;
+}
 
 // Clamped per-sequence lengths (bad metadata must never index out of bounds).
 __device__ __forceinline__ void seq_lens(const AttnArgs& a, int s, int& L, int& T) {
@@ -140,6 +154,15 @@ __device__ __forceinline__ size_t tile_offset(const int32_t* table_row, int pos,
   blk = ((unsigned)blk < (unsigned)num_blocks) ? blk : 0;
   int sub = (pos % block_size) / TILE;
   size_t tile = ((size_t)blk * num_kv_heads + h) * (size_t)(block_size / TILE) + sub;
+  return tile * (size_t)(TILE * head_dim);
+}
+
+// Element offset of tile `sub` of block `blk` for KV head h within one layer (blk clamped).
+__device__ __forceinline__ size_t block_tile_offset(int blk, int sub, int h, int block_shift,
+                                                    int num_blocks, int num_kv_heads,
+                                                    int head_dim) {
+  blk = ((unsigned)blk < (unsigned)num_blocks) ? blk : 0;
+  const size_t tile = (((size_t)blk * num_kv_heads + h) << (block_shift - 4)) + sub;
   return tile * (size_t)(TILE * head_dim);
 }
 

@@ -9,6 +9,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -49,13 +50,22 @@ bool env_flag(const char* name) {
   return v && *v && strcmp(v, "0") != 0;
 }
 
-// Keys per split in split mode.  A fixed count (never derived from the batch) keeps each
-// sequence's reduction order a function of its own length only.
+// Keys per split in split mode: 0 selects the per-length rule the kernels apply to each
+// sequence (a power of two in [256, 2048], about L/128), KVATTN_SPLIT_TOKENS fixes a count for
+// tuning sweeps.  Neither depends on the rest of the batch, so each sequence's reduction order
+// is a function of its own length only.
 int split_tokens() {
   const char* v = getenv("KVATTN_SPLIT_TOKENS");
-  int s = v ? atoi(v) : 256;
-  s = std::max(32, std::min(s, 1 << 20));
+  if (!v || !*v) return 0;
+  int s = std::max(32, std::min(atoi(v), 1 << 20));
   return (s + 31) / 32 * 32;
+}
+
+// Upper bound of a sequence's split count over all lengths <= max_ctx.
+int max_split_count(int split, int max_ctx) {
+  if (split > 0) return std::max(1, (max_ctx + split - 1) / split);
+  // split >= floor(L/128) gives at most 129 splits; past the clamp, L/2048.
+  return std::max(std::max(1, std::min(129, (max_ctx + 255) / 256)), (max_ctx + 2047) / 2048);
 }
 
 // Split mode serves decode and verification (few query rows per KV head): the context is cut
@@ -127,9 +137,82 @@ int validate_meta(const kvpool* p, const HostMeta& m, int32_t max_blocks, int32_
   return KV_OK;
 }
 
+// Opt-in per-kernel timing: a HIP event pair around every launch, on the launch's stream.
+enum KernelId { K_APPEND, K_COPY, K_SPLIT_MFMA, K_VEC, K_PREFILL_MFMA, K_REDUCE, K_COUNT };
+const char* const kKernelNames[K_COUNT] = {"kv_append", "kv_copy_blocks", "attn_split_mfma",
+                                           "attn_vec", "attn_prefill_mfma", "attn_reduce"};
+struct ProfRec {
+  int kernel;
+  hipEvent_t a, b;
+};
+std::mutex g_prof_mu;
+bool g_prof_on = false;
+std::vector<ProfRec> g_prof_recs;
+std::vector<hipEvent_t> g_prof_free;
+
+hipEvent_t prof_event() {
+  if (!g_prof_free.empty()) {
+    hipEvent_t e = g_prof_free.back();
+    g_prof_free.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+template <class F>
+hipError_t timed(int kernel, hipStream_t st, F launch) {
+  std::unique_lock<std::mutex> lk(g_prof_mu);
+  if (!g_prof_on) {
+    lk.unlock();
+    return launch();
+  }
+  hipEvent_t a = prof_event(), b = prof_event();
+  if (a) hipEventRecord(a, st);
+  hipError_t e = launch();
+  if (b) hipEventRecord(b, st);
+  if (a && b) g_prof_recs.push_back({kernel, a, b});
+  return e;
+}
+
 }  // namespace
 
 extern "C" {
+
+int kvpool_profile(int32_t enable) {
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  if (enable) {
+    for (auto& r : g_prof_recs) {
+      g_prof_free.push_back(r.a);
+      g_prof_free.push_back(r.b);
+    }
+    g_prof_recs.clear();
+  }
+  g_prof_on = enable != 0;
+  return ok();
+}
+
+int kvpool_profile_kernel(int32_t index, const char** name, int32_t* launches, double* total_ms) {
+  if (index < 0 || index >= K_COUNT) return fail(KV_ERANGE, "kernel index %d out of range", index);
+  if (!name || !launches || !total_ms) return fail(KV_EINVAL, "NULL output pointer");
+  std::lock_guard<std::mutex> lk(g_prof_mu);
+  int n = 0;
+  double ms = 0.0;
+  for (auto& r : g_prof_recs) {
+    if (r.kernel != index) continue;
+    hipError_t e = hipEventSynchronize(r.b);
+    float t = 0.f;
+    if (e == hipSuccess) e = hipEventElapsedTime(&t, r.a, r.b);
+    if (e != hipSuccess) return fail(KV_EDEVICE, "event timing: %s", hipGetErrorString(e));
+    ms += t;
+    ++n;
+  }
+  *name = kKernelNames[index];
+  *launches = n;
+  *total_ms = ms;
+  return ok();
+}
 
 int kvpool_storage_bytes(int32_t num_layers, int32_t num_blocks, int32_t block_size,
                          int32_t num_kv_heads, int32_t head_dim, int32_t dtype, size_t* bytes) {
@@ -226,7 +309,7 @@ int kvpool_append(kvpool_t* pool, int32_t layer, const void* k_new, const void* 
   a.block_size = pool->block_size;
   a.num_blocks = pool->num_blocks;
   a.max_blocks_per_seq = max_blocks_per_seq;
-  hipError_t e = kvp::launch_append(a, elt_bytes(pool->dtype), max_q_len, st);
+  hipError_t e = timed(K_APPEND, st, [&] { return kvp::launch_append(a, elt_bytes(pool->dtype), max_q_len, st); });
   if (e != hipSuccess) return fail(KV_EDEVICE, "append launch: %s", hipGetErrorString(e));
   return ok();
 }
@@ -266,7 +349,7 @@ int kvpool_copy_blocks(kvpool_t* pool, const int32_t* src, const int32_t* dst, i
   a.dst = dst;
   a.num_blocks = pool->num_blocks;
   a.block_bytes = (size_t)pool->num_kv_heads * pool->block_size * pool->head_dim * elt_bytes(pool->dtype);
-  hipError_t e = kvp::launch_copy_blocks(a, n, pool->num_layers, st);
+  hipError_t e = timed(K_COPY, st, [&] { return kvp::launch_copy_blocks(a, n, pool->num_layers, st); });
   if (e != hipSuccess) return fail(KV_EDEVICE, "copy launch: %s", hipGetErrorString(e));
   return ok();
 }
@@ -286,7 +369,7 @@ Plan make_plan(const kvpool* p, int32_t num_q_heads, int32_t total_q, int32_t ma
   const int G = num_q_heads / p->num_kv_heads;
   pl.split_mode = (long long)max_q_len * G <= kSplitRowsMax;
   pl.split = split_tokens();
-  pl.max_splits = pl.split_mode ? std::max(1, (max_ctx_len + pl.split - 1) / pl.split) : 1;
+  pl.max_splits = pl.split_mode ? max_split_count(pl.split, max_ctx_len) : 1;
   if (pl.split_mode) {
     const size_t slots = (size_t)total_q * num_q_heads * pl.max_splits;
     const size_t o_bytes = (slots * p->head_dim * 4 + 255) / 256 * 256;
@@ -369,6 +452,7 @@ int kvattn_forward(kvpool_t* pool, int32_t layer, const void* q, void* out, int3
   a.num_kv_heads = pool->num_kv_heads;
   a.group = G;
   a.block_size = pool->block_size;
+  a.block_shift = pool->block_size == 64 ? 6 : 4;
   a.num_blocks = pool->num_blocks;
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.split_tokens = pl.split;
@@ -384,15 +468,15 @@ int kvattn_forward(kvpool_t* pool, int32_t layer, const void* q, void* out, int3
     const int r8 = std::min(rows, 8);
     const int rpt = r8 <= 1 ? 1 : r8 <= 2 ? 2 : r8 <= 4 ? 4 : r8 <= 5 ? 5 : 8;
     a.row_tiles = (rows + rpt - 1) / rpt;
-    e = kvp::launch_attn_vec(a, eb, pool->head_dim, rpt, a.row_tiles * pl.max_splits, st);
+    e = timed(K_VEC, st, [&] { return kvp::launch_attn_vec(a, eb, pool->head_dim, rpt, a.row_tiles * pl.max_splits, st); });
   } else {
     const int rpt = rows <= 16 ? 16 : 32;
     a.row_tiles = (rows + rpt - 1) / rpt;
-    e = kvp::launch_attn_split_mfma(a, pool->head_dim, rpt, a.row_tiles * pl.max_splits, st);
+    e = timed(K_SPLIT_MFMA, st, [&] { return kvp::launch_attn_split_mfma(a, pool->head_dim, rpt, a.row_tiles * pl.max_splits, st); });
   }
   if (e != hipSuccess) return fail(KV_EDEVICE, "attention launch: %s", hipGetErrorString(e));
   if (pl.split_mode) {
-    e = kvp::launch_attn_reduce(a, eb, pool->head_dim, max_q_len, st);
+    e = timed(K_REDUCE, st, [&] { return kvp::launch_attn_reduce(a, eb, pool->head_dim, max_q_len, st); });
     if (e != hipSuccess) return fail(KV_EDEVICE, "reduce launch: %s", hipGetErrorString(e));
   }
   return ok();

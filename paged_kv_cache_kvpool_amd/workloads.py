@@ -191,12 +191,12 @@ def tiny_decode(seed: int = 0) -> Workload:
 def batched_gqa_decode(seed: int = 1, num_seqs: int = 32, host_pool: bool = True) -> Workload:
     """32 sequences x 1 query token, 32 q-heads / 8 kv-heads, D=128, bf16, B=16, contexts
     uniform on [1024, 8192]; the pool is exactly the blocks the contexts need, dealt out as
-    disjoint random slices of one permutation."""
+    disjoint random slices of one permutation.  The current token's K/V is appended first."""
     rng = np.random.default_rng(seed)
     ctx = rng.integers(1024, 8193, size=num_seqs).astype(np.int32)
     return make("batched_gqa_decode", seed=seed + 1000, dtype=BF16, num_seqs_ctx=ctx,
                 q_lens=np.ones(num_seqs, np.int32), num_q_heads=32, num_kv_heads=8,
-                head_dim=128, append=False, host_pool=host_pool)
+                head_dim=128, append=True, host_pool=host_pool)
 
 
 def spec_verify(seed: int = 2, cached: int = 32768, drafts: int = 3,
@@ -223,7 +223,7 @@ def long_decode(seed: int = 4, host_pool: bool = False) -> Workload:
     """2 concurrent sequences at 262144 and 131072 tokens, 1 query token each, 40/8 heads,
     D=128, bf16, pool of 24576 blocks (393216 tokens) with random placement."""
     return make("long_decode", seed=seed, dtype=BF16, num_seqs_ctx=[262144, 131072],
-                q_lens=[1, 1], num_q_heads=40, num_kv_heads=8, head_dim=128, append=False,
+                q_lens=[1, 1], num_q_heads=40, num_kv_heads=8, head_dim=128, append=True,
                 num_blocks=24576, host_pool=host_pool)
 
 

@@ -170,6 +170,7 @@ def test_batched_gqa_decode_full():
     announce("batched_gqa_decode (32 seqs, 1024..8192 keys, 32/8 heads)")
     w = wl.batched_gqa_decode()
     c = DeviceCase(w)
+    c.append()
     out = c.forward()
     torch.cuda.synchronize()
     assert_close(out_f64(out), c.oracle(), wl.BF16, w.name)
@@ -201,6 +202,7 @@ def test_long_decode_full():
     w = wl.long_decode()
     c = DeviceCase(w)
     kh, vh = c.host_pools()
+    c.append()
     out = c.forward()
     torch.cuda.synchronize()
     assert_close(out_f64(out), c.oracle(kh, vh), wl.BF16, w.name)
