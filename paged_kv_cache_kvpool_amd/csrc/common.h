@@ -32,6 +32,11 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
 __device__ __forceinline__ float round_to_bf16(float f) {
   return __uint_as_float(f32_to_bf16_bits(f) << 16);
 }
+// Two floats -> packed nearest-even bf16 pair (lo in bits 0..15): v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+  const floatx2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
 // Two floats that are already exact bf16 values -> packed pair (lo in bits 0..15).
 __device__ __forceinline__ uint32_t pack_exact_bf16(float lo, float hi) {
   return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xffff0000u);
@@ -99,6 +104,17 @@ __device__ __forceinline__ int wave_prefix_total(const int32_t* v, int n) {
   f = row_sum(f);
   f = xrow_sum(f);
   return (int)f;
+}
+
+// Workgroup barrier without a memory fence.  __syncthreads() also waits for every outstanding
+// vector memory operation (vmcnt(0)), which would drain LDS-DMA loads still meant to be in
+// flight; callers of this one have already waited for what must be visible (an explicit vmcnt
+// wait for LDS-DMA data, ds_read results before their use).  The empty asm statements keep the
+// compiler from moving memory operations across the barrier.
+__device__ __forceinline__ void barrier_no_fence() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 // exp2 that maps -inf to 0 without a branch (hardware v_exp_f32 already does).

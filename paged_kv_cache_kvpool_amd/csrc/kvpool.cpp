@@ -22,6 +22,7 @@ struct kvpool {
   void* v;
   size_t layer_elems;  // elements of one layer of K (or V)
   int device;
+  int num_cus;         // compute units of that device
 };
 
 namespace {
@@ -248,6 +249,10 @@ int kvpool_create(kvpool_t** out, int32_t num_layers, int32_t num_blocks, int32_
   p->v = v_storage;
   p->layer_elems = (size_t)num_blocks * num_kv_heads * block_size * head_dim;
   p->device = dev;
+  p->num_cus = 256;
+  int cus = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0)
+    p->num_cus = cus;
   *out = p;
   return ok();
 }
@@ -469,10 +474,15 @@ int kvattn_forward(kvpool_t* pool, int32_t layer, const void* q, void* out, int3
     const int rpt = r8 <= 1 ? 1 : r8 <= 2 ? 2 : r8 <= 4 ? 4 : r8 <= 5 ? 5 : 8;
     a.row_tiles = (rows + rpt - 1) / rpt;
     e = timed(K_VEC, st, [&] { return kvp::launch_attn_vec(a, eb, pool->head_dim, rpt, a.row_tiles * pl.max_splits, st); });
-  } else {
+  } else if (pl.split_mode) {
     const int rpt = rows <= 16 ? 16 : 32;
     a.row_tiles = (rows + rpt - 1) / rpt;
     e = timed(K_SPLIT_MFMA, st, [&] { return kvp::launch_attn_split_mfma(a, pool->head_dim, rpt, a.row_tiles * pl.max_splits, st); });
+  } else {
+    int ntw = kvp::prefill_rows_per_wave_choice(rows, num_seqs * pool->num_kv_heads, pool->num_cus);
+    if (const char* v = getenv("KVATTN_PREFILL_NTW")) ntw = std::max(2, std::min(5, atoi(v)));  // sweeps
+    a.row_tiles = (rows + 64 * ntw - 1) / (64 * ntw);
+    e = timed(K_PREFILL_MFMA, st, [&] { return kvp::launch_attn_prefill_mfma(a, pool->head_dim, ntw, st); });
   }
   if (e != hipSuccess) return fail(KV_EDEVICE, "attention launch: %s", hipGetErrorString(e));
   if (pl.split_mode) {
