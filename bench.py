@@ -213,6 +213,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="batched_gqa_decode", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (scale for HBM counters)")
     ap.add_argument("--flush", default="read", choices=["read", "write", "none"],
                     help="evict MALL and L2 between steps by reading (default) or writing 1 GiB")
     args = ap.parse_args()
@@ -226,6 +228,16 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        # A plain copy of known size: reads and writes exactly 1 GiB per launch.
+        src = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(max(1, args.steps)):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": FLUSH_BYTES, "launches": max(1, args.steps)}),
+              flush=True)
+        return
     wname = args.workload
     info = WORKLOADS[wname]
     t_setup = time.perf_counter()

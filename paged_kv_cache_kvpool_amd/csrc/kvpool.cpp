@@ -485,7 +485,10 @@ int kvattn_forward(kvpool_t* pool, int32_t layer, const void* q, void* out, int3
     e = timed(K_PREFILL_MFMA, st, [&] { return kvp::launch_attn_prefill_mfma(a, pool->head_dim, ntw, st); });
   }
   if (e != hipSuccess) return fail(KV_EDEVICE, "attention launch: %s", hipGetErrorString(e));
-  if (pl.split_mode) {
+  // Rows whose keys all fall in split 0 are finished by the attention kernel; when no sequence
+  // can have a second split (every split holds >= 256 keys) the reduce has nothing to do.
+  const bool need_reduce = pl.split_mode && max_ctx_len > (pl.split > 0 ? pl.split : 256);
+  if (need_reduce) {
     e = timed(K_REDUCE, st, [&] { return kvp::launch_attn_reduce(a, eb, pool->head_dim, max_q_len, st); });
     if (e != hipSuccess) return fail(KV_EDEVICE, "reduce launch: %s", hipGetErrorString(e));
   }
