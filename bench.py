@@ -213,6 +213,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="batched_gqa_decode", choices=sorted(WORKLOADS))
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--graph", type=int, default=0,
+                    help="1: time the step as a captured HIP graph replay (as a serving loop would; "
+                         "slower than eager launches on this ROCm); 0: eager launches")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (scale for HBM counters)")
     ap.add_argument("--flush", default="read", choices=["read", "write", "none"],
@@ -254,25 +257,52 @@ def main():
         dev.step()
     torch.cuda.synchronize()
 
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    kb.kvpool_profile(True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
     flush_f32 = scratch.view(torch.float32)
-    for k in range(args.steps):
+
+    def flush(k):
         if args.flush == "read":
-            flush_f32.sum()        # reads 1 GiB: evicts with clean lines only
+            flush_f32.sum()          # reads 1 GiB: evicts with clean lines only
         elif args.flush == "write":
             scratch.fill_(k & 0xFF)  # leaves dirty lines that later reads must write back
-        starts[k].record()
+
+    # Per-kernel timing: an eager pass with the library's HIP-event pairs around every launch.
+    kb.kvpool_profile(True)
+    for k in range(args.steps):
+        flush(k)
         dev.step()
+    torch.cuda.synchronize()
+    kb.kvpool_profile(False)
+    ktimes = kb.kernel_times()
+
+    run = dev.step
+    if args.graph:
+        # Capture one step (append + attention + reduce) and replay it: the library makes no
+        # host synchronisation and no memset, so the captured kernels are exactly the eager ones.
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            dev.step()
+        torch.cuda.current_stream().wait_stream(side)
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            dev.step()
+        run = graph.replay
+        for _ in range(args.warmup):
+            run()
+        torch.cuda.synchronize()
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        flush(k)
+        starts[k].record()
+        run()
         ends[k].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    kb.kvpool_profile(False)
     step_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    ktimes = kb.kernel_times()
     ms = float(np.mean(step_ms))
 
     attn_kernels = [k for k in ("attn_prefill_mfma", "attn_split_mfma", "attn_vec") if k in ktimes]
@@ -318,7 +348,7 @@ def main():
         "config": {"workload": wname, "desc": info["desc"], "kv_tokens": alg["kv_tokens"],
                    "num_seqs": w.num_seqs, "total_q": w.total_q, "block_size": w.block_size,
                    "head_dim": w.head_dim, "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
-                   "mall_flush": args.flush},
+                   "mall_flush": args.flush, "hip_graph": bool(args.graph)},
         "kv_tokens_per_s": alg["kv_tokens"] / (ms * 1e-3),
         "step_ms_p10_p50_p90": [float(np.percentile(step_ms, p)) for p in (10, 50, 90)],
         "kernel_ms_per_launch": {k: v[1] / v[0] for k, v in ktimes.items()},
