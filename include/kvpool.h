@@ -138,7 +138,8 @@ KVPOOL_API int kvattn_workspace_size(const kvpool_t *pool, int32_t num_q_heads,
  *                    <= max_blocks_per_seq * block_size; q_lens[s] == 0 produces no rows
  *   max_ctx_len, max_q_len  host upper bounds of ctx_lens / q_lens (size the grid)
  *   workspace        device scratch of at least kvattn_workspace_size() bytes, 256-byte
- *                    aligned; contents on entry don't matter
+ *                    aligned; contents on entry don't matter.  Calls that may run at the same
+ *                    time (other streams) need workspaces of their own.
  * num_q_heads must be a multiple of the pool's num_kv_heads with at most 16 q-heads per KV
  * head. */
 KVPOOL_API int kvattn_forward(kvpool_t *pool, int32_t layer, const void *q, void *out,

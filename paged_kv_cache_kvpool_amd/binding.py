@@ -17,7 +17,9 @@ from typing import Optional
 
 import torch
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvpool.so")
+# KVPOOL_LIB: load a library built elsewhere (e.g. another build of the same sources).
+LIB_PATH = os.environ.get("KVPOOL_LIB") or os.path.join(os.path.dirname(os.path.abspath(__file__)),
+                                                        "libkvpool.so")
 
 KV_OK, KV_EINVAL, KV_ERANGE, KV_EUNSUPPORTED, KV_EDEVICE, KV_ENOMEM = 0, -1, -2, -3, -4, -5
 KV_F32, KV_BF16 = 0, 1

@@ -3,15 +3,23 @@
 // Serves single-token decode of a batch (NInfer serving doc, "Execution behavior") and the
 // verification of 1 + k draft tokens (sparkinfer server README, "Serve Qwen3.8 with DSpark"):
 // few query rows per KV head against a long paged context.  Each sequence's context is cut
-// into splits of a fixed number of keys (so the cut depends only on that sequence's length)
-// and one workgroup reduces one split to a partial (max, sum, unnormalised output); the
-// reduce kernel merges splits in split order, so there are no float atomics (sparkinfer
-// server README, "Determinism": the decode path has none).  A row whose keys all fall in split
-// 0 is finished here and skips the reduce.
+// into splits whose size depends on that sequence's length alone, and one wave reduces one
+// item, (split, KV head, row tile of <= 16*NT rows), to a partial (max, sum, unnormalised
+// output); the reduce kernel merges splits in split order, so there are no float atomics
+// (sparkinfer server README, "Determinism": the decode path has none).  A row whose keys all
+// fall in split 0 is finished here and skips the reduce.
 //
-// Workgroup = 4 waves over one (row tile of <= 16*NT rows, split, KV head, sequence).  Rows are
-// (token, head-in-group) pairs, so the G q-heads sharing a KV head use one read of K/V.  Each
-// wave takes a contiguous quarter of the split and walks it in 32-key chunks:
+// Scheduling: persistent waves.  The grid holds as many one-wave workgroups as the GPU keeps
+// resident at once, and each wave takes items from a ticket counter (one integer atomic per
+// item) until none are left.  Items are numbered sequence by sequence and found from prefix
+// sums of per-sequence item counts held one sequence per lane.  While a wave streams one item,
+// the ticket and block ids of its next item are already in registers, so it moves from the
+// last chunk of one item to the loads of the next with no metadata round trip, and no slot of
+// the GPU waits on a workgroup that turns out to have no keys.  Which wave computes an item
+// never changes that item's result.
+//
+// Per item, rows are (token, head-in-group) pairs, so the G q-heads sharing a KV head use one
+// read of K/V, walked in 32-key chunks:
 //   S^T[key][row] = K[key][:] . Q[row][:]          2 x (D/32) v_mfma_f32_16x16x32_bf16 / N-tile
 //   online softmax on the fp32 scores (exp2, scale*log2e folded in)
 //   O^T[dim][row] += V^T[dim][key] . P^T[key][row]  D/16 MFMAs per N-tile
@@ -19,13 +27,18 @@
 // tokens, V tiles are dims-major), every byte of a tile read once, and every load instruction
 // reads one tile from a wave-uniform base: 1 KiB contiguous for K, 512 bytes for V.  Loads are
 // double-buffered: chunk i+1 is in flight while chunk i is computed (32 KiB per wave), and the
-// block ids of the wave's tiles are read once into lanes and broadcast with v_readlane, so no
+// block ids of the item's tiles are read once into lanes and broadcast with v_readlane, so no
 // table read sits between a chunk and its data.  Score tile h of a chunk is pool tile h, so a
 // lane of the score output holds keys 4*g .. 4*g+3 of both tiles for its row; the PV product
 // takes exactly those 8 keys as its k-slice (V^T rows read as two 8-byte runs), so P stays in
-// registers.  The 4 waves' partials merge through LDS at the end.
+// registers.
+//
+// Forced splits longer than 2048 keys (a test and tuning knob) run a non-persistent variant:
+// 4 waves share one split and merge their partials through LDS.
 #include "common.h"
 #include "kernels.h"
+
+#include <algorithm>
 
 namespace kvp {
 
@@ -35,11 +48,21 @@ __device__ __forceinline__ bf16x8 load16(const uint16_t* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
 }
 
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Pool reads are streamed: each K/V byte is read once per call (a whole GQA group shares the
+// wave), so the loads carry the nontemporal hint, which measurably raises the rate at which
+// random 4 KiB tiles come in from HBM over plain loads.
+__device__ __forceinline__ bf16x8 stream16(const uint16_t* p) {
+  return __builtin_bit_cast(bf16x8, __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p)));
+}
+__device__ __forceinline__ u32x2 stream8(const uint16_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+}
+
 __device__ __forceinline__ floatx4 mfma16(bf16x8 a, bf16x8 b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
-
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 template <int D>
 struct Chunk {
@@ -47,66 +70,74 @@ struct Chunk {
   u32x2 v[2][D / 16];   // V^T operand halves: keys 4g..4g+3 of pool tile 0 and of tile 1
 };
 
-}  // namespace
+// One work item: split `sp` of sequence s for KV head kvh and row tile rt.
+struct Item {
+  int s, kvh, rt, sp;
+  int L, T;     // keys of the sequence, query rows (tokens) of the sequence
+  int q_start;  // index of the sequence's first query token in q / out
+  int kb, ke;   // the item's keys [kb, ke): its split, cut at its last row's position + 1
+  int split;    // keys per split of this sequence
+};
 
-// NW: waves per workgroup sharing one split (their partials merge through LDS); NW == 1 gives
-// one independent wave per split, which the dispatcher balances at the finest grain.
-// RELOAD: the wave's span may exceed 128 tiles (calls without splits), so block ids are
-// reloaded every 128 tiles.  Without it (split mode, span <= 2048 keys per wave) they are read
-// once, and no load in the chunk loop can force a wait on the chunks in flight.
+// Key range of an item; false if no row of the item sees a key of its split.
+template <int NT>
+__device__ __forceinline__ bool item_keys(const AttnArgs& a, Item& it) {
+  const int rows = it.T * a.group;
+  const int r0 = it.rt * 16 * NT;
+  if (r0 >= rows) return false;
+  const int p_last = it.L - it.T + (min(r0 + 16 * NT, rows) - 1) / a.group;
+  it.split = seq_split(a, it.L);
+  it.kb = 0;
+  it.ke = min(it.L, p_last + 1);
+  if (a.split_mode) {
+    it.kb = it.sp * it.split;
+    it.ke = min(it.ke, it.kb + it.split);
+  }
+  return it.kb < it.ke;
+}
+
+// Block id of tile (wb/16 + base + lane) of sequence s, the tile index clamped into the wave's
+// ntile tiles and the position into the item's keys (ke >= 1), so the read is always in the
+// sequence's own table row.
+__device__ __forceinline__ int tile_block_id(const AttnArgs& a, int s, int wb, int ntile, int ke,
+                                             int base) {
+  const int lane = threadIdx.x & (WAVE - 1);
+  const int32_t* tbl = a.block_tables + (size_t)s * a.max_blocks_per_seq;
+  const int ti = min(base + lane, max(ntile - 1, 0));
+  return tbl[min(((wb >> 4) + ti) << 4, ke - 1) >> a.block_shift];
+}
+
+// Reduces the keys [wb, we) of item `it` for one wave.  ids0/ids1: lane i holds the block id of
+// the wave's tile i / 64 + i (from tile_block_id).  NW: waves sharing the item, whose partials
+// merge through LDS (NW == 1: the wave finishes the item from registers).  RELOAD: the wave's
+// keys may span more than 128 tiles, so block ids are reloaded every 128 tiles; without it no
+// load in the chunk loop can force a wait on the chunks in flight.
 template <int D, int NT, bool RELOAD, int NW>
-__global__ __launch_bounds__(64 * NW) void attn_split_mfma_kernel(AttnArgs a) {
+__device__ __forceinline__ void run_item(const AttnArgs& a, const Item& it, int wave, int wb,
+                                         int we, int ids0, int ids1) {
   constexpr int KK = D / 32;  // 32-dim steps of the score product
   constexpr int MT = D / 16;  // 16-dim tiles of the output
-  // The wave index is uniform within a wave: say so, so that every per-wave bound below lives
-  // in scalar registers and the chunk loop is a scalar loop.
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = threadIdx.x & (WAVE - 1);
   const int n = lane & 15, g = lane >> 4;
-  const int s = blockIdx.z, kvh = blockIdx.y;
-  const int rt = blockIdx.x % a.row_tiles, sp = blockIdx.x / a.row_tiles;
-  int L, T;
-  seq_lens(a, s, L, T);
+  const int s = it.s, kvh = it.kvh, sp = it.sp, L = it.L, T = it.T, q_start = it.q_start;
+  const int kb = it.kb, split = it.split;
   const int G = a.group;
   const int rows = T * G;
-  const int r0 = rt * 16 * NT;
-  if (r0 >= rows) return;
-  const int p_last = L - T + (min(r0 + 16 * NT, rows) - 1) / G;
-  const int split = seq_split(a, L);
-  int kb = 0, ke = min(L, p_last + 1);
-  if (a.split_mode) {
-    kb = sp * split;
-    ke = min(ke, kb + split);
-  }
-  if (kb >= ke) return;
-
-  // This wave's keys: a contiguous, 32-aligned quarter of [kb, ke).
-  const int span = (ke - kb + NW * 32 - 1) / (NW * 32) * 32;
-  const int wb = kb + wave * span;
-  const int we = min(ke, wb + span);
+  const int r0 = it.rt * 16 * NT;
   const int nch = wb < we ? (we - wb + 31) >> 5 : 0;
   const int ntile = wb < we ? (we - wb + 15) >> 4 : 0;
   const int tile0 = wb >> 4;
-
-  const int32_t* tbl = a.block_tables + (size_t)s * a.max_blocks_per_seq;
   const uint16_t* kl = reinterpret_cast<const uint16_t*>(a.k_layer);
   const uint16_t* vl = reinterpret_cast<const uint16_t*>(a.v_layer);
   const int bmask = a.block_size - 1;
 
-  // Lane i of ids[k] holds the block id of the wave's tile tb + 64*k + i (128 tiles per batch).
   int tb = 0;
-  auto load_id = [&](int base) -> int {
-    // Unconditional load with the index clamped into the sequence's own blocks (ke >= 1).
-    const int ti = min(base + lane, max(ntile - 1, 0));
-    return tbl[(min((tile0 + ti) << 4, ke - 1)) >> a.block_shift];
-  };
-  int ids0 = load_id(0), ids1 = load_id(64);
   auto tile_off = [&](int ti) -> size_t {
     ti = min(ti, ntile - 1);  // past the end: re-read the last tile (a cache hit; masked out)
     if (RELOAD && ti - tb >= 128) {
       tb = ti & ~127;
-      ids0 = load_id(tb);
-      ids1 = load_id(tb + 64);
+      ids0 = tile_block_id(a, s, wb, ntile, it.ke, tb);
+      ids1 = tile_block_id(a, s, wb, ntile, it.ke, tb + 64);
     }
     const int r = ti - tb;
     const int blk = r < 64 ? __builtin_amdgcn_readlane(ids0, r) : __builtin_amdgcn_readlane(ids1, r - 64);
@@ -120,19 +151,12 @@ __global__ __launch_bounds__(64 * NW) void attn_split_mfma_kernel(AttnArgs a) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) c.k[h][kk] = load16(kt[h] + ((4 * kk + g) * 16 + n) * 8);
+      for (int kk = 0; kk < KK; ++kk) c.k[h][kk] = stream16(kt[h] + ((4 * kk + g) * 16 + n) * 8);
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt)
-        c.v[h][mt] = *reinterpret_cast<const u32x2*>(vt[h] + (16 * mt + n) * 16 + 4 * g);
+      for (int mt = 0; mt < MT; ++mt) c.v[h][mt] = stream8(vt[h] + (16 * mt + n) * 16 + 4 * g);
     }
   };
 
-  // The q_lens prefix sum waits on its loads (and the block ids): do it before any chunk is in
-  // flight, so that the chunk loop only ever waits for the chunk it computes.
-  const int q_start = wave_prefix_total(a.q_lens, s);
-  // vmcnt(0) on every path (encoding: vmcnt 0, expcnt 7, lgkmcnt 15), so the compiler knows the
-  // block ids have arrived and never waits for them inside the chunk loop.
-  __builtin_amdgcn_s_waitcnt(0x0F70);
   Chunk<D> bufA, bufB;
   if (nch) load_chunk(bufA, 0);
 
@@ -229,13 +253,22 @@ __global__ __launch_bounds__(64 * NW) void attn_split_mfma_kernel(AttnArgs a) {
     }
   };
 
-  // Double-buffered walk: the loads of chunk i+1 are issued before chunk i is computed.  Loads
-  // past the last chunk re-read it (cache hits) so that no branch sits between issue and use.
-  for (int ci = 0; ci < nch; ci += 2) {
-    load_chunk(bufB, min(ci + 1, nch - 1));
+  // Double-buffered walk: the loads of chunk i+1 are issued before chunk i is computed.  The
+  // last one or two chunks are peeled off, so that no load is left in flight after the walk
+  // (the registers it would land in are reused right after).
+  int ci = 0;
+  for (; ci + 2 < nch; ci += 2) {
+    load_chunk(bufB, ci + 1);
     compute(bufA, ci);
-    load_chunk(bufA, min(ci + 2, nch - 1));
-    if (ci + 1 < nch) compute(bufB, ci + 1);
+    load_chunk(bufA, ci + 2);
+    compute(bufB, ci + 1);
+  }
+  if (ci + 1 < nch) {
+    load_chunk(bufB, ci + 1);
+    compute(bufA, ci);
+    compute(bufB, ci + 1);
+  } else if (ci < nch) {
+    compute(bufA, ci);
   }
 
   if constexpr (NW == 1) {
@@ -266,90 +299,269 @@ __global__ __launch_bounds__(64 * NW) void attn_split_mfma_kernel(AttnArgs a) {
           *reinterpret_cast<floatx4*>(a.part_o + slot * D + 16 * mt + 4 * g) = o[nt][mt];
       }
     }
-    return;
-  }
-
-  // ---- merge the NW waves (rows are the same, keys differ) --------------------------------
-  __shared__ float s_m[NW][NT][16], s_l[NW][NT][16];
-  __shared__ floatx4 s_o[NW][MT][64];
-  float lw[NT];
+  } else {
+    // ---- merge the NW waves (rows are the same, keys differ) --------------------------------
+    __shared__ float s_m[NW][NT][16], s_l[NW][NT][16];
+    __shared__ floatx4 s_o[NW][MT][64];
+    float lw[NT];
 #pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    lw[nt] = xrow_sum(l_run[nt]);
-    if (g == 0) {
-      s_m[wave][nt][n] = m_run[nt];
-      s_l[wave][nt][n] = lw[nt];
-    }
-  }
-  __syncthreads();
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    float M = -INFINITY;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, s_m[w][nt][n]);
-    float Lsum = 0.f;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      const float mw = s_m[w][nt][n];
-      Lsum += mw == -INFINITY ? 0.f : s_l[w][nt][n] * fast_exp2((mw - M) * c);
-    }
-    const float myscale = m_run[nt] == -INFINITY ? 0.f : fast_exp2((m_run[nt] - M) * c);
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) s_o[wave][mt][lane] = o[nt][mt] * myscale;
-    __syncthreads();
-    const bool row_ok = prow[nt] >= kb;  // a real row that sees a key of this split
-    const bool final_here = !a.split_mode || prow[nt] < split;
-    if (row_ok) {
-      if (final_here) {
-        const float inv = 1.f / Lsum;
-        uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + rh[nt] * D;
-        for (int mt = wave; mt < MT; mt += NW) {
-          floatx4 v = s_o[0][mt][lane];
-#pragma unroll
-          for (int w = 1; w < NW; ++w) v += s_o[w][mt][lane];
-          v *= inv;
-          const uint32_t w0 = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
-          const uint32_t w1 = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
-          *reinterpret_cast<uint2*>(op + 16 * mt + 4 * g) = make_uint2(w0, w1);
-        }
-      } else {
-        const size_t slot = rh[nt] * a.max_splits + sp;
-        if (wave == 0 && g == 0) {
-          a.part_ml[2 * slot] = M;
-          a.part_ml[2 * slot + 1] = Lsum;
-        }
-        for (int mt = wave; mt < MT; mt += NW) {
-          floatx4 v = s_o[0][mt][lane];
-#pragma unroll
-          for (int w = 1; w < NW; ++w) v += s_o[w][mt][lane];
-          *reinterpret_cast<floatx4*>(a.part_o + slot * D + 16 * mt + 4 * g) = v;
-        }
+    for (int nt = 0; nt < NT; ++nt) {
+      lw[nt] = xrow_sum(l_run[nt]);
+      if (g == 0) {
+        s_m[wave][nt][n] = m_run[nt];
+        s_l[wave][nt][n] = lw[nt];
       }
     }
     __syncthreads();
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      float M = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) M = fmaxf(M, s_m[w][nt][n]);
+      float Lsum = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float mw = s_m[w][nt][n];
+        Lsum += mw == -INFINITY ? 0.f : s_l[w][nt][n] * fast_exp2((mw - M) * c);
+      }
+      const float myscale = m_run[nt] == -INFINITY ? 0.f : fast_exp2((m_run[nt] - M) * c);
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) s_o[wave][mt][lane] = o[nt][mt] * myscale;
+      __syncthreads();
+      const bool row_ok = prow[nt] >= kb;  // a real row that sees a key of this split
+      const bool final_here = !a.split_mode || prow[nt] < split;
+      if (row_ok) {
+        if (final_here) {
+          const float inv = 1.f / Lsum;
+          uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + rh[nt] * D;
+          for (int mt = wave; mt < MT; mt += NW) {
+            floatx4 v = s_o[0][mt][lane];
+#pragma unroll
+            for (int w = 1; w < NW; ++w) v += s_o[w][mt][lane];
+            v *= inv;
+            const uint32_t w0 = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
+            const uint32_t w1 = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+            *reinterpret_cast<uint2*>(op + 16 * mt + 4 * g) = make_uint2(w0, w1);
+          }
+        } else {
+          const size_t slot = rh[nt] * a.max_splits + sp;
+          if (wave == 0 && g == 0) {
+            a.part_ml[2 * slot] = M;
+            a.part_ml[2 * slot + 1] = Lsum;
+          }
+          for (int mt = wave; mt < MT; mt += NW) {
+            floatx4 v = s_o[0][mt][lane];
+#pragma unroll
+            for (int w = 1; w < NW; ++w) v += s_o[w][mt][lane];
+            *reinterpret_cast<floatx4*>(a.part_o + slot * D + 16 * mt + 4 * g) = v;
+          }
+        }
+      }
+      __syncthreads();
+    }
   }
 }
 
-hipError_t launch_attn_split_mfma(const AttnArgs& a, int head_dim, int rows_per_tile,
-                                  int grid_x, hipStream_t st) {
-  dim3 grid(grid_x, a.num_kv_heads, a.num_seqs);
-  // One wave per split (splits of at most 2048 keys); longer fixed splits and calls without
-  // splits use 4 waves per workgroup.
-  const bool one_wave = a.split_mode && a.split_tokens <= 2048;
-  const bool reload = !a.split_mode || a.split_tokens > 8192;
-#define KVP_SPLIT_LAUNCH(D, NT)                                                         \
-  (one_wave ? attn_split_mfma_kernel<D, NT, false, 1><<<grid, 64, 0, st>>>(a)           \
-   : reload ? attn_split_mfma_kernel<D, NT, true, 4><<<grid, 256, 0, st>>>(a)           \
-            : attn_split_mfma_kernel<D, NT, false, 4><<<grid, 256, 0, st>>>(a))
-  if (head_dim == 128) {
-    if (rows_per_tile <= 16) KVP_SPLIT_LAUNCH(128, 1);
-    else KVP_SPLIT_LAUNCH(128, 2);
-  } else {
-    if (rows_per_tile <= 16) KVP_SPLIT_LAUNCH(64, 1);
-    else KVP_SPLIT_LAUNCH(64, 2);
+// ---- persistent scheduling ----------------------------------------------------------------
+
+// Inclusive prefix sum over the wave.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & (WAVE - 1);
+#pragma unroll
+  for (int d = 1; d < WAVE; d <<= 1) {
+    const int t = __shfl_up(v, d);
+    if (lane >= d) v += t;
   }
-#undef KVP_SPLIT_LAUNCH
+  return v;
+}
+
+// Items of one sequence: splits x KV heads x row tiles, bounded by the launch's workspace
+// geometry (max_splits, row_tiles) whatever the device metadata says.
+template <int NT>
+__device__ __forceinline__ int seq_items(const AttnArgs& a, int L, int T) {
+  if (T <= 0) return 0;
+  const int split = seq_split(a, L);
+  const int ns = min(L / split + (L % split != 0), a.max_splits);
+  const int rts = min((T * a.group + 16 * NT - 1) / (16 * NT), a.row_tiles);
+  return ns * a.num_kv_heads * rts;
+}
+
+// The item table of 64 consecutive sequences, sequence base + i in lane i.
+struct SeqGroup {
+  int base;       // first sequence of the group
+  int item_base;  // items of the sequences before the group
+  int q_base;     // query tokens of the sequences before the group
+  int items;      // items of the group
+  int q_total;    // query tokens of the group
+  int incl;       // lane: items of sequences base .. base + lane
+  int L, T, qx;   // lane: its lengths and the query tokens of the group's sequences before it
+};
+
+template <int NT>
+__device__ __forceinline__ void load_group(const AttnArgs& a, SeqGroup& gp, int base) {
+  const int lane = threadIdx.x & (WAVE - 1);
+  const int s = base + lane;
+  const int sc = min(s, a.num_seqs - 1);
+  int L, T;
+  seq_lens(a, sc, L, T);
+  int q = max(0, a.q_lens[sc]);  // row offsets count the raw q_lens, like the other kernels
+  if (s >= a.num_seqs) L = T = q = 0;
+  gp.base = base;
+  gp.incl = wave_incl_scan(seq_items<NT>(a, L, T));
+  const int qi = wave_incl_scan(q);
+  gp.qx = qi - q;
+  gp.L = L;
+  gp.T = T;
+  gp.items = __builtin_amdgcn_readlane(gp.incl, WAVE - 1);
+  gp.q_total = __builtin_amdgcn_readlane(qi, WAVE - 1);
+}
+
+// Decodes ticket t (wave-uniform) into an item; false once t is past the last item.  Within a
+// sequence the KV head varies fastest, then the row tile, then the split.
+template <int NT>
+__device__ __forceinline__ bool find_item(const AttnArgs& a, SeqGroup& gp, int t, Item& it) {
+  if (t < gp.item_base) {  // tickets of a wave normally increase; restart the scan if not
+    gp.item_base = 0;
+    gp.q_base = 0;
+    load_group<NT>(a, gp, 0);
+  }
+  while (t - gp.item_base >= gp.items) {
+    if (gp.base + WAVE >= a.num_seqs) return false;
+    gp.item_base += gp.items;
+    gp.q_base += gp.q_total;
+    load_group<NT>(a, gp, gp.base + WAVE);
+  }
+  const int r_in = t - gp.item_base;
+  const int j = __builtin_popcountll(__builtin_amdgcn_ballot_w64(gp.incl <= r_in));
+  int r = r_in - (j ? __builtin_amdgcn_readlane(gp.incl, j - 1) : 0);
+  it.s = gp.base + j;
+  it.L = __builtin_amdgcn_readlane(gp.L, j);
+  it.T = __builtin_amdgcn_readlane(gp.T, j);
+  it.q_start = gp.q_base + __builtin_amdgcn_readlane(gp.qx, j);
+  const int rts = min((it.T * a.group + 16 * NT - 1) / (16 * NT), a.row_tiles);
+  it.kvh = r % a.num_kv_heads;
+  r /= a.num_kv_heads;
+  it.rt = r % rts;
+  it.sp = r / rts;
+  return true;
+}
+
+}  // namespace
+
+// Wave w of W takes items w, w + W, w + 2W, ... in increasing order.  W is what the GPU holds at
+// once, so all waves start together; a wave's next item is known in advance, and its block ids
+// are loaded before the current item's chunks.
+template <int D, int NT>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2 : 1)))
+void attn_split_persist_kernel(AttnArgs a) {
+  const int W = gridDim.x;
+  SeqGroup gp;
+  gp.item_base = 0;
+  gp.q_base = 0;
+  load_group<NT>(a, gp, 0);
+  Item cur;
+  int t = blockIdx.x;
+  bool have = find_item<NT>(a, gp, t, cur);
+  bool cur_keys = have && item_keys<NT>(a, cur);
+  int ids0 = 0, ids1 = 0;
+  if (have) {
+    const int nt = (cur.ke - cur.kb + 15) >> 4;
+    ids0 = tile_block_id(a, cur.s, cur.kb, nt, cur.ke, 0);
+    ids1 = tile_block_id(a, cur.s, cur.kb, nt, cur.ke, 64);
+  }
+  while (have) {
+    t += W;
+    Item nxt;
+    const bool nhave = t < (1 << 30) && find_item<NT>(a, gp, t, nxt);
+    const bool nkeys = nhave && item_keys<NT>(a, nxt);
+    // Unconditional loads (the current item's ids again when there is no next item), so that
+    // no branch around a load makes the chunk loop wait for these.
+    const int ps = nhave ? nxt.s : cur.s;
+    const int pb = nhave ? nxt.kb : cur.kb;
+    const int pe = nhave ? nxt.ke : cur.ke;
+    const int pt = (pe - pb + 15) >> 4;
+    const int nid0 = tile_block_id(a, ps, pb, pt, pe, 0);
+    const int nid1 = tile_block_id(a, ps, pb, pt, pe, 64);
+    if (cur_keys) run_item<D, NT, false, 1>(a, cur, 0, cur.kb, cur.ke, ids0, ids1);
+    if (!nhave) break;
+    cur = nxt;
+    cur_keys = nkeys;
+    ids0 = nid0;
+    ids1 = nid1;
+  }
+}
+
+// Forced splits longer than 2048 keys: one workgroup of 4 waves per item, on the grid
+// x = (KV head, sequence, row tile) with the KV head fastest, y = split.
+template <int D, int NT, bool RELOAD>
+__global__ __launch_bounds__(256) void attn_split_mfma_kernel(AttnArgs a) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  Item it;
+  it.kvh = blockIdx.x % a.num_kv_heads;
+  const int pair = blockIdx.x / a.num_kv_heads;
+  it.s = pair % a.num_seqs;
+  it.rt = pair / a.num_seqs;
+  it.sp = blockIdx.y;
+  seq_lens(a, it.s, it.L, it.T);
+  if (!item_keys<NT>(a, it)) return;
+  // This wave's keys: a contiguous, 32-aligned quarter of [kb, ke).
+  const int span = (it.ke - it.kb + 4 * 32 - 1) / (4 * 32) * 32;
+  const int wb = it.kb + wave * span;
+  const int we = min(it.ke, wb + span);
+  const int ntile = wb < we ? (we - wb + 15) >> 4 : 0;
+  const int ids0 = tile_block_id(a, it.s, wb, ntile, it.ke, 0);
+  const int ids1 = tile_block_id(a, it.s, wb, ntile, it.ke, 64);
+  it.q_start = wave_prefix_total(a.q_lens, it.s);
+  // vmcnt(0) (encoding: vmcnt 0, expcnt 7, lgkmcnt 15), so the compiler knows the block ids
+  // have arrived and never waits for them inside the chunk loop.
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+  run_item<D, NT, RELOAD, 4>(a, it, wave, wb, we, ids0, ids1);
+}
+
+namespace {
+
+// Workgroups of the persistent kernel the GPU holds at once (per CU, from the occupancy API).
+template <int D, int NT>
+int persist_blocks_per_cu() {
+  static const int n = [] {
+    int b = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+            &b, reinterpret_cast<const void*>(&attn_split_persist_kernel<D, NT>), 64, 0) != hipSuccess)
+      return 0;
+    return b;
+  }();
+  return n;
+}
+
+template <int D, int NT>
+hipError_t launch_split(const AttnArgs& a, int splits, int num_cus, hipStream_t st) {
+  const bool persistent = a.split_mode && a.split_tokens <= 2048;
+  if (persistent) {
+    const int per_cu = persist_blocks_per_cu<D, NT>();
+    if (per_cu <= 0) return hipErrorInvalidConfiguration;
+    const long long items = (long long)a.num_seqs * a.num_kv_heads * a.row_tiles * splits;
+    const long long waves = std::min<long long>(items, (long long)per_cu * std::max(num_cus, 1));
+    attn_split_persist_kernel<D, NT><<<(unsigned)waves, 64, 0, st>>>(a);
+  } else {
+    if (splits > 65535) return hipErrorInvalidConfiguration;
+    const dim3 grid(a.num_kv_heads * a.num_seqs * a.row_tiles, splits, 1);
+    if (!a.split_mode || a.split_tokens > 8192)
+      attn_split_mfma_kernel<D, NT, true><<<grid, 256, 0, st>>>(a);
+    else
+      attn_split_mfma_kernel<D, NT, false><<<grid, 256, 0, st>>>(a);
+  }
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_attn_split_mfma(const AttnArgs& a, int head_dim, int rows_per_tile, int splits,
+                                  int num_cus, hipStream_t st) {
+  if (head_dim == 128)
+    return rows_per_tile <= 16 ? launch_split<128, 1>(a, splits, num_cus, st)
+                               : launch_split<128, 2>(a, splits, num_cus, st);
+  return rows_per_tile <= 16 ? launch_split<64, 1>(a, splits, num_cus, st)
+                             : launch_split<64, 2>(a, splits, num_cus, st);
 }
 
 }  // namespace kvp

@@ -142,15 +142,14 @@ struct AttnArgs {
 };
 
 // Keys per split of a sequence with L keys (split mode): a fixed count if the caller set one,
-// else the smallest power of two >= floor(L/128) within [256, 2048] (at most ~128 splits per
-// sequence up to 262144 keys).  It depends on the sequence's own length only, so its reduction
-// order does too.
+// else ceil(L/128) rounded up to a multiple of 32 and clamped to [256, 2048].  That gives at
+// most 128 splits up to 262144 keys (so one long sequence's splits fit the GPU in one pass, with
+// no sliver of a split left over), and it depends on the sequence's own length only, so its
+// reduction order does too.
 __device__ __forceinline__ int seq_split(const AttnArgs& a, int L) {
   if (a.split_tokens > 0) return a.split_tokens;
-  const int t = L >> 7;
-  int sp = 256;
-  while (sp < t && sp < 2048) sp <<= 1;
-  return sp;
+  const int per = (L >> 7) + ((L & 127) != 0);  // ceil(L / 128) without overflow
+  return min(max((per + 31) & ~31, 256), 2048);
 }
 
 // Clamped per-sequence lengths (bad metadata must never index out of bounds).

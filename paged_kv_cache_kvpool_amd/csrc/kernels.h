@@ -32,10 +32,12 @@ struct CopyArgs {
 hipError_t launch_append(const AppendArgs& a, int elt_bytes, int max_q_len, hipStream_t st);
 hipError_t launch_copy_blocks(const CopyArgs& a, int n, int num_layers, hipStream_t st);
 
-// Split-K attention on the matrix cores (bf16): one wave per (row tile of <= 32 rows, split,
-// KV head, sequence).  Used for decode and verification, and for any call without splits.
+// Split-K attention on the matrix cores (bf16), split mode: items of (row tile of <= 32 rows,
+// split, KV head, sequence) dealt round-robin to persistent waves (num_cus sizes the grid), or,
+// for forced splits longer than 2048 keys, one 4-wave workgroup per item.  `splits`: most
+// splits of any sequence (at most 65535 for the 4-wave variant).
 hipError_t launch_attn_split_mfma(const AttnArgs& a, int head_dim, int rows_per_tile,
-                                  int grid_x, hipStream_t st);
+                                  int splits, int num_cus, hipStream_t st);
 // Vector-ALU attention (fp32 and bf16), one wave per (row tile of <= 8 rows, split, KV head,
 // sequence).
 hipError_t launch_attn_vec(const AttnArgs& a, int elt_bytes, int head_dim, int rows_per_tile,

@@ -65,8 +65,9 @@ int split_tokens() {
 // Upper bound of a sequence's split count over all lengths <= max_ctx.
 int max_split_count(int split, int max_ctx) {
   if (split > 0) return std::max(1, (max_ctx + split - 1) / split);
-  // split >= floor(L/128) gives at most 129 splits; past the clamp, L/2048.
-  return std::max(std::max(1, std::min(129, (max_ctx + 255) / 256)), (max_ctx + 2047) / 2048);
+  // The rule (ceil(L/128) rounded up to 32, within [256, 2048]) gives at most
+  // min(128, ceil(L/256)) splits up to 262144 keys and ceil(L/2048) past that.
+  return std::max(std::max(1, std::min(128, (max_ctx + 255) / 256)), (max_ctx + 2047) / 2048);
 }
 
 // Split mode serves decode and verification (few query rows per KV head): the context is cut
@@ -376,6 +377,7 @@ Plan make_plan(const kvpool* p, int32_t num_q_heads, int32_t total_q, int32_t ma
   pl.split = split_tokens();
   pl.max_splits = pl.split_mode ? max_split_count(pl.split, max_ctx_len) : 1;
   if (pl.split_mode) {
+    // [partial outputs, fp32][partial (max, sum) pairs, fp32]
     const size_t slots = (size_t)total_q * num_q_heads * pl.max_splits;
     const size_t o_bytes = (slots * p->head_dim * 4 + 255) / 256 * 256;
     pl.bytes = o_bytes + slots * 2 * 4;
@@ -415,6 +417,8 @@ int kvattn_forward(kvpool_t* pool, int32_t layer, const void* q, void* out, int3
   if (!(scale == scale) || scale == INFINITY || scale == -INFINITY) return fail(KV_EINVAL, "scale must be finite");
   if (num_seqs == 0 || total_q == 0 || max_q_len == 0 || max_ctx_len == 0) return ok();
   if (max_q_len > max_ctx_len) return fail(KV_EINVAL, "max_q_len > max_ctx_len");
+  // Every context length is capped at max_blocks_per_seq * block_size: no key, no row.
+  if (max_blocks_per_seq == 0) return ok();
   if (!q || !out || !block_tables || !ctx_lens || !q_lens)
     return fail(KV_EINVAL, "NULL device pointer");
   if (!aligned16(q) || !aligned16(out)) return fail(KV_EINVAL, "q and out must be 16-byte aligned");
@@ -422,6 +426,12 @@ int kvattn_forward(kvpool_t* pool, int32_t layer, const void* q, void* out, int3
   if (current_device_matches(pool) != hipSuccess)
     return fail(KV_EINVAL, "current HIP device is not the pool's device %d", pool->device);
   const Plan pl = make_plan(pool, num_q_heads, total_q, max_ctx_len, max_q_len);
+  if (pl.max_splits > 65535)
+    return fail(KV_ERANGE, "%d splits per sequence exceed the launch grid (65535)", pl.max_splits);
+  if ((long long)total_q * num_q_heads >= (1ll << 31))
+    return fail(KV_ERANGE, "total_q * num_q_heads must stay below 2^31");
+  if ((long long)num_seqs * pool->num_kv_heads * 8 * pl.max_splits >= (1ll << 30))
+    return fail(KV_ERANGE, "too many work items (splits x KV heads x row tiles) in one call");
   if (pl.bytes) {
     if (!workspace) return fail(KV_ENOMEM, "workspace of %zu bytes required", pl.bytes);
     if (workspace_bytes < pl.bytes)
@@ -447,9 +457,9 @@ int kvattn_forward(kvpool_t* pool, int32_t layer, const void* q, void* out, int3
   a.ctx_lens = ctx_lens;
   a.q_lens = q_lens;
   const size_t slots = (size_t)total_q * num_q_heads * pl.max_splits;
-  a.part_o = static_cast<float*>(workspace);
-  a.part_ml = pl.bytes ? reinterpret_cast<float*>(static_cast<char*>(workspace) +
-                                                  (slots * pool->head_dim * 4 + 255) / 256 * 256)
+  char* ws = static_cast<char*>(workspace);
+  a.part_o = pl.bytes ? reinterpret_cast<float*>(ws) : nullptr;
+  a.part_ml = pl.bytes ? reinterpret_cast<float*>(ws + (slots * pool->head_dim * 4 + 255) / 256 * 256)
                        : nullptr;
   a.num_seqs = num_seqs;
   a.total_q = total_q;
@@ -477,7 +487,7 @@ int kvattn_forward(kvpool_t* pool, int32_t layer, const void* q, void* out, int3
   } else if (pl.split_mode) {
     const int rpt = rows <= 16 ? 16 : 32;
     a.row_tiles = (rows + rpt - 1) / rpt;
-    e = timed(K_SPLIT_MFMA, st, [&] { return kvp::launch_attn_split_mfma(a, pool->head_dim, rpt, a.row_tiles * pl.max_splits, st); });
+    e = timed(K_SPLIT_MFMA, st, [&] { return kvp::launch_attn_split_mfma(a, pool->head_dim, rpt, pl.max_splits, pool->num_cus, st); });
   } else {
     int ntw = kvp::prefill_rows_per_wave_choice(rows, num_seqs * pool->num_kv_heads, pool->num_cus);
     if (const char* v = getenv("KVATTN_PREFILL_NTW")) ntw = std::max(2, std::min(5, atoi(v)));  // sweeps
