@@ -3,19 +3,23 @@
 // (sparkinfer server README, "Automatic prefix cache": only the suffix is prefilled, over the
 // shared prefix blocks; "Request isolation & continuous batching": prefill in chunks).
 //
-// Workgroup = 4 waves over one row tile of one (sequence, KV head); a wave owns 16*NTW rows
+// Workgroup = W waves (4..12) over one row tile of one (sequence, KV head); a wave owns 32 rows
 // (row = token * G + head-in-group, so every row of a workgroup reads the same K/V).  K/V are
 // walked in tiles of 64 keys = 4 pool tiles, each streamed verbatim from the pool into LDS with
-// global_load_lds (no register staging; the pool's tile layout is already the order the matrix
-// cores read: K as 16-byte dim chunks of 16 tokens, V dims-major) through 3 LDS stages: tiles
-// j+1 and j+2 are in flight while tile j is computed; one vmcnt wait and one barrier per tile.
-// Per wave and tile:
-//   S^T[key][row] = K . Q^T   4 key tiles x NTW row tiles x D/32 v_mfma_f32_16x16x32_bf16,
-//                             each K operand (one conflict-free ds_read_b128) feeding NTW MFMAs
-//   causal mask only on tiles that reach past the wave's first row; online softmax in fp32
-//   O^T[dim][row] += V^T . P^T   2 key halves x D/16 dim tiles x NTW; P never leaves registers
-//                             (a lane of the score tile already holds the 8 keys the PV k-slice
-//                             needs: keys 4g..4g+3 of two pool tiles)
+// global_load_lds (no register staging; the pool's tile layout is the order the matrix cores
+// read) through 3 LDS stages: tiles j+1 and j+2 are in flight while tile j is computed; one
+// vmcnt wait and one barrier per tile.  Each 64-key tile is two 32-key blocks; per wave and
+// block, on v_mfma_f32_32x32x16_bf16 (the 32x32 shape runs at twice the rate of 16x16x32 on
+// gfx950):
+//   S^T[key][row] = K . Q^T      D/16 MFMAs, K rows read from LDS in a key order (bits 2 and 3
+//                                of the key index swapped) that leaves each lane holding, for
+//                                its row, exactly the 8 + 8 keys the PV step takes as its
+//                                k-slices, so P goes from the score registers to the PV operand
+//                                with a convert and nothing else
+//   causal mask only on blocks that reach past the wave's first row or the context (V slots
+//   past the context are zeroed in LDS once, in the last tile); online softmax in fp32 with
+//   exp2 and a lazily raised running max; row sums on the VALU
+//   O^T[dim][row] += V^T . P^T   2 k-steps x D/32 MFMAs
 // The logical workgroup order is remapped so that the row tiles of one (sequence, KV head) run
 // on the same XCD (workgroups are dealt to the 8 XCDs round-robin) and share its L2.
 #include "common.h"
@@ -25,10 +29,10 @@ namespace kvp {
 
 namespace {
 
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
 
-__device__ __forceinline__ floatx4 mfma16(bf16x8 a, bf16x8 b, floatx4 c) {
-  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+__device__ __forceinline__ floatx16 mfma32(bf16x8 a, bf16x8 b, floatx16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
 constexpr int NXCD = 8;
@@ -57,18 +61,33 @@ __device__ __forceinline__ int xcd_logical(int id, int n) {
   return x < r ? x * (q + 1) + k : r * (q + 1) + (x - r) * q + k;
 }
 
+// vmcnt(n) for the n DMA pieces a wave may have issued for the stage after next (0..8).
+__device__ __forceinline__ void wait_vmcnt(int n) {
+  switch (n) {
+    case 0: __builtin_amdgcn_s_waitcnt(0x0F70); break;
+    case 1: __builtin_amdgcn_s_waitcnt(0x0F71); break;
+    case 2: __builtin_amdgcn_s_waitcnt(0x0F72); break;
+    case 3: __builtin_amdgcn_s_waitcnt(0x0F73); break;
+    case 4: __builtin_amdgcn_s_waitcnt(0x0F74); break;
+    case 5: __builtin_amdgcn_s_waitcnt(0x0F75); break;
+    case 6: __builtin_amdgcn_s_waitcnt(0x0F76); break;
+    case 7: __builtin_amdgcn_s_waitcnt(0x0F77); break;
+    default: __builtin_amdgcn_s_waitcnt(0x0F78); break;
+  }
+}
+
 }  // namespace
 
-template <int D, int NTW>
-__global__ __launch_bounds__(256) void attn_prefill_mfma_kernel(AttnArgs a) {
-  constexpr int KK = D / 32;           // 32-dim steps of the score product
-  constexpr int MT = D / 16;           // 16-dim tiles of the output
-  constexpr int ROWS_W = 16 * NTW;     // rows per wave
-  constexpr int ROWS_WG = 4 * ROWS_W;  // rows per workgroup
-  constexpr int TE = 16 * D;           // elements of one pool tile (K or V)
-  constexpr int TQ = TE * 2 / 1024;    // 1 KiB wave loads per pool tile
-  constexpr int NST = 3;               // LDS stages: tile j computed while j+1, j+2 arrive
-  constexpr int IDS = 1024;            // block ids of pool tiles held in LDS
+// Up to 12 waves per workgroup, 3 per SIMD: at most 168 registers per wave.
+template <int D>
+__global__ __launch_bounds__(768) __attribute__((amdgpu_waves_per_eu(3)))
+void attn_prefill_mfma_kernel(AttnArgs a) {
+  constexpr int KS = D / 16;          // 16-dim k-steps of the score product
+  constexpr int MB = D / 32;          // 32-dim blocks of the output
+  constexpr int TE = 16 * D;          // elements of one pool tile (K or V)
+  constexpr int TQ = TE * 2 / 1024;   // 1 KiB DMA pieces per pool tile
+  constexpr int NPIECE = 8 * TQ;      // pieces per 64-key stage (4 K + 4 V pool tiles)
+  constexpr int IDS = 1024;           // block ids of pool tiles held in LDS
   // One array per LDS stage ([K0..K3, V0..V3] each): with every access naming its array, the
   // compiler can tell the stage being computed from the ones the DMA is filling, and does not
   // wait for those loads before reading.
@@ -77,9 +96,10 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t lds2[8][TE];
   __shared__ int s_ids[IDS];
 
+  const int W = blockDim.x >> 6;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int n = lane & 15, g = lane >> 4;
+  const int col = lane & 31, h = lane >> 5;  // MFMA column (query row of the wave) and half
   const int logical = xcd_logical(blockIdx.x, gridDim.x);
   const int rt = logical % a.row_tiles;
   const int pair = logical / a.row_tiles;
@@ -88,13 +108,13 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma_kernel(AttnArgs a) {
   seq_lens(a, s, L, T);
   const int G = a.group;
   const int rows = T * G;
-  const int r0 = rt * ROWS_WG;
+  const int r0 = rt * 32 * W;
   if (r0 >= rows) return;
-  const int ke = min(L, L - T + (min(r0 + ROWS_WG, rows) - 1) / G + 1);  // keys the WG needs
+  const int ke = min(L, L - T + (min(r0 + 32 * W, rows) - 1) / G + 1);  // keys the WG needs
   const int ntiles = (ke + 63) >> 6;
   const int npt = (ke + 15) >> 4;  // pool tiles the WG reads
-  const int rw0 = r0 + wave * ROWS_W;
-  const int kew = rw0 < rows ? min(L, L - T + (min(rw0 + ROWS_W, rows) - 1) / G + 1) : 0;
+  const int rw0 = r0 + 32 * wave;
+  const int kew = rw0 < rows ? min(L, L - T + (min(rw0 + 32, rows) - 1) / G + 1) : 0;
   const int pw0 = L - T + rw0 / G;  // keys <= pw0 are visible to every row of this wave
 
   const int32_t* tbl = a.block_tables + (size_t)s * a.max_blocks_per_seq;
@@ -105,7 +125,7 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma_kernel(AttnArgs a) {
   // Block ids of pool tiles [ids0, ids0 + IDS) of this sequence, in LDS.
   int ids0 = 0;
   auto load_ids = [&](int base) {
-    for (int i = tid; i < IDS; i += 256) {
+    for (int i = tid; i < IDS; i += blockDim.x) {
       const int pt = min(base + i, npt - 1);
       s_ids[i] = tbl[(pt << 4) >> a.block_shift];
     }
@@ -113,156 +133,151 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma_kernel(AttnArgs a) {
   load_ids(0);
   __syncthreads();
 
-  // ---- K/V staging: wave w streams pool tiles 2w and 2w+1 of [K0..K3, V0..V3] of a 64-key
-  // tile straight into LDS (global_load_lds: lane l's 16 bytes land at base + 16*l).  Pool tiles
-  // past the context re-read the last one; those keys are masked and their V zeroed.
+  // ---- K/V staging: the NPIECE 1 KiB pieces of a stage ([K0..K3, V0..V3] pool tiles of a
+  // 64-key tile) are dealt round-robin to the waves, each streamed straight into LDS
+  // (global_load_lds: lane l's 16 bytes land at base + 16*l).  Pool tiles past the context
+  // re-read the last one; those keys are masked and their V zeroed.
   const uint32_t lane_off = 16u * lane;
+  const int my_pieces = (NPIECE - wave + W - 1) / W;  // pieces this wave issues per stage
   auto fetch = [&](int j, uint16_t (&stage)[8][TE]) {
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int slot = 2 * wave + u;        // 0..3: K tiles, 4..7: V tiles
+    for (int q = wave; q < NPIECE; q += W) {
+      const int slot = q / TQ, part = q % TQ;  // slot 0..3: K tiles, 4..7: V tiles
       const int pt = min(4 * j + (slot & 3), npt - 1);
       const int blk = s_ids[pt - ids0];
       const size_t off = block_tile_offset(blk, ((pt << 4) & bmask) >> 4, kvh, a.block_shift,
                                            a.num_blocks, a.num_kv_heads, D) * 2;
-      // wave-uniform base (scalar registers) + a fixed per-lane offset
-      const char* base = (slot < 4 ? kbase : vbase) + off;
-      const uint32_t dst = lds_address(stage[slot]);
-#pragma unroll
-      for (int q = 0; q < TQ; ++q) dma16(base + 1024 * q, lane_off, dst + 1024 * q);
+      const char* base = (slot < 4 ? kbase : vbase) + off + 1024 * part;
+      dma16(base, lane_off, lds_address(stage[slot]) + 1024 * part);
     }
   };
   fetch(0, lds0);
   if (ntiles > 1) fetch(1, lds1);
 
   // ---- Q^T operands and per-row state ----------------------------------------------------
+  // B operand of k-step k: lane (col, h) holds dims 16k + 8h .. +8 of the wave's row col.
   const int q_start = wave_prefix_total(a.q_lens, s);
   const int Hq = a.num_q_heads;
-  bf16x8 qb[NTW][KK];
-  int prow[NTW];
-  size_t rh[NTW];
+  const int r = rw0 + col;
+  const int qi = r / G;
+  const bool valid = r < rows && q_start + qi < a.total_q;
+  const int prow = valid ? L - T + qi : -1;  // the row's position (keys <= prow are visible)
+  const size_t rh = valid ? (size_t)(q_start + qi) * Hq + kvh * G + r % G : 0;
+  bf16x8 qb[KS];
+  {
+    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + rh * D + 8 * h;
 #pragma unroll
-  for (int nt = 0; nt < NTW; ++nt) {
-    const int r = rw0 + 16 * nt + n;
-    const int i = r / G;
-    const int grow = q_start + i;
-    const bool valid = r < rows && grow < a.total_q;
-    prow[nt] = valid ? L - T + i : -1;
-    rh[nt] = valid ? (size_t)grow * Hq + kvh * G + r % G : 0;
-    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + rh[nt] * D;
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
+    for (int k = 0; k < KS; ++k) {
       const u32x4 z = {0u, 0u, 0u, 0u};
-      qb[nt][kk] = __builtin_bit_cast(
-          bf16x8, valid ? *reinterpret_cast<const u32x4*>(qp + 32 * kk + 8 * g) : z);
+      qb[k] = __builtin_bit_cast(bf16x8, valid ? *reinterpret_cast<const u32x4*>(qp + 16 * k) : z);
     }
   }
-  // m_run: running row max (raw score units); o: O^T accumulators; osum: the same product
-  // with a ones tile in place of V^T, i.e. the row sum of the very bf16 P values that feed o
-  // (rescaled together with o).
-  float m_run[NTW];
-  floatx4 o[NTW][MT], osum[NTW];
+  // m_run: running row max (raw score units, the same in both lanes of a row); l_lane: this
+  // lane's share of the row sum; o: O^T, element e of block mb = dim 32mb + 8(e/4) + 4h + e%4.
+  float m_run = -INFINITY, l_lane = 0.f;
+  floatx16 o[MB];
 #pragma unroll
-  for (int nt = 0; nt < NTW; ++nt) {
-    m_run[nt] = -INFINITY;
-    osum[nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) o[nt][mt] = floatx4{0.f, 0.f, 0.f, 0.f};
-  }
-  const bf16x8 ones = __builtin_bit_cast(bf16x8, u32x4{0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u});
+    for (int e = 0; e < 16; ++e) o[mb][e] = 0.f;
   const float c = a.scale_log2;
+
+  // Key order of the score product: MFMA row m of a 32-key block reads key swap23(m), so that
+  // output element e of lane (col, h) is key 16(e/8) + 8h + e%8 of the block.
+  const int kq = (col & ~12) | ((col & 4) << 1) | ((col & 8) >> 1);
+  // K: chunk h (dims 8h .. +8 of k-step 0) of the key's token; k-step k adds 2k chunks.
+  const uint32_t k_lane = (uint32_t)(((kq >> 4) * TE + (h * 16 + (kq & 15)) * 8) * 2);  // bytes
+  // V^T: dim col of the 32-dim block, tokens 8h .. +8 of the k-step's pool tile.
+  const uint32_t v_lane = (uint32_t)((col * 16 + 8 * h) * 2);  // bytes
 
   // Tile 0 must have landed (the prologue's own waits may already have drained more).
   __builtin_amdgcn_s_waitcnt(0x0F70);
   __syncthreads();
 
-  // Attention of this wave's rows against one 64-key tile held in LDS (K tiles at kt, V^T tiles
-  // at vt, 4 pool tiles each), in two halves of 32 keys (pool tiles 2h and 2h+1).  `edge`: the
-  // tile reaches past the wave's first row (causal diagonal) or past the context.
-  auto tile = [&](const uint16_t* kt, const uint16_t* vt, int k0, bool edge) {
+  // V slots of keys at or past the context (only in the last 64-key tile) may hold anything,
+  // NaN included, and p = 0 times NaN is NaN: once that tile has landed, the workgroup zeroes
+  // them in LDS and meets at one more barrier before anyone reads it.
+  auto zero_tail = [&](uint16_t (&stage)[8][TE], int jt) {
+    if (jt != ntiles - 1 || 64 * ntiles <= L) return;  // workgroup-uniform
+    for (int i = tid; i < 4 * D; i += blockDim.x) {
+      const int t = i / D, d = i % D;  // V pool tile t of the stage, dim d: 16 tokens
+      uint16_t* row = &stage[4 + t][d * 16];
+      const int k0 = 64 * jt + 16 * t;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int kh = k0 + 32 * h;
-      // ---- S^T = K Q^T over keys kh .. kh+31 -------------------------------------------------
-      floatx4 sc[2][NTW];
+      for (int u = 0; u < 16; ++u)
+        if (k0 + u >= L) row[u] = 0;
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this thread's LDS writes are done
+    barrier_no_fence();
+  };
+  zero_tail(lds0, 0);
+
+  // Attention of this wave's 32 rows against one 32-key block (pool tiles 2b, 2b+1 of the
+  // stage).  `edge`: the block reaches past the wave's first row (causal diagonal) or past the
+  // context, so its scores are masked.
+  auto block = [&](const uint16_t (&stage)[8][TE], int b, int kb, bool edge) {
+    const char* kt = reinterpret_cast<const char*>(stage[2 * b]) + k_lane;
+    floatx16 sc;
 #pragma unroll
-      for (int t = 0; t < 2; ++t)
+    for (int e = 0; e < 16; ++e) sc[e] = 0.f;
 #pragma unroll
-        for (int nt = 0; nt < NTW; ++nt) sc[t][nt] = floatx4{0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < KS; ++k) {
+      // chunk 2k + h of the key's pool tile
+      const bf16x8 ka = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kt + k * 2 * 16 * 16));
+      sc = mfma32(ka, qb[k], sc);
+    }
+    if (edge) {
 #pragma unroll
-      for (int t = 0; t < 2; ++t) {
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-          const bf16x8 ka = __builtin_bit_cast(
-              bf16x8,
-              *reinterpret_cast<const u32x4*>(kt + (2 * h + t) * TE + ((4 * kk + g) * 16 + n) * 8));
-#pragma unroll
-          for (int nt = 0; nt < NTW; ++nt) sc[t][nt] = mfma16(ka, qb[nt][kk], sc[t][nt]);
-        }
+      for (int e = 0; e < 16; ++e) {
+        const int key = kb + 16 * (e >> 3) + 8 * h + (e & 7);
+        if (key > prow || key >= L) sc[e] = -INFINITY;
       }
-      // lane (n, g) holds row n's scores for keys kh + 16*t + 4*g + i
-      uint32_t vkeep[2][2] = {{~0u, ~0u}, {~0u, ~0u}};  // V words to keep (slots < L)
-      if (edge) {
+    }
+    // ---- online softmax (lazy: the running max moves only when a row's max grows by more
+    // than 2^8 in exp2 units, so P stays <= 256 and the rescale is rare) --------------------
+    float cmax = fmaxf(fmaxf(sc[0], sc[1]), sc[2]);
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
+    for (int e = 3; e < 15; e += 2) cmax = fmaxf(fmaxf(cmax, sc[e]), sc[e + 1]);
+    cmax = fmaxf(cmax, sc[15]);
+    {
+      float x, y;
+      swap32(cmax, x, y);
+      cmax = fmaxf(x, y);
+    }
+    const bool grow = (cmax - m_run) * c > 8.f;  // false for NaN (both -inf)
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      const float m_new = grow ? cmax : m_run;
+      const float alpha = grow ? fast_exp2((m_run - m_new) * c) : 1.f;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int key = kh + 16 * t + 4 * g + i;
+      for (int mb = 0; mb < MB; ++mb) o[mb] *= alpha;
+      l_lane *= alpha;
+      m_run = m_new;
+    }
+    const float msub = m_run == -INFINITY ? 0.f : m_run * c;
+    uint32_t pk[8];
+    float psum = 0.f;
 #pragma unroll
-            for (int nt = 0; nt < NTW; ++nt)
-              if (key > prow[nt] || key >= L) sc[t][nt][i] = -INFINITY;
-            if (key >= L) vkeep[t][i >> 1] &= (i & 1) ? 0x0000ffffu : 0xffff0000u;
-          }
-        }
+    for (int e = 0; e < 16; e += 2) {
+      const float p0 = fast_exp2(sc[e] * c - msub), p1 = fast_exp2(sc[e + 1] * c - msub);
+      psum += p0 + p1;
+      pk[e >> 1] = cvt_pk_bf16(p0, p1);
+    }
+    l_lane += psum;
+    // ---- O^T += V^T P^T: k-step j takes keys 16j + 8h .. +8 (pool tile 2b + j) ---------------
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pk[4 * j], pk[4 * j + 1], pk[4 * j + 2], pk[4 * j + 3]});
+      const char* vt = reinterpret_cast<const char*>(stage[4 + 2 * b + j]) + v_lane;
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const u32x4 v = *reinterpret_cast<const u32x4*>(vt + mb * 32 * 16 * 2);
+        o[mb] = mfma32(__builtin_bit_cast(bf16x8, v), pb, o[mb]);
       }
-      // ---- online softmax (lazy: the running max moves only when a row's max grows by more
-      // than 2^8 in exp2 units, so P stays <= 256 and the rescale is rare) ------------------
-      bf16x8 pb[NTW];
-#pragma unroll
-      for (int nt = 0; nt < NTW; ++nt) {
-        float cmax = -INFINITY;
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int i = 0; i < 4; ++i) cmax = fmaxf(cmax, sc[t][nt][i]);
-        cmax = xrow_max(cmax);
-        const bool grow = (cmax - m_run[nt]) * c > 8.f;  // false for NaN (both -inf)
-        const float m_new = grow ? cmax : m_run[nt];
-        if (__builtin_amdgcn_ballot_w64(grow)) {
-          const float alpha = grow ? fast_exp2((m_run[nt] - m_new) * c) : 1.f;
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt) o[nt][mt] *= alpha;
-          osum[nt] *= alpha;
-        }
-        m_run[nt] = m_new;
-        const float msub = m_new == -INFINITY ? 0.f : m_new * c;
-        uint32_t pk[4];
-#pragma unroll
-        for (int t = 0; t < 2; ++t)
-#pragma unroll
-          for (int i = 0; i < 4; i += 2)
-            pk[2 * t + (i >> 1)] = cvt_pk_bf16(fast_exp2(sc[t][nt][i] * c - msub),
-                                               fast_exp2(sc[t][nt][i + 1] * c - msub));
-        pb[nt] = __builtin_bit_cast(bf16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
-      }
-      // ---- O^T += V^T P^T (and the ones tile for the row sums) ------------------------------
-#pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-        const u32x2 v0 = *reinterpret_cast<const u32x2*>(vt + (2 * h) * TE + (16 * mt + n) * 16 + 4 * g);
-        const u32x2 v1 = *reinterpret_cast<const u32x2*>(vt + (2 * h + 1) * TE + (16 * mt + n) * 16 + 4 * g);
-        const bf16x8 va = __builtin_bit_cast(
-            bf16x8, u32x4{v0[0] & vkeep[0][0], v0[1] & vkeep[0][1], v1[0] & vkeep[1][0],
-                          v1[1] & vkeep[1][1]});
-#pragma unroll
-        for (int nt = 0; nt < NTW; ++nt) o[nt][mt] = mfma16(va, pb[nt], o[nt][mt]);
-      }
-#pragma unroll
-      for (int nt = 0; nt < NTW; ++nt) osum[nt] = mfma16(ones, pb[nt], osum[nt]);
     }
   };
 
-  // One 64-key tile: compute tile j from `cur` while tile j+2 streams into `nxt2`.
-  auto step = [&](int j, uint16_t (&cur)[8][TE], uint16_t (&nxt2)[8][TE]) {
+  // One 64-key tile: compute tile j from `cur` while tile j+2 streams into `nxt2`; tile j+1
+  // (in `nxt1`) is published at the end.
+  auto step = [&](int j, uint16_t (&cur)[8][TE], uint16_t (&nxt1)[8][TE], uint16_t (&nxt2)[8][TE]) {
     // refill the id cache every IDS pool tiles (rare: only past 16K keys)
     if (4 * (j + 2) + 3 - ids0 >= IDS && 4 * (j + 2) < npt) {
       __builtin_amdgcn_s_waitcnt(0x0F70);
@@ -272,77 +287,72 @@ __global__ __launch_bounds__(256) void attn_prefill_mfma_kernel(AttnArgs a) {
       __syncthreads();
     }
     fetch(min(j + 2, ntiles - 1), nxt2);
-    const int k0 = 64 * j;
-    if (k0 < kew) {
-      // Tiles that reach past the wave's first row (causal diagonal) or past the context take
+#pragma unroll
+    for (int b = 0; b < 2; ++b) {
+      const int kb = 64 * j + 32 * b;
+      // Blocks that reach past the wave's first row (causal diagonal) or past the context take
       // the masked path; all others run branch-free.
-      tile(cur[0], cur[4], k0, k0 + 63 > pw0 || k0 + 64 > L);
+      if (kb < kew) block(cur, b, kb, kb + 31 > pw0 || kb + 32 > L);
     }
-    // tile j+1 (issued one iteration ago) has landed once at most the 2*TQ loads of tile j+2
+    // tile j+1 (issued one step ago) has landed once at most this wave's pieces of tile j+2
     // are outstanding; every wave's share of it is visible after the barrier
-    __builtin_amdgcn_s_waitcnt(TQ == 4 ? 0x0F78 : 0x0F74);
+    wait_vmcnt(my_pieces);
     barrier_no_fence();
+    zero_tail(nxt1, j + 1);
   };
-  for (int j = 0; j < ntiles; j += NST) {
-    step(j, lds0, lds2);
-    if (j + 1 < ntiles) step(j + 1, lds1, lds0);
-    if (j + 2 < ntiles) step(j + 2, lds2, lds1);
+  for (int j = 0; j < ntiles; j += 3) {
+    step(j, lds0, lds1, lds2);
+    if (j + 1 < ntiles) step(j + 1, lds1, lds2, lds0);
+    if (j + 2 < ntiles) step(j + 2, lds2, lds0, lds1);
   }
 
-  // ---- normalise and store ---------------------------------------------------------------
+  // ---- normalise and store: lane (col, h) holds dims 32mb + 8q + 4h .. +4 of its row --------
+  {
+    float x, y;
+    swap32(l_lane, x, y);
+    const float lrow = x + y;
+    if (valid) {
+      const float inv = 1.f / lrow;
+      uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + rh * D + 4 * h;
 #pragma unroll
-  for (int nt = 0; nt < NTW; ++nt) {
-    if (prow[nt] < 0) continue;
-    const float inv = 1.f / osum[nt][0];
-    uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + rh[nt] * D;
+      for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) {
-      const floatx4 v = o[nt][mt] * inv;
-      const uint32_t w0 = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
-      const uint32_t w1 = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
-      *reinterpret_cast<uint2*>(op + 16 * mt + 4 * g) = make_uint2(w0, w1);
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t w0 = f32_to_bf16_bits(o[mb][4 * q] * inv) | (f32_to_bf16_bits(o[mb][4 * q + 1] * inv) << 16);
+          const uint32_t w1 = f32_to_bf16_bits(o[mb][4 * q + 2] * inv) | (f32_to_bf16_bits(o[mb][4 * q + 3] * inv) << 16);
+          *reinterpret_cast<uint2*>(op + 32 * mb + 8 * q) = make_uint2(w0, w1);
+        }
+      }
     }
   }
 }
 
-int prefill_rows_per_wave_choice(int rows_per_pair, int pairs, int num_cus) {
-  // Makespan model: one workgroup per CU at a time (the kernel runs at occupancy 1); pick the
-  // rows per wave (16*NTW) that minimises rounds x rows per workgroup, preferring larger tiles
-  // (more K/V reuse) on ties.
-  int best = 5;
+int prefill_waves_choice(int rows_per_pair, int pairs, int num_cus) {
+  // Makespan model: one workgroup per CU at a time (LDS-bound); a workgroup of W waves of 32
+  // rows takes ceil(W/4) wave-times on its busiest SIMD.  Pick W in 4..12 minimising
+  // rounds x ceil(W/4), then the fewest idle wave slots.
+  int best = 8;
   double best_cost = 1e300;
-  for (int ntw = 5; ntw >= 2; --ntw) {
-    const int rows_wg = 64 * ntw;
+  for (int w = 4; w <= 12; ++w) {
+    const long long rows_wg = 32LL * w;
     const long long wgs = (long long)pairs * ((rows_per_pair + rows_wg - 1) / rows_wg);
     const long long rounds = (wgs + num_cus - 1) / num_cus;
-    const double cost = (double)rounds * rows_wg;
-    if (cost < best_cost * 0.999) {
+    const double cost = (double)rounds * ((w + 3) / 4) + 1e-3 * (double)rounds * w;
+    if (cost < best_cost) {
       best_cost = cost;
-      best = ntw;
+      best = w;
     }
   }
   return best;
 }
 
-hipError_t launch_attn_prefill_mfma(const AttnArgs& a, int head_dim, int ntw, hipStream_t st) {
-  dim3 grid(a.row_tiles * a.num_kv_heads * a.num_seqs);
-#define KVP_PREFILL(D, NTW) attn_prefill_mfma_kernel<D, NTW><<<grid, 256, 0, st>>>(a)
-  if (head_dim == 128) {
-    switch (ntw) {
-      case 2: KVP_PREFILL(128, 2); break;
-      case 3: KVP_PREFILL(128, 3); break;
-      case 4: KVP_PREFILL(128, 4); break;
-      default: KVP_PREFILL(128, 5); break;
-    }
-  } else {
-    switch (ntw) {
-      case 2: KVP_PREFILL(64, 2); break;
-      case 3: KVP_PREFILL(64, 3); break;
-      case 4: KVP_PREFILL(64, 4); break;
-      default: KVP_PREFILL(64, 5); break;
-    }
-  }
-#undef KVP_PREFILL
+hipError_t launch_attn_prefill_mfma(const AttnArgs& a, int head_dim, int waves, hipStream_t st) {
+  if (waves < 1 || waves > 12) return hipErrorInvalidConfiguration;
+  const dim3 grid(a.row_tiles * a.num_kv_heads * a.num_seqs);
+  if (head_dim == 128)
+    attn_prefill_mfma_kernel<128><<<grid, 64 * waves, 0, st>>>(a);
+  else
+    attn_prefill_mfma_kernel<64><<<grid, 64 * waves, 0, st>>>(a);
   return hipGetLastError();
 }
 

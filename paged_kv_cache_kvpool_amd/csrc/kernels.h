@@ -42,11 +42,11 @@ hipError_t launch_attn_split_mfma(const AttnArgs& a, int head_dim, int rows_per_
 // sequence).
 hipError_t launch_attn_vec(const AttnArgs& a, int elt_bytes, int head_dim, int rows_per_tile,
                            int grid_x, hipStream_t st);
-// Prefill attention on the matrix cores (bf16): 4 waves x 16*ntw rows share LDS-staged K/V
-// tiles; one workgroup per (row tile, KV head, sequence), a.row_tiles row tiles per pair.
-hipError_t launch_attn_prefill_mfma(const AttnArgs& a, int head_dim, int ntw, hipStream_t st);
-// Rows per wave / 16 (2..5) for a prefill call: balances workgroups over the CUs.
-int prefill_rows_per_wave_choice(int rows_per_pair, int pairs, int num_cus);
+// Prefill attention on the matrix cores (bf16): `waves` (1..12) waves x 32 rows share LDS-staged
+// K/V tiles; one workgroup per (row tile, KV head, sequence), a.row_tiles row tiles per pair.
+hipError_t launch_attn_prefill_mfma(const AttnArgs& a, int head_dim, int waves, hipStream_t st);
+// Waves per workgroup (4..12) for a prefill call: balances workgroups over the CUs.
+int prefill_waves_choice(int rows_per_pair, int pairs, int num_cus);
 // Cross-split merge of the partials written in split mode.
 hipError_t launch_attn_reduce(const AttnArgs& a, int elt_bytes, int head_dim, int max_q_len,
                               hipStream_t st);

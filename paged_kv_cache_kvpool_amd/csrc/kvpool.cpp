@@ -489,10 +489,10 @@ int kvattn_forward(kvpool_t* pool, int32_t layer, const void* q, void* out, int3
     a.row_tiles = (rows + rpt - 1) / rpt;
     e = timed(K_SPLIT_MFMA, st, [&] { return kvp::launch_attn_split_mfma(a, pool->head_dim, rpt, pl.max_splits, pool->num_cus, st); });
   } else {
-    int ntw = kvp::prefill_rows_per_wave_choice(rows, num_seqs * pool->num_kv_heads, pool->num_cus);
-    if (const char* v = getenv("KVATTN_PREFILL_NTW")) ntw = std::max(2, std::min(5, atoi(v)));  // sweeps
-    a.row_tiles = (rows + 64 * ntw - 1) / (64 * ntw);
-    e = timed(K_PREFILL_MFMA, st, [&] { return kvp::launch_attn_prefill_mfma(a, pool->head_dim, ntw, st); });
+    int waves = kvp::prefill_waves_choice(rows, num_seqs * pool->num_kv_heads, pool->num_cus);
+    if (const char* v = getenv("KVATTN_PREFILL_WAVES")) waves = std::max(1, std::min(12, atoi(v)));  // sweeps
+    a.row_tiles = (rows + 32 * waves - 1) / (32 * waves);
+    e = timed(K_PREFILL_MFMA, st, [&] { return kvp::launch_attn_prefill_mfma(a, pool->head_dim, waves, st); });
   }
   if (e != hipSuccess) return fail(KV_EDEVICE, "attention launch: %s", hipGetErrorString(e));
   // Rows whose keys all fall in split 0 are finished by the attention kernel; when no sequence
