@@ -37,15 +37,37 @@ __device__ __forceinline__ floatx16 mfma32(bf16x8 a, bf16x8 b, floatx16 c) {
 
 constexpr int NXCD = 8;
 
-// 16 bytes per lane from gbase + voff into LDS at lds_addr + 16*lane (global_load_lds_dwordx4,
-// scalar base + per-lane offset).  Issued as inline asm so that the compiler's wait insertion
-// never ties these loads to LDS reads of other stages or to reused address registers: the
-// kernel waits for them itself (vmcnt) before the barrier that publishes a stage.
-__device__ __forceinline__ void dma16(const void* gbase, uint32_t voff, uint32_t lds_addr) {
-  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
-               :
-               : "v"(voff), "s"(gbase), "s"(lds_addr)
-               : "memory", "m0");
+// One pool tile (NQ KiB) from gbase + voff into LDS at lds_addr: NQ global_load_lds_dwordx4
+// with instruction offsets 0, 1024, ... (the offset advances the global and the LDS address
+// alike; lane l's 16 bytes of piece q land at lds_addr + 1024*q + 16*l), one M0 write per tile.
+// Issued as inline asm so that the compiler's wait insertion never ties these loads to LDS
+// reads of other stages or to reused address registers: the kernel waits for them itself
+// (vmcnt) before the barrier that publishes a stage.  The base and the LDS address are
+// wave-uniform by construction; readfirstlane makes that explicit so that they always live in
+// scalar registers, as the instruction requires.
+template <int NQ>
+__device__ __forceinline__ void dma_tile(const void* gbase, uint32_t voff, uint32_t lds_addr) {
+  // (readfirstlane returns a signed int: widen through uint32_t, never sign-extend the low word)
+  const uint64_t g = reinterpret_cast<uint64_t>(gbase);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)g);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(g >> 32));
+  const uint64_t gs = ((uint64_t)hi << 32) | (uint64_t)lo;
+  const uint32_t ls = (uint32_t)__builtin_amdgcn_readfirstlane(lds_addr);
+  static_assert(NQ == 2 || NQ == 4, "pool tiles of 2 or 4 KiB");
+  if constexpr (NQ == 4)
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1\n\t"
+                 "global_load_lds_dwordx4 %0, %1 offset:1024\n\t"
+                 "global_load_lds_dwordx4 %0, %1 offset:2048\n\t"
+                 "global_load_lds_dwordx4 %0, %1 offset:3072"
+                 :
+                 : "v"(voff), "s"(reinterpret_cast<const void*>(gs)), "s"(ls)
+                 : "memory", "m0");
+  else
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1\n\t"
+                 "global_load_lds_dwordx4 %0, %1 offset:1024"
+                 :
+                 : "v"(voff), "s"(reinterpret_cast<const void*>(gs)), "s"(ls)
+                 : "memory", "m0");
 }
 
 template <typename P>
@@ -86,7 +108,6 @@ void attn_prefill_mfma_kernel(AttnArgs a) {
   constexpr int MB = D / 32;          // 32-dim blocks of the output
   constexpr int TE = 16 * D;          // elements of one pool tile (K or V)
   constexpr int TQ = TE * 2 / 1024;   // 1 KiB DMA pieces per pool tile
-  constexpr int NPIECE = 8 * TQ;      // pieces per 64-key stage (4 K + 4 V pool tiles)
   constexpr int IDS = 1024;           // block ids of pool tiles held in LDS
   // One array per LDS stage ([K0..K3, V0..V3] each): with every access naming its array, the
   // compiler can tell the stage being computed from the ones the DMA is filling, and does not
@@ -94,7 +115,7 @@ void attn_prefill_mfma_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t lds0[8][TE];
   __shared__ __attribute__((aligned(16))) uint16_t lds1[8][TE];
   __shared__ __attribute__((aligned(16))) uint16_t lds2[8][TE];
-  __shared__ int s_ids[IDS];
+  __shared__ __attribute__((aligned(16))) int s_ids[IDS];
 
   const int W = blockDim.x >> 6;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -133,25 +154,42 @@ void attn_prefill_mfma_kernel(AttnArgs a) {
   load_ids(0);
   __syncthreads();
 
-  // ---- K/V staging: the NPIECE 1 KiB pieces of a stage ([K0..K3, V0..V3] pool tiles of a
-  // 64-key tile) are dealt round-robin to the waves, each streamed straight into LDS
-  // (global_load_lds: lane l's 16 bytes land at base + 16*l).  Pool tiles past the context
-  // re-read the last one; those keys are masked and their V zeroed.
+  // ---- K/V staging: the 8 pool tiles of a stage ([K0..K3, V0..V3] of a 64-key tile) are dealt
+  // round-robin to the issuing waves, each streamed straight into LDS (global_load_lds: lane
+  // l's 16 bytes land at base + 16*l).  Pool tiles past the context re-read the last one;
+  // those keys are masked and their V zeroed.
+  // The 4 block ids a stage needs (pool tiles 4j .. 4j+3, already clamped in the cache) are
+  // read from the cache with one ds_read_b128 a step ahead of their use, so the issue of a
+  // stage's DMA never waits on LDS, and its addresses are computed in scalar registers.
+  typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+  // The DMA issue goes to the waves of the least loaded SIMDs (waves are placed on the 4 SIMDs
+  // round-robin, so with W % 4 != 0 the SIMDs holding wave indices >= W % 4 mod 4 carry one
+  // wave less): the tile time is set by the busiest SIMD, and the others have the slack.
+  // Fewer than 4 such waves would make the issue itself the bottleneck: then all waves issue.
+  const int wrem = W & 3;
+  const bool split = wrem != 0 && (W >> 2) * (4 - wrem) >= 4;
+  const int nissue = split ? (W >> 2) * (4 - wrem) : W;  // waves that issue DMA
+  const int issue_rank = !split ? wave
+                         : (wave & 3) >= wrem ? (wave >> 2) * (4 - wrem) + (wave & 3) - wrem : -1;
   const uint32_t lane_off = 16u * lane;
-  const int my_pieces = (NPIECE - wave + W - 1) / W;  // pieces this wave issues per stage
-  auto fetch = [&](int j, uint16_t (&stage)[8][TE]) {
-    for (int q = wave; q < NPIECE; q += W) {
-      const int slot = q / TQ, part = q % TQ;  // slot 0..3: K tiles, 4..7: V tiles
-      const int pt = min(4 * j + (slot & 3), npt - 1);
-      const int blk = s_ids[pt - ids0];
-      const size_t off = block_tile_offset(blk, ((pt << 4) & bmask) >> 4, kvh, a.block_shift,
+  const int my_pieces = issue_rank < 0 ? 0 : (8 - issue_rank + nissue - 1) / nissue * TQ;
+  auto read_ids = [&](int j) -> i32x4 { return *reinterpret_cast<const i32x4*>(&s_ids[4 * j - ids0]); };
+  auto fetch = [&](int j, const i32x4& ids, uint16_t (&stage)[8][TE]) {
+    int blk[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) blk[t] = __builtin_amdgcn_readfirstlane(ids[t]);
+    for (int slot = issue_rank; slot >= 0 && slot < 8; slot += nissue) {  // 0..3: K, 4..7: V
+      const int t = slot & 3;
+      const int pt = min(4 * j + t, npt - 1);
+      const int b = t == 0 ? blk[0] : t == 1 ? blk[1] : t == 2 ? blk[2] : blk[3];
+      const size_t off = block_tile_offset(b, ((pt << 4) & bmask) >> 4, kvh, a.block_shift,
                                            a.num_blocks, a.num_kv_heads, D) * 2;
-      const char* base = (slot < 4 ? kbase : vbase) + off + 1024 * part;
-      dma16(base, lane_off, lds_address(stage[slot]) + 1024 * part);
+      dma_tile<TQ>((slot < 4 ? kbase : vbase) + off, lane_off, lds_address(stage[slot]));
     }
   };
-  fetch(0, lds0);
-  if (ntiles > 1) fetch(1, lds1);
+  fetch(0, read_ids(0), lds0);
+  if (ntiles > 1) fetch(1, read_ids(1), lds1);
+  i32x4 ids_next = read_ids(min(2, ntiles - 1));  // for the fetch of step 0
 
   // ---- Q^T operands and per-row state ----------------------------------------------------
   // B operand of k-step k: lane (col, h) holds dims 16k + 8h .. +8 of the wave's row col.
@@ -214,7 +252,8 @@ void attn_prefill_mfma_kernel(AttnArgs a) {
   // Attention of this wave's 32 rows against one 32-key block (pool tiles 2b, 2b+1 of the
   // stage).  `edge`: the block reaches past the wave's first row (causal diagonal) or past the
   // context, so its scores are masked.
-  auto block = [&](const uint16_t (&stage)[8][TE], int b, int kb, bool edge) {
+  // The three phases of a 32-key block (pool tiles 2b, 2b+1 of the stage).
+  auto qk = [&](const uint16_t (&stage)[8][TE], int b) -> floatx16 {
     const char* kt = reinterpret_cast<const char*>(stage[2 * b]) + k_lane;
     floatx16 sc;
 #pragma unroll
@@ -225,6 +264,11 @@ void attn_prefill_mfma_kernel(AttnArgs a) {
       const bf16x8 ka = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kt + k * 2 * 16 * 16));
       sc = mfma32(ka, qb[k], sc);
     }
+    return sc;
+  };
+  // `edge`: the block reaches past the wave's first row (causal diagonal) or past the context,
+  // so its scores are masked.  Returns P (bf16 pairs, keys in PV order).
+  auto softmax = [&](floatx16 sc, int kb, bool edge, uint32_t (&pk)[8]) {
     if (edge) {
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
@@ -232,8 +276,8 @@ void attn_prefill_mfma_kernel(AttnArgs a) {
         if (key > prow || key >= L) sc[e] = -INFINITY;
       }
     }
-    // ---- online softmax (lazy: the running max moves only when a row's max grows by more
-    // than 2^8 in exp2 units, so P stays <= 256 and the rescale is rare) --------------------
+    // lazy: the running max moves only when a row's max grows by more than 2^8 in exp2 units,
+    // so P stays <= 256 and the rescale is rare
     float cmax = fmaxf(fmaxf(sc[0], sc[1]), sc[2]);
 #pragma unroll
     for (int e = 3; e < 15; e += 2) cmax = fmaxf(fmaxf(cmax, sc[e]), sc[e + 1]);
@@ -253,7 +297,6 @@ void attn_prefill_mfma_kernel(AttnArgs a) {
       m_run = m_new;
     }
     const float msub = m_run == -INFINITY ? 0.f : m_run * c;
-    uint32_t pk[8];
     float psum = 0.f;
 #pragma unroll
     for (int e = 0; e < 16; e += 2) {
@@ -262,7 +305,9 @@ void attn_prefill_mfma_kernel(AttnArgs a) {
       pk[e >> 1] = cvt_pk_bf16(p0, p1);
     }
     l_lane += psum;
-    // ---- O^T += V^T P^T: k-step j takes keys 16j + 8h .. +8 (pool tile 2b + j) ---------------
+  };
+  // O^T += V^T P^T: k-step j takes keys 16j + 8h .. +8 (pool tile 2b + j)
+  auto pv = [&](const uint16_t (&stage)[8][TE], int b, const uint32_t (&pk)[8]) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pk[4 * j], pk[4 * j + 1], pk[4 * j + 2], pk[4 * j + 3]});
@@ -278,21 +323,28 @@ void attn_prefill_mfma_kernel(AttnArgs a) {
   // One 64-key tile: compute tile j from `cur` while tile j+2 streams into `nxt2`; tile j+1
   // (in `nxt1`) is published at the end.
   auto step = [&](int j, uint16_t (&cur)[8][TE], uint16_t (&nxt1)[8][TE], uint16_t (&nxt2)[8][TE]) {
-    // refill the id cache every IDS pool tiles (rare: only past 16K keys)
-    if (4 * (j + 2) + 3 - ids0 >= IDS && 4 * (j + 2) < npt) {
-      __builtin_amdgcn_s_waitcnt(0x0F70);
+    fetch(min(j + 2, ntiles - 1), ids_next, nxt2);
+    // the ids of the next step's stage; refill the id cache first when they lie past it (rare:
+    // only past 16K keys)
+    const int jn = min(j + 3, ntiles - 1);
+    if (4 * jn + 3 - ids0 >= IDS) {
       __syncthreads();
-      ids0 = 4 * (j + 2);
+      ids0 = 4 * jn;
       load_ids(ids0);
       __syncthreads();
     }
-    fetch(min(j + 2, ntiles - 1), nxt2);
+    ids_next = read_ids(jn);
+    // Blocks that reach past the wave's first row (causal diagonal) or past the context take
+    // the masked path.
+    const int kb0 = 64 * j;
 #pragma unroll
     for (int b = 0; b < 2; ++b) {
-      const int kb = 64 * j + 32 * b;
-      // Blocks that reach past the wave's first row (causal diagonal) or past the context take
-      // the masked path; all others run branch-free.
-      if (kb < kew) block(cur, b, kb, kb + 31 > pw0 || kb + 32 > L);
+      const int kb = kb0 + 32 * b;
+      if (kb < kew) {
+        uint32_t p[8];
+        softmax(qk(cur, b), kb, kb + 31 > pw0 || kb + 32 > L, p);
+        pv(cur, b, p);
+      }
     }
     // tile j+1 (issued one step ago) has landed once at most this wave's pieces of tile j+2
     // are outstanding; every wave's share of it is visible after the barrier
