@@ -4,7 +4,8 @@
 // shared prefix blocks; "Request isolation & continuous batching": prefill in chunks).
 //
 // Workgroup = W waves (4..12) over one row tile of one (sequence, KV head); a wave owns 32 rows
-// (row = token * G + head-in-group, so every row of a workgroup reads the same K/V).  K/V are
+// (row = token * G + head-in-group, so every row of a workgroup reads the same K/V), the row
+// blocks of a (sequence, KV head) dealt to its workgroups strided.  K/V are
 // walked in tiles of 64 keys = 4 pool tiles, each streamed verbatim from the pool into LDS with
 // global_load_lds (no register staging; the pool's tile layout is the order the matrix cores
 // read) through 3 LDS stages: tiles j+1 and j+2 are in flight while tile j is computed; one
@@ -129,12 +130,16 @@ void attn_prefill_mfma_kernel(AttnArgs a) {
   seq_lens(a, s, L, T);
   const int G = a.group;
   const int rows = T * G;
-  const int r0 = rt * 32 * W;
-  if (r0 >= rows) return;
-  const int ke = min(L, L - T + (min(r0 + 32 * W, rows) - 1) / G + 1);  // keys the WG needs
+  // Row blocks of 32 rows are dealt to the workgroups of a (sequence, KV head) strided: wave w
+  // of row tile rt owns block rt + row_tiles * w.  Every workgroup then holds early and late
+  // rows alike, so under the causal mask all of them carry about the same work.
+  const int nblk = (rows + 31) >> 5;
+  if (rt >= nblk) return;
+  const int last_blk = rt + a.row_tiles * min(W - 1, (nblk - 1 - rt) / a.row_tiles);
+  const int ke = min(L, L - T + (min(32 * last_blk + 32, rows) - 1) / G + 1);  // keys the WG needs
   const int ntiles = (ke + 63) >> 6;
   const int npt = (ke + 15) >> 4;  // pool tiles the WG reads
-  const int rw0 = r0 + 32 * wave;
+  const int rw0 = 32 * (rt + a.row_tiles * wave);
   const int kew = rw0 < rows ? min(L, L - T + (min(rw0 + 32, rows) - 1) / G + 1) : 0;
   const int pw0 = L - T + rw0 / G;  // keys <= pw0 are visible to every row of this wave
 
