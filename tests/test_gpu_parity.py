@@ -140,6 +140,23 @@ def test_attention_prefill_shapes(q_len, dtype):
     assert_close(out_f64(out), c.oracle(), dtype, w.name)
 
 
+@pytest.mark.parametrize("plan", ["4", "8", "10", "12"])
+@pytest.mark.parametrize("head_dim", [128, 64])
+def test_attention_prefill_plans(plan, head_dim, monkeypatch):
+    """Prefill workgroups of 4, 8, 10 and 12 waves (forced through KVATTN_PREFILL_WAVES), over
+    ragged sequences whose row counts leave partial row tiles and waves with no rows."""
+    monkeypatch.setenv("KVATTN_PREFILL_WAVES", plan)
+    announce(f"prefill plan {plan} D={head_dim}")
+    w = wl.make(f"prefill_plan_{plan}_{head_dim}", seed=61, dtype=wl.BF16,
+                num_seqs_ctx=[700, 450, 130, 1300], q_lens=[300, 450, 97, 64],
+                num_q_heads=10, num_kv_heads=2, head_dim=head_dim)
+    c = DeviceCase(w)
+    c.append()
+    out = c.forward()
+    torch.cuda.synchronize()
+    assert_close(out_f64(out), c.oracle(), wl.BF16, w.name)
+
+
 def test_decode_vec_kernel_bf16(monkeypatch):
     """The vector-ALU bf16 decode variant (selected by KVATTN_DECODE_VEC=1)."""
     monkeypatch.setenv("KVATTN_DECODE_VEC", "1")
