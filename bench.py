@@ -43,6 +43,8 @@ WORKLOADS = {
     "spec_verify_128k": dict(kind="hbm", desc="1 seq, 1+3 tokens causal, ctx 131072+4, 40/8 heads, D=128, bf16"),
     "prefix_prefill": dict(kind="mfma", desc="4 seqs x (4096 cached + 512 new causal), 40/8 heads, D=128, bf16"),
     "long_decode": dict(kind="hbm", desc="2 seqs x 1 token at 262144 and 131072, 40/8 heads, D=128, bf16, pool 24576 blocks"),
+    "mixed_step": dict(kind="hbm", desc="one call: 32 decode seqs (ctx U[1024,8192]) + 1 verify (1+3 at 32768) + "
+                                        "1 prefill chunk (512 over 4096 cached), 40/8 heads, D=128, bf16"),
 }
 
 
@@ -60,25 +62,56 @@ def make_workload(name):
         return wl.prefix_prefill(host_pool=False)
     if name == "long_decode":
         return wl.long_decode(host_pool=False)
+    if name == "mixed_step":
+        return wl.mixed_step(host_pool=False)
     raise SystemExit(f"unknown workload {name}")
 
 
+# Sequences with q_len * (Hq / Hkv) up to this many rows per KV head take the split-K kernel,
+# longer query blocks the prefill kernel (the library's rule, stated in include/kvpool.h).
+SPLIT_ROWS_MAX = 128
+
+
 def algorithmic(w):
-    """Per-step algorithmic bytes and flops (and attended KV tokens), from the definition."""
+    """Per-step algorithmic bytes and flops (and attended KV tokens), from the definition, for
+    the whole step and for the sequences each attention kernel serves."""
     eb = w.elt_bytes
     d, hq, hkv = w.head_dim, w.num_q_heads, w.num_kv_heads
-    kv_tokens = int(w.ctx_lens.astype(np.int64).sum())
-    kv_bytes = kv_tokens * hkv * d * 2 * eb
-    qo_bytes = 2 * w.total_q * hq * d * eb
-    table_bytes = int(sum((int(c) + w.block_size - 1) // w.block_size for c in w.ctx_lens)) * 4
-    append_bytes = 2 * 2 * w.total_q * hkv * d * eb if w.k_new is not None else 0
-    pairs = 0
+    g = hq // hkv
+    out = dict(kv_tokens=0, kv_bytes=0, attn_bytes=0, append_bytes=0, flops=0, pairs=0,
+               split_bytes=0, split_flops=0, prefill_bytes=0, prefill_flops=0)
     for L, T in zip(w.ctx_lens.astype(np.int64), w.q_lens.astype(np.int64)):
-        pairs += T * (L - T) + T * (T + 1) // 2   # row i sees L - T + i + 1 keys
-    flops = 4 * d * hq * int(pairs)
-    return dict(kv_tokens=kv_tokens, kv_bytes=kv_bytes, attn_bytes=kv_bytes + qo_bytes + table_bytes,
-                append_bytes=append_bytes, step_bytes=kv_bytes + qo_bytes + table_bytes + append_bytes,
-                flops=flops, pairs=int(pairs))
+        L, T = int(L), int(T)
+        kv = L * hkv * d * 2 * eb                       # K and V of every key, once per KV head
+        qo = 2 * T * hq * d * eb
+        tab = (L + w.block_size - 1) // w.block_size * 4
+        pairs = T * (L - T) + T * (T + 1) // 2          # row i sees L - T + i + 1 keys
+        fl = 4 * d * hq * pairs
+        out["kv_tokens"] += L
+        out["kv_bytes"] += kv
+        out["attn_bytes"] += kv + qo + tab
+        out["pairs"] += pairs
+        out["flops"] += fl
+        # a kernel's own bytes: K/V, Q and the table (its output write is small beside them)
+        cls = "split" if T * g <= SPLIT_ROWS_MAX else "prefill"
+        out[cls + "_bytes"] += kv + T * hq * d * eb + tab
+        out[cls + "_flops"] += fl
+    if w.k_new is not None:
+        out["append_bytes"] = 2 * 2 * w.total_q * hkv * d * eb
+    out["step_bytes"] = out["attn_bytes"] + out["append_bytes"]
+    return out
+
+
+def kernel_roofline(kernel, alg, ms):
+    """Roofline entry of one attention kernel: HBM-bound for the split-K and vector kernels
+    (the bytes of the sequences they serve), MFMA-bound for the prefill kernel (its flops)."""
+    if kernel == "attn_prefill_mfma":
+        achieved = alg["prefill_flops"] / (ms * 1e-3) / 1e12
+        return dict(bound="mfma", achieved=achieved, peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s",
+                    frac=achieved / MFMA_BF16_PEAK_TFLOPS)
+    achieved = alg["split_bytes"] / (ms * 1e-3) / 1e9
+    return dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
+                frac=achieved / HBM_PEAK_GBS)
 
 
 def kernel_sha(path):
@@ -180,7 +213,10 @@ class Device:
         self.ql = torch.from_numpy(w.q_lens).cuda()
         self.out = torch.empty_like(self.q)
         self.max_ctx, self.max_q = int(w.ctx_lens.max()), int(w.q_lens.max())
-        self.pool.workspace(w.num_q_heads, w.num_seqs, w.total_q, self.max_ctx, self.max_q)
+        # the serving loop knows its batch's q_lens on the host: hand the library that mirror
+        self.ql_host = np.ascontiguousarray(w.q_lens, dtype=np.int32)
+        self.pool.workspace(w.num_q_heads, w.num_seqs, w.total_q, self.max_ctx, self.max_q,
+                            self.ql_host)
 
     def pre_append_host(self):
         """Host copy of the pool as drawn (taken before the first append)."""
@@ -203,7 +239,8 @@ class Device:
             self.pool.append(w.layer, self.k_new, self.v_new, self.tables, self.ctx, self.ql,
                              max_q_len=self.max_q)
         self.pool.forward(w.layer, self.q, self.tables, self.ctx, self.ql, scale=w.scale,
-                          max_ctx_len=self.max_ctx, max_q_len=self.max_q, out=self.out)
+                          max_ctx_len=self.max_ctx, max_q_len=self.max_q, out=self.out,
+                          q_lens_host=self.ql_host)
 
 
 def main():
@@ -305,28 +342,27 @@ def main():
     step_ms = [s.elapsed_time(e) for s, e in zip(starts, ends)]
     ms = float(np.mean(step_ms))
 
+    # The dominant kernel: the attention kernel with the most time per step.
     attn_kernels = [k for k in ("attn_prefill_mfma", "attn_split_mfma", "attn_vec") if k in ktimes]
-    dom = attn_kernels[0]
+    per_step = {k: ktimes[k][1] / args.steps for k in attn_kernels}
+    dom = max(attn_kernels, key=lambda k: per_step[k])
     launches, total = ktimes[dom]
     dom_ms = total / launches
     kind = info["kind"]
-    dom_bytes = alg["kv_bytes"] + w.total_q * w.num_q_heads * w.head_dim * w.elt_bytes + \
-        int(sum((int(c) + w.block_size - 1) // w.block_size for c in w.ctx_lens)) * 4
     if kind == "mfma":
-        achieved = alg["flops"] / (dom_ms * 1e-3) / 1e12
-        roof = dict(bound="mfma", achieved=achieved, peak=MFMA_BF16_PEAK_TFLOPS, unit="TFLOP/s",
-                    frac=achieved / MFMA_BF16_PEAK_TFLOPS)
         value, unit = alg["flops"] / (ms * 1e-3) / 1e12, "TFLOP/s"
     else:
-        achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
-        roof = dict(bound="hbm", achieved=achieved, peak=HBM_PEAK_GBS, unit="GB/s",
-                    frac=achieved / HBM_PEAK_GBS)
         value, unit = alg["step_bytes"] / (ms * 1e-3) / 1e9, "GB/s"
+    roof = kernel_roofline(dom, alg, dom_ms)
+    dom_bytes = alg["prefill_bytes"] if dom == "attn_prefill_mfma" else alg["split_bytes"]
     src = {"attn_split_mfma": "attn_split_mfma.hip", "attn_vec": "attn_vec.hip",
            "attn_prefill_mfma": "attn_prefill_mfma.hip"}[dom]
     roof["kernel"] = dom
     roof["kernel_ms"] = dom_ms
     roof["traffic"] = load_traffic(wname, dom)
+    # every attention kernel of the step (more than one when a call mixes sequence kinds)
+    rooflines = {k: dict(kernel_roofline(k, alg, ktimes[k][1] / ktimes[k][0]),
+                         kernel_ms=ktimes[k][1] / ktimes[k][0]) for k in attn_kernels}
 
     cpu = None
     if want_cpu:
@@ -355,6 +391,7 @@ def main():
         "algorithmic": {"step_bytes": alg["step_bytes"], "dominant_kernel_bytes": dom_bytes,
                         "flops": alg["flops"]},
         "roofline": roof,
+        "rooflines": rooflines,
         "cpu_baseline": cpu,
         "wall_s_timed_region": wall,
         "setup_s": setup_s,

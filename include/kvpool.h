@@ -122,13 +122,23 @@ KVPOOL_API int kvpool_append(kvpool_t *pool, int32_t layer, const void *k_new,
 KVPOOL_API int kvpool_copy_blocks(kvpool_t *pool, const int32_t *src, const int32_t *dst,
                                   int32_t n, void *stream);
 
-/* Workspace bytes kvattn_forward needs for these bounds (written to *bytes; may be 0). */
+/* Workspace bytes kvattn_forward needs for these bounds (written to *bytes; may be 0).
+ * q_lens_host: the optional host mirror of q_lens that kvattn_forward will get (NULL: sized for
+ * any q_lens within the bounds). */
 KVPOOL_API int kvattn_workspace_size(const kvpool_t *pool, int32_t num_q_heads,
                                      int32_t num_seqs, int32_t total_q, int32_t max_ctx_len,
-                                     int32_t max_q_len, size_t *bytes);
+                                     int32_t max_q_len, const int32_t *q_lens_host,
+                                     size_t *bytes);
 
 /* Attention of every sequence's q_lens[s] query rows against its ctx_lens[s] keys (the new
- * tokens' K/V must already be appended).
+ * tokens' K/V must already be appended).  One call may batch every kind of sequence: decode
+ * (q_len 1), verification of 1 + k drafts and prefill chunks over a cached prefix, as a serving
+ * step packs every ready request into one batch (NInfer serving doc, "Execution behavior";
+ * sparkinfer server README, "Request isolation & continuous batching").  A sequence with
+ * q_len * (num_q_heads / num_kv_heads) <= 128 takes the split-K kernel (its keys cut into splits
+ * of a size set by its own ctx_len, merged in a fixed order); a longer one takes the prefill
+ * kernel.  The path and the arithmetic of a sequence follow from its own lengths, so its output
+ * bits do not depend on the rest of the batch or on the bounds passed here.
  *   q    device, [total_q][num_q_heads][head_dim], pool dtype, rows packed in sequence order
  *   out  device, same shape and dtype as q; each element is written exactly once, rounded to
  *        nearest-even from the fp32 result
@@ -137,16 +147,21 @@ KVPOOL_API int kvattn_workspace_size(const kvpool_t *pool, int32_t num_q_heads,
  *   ctx_lens, q_lens device int32 [num_seqs]; 0 <= q_lens[s] <= ctx_lens[s]
  *                    <= max_blocks_per_seq * block_size; q_lens[s] == 0 produces no rows
  *   max_ctx_len, max_q_len  host upper bounds of ctx_lens / q_lens (size the grid)
- *   workspace        device scratch of at least kvattn_workspace_size() bytes, 256-byte
- *                    aligned; contents on entry don't matter.  Calls that may run at the same
- *                    time (other streams) need workspaces of their own.
+ *   q_lens_host      optional host copy of q_lens (read during the call, not kept; NULL
+ *                    allowed).  With it, the grids and the workspace are exact and no kernel is
+ *                    launched for a path no sequence takes; without it they are sized from the
+ *                    bounds.  It must equal the device q_lens (checked under KVPOOL_VALIDATE=1).
+ *   workspace        device scratch of at least kvattn_workspace_size() bytes (same bounds and
+ *                    mirror), 256-byte aligned; contents on entry don't matter.  Calls that may
+ *                    run at the same time (other streams) need workspaces of their own.
  * num_q_heads must be a multiple of the pool's num_kv_heads with at most 16 q-heads per KV
  * head. */
 KVPOOL_API int kvattn_forward(kvpool_t *pool, int32_t layer, const void *q, void *out,
                               int32_t num_q_heads, float scale, const int32_t *block_tables,
                               int32_t max_blocks_per_seq, const int32_t *ctx_lens,
                               const int32_t *q_lens, int32_t num_seqs, int32_t total_q,
-                              int32_t max_ctx_len, int32_t max_q_len, void *workspace,
+                              int32_t max_ctx_len, int32_t max_q_len,
+                              const int32_t *q_lens_host, void *workspace,
                               size_t workspace_bytes, void *stream);
 
 /* Opt-in per-kernel timing for measurement.  With enable != 0, every kernel launch made by this

@@ -15,6 +15,7 @@ import math
 import os
 from typing import Optional
 
+import numpy as np
 import torch
 
 # KVPOOL_LIB: load a library built elsewhere (e.g. another build of the same sources).
@@ -35,9 +36,9 @@ SIGNATURES = {
     "kvpool_destroy": (_i32, [_vp]),
     "kvpool_append": (_i32, [_vp, _i32, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _vp]),
     "kvpool_copy_blocks": (_i32, [_vp, _vp, _vp, _i32, _vp]),
-    "kvattn_workspace_size": (_i32, [_vp, _i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_sz)]),
+    "kvattn_workspace_size": (_i32, [_vp, _i32, _i32, _i32, _i32, _i32, _vp, ctypes.POINTER(_sz)]),
     "kvattn_forward": (_i32, [_vp, _i32, _vp, _vp, _i32, _f32, _vp, _i32, _vp, _vp, _i32, _i32,
-                              _i32, _i32, _vp, _sz, _vp]),
+                              _i32, _i32, _vp, _vp, _sz, _vp]),
     "kvpool_last_error": (ctypes.c_char_p, []),
     "kvpool_profile": (_i32, [_i32]),
     "kvpool_profile_kernel": (_i32, [_i32, ctypes.POINTER(ctypes.c_char_p),
@@ -150,20 +151,33 @@ def kvpool_copy_blocks(handle, src, dst, n, stream=None) -> None:
     _check(lib().kvpool_copy_blocks(handle, _ptr(src), _ptr(dst), n, _stream(stream)))
 
 
-def kvattn_workspace_size(handle, num_q_heads, num_seqs, total_q, max_ctx_len, max_q_len) -> int:
+def _host_i32(x):
+    """Host int32 array (kept alive by the caller) and its address, for the q_lens mirror."""
+    if x is None:
+        return None, None
+    arr = np.ascontiguousarray(np.asarray(x, dtype=np.int32))
+    return arr, arr.ctypes.data
+
+
+def kvattn_workspace_size(handle, num_q_heads, num_seqs, total_q, max_ctx_len, max_q_len,
+                          q_lens_host=None) -> int:
     out = _sz(0)
+    arr, addr = _host_i32(q_lens_host)
     _check(lib().kvattn_workspace_size(handle, num_q_heads, num_seqs, total_q, max_ctx_len,
-                                       max_q_len, ctypes.byref(out)))
+                                       max_q_len, addr, ctypes.byref(out)))
+    del arr
     return out.value
 
 
 def kvattn_forward(handle, layer, q, out, num_q_heads, scale, block_tables, max_blocks_per_seq,
                    ctx_lens, q_lens, num_seqs, total_q, max_ctx_len, max_q_len, workspace,
-                   workspace_bytes, stream=None) -> None:
+                   workspace_bytes, stream=None, q_lens_host=None) -> None:
+    arr, addr = _host_i32(q_lens_host)
     _check(lib().kvattn_forward(handle, layer, _ptr(q), _ptr(out), num_q_heads, float(scale),
                                 _ptr(block_tables), max_blocks_per_seq, _ptr(ctx_lens),
-                                _ptr(q_lens), num_seqs, total_q, max_ctx_len, max_q_len,
+                                _ptr(q_lens), num_seqs, total_q, max_ctx_len, max_q_len, addr,
                                 _ptr(workspace), workspace_bytes, _stream(stream)))
+    del arr
 
 
 # ---------------------------------------------------------------------------------------------
@@ -220,22 +234,26 @@ class PagedKVPool:
     def copy_blocks(self, src, dst, stream=None):
         kvpool_copy_blocks(self.handle, src, dst, src.shape[0], stream)
 
-    def workspace(self, num_q_heads, num_seqs, total_q, max_ctx_len, max_q_len):
+    def workspace(self, num_q_heads, num_seqs, total_q, max_ctx_len, max_q_len,
+                  q_lens_host=None):
         need = kvattn_workspace_size(self.handle, num_q_heads, num_seqs, total_q, max_ctx_len,
-                                     max_q_len)
+                                     max_q_len, q_lens_host)
         if need and (self._ws is None or self._ws.numel() < need):
             self._ws = torch.empty(need, dtype=torch.uint8, device=self.k_storage.device)
         return self._ws, need
 
     def forward(self, layer, q, block_tables, ctx_lens, q_lens, scale=None, max_ctx_len=None,
-                max_q_len=None, out=None, stream=None):
+                max_q_len=None, out=None, stream=None, q_lens_host=None):
+        """Attention for one call.  ``q_lens_host``: optional host copy of ``q_lens`` (list or
+        numpy); with it the library sizes grids and workspace exactly."""
         total_q, hq, d = q.shape
         scale = 1.0 / math.sqrt(d) if scale is None else scale
         max_ctx_len = int(ctx_lens.max().item()) if max_ctx_len is None else max_ctx_len
         max_q_len = int(q_lens.max().item()) if max_q_len is None else max_q_len
         out = torch.empty_like(q) if out is None else out
-        ws, need = self.workspace(hq, ctx_lens.shape[0], total_q, max_ctx_len, max_q_len)
+        ws, need = self.workspace(hq, ctx_lens.shape[0], total_q, max_ctx_len, max_q_len,
+                                  q_lens_host)
         kvattn_forward(self.handle, layer, q, out, hq, scale, block_tables, block_tables.shape[1],
                        ctx_lens, q_lens, ctx_lens.shape[0], total_q, max_ctx_len, max_q_len,
-                       ws, need, stream)
+                       ws, need, stream, q_lens_host)
         return out

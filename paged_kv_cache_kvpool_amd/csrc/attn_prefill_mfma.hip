@@ -99,6 +99,69 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
   }
 }
 
+// Row tiles of one (sequence, KV head) pair of a prefill-class sequence (q_len > split_q_max):
+// its 32-row blocks dealt to workgroups of W waves; 0 for a sequence of the split-K path.
+__device__ __forceinline__ int seq_row_tiles(const AttnArgs& a, int T, int W) {
+  if (T <= a.split_q_max) return 0;
+  const int nblk = (min(T, a.total_q) * a.group + 31) >> 5;  // T <= total_q for valid metadata
+  return (nblk + W - 1) / W;
+}
+
+// Workgroups are numbered sequence by sequence: a prefill-class sequence holds num_kv_heads *
+// row tiles of them, in (KV head, row tile) order.  Total number of them (every lane).
+__device__ __forceinline__ int prefill_wg_total(const AttnArgs& a, int W) {
+  const int lane = threadIdx.x & (WAVE - 1);
+  int acc = 0;
+  for (int base = 0; base < a.num_seqs; base += WAVE) {  // uniform trip count
+    const int j = base + lane;
+    if (j < a.num_seqs) {
+      int L, T;
+      seq_lens(a, j, L, T);
+      acc += seq_row_tiles(a, T, W) * a.num_kv_heads;
+    }
+  }
+  return wave_sum_i(acc);
+}
+
+// Sequence, KV head and row tile of workgroup n (in the numbering above), the sequence's row
+// tiles and the index of its first query token in q / out.  Wave-uniform; the whole wave must be
+// active.
+__device__ __forceinline__ void find_prefill_tile(const AttnArgs& a, int n, int W, int& s,
+                                                  int& kvh, int& rt, int& rts, int& q_start) {
+  const int lane = threadIdx.x & (WAVE - 1);
+  int wbase = 0, qbase = 0;
+  s = kvh = rt = q_start = 0;
+  rts = 1;
+  for (int base = 0; base < a.num_seqs; base += WAVE) {
+    const int j = base + lane;
+    int r = 0, q = 0;
+    if (j < a.num_seqs) {
+      int L, T;
+      seq_lens(a, j, L, T);
+      r = seq_row_tiles(a, T, W);
+      q = max(0, a.q_lens[j]);
+    }
+    const int wg = r * a.num_kv_heads;
+    const int win = wave_incl_scan(wg);
+    const int qin = wave_incl_scan(q);
+    const int wtot = __builtin_amdgcn_readlane(win, WAVE - 1);
+    const int nn = n - wbase;
+    if (nn < wtot) {
+      // Inclusive counts are nondecreasing: the workgroup's sequence is the first lane past nn.
+      const int k = __builtin_popcountll(__builtin_amdgcn_ballot_w64(win <= nn));
+      s = base + k;
+      const int within = nn - (__builtin_amdgcn_readlane(win, k) - __builtin_amdgcn_readlane(wg, k));
+      rts = __builtin_amdgcn_readlane(r, k);
+      kvh = within / rts;
+      rt = within - kvh * rts;
+      q_start = qbase + __builtin_amdgcn_readlane(qin, k) - __builtin_amdgcn_readlane(q, k);
+      return;
+    }
+    wbase += wtot;
+    qbase += __builtin_amdgcn_readlane(qin, WAVE - 1);
+  }
+}
+
 }  // namespace
 
 // Up to 12 waves per workgroup, 3 per SIMD: at most 168 registers per wave.
@@ -122,24 +185,27 @@ void attn_prefill_mfma_kernel(AttnArgs a) {
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int col = lane & 31, h = lane >> 5;  // MFMA column (query row of the wave) and half
-  const int logical = xcd_logical(blockIdx.x, gridDim.x);
-  const int rt = logical % a.row_tiles;
-  const int pair = logical / a.row_tiles;
-  const int s = pair / a.num_kv_heads, kvh = pair % a.num_kv_heads;
+  // The grid may exceed the workgroups there are (the host sized it from bounds); the ones
+  // there are get ids [0, n) and are remapped over the XCDs, the rest leave at once.
+  const int n_wg = prefill_wg_total(a, W);
+  if ((int)blockIdx.x >= n_wg) return;
+  const int logical = xcd_logical(blockIdx.x, n_wg);
+  int s, kvh, rt, rts, q_start;
+  find_prefill_tile(a, logical, W, s, kvh, rt, rts, q_start);
   int L, T;
   seq_lens(a, s, L, T);
   const int G = a.group;
   const int rows = T * G;
   // Row blocks of 32 rows are dealt to the workgroups of a (sequence, KV head) strided: wave w
-  // of row tile rt owns block rt + row_tiles * w.  Every workgroup then holds early and late
-  // rows alike, so under the causal mask all of them carry about the same work.
+  // of row tile rt owns block rt + rts * w.  Every workgroup then holds early and late rows
+  // alike, so under the causal mask all of them carry about the same work.
   const int nblk = (rows + 31) >> 5;
   if (rt >= nblk) return;
-  const int last_blk = rt + a.row_tiles * min(W - 1, (nblk - 1 - rt) / a.row_tiles);
+  const int last_blk = rt + rts * min(W - 1, (nblk - 1 - rt) / rts);
   const int ke = min(L, L - T + (min(32 * last_blk + 32, rows) - 1) / G + 1);  // keys the WG needs
   const int ntiles = (ke + 63) >> 6;
   const int npt = (ke + 15) >> 4;  // pool tiles the WG reads
-  const int rw0 = 32 * (rt + a.row_tiles * wave);
+  const int rw0 = 32 * (rt + rts * wave);
   const int kew = rw0 < rows ? min(L, L - T + (min(rw0 + 32, rows) - 1) / G + 1) : 0;
   const int pw0 = L - T + rw0 / G;  // keys <= pw0 are visible to every row of this wave
 
@@ -198,7 +264,6 @@ void attn_prefill_mfma_kernel(AttnArgs a) {
 
   // ---- Q^T operands and per-row state ----------------------------------------------------
   // B operand of k-step k: lane (col, h) holds dims 16k + 8h .. +8 of the wave's row col.
-  const int q_start = wave_prefix_total(a.q_lens, s);
   const int Hq = a.num_q_heads;
   const int r = rw0 + col;
   const int qi = r / G;
@@ -384,15 +449,23 @@ void attn_prefill_mfma_kernel(AttnArgs a) {
   }
 }
 
-int prefill_waves_choice(int rows_per_pair, int pairs, int num_cus) {
+long long prefill_wg_count(const int* rows, int n, int num_kv_heads, int waves) {
+  long long wgs = 0;
+  for (int i = 0; i < n; ++i) {
+    const long long nblk = ((long long)rows[i] + 31) / 32;
+    wgs += (nblk + waves - 1) / waves * num_kv_heads;
+  }
+  return wgs;
+}
+
+int prefill_waves_choice(const int* rows, int n, int num_kv_heads, int num_cus) {
   // Makespan model: one workgroup per CU at a time (LDS-bound); a workgroup of W waves of 32
   // rows takes ceil(W/4) wave-times on its busiest SIMD.  Pick W in 4..12 minimising
   // rounds x ceil(W/4), then the fewest idle wave slots.
   int best = 8;
   double best_cost = 1e300;
   for (int w = 4; w <= 12; ++w) {
-    const long long rows_wg = 32LL * w;
-    const long long wgs = (long long)pairs * ((rows_per_pair + rows_wg - 1) / rows_wg);
+    const long long wgs = prefill_wg_count(rows, n, num_kv_heads, w);
     const long long rounds = (wgs + num_cus - 1) / num_cus;
     const double cost = (double)rounds * ((w + 3) / 4) + 1e-3 * (double)rounds * w;
     if (cost < best_cost) {
@@ -403,9 +476,11 @@ int prefill_waves_choice(int rows_per_pair, int pairs, int num_cus) {
   return best;
 }
 
-hipError_t launch_attn_prefill_mfma(const AttnArgs& a, int head_dim, int waves, hipStream_t st) {
-  if (waves < 1 || waves > 12) return hipErrorInvalidConfiguration;
-  const dim3 grid(a.row_tiles * a.num_kv_heads * a.num_seqs);
+hipError_t launch_attn_prefill_mfma(const AttnArgs& a, int head_dim, int waves, long long wgs,
+                                    hipStream_t st) {
+  if (waves < 1 || waves > 12 || wgs < 0 || wgs > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  if (wgs == 0) return hipSuccess;
+  const dim3 grid((unsigned)wgs);
   if (head_dim == 128)
     attn_prefill_mfma_kernel<128><<<grid, 64 * waves, 0, st>>>(a);
   else

@@ -3,7 +3,8 @@
 // order, so the result is reproducible run to run (no float atomics: sparkinfer server README,
 // "Determinism").  Rows whose keys all fall in split 0 were finished by the attention kernel.
 //
-// One 256-thread workgroup per (query row, q-head).  The weights 2^{(m_i - M)c} are computed
+// One 256-thread workgroup per (row of the partial buffers, q-head); the row's sequence is
+// found from the per-sequence counts of split-K tokens.  The weights 2^{(m_i - M)c} are computed
 // once into LDS; then thread t accumulates dims 4*(t % (D/4)) .. +4 over splits
 // t / (D/4), + 256/(D/4), ..., so each pass over the partials reads whole rows of D floats
 // with 16-byte loads; the split groups are summed in LDS in a fixed order at the end.
@@ -22,16 +23,17 @@ __global__ __launch_bounds__(256) void attn_reduce_kernel(AttnArgs a) {
   constexpr int DQ = D / 4;        // float4 columns
   constexpr int SG = RT / DQ;      // split groups
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int s = blockIdx.z, hh = blockIdx.y, i = blockIdx.x;
+  const int r = blockIdx.x, hh = blockIdx.y;
+  int s, i, q_start;
+  if (!find_split_row(a, r, s, i, q_start)) return;
   int L, T;
   seq_lens(a, s, L, T);
-  if (i >= T) return;
   const int p = L - T + i;
   const int ns = min(a.max_splits, p / seq_split(a, L) + 1);
   if (ns <= 1) return;
-  const int grow = wave_prefix_total(a.q_lens, s) + i;
+  const int grow = q_start + i;
   if (grow >= a.total_q) return;
-  const size_t slot0 = ((size_t)grow * a.num_q_heads + hh) * a.max_splits;
+  const size_t slot0 = ((size_t)r * a.num_q_heads + hh) * a.max_splits;
   const float c = a.scale_log2;
 
   __shared__ float s_w[WMAX];
@@ -86,9 +88,9 @@ __global__ __launch_bounds__(256) void attn_reduce_kernel(AttnArgs a) {
   }
 }
 
-hipError_t launch_attn_reduce(const AttnArgs& a, int elt_bytes, int head_dim, int max_q_len,
-                              hipStream_t st) {
-  dim3 grid(max_q_len, a.num_q_heads, a.num_seqs);
+hipError_t launch_attn_reduce(const AttnArgs& a, int elt_bytes, int head_dim, hipStream_t st) {
+  if (a.part_rows <= 0) return hipSuccess;
+  dim3 grid(a.part_rows, a.num_q_heads);
   if (elt_bytes == 2) {
     if (head_dim == 128) attn_reduce_kernel<uint16_t, 128><<<grid, RT, 0, st>>>(a);
     else attn_reduce_kernel<uint16_t, 64><<<grid, RT, 0, st>>>(a);

@@ -10,13 +10,16 @@
 // fall in split 0 is finished here and skips the reduce.
 //
 // Scheduling: persistent waves.  The grid holds as many one-wave workgroups as the GPU keeps
-// resident at once, and each wave takes items from a ticket counter (one integer atomic per
-// item) until none are left.  Items are numbered sequence by sequence and found from prefix
-// sums of per-sequence item counts held one sequence per lane.  While a wave streams one item,
-// the ticket and block ids of its next item are already in registers, so it moves from the
-// last chunk of one item to the loads of the next with no metadata round trip, and no slot of
-// the GPU waits on a workgroup that turns out to have no keys.  Which wave computes an item
-// never changes that item's result.
+// resident at once, W, and wave w takes items w, w + W, w + 2W, ... (a fixed round robin, no
+// atomics).  Items are numbered sequence by sequence and found from prefix sums of per-sequence
+// item counts held one sequence per lane.  While a wave streams one item, the block ids of its
+// next item are already in registers, so it moves from the last chunk of one item to the loads
+// of the next with no metadata round trip.  Which wave computes an item never changes that
+// item's result.
+//
+// Only sequences whose q_len is at most split_q_max are served here; longer query blocks of
+// the same call (a prefill chunk batched with decode rows) are left to the prefill kernel.
+// Partials are stored at the row's index among the split-K tokens of the call.
 //
 // Per item, rows are (token, head-in-group) pairs, so the G q-heads sharing a KV head use one
 // read of K/V, walked in 32-key chunks:
@@ -75,6 +78,7 @@ struct Item {
   int s, kvh, rt, sp;
   int L, T;     // keys of the sequence, query rows (tokens) of the sequence
   int q_start;  // index of the sequence's first query token in q / out
+  int p_start;  // its first row in the partial buffers
   int kb, ke;   // the item's keys [kb, ke): its split, cut at its last row's position + 1
   int split;    // keys per split of this sequence
 };
@@ -82,17 +86,14 @@ struct Item {
 // Key range of an item; false if no row of the item sees a key of its split.
 template <int NT>
 __device__ __forceinline__ bool item_keys(const AttnArgs& a, Item& it) {
+  if (it.T > a.split_q_max) return false;  // a prefill-class sequence
   const int rows = it.T * a.group;
   const int r0 = it.rt * 16 * NT;
   if (r0 >= rows) return false;
   const int p_last = it.L - it.T + (min(r0 + 16 * NT, rows) - 1) / a.group;
   it.split = seq_split(a, it.L);
-  it.kb = 0;
-  it.ke = min(it.L, p_last + 1);
-  if (a.split_mode) {
-    it.kb = it.sp * it.split;
-    it.ke = min(it.ke, it.kb + it.split);
-  }
+  it.kb = it.sp * it.split;
+  it.ke = min(min(it.L, p_last + 1), it.kb + it.split);
   return it.kb < it.ke;
 }
 
@@ -271,13 +272,16 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, const Item& it, int 
     compute(bufA, ci);
   }
 
+  // Adds to a row's output index (q_start + i) * Hq + head to give its partial row index
+  // (p_start + i) * Hq + head (modulo 2^64: the sum is never negative).
+  const size_t pofs = (size_t)(((long long)it.p_start - q_start) * Hq);
   if constexpr (NW == 1) {
     // One wave per split: finish straight from registers.
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const float lt = xrow_sum(l_run[nt]);
       if (prow[nt] < kb) continue;  // padding row, or a row that sees no key of this split
-      const bool final_here = !a.split_mode || prow[nt] < split;
+      const bool final_here = prow[nt] < split;
       if (final_here) {
         const float inv = 1.f / lt;
         uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + rh[nt] * D;
@@ -289,7 +293,9 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, const Item& it, int 
           *reinterpret_cast<uint2*>(op + 16 * mt + 4 * g) = make_uint2(w0, w1);
         }
       } else {
-        const size_t slot = rh[nt] * a.max_splits + sp;
+        const size_t prh = rh[nt] + pofs;  // (p_start + i) * Hq + head
+        if (prh >= (size_t)a.part_rows * Hq) continue;
+        const size_t slot = prh * a.max_splits + sp;
         if (g == 0) {
           a.part_ml[2 * slot] = m_run[nt];
           a.part_ml[2 * slot + 1] = lt;
@@ -329,7 +335,7 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, const Item& it, int 
       for (int mt = 0; mt < MT; ++mt) s_o[wave][mt][lane] = o[nt][mt] * myscale;
       __syncthreads();
       const bool row_ok = prow[nt] >= kb;  // a real row that sees a key of this split
-      const bool final_here = !a.split_mode || prow[nt] < split;
+      const bool final_here = prow[nt] < split;
       if (row_ok) {
         if (final_here) {
           const float inv = 1.f / Lsum;
@@ -343,8 +349,8 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, const Item& it, int 
             const uint32_t w1 = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
             *reinterpret_cast<uint2*>(op + 16 * mt + 4 * g) = make_uint2(w0, w1);
           }
-        } else {
-          const size_t slot = rh[nt] * a.max_splits + sp;
+        } else if (rh[nt] + pofs < (size_t)a.part_rows * Hq) {
+          const size_t slot = (rh[nt] + pofs) * a.max_splits + sp;
           if (wave == 0 && g == 0) {
             a.part_ml[2 * slot] = M;
             a.part_ml[2 * slot + 1] = Lsum;
@@ -364,22 +370,11 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, const Item& it, int 
 
 // ---- persistent scheduling ----------------------------------------------------------------
 
-// Inclusive prefix sum over the wave.
-__device__ __forceinline__ int wave_incl_scan(int v) {
-  const int lane = threadIdx.x & (WAVE - 1);
-#pragma unroll
-  for (int d = 1; d < WAVE; d <<= 1) {
-    const int t = __shfl_up(v, d);
-    if (lane >= d) v += t;
-  }
-  return v;
-}
-
 // Items of one sequence: splits x KV heads x row tiles, bounded by the launch's workspace
 // geometry (max_splits, row_tiles) whatever the device metadata says.
 template <int NT>
 __device__ __forceinline__ int seq_items(const AttnArgs& a, int L, int T) {
-  if (T <= 0) return 0;
+  if (T <= 0 || T > a.split_q_max) return 0;  // no rows, or a prefill-class sequence
   const int split = seq_split(a, L);
   const int ns = min(L / split + (L % split != 0), a.max_splits);
   const int rts = min((T * a.group + 16 * NT - 1) / (16 * NT), a.row_tiles);
@@ -391,10 +386,13 @@ struct SeqGroup {
   int base;       // first sequence of the group
   int item_base;  // items of the sequences before the group
   int q_base;     // query tokens of the sequences before the group
+  int p_base;     // split-K tokens (partial rows) of the sequences before the group
   int items;      // items of the group
   int q_total;    // query tokens of the group
+  int p_total;    // split-K tokens of the group
   int incl;       // lane: items of sequences base .. base + lane
   int L, T, qx;   // lane: its lengths and the query tokens of the group's sequences before it
+  int px;         // lane: split-K tokens of the group's sequences before it
 };
 
 template <int NT>
@@ -410,6 +408,10 @@ __device__ __forceinline__ void load_group(const AttnArgs& a, SeqGroup& gp, int 
   gp.incl = wave_incl_scan(seq_items<NT>(a, L, T));
   const int qi = wave_incl_scan(q);
   gp.qx = qi - q;
+  const int pr = T <= a.split_q_max ? T : 0;
+  const int pi = wave_incl_scan(pr);
+  gp.px = pi - pr;
+  gp.p_total = __builtin_amdgcn_readlane(pi, WAVE - 1);
   gp.L = L;
   gp.T = T;
   gp.items = __builtin_amdgcn_readlane(gp.incl, WAVE - 1);
@@ -423,12 +425,14 @@ __device__ __forceinline__ bool find_item(const AttnArgs& a, SeqGroup& gp, int t
   if (t < gp.item_base) {  // tickets of a wave normally increase; restart the scan if not
     gp.item_base = 0;
     gp.q_base = 0;
+    gp.p_base = 0;
     load_group<NT>(a, gp, 0);
   }
   while (t - gp.item_base >= gp.items) {
     if (gp.base + WAVE >= a.num_seqs) return false;
     gp.item_base += gp.items;
     gp.q_base += gp.q_total;
+    gp.p_base += gp.p_total;
     load_group<NT>(a, gp, gp.base + WAVE);
   }
   const int r_in = t - gp.item_base;
@@ -438,6 +442,7 @@ __device__ __forceinline__ bool find_item(const AttnArgs& a, SeqGroup& gp, int t
   it.L = __builtin_amdgcn_readlane(gp.L, j);
   it.T = __builtin_amdgcn_readlane(gp.T, j);
   it.q_start = gp.q_base + __builtin_amdgcn_readlane(gp.qx, j);
+  it.p_start = gp.p_base + __builtin_amdgcn_readlane(gp.px, j);
   const int rts = min((it.T * a.group + 16 * NT - 1) / (16 * NT), a.row_tiles);
   it.kvh = r % a.num_kv_heads;
   r /= a.num_kv_heads;
@@ -458,6 +463,7 @@ void attn_split_persist_kernel(AttnArgs a) {
   SeqGroup gp;
   gp.item_base = 0;
   gp.q_base = 0;
+  gp.p_base = 0;
   load_group<NT>(a, gp, 0);
   Item cur;
   int t = blockIdx.x;
@@ -511,7 +517,7 @@ __global__ __launch_bounds__(256) void attn_split_mfma_kernel(AttnArgs a) {
   const int ntile = wb < we ? (we - wb + 15) >> 4 : 0;
   const int ids0 = tile_block_id(a, it.s, wb, ntile, it.ke, 0);
   const int ids1 = tile_block_id(a, it.s, wb, ntile, it.ke, 64);
-  it.q_start = wave_prefix_total(a.q_lens, it.s);
+  seq_starts(a, it.s, it.q_start, it.p_start);
   // vmcnt(0) (encoding: vmcnt 0, expcnt 7, lgkmcnt 15), so the compiler knows the block ids
   // have arrived and never waits for them inside the chunk loop.
   __builtin_amdgcn_s_waitcnt(0x0F70);
@@ -535,7 +541,7 @@ int persist_blocks_per_cu() {
 
 template <int D, int NT>
 hipError_t launch_split(const AttnArgs& a, int splits, int num_cus, hipStream_t st) {
-  const bool persistent = a.split_mode && a.split_tokens <= 2048;
+  const bool persistent = a.split_tokens <= 2048;
   if (persistent) {
     const int per_cu = persist_blocks_per_cu<D, NT>();
     if (per_cu <= 0) return hipErrorInvalidConfiguration;
@@ -545,7 +551,7 @@ hipError_t launch_split(const AttnArgs& a, int splits, int num_cus, hipStream_t 
   } else {
     if (splits > 65535) return hipErrorInvalidConfiguration;
     const dim3 grid(a.num_kv_heads * a.num_seqs * a.row_tiles, splits, 1);
-    if (!a.split_mode || a.split_tokens > 8192)
+    if (a.split_tokens > 8192)
       attn_split_mfma_kernel<D, NT, true><<<grid, 256, 0, st>>>(a);
     else
       attn_split_mfma_kernel<D, NT, false><<<grid, 256, 0, st>>>(a);

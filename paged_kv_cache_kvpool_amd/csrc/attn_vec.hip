@@ -3,7 +3,8 @@
 // The fp32 path of every call, and an alternative bf16 decode path.  Same work split as the
 // matrix-core kernel: one wave per (row tile, split, KV head, sequence), partials merged by
 // the reduce kernel in fixed split order (no float atomics: sparkinfer server README,
-// "Determinism").
+// "Determinism").  Sequences with more than split_q_max query tokens make one pass (split 0
+// only) in the same launch.
 //
 // Per 16-token tile the wave reads K and V with contiguous 1 KiB wave loads (16 bytes per
 // lane).  With the pool's tile layout, lane l of K load j holds dim chunk 4*j + l/16 of token
@@ -58,14 +59,16 @@ __global__ __launch_bounds__(64) void attn_vec_kernel(AttnArgs a) {
   const int r0 = rt * ROWS;
   if (r0 >= rows) return;
   const int p_last = L - T + (min(r0 + ROWS, rows) - 1) / G;
-  const int split = seq_split(a, L);
-  int kb = 0, ke = min(L, p_last + 1);
-  if (a.split_mode) {
-    kb = sp * split;
-    ke = min(ke, kb + split);
-  }
+  // Split-K sequences (q_len <= split_q_max) cut their keys into splits; longer query blocks
+  // make one pass over all their keys, in split slot 0.
+  const bool split_k = T <= a.split_q_max;
+  if (!split_k && sp > 0) return;
+  const int split = split_k ? seq_split(a, L) : L;
+  const int kb = split_k ? sp * split : 0;
+  const int ke = min(min(L, p_last + 1), kb + split);
   if (kb >= ke) return;
-  const int q_start = wave_prefix_total(a.q_lens, s);
+  int q_start, p_start;
+  seq_starts(a, s, q_start, p_start);
   const int Hq = a.num_q_heads;
 
   // q[r][j][w]: the dims of chunk 4*j + g (fp32 values, or packed bf16 pairs).
@@ -197,8 +200,10 @@ __global__ __launch_bounds__(64) void attn_vec_kernel(AttnArgs a) {
     }
     if (prow[r] < kb) continue;
     // Rows whose keys all lie in split 0 are finished here (the reduce skips them).
-    if (a.split_mode && prow[r] >= split) {
-      const size_t slot = rh[r] * a.max_splits + sp;
+    if (prow[r] >= split) {
+      const size_t prh = rh[r] + (size_t)(((long long)p_start - q_start) * Hq);  // partial row
+      if (prh >= (size_t)a.part_rows * Hq) continue;
+      const size_t slot = prh * a.max_splits + sp;
       if (lane == 0) {
         a.part_ml[2 * slot] = m_run[r];
         a.part_ml[2 * slot + 1] = lt;

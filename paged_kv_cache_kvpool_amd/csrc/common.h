@@ -94,16 +94,40 @@ __device__ __forceinline__ float row_max(float x) {
   return x;
 }
 
-// Sum of v[0 .. n) over the wave, every lane gets it (n small: a few thousand at most).
+// Integer reductions over the wave (exact at any size), result in every lane.
+template <int CTRL>
+__device__ __forceinline__ int dpp_i(int x) {
+  return __builtin_amdgcn_update_dpp(0, x, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ int wave_sum_i(int x) {
+  x += dpp_i<DPP_ROR8>(x);
+  x += dpp_i<DPP_ROR4>(x);
+  x += dpp_i<DPP_XOR2>(x);
+  x += dpp_i<DPP_XOR1>(x);
+  auto r = __builtin_amdgcn_permlane32_swap((uint32_t)x, (uint32_t)x, false, false);
+  x = (int)(r[0] + r[1]);
+  r = __builtin_amdgcn_permlane16_swap((uint32_t)x, (uint32_t)x, false, false);
+  return (int)(r[0] + r[1]);
+}
+
+// Inclusive prefix sum over the wave.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & (WAVE - 1);
+#pragma unroll
+  for (int d = 1; d < WAVE; d <<= 1) {
+    const int t = __shfl_up(v, d);
+    if (lane >= d) v += t;
+  }
+  return v;
+}
+
+// Sum of v[0 .. n) over the wave (negative entries count 0), every lane gets it.
 __device__ __forceinline__ int wave_prefix_total(const int32_t* v, int n) {
   const int lane = threadIdx.x & (WAVE - 1);
   int acc = 0;
   for (int base = 0; base < n; base += WAVE)  // uniform trip count
     acc += (base + lane < n) ? max(0, v[base + lane]) : 0;
-  float f = (float)acc;  // exact: totals stay far below 2^24
-  f = row_sum(f);
-  f = xrow_sum(f);
-  return (int)f;
+  return wave_sum_i(acc);
 }
 
 // Workgroup barrier without a memory fence.  __syncthreads() also waits for every outstanding
@@ -129,19 +153,20 @@ struct AttnArgs {
   const int32_t* block_tables;
   const int32_t* ctx_lens;
   const int32_t* q_lens;
-  float* part_o;            // [total_q][Hq][max_splits][D]   (split mode)
-  float* part_ml;           // [total_q][Hq][max_splits][2]   (split mode: max, sum)
+  float* part_o;            // [part_rows][Hq][max_splits][D]  split-K partial outputs
+  float* part_ml;           // [part_rows][Hq][max_splits][2]  their (max, sum) pairs
   int32_t num_seqs, total_q, num_q_heads, num_kv_heads, group, block_size, num_blocks;
   int32_t block_shift;      // log2(block_size)
   int32_t max_blocks_per_seq;
-  int32_t split_tokens;     // split mode: keys per split if > 0, else the per-length rule
-  int32_t max_splits;       // splits per row slot in the workspace (split mode)
-  int32_t row_tiles;        // row tiles per (sequence, kv head)
-  int32_t split_mode;       // 1: write partials for the reduce kernel; 0: write `out`
+  int32_t split_tokens;     // split-K path: keys per split if > 0, else the per-length rule
+  int32_t max_splits;       // splits per partial row in the workspace
+  int32_t row_tiles;        // split-K and vector kernels: row tiles per (sequence, kv head)
+  int32_t split_q_max;      // sequences with q_len <= split_q_max take the split-K path
+  int32_t part_rows;        // rows of the partial buffers (query tokens of the split-K path)
   float scale_log2;         // softmax scale * log2(e)
 };
 
-// Keys per split of a sequence with L keys (split mode): a fixed count if the caller set one,
+// Keys per split of a sequence with L keys on the split-K path: a fixed count if the caller set one,
 // else ceil(L/128) rounded up to a multiple of 32 and clamped to [256, 2048].  That gives at
 // most 128 splits up to 262144 keys (so one long sequence's splits fit the GPU in one pass, with
 // no sliver of a split left over), and it depends on the sequence's own length only, so its
@@ -157,6 +182,61 @@ __device__ __forceinline__ void seq_lens(const AttnArgs& a, int s, int& L, int& 
   int cap = a.max_blocks_per_seq * a.block_size;
   L = min(max(a.ctx_lens[s], 0), cap);
   T = min(max(a.q_lens[s], 0), L);
+}
+
+// Query tokens the split-K path holds for sequence s: its q_len if that is at most split_q_max
+// (decode and verification), else 0 (its rows make one pass in the prefill kernel).  The class
+// depends on the sequence alone, so a sequence's rows take the same path in any batch.
+__device__ __forceinline__ int split_rows_of(const AttnArgs& a, int s) {
+  int L, T;
+  seq_lens(a, s, L, T);
+  return T <= a.split_q_max ? T : 0;
+}
+
+// First rows of sequence s: in q / out (the raw q_lens of the sequences before it, as the
+// packing counts them) and in the partial buffers (the split-K tokens of the sequences before
+// it).  Every lane gets both.
+__device__ __forceinline__ void seq_starts(const AttnArgs& a, int s, int& q_start, int& p_start) {
+  const int lane = threadIdx.x & (WAVE - 1);
+  int qa = 0, pa = 0;
+  for (int base = 0; base < s; base += WAVE) {  // uniform trip count
+    const int j = base + lane;
+    if (j < s) {
+      qa += max(0, a.q_lens[j]);
+      pa += split_rows_of(a, j);
+    }
+  }
+  q_start = wave_sum_i(qa);
+  p_start = wave_sum_i(pa);
+}
+
+// Sequence s and query row i of partial row r (the split-K tokens of the call, numbered in
+// sequence order), and the sequence's first row in q / out.  False if r is past the last one.
+// Wave-uniform; the whole wave must be active.
+__device__ __forceinline__ bool find_split_row(const AttnArgs& a, int r, int& s, int& i,
+                                               int& q_start) {
+  const int lane = threadIdx.x & (WAVE - 1);
+  int pbase = 0, qbase = 0;
+  for (int base = 0; base < a.num_seqs; base += WAVE) {
+    const int j = base + lane;
+    const int pr = j < a.num_seqs ? split_rows_of(a, j) : 0;
+    const int q = j < a.num_seqs ? max(0, a.q_lens[j]) : 0;
+    const int pin = wave_incl_scan(pr);
+    const int qin = wave_incl_scan(q);
+    const int ptot = __builtin_amdgcn_readlane(pin, WAVE - 1);
+    const int rr = r - pbase;
+    if (rr < ptot) {
+      // Inclusive counts are nondecreasing: the row's sequence is the first lane past rr.
+      const int k = __builtin_popcountll(__builtin_amdgcn_ballot_w64(pin <= rr));
+      s = base + k;
+      i = rr - (__builtin_amdgcn_readlane(pin, k) - __builtin_amdgcn_readlane(pr, k));
+      q_start = qbase + __builtin_amdgcn_readlane(qin, k) - __builtin_amdgcn_readlane(q, k);
+      return true;
+    }
+    pbase += ptot;
+    qbase += __builtin_amdgcn_readlane(qin, WAVE - 1);
+  }
+  return false;
 }
 
 // Element offset of the 16-token tile holding logical position `pos` of sequence s for KV head

@@ -32,23 +32,28 @@ struct CopyArgs {
 hipError_t launch_append(const AppendArgs& a, int elt_bytes, int max_q_len, hipStream_t st);
 hipError_t launch_copy_blocks(const CopyArgs& a, int n, int num_layers, hipStream_t st);
 
-// Split-K attention on the matrix cores (bf16), split mode: items of (row tile of <= 32 rows,
-// split, KV head, sequence) dealt round-robin to persistent waves (num_cus sizes the grid), or,
-// for forced splits longer than 2048 keys, one 4-wave workgroup per item.  `splits`: most
-// splits of any sequence (at most 65535 for the 4-wave variant).
+// Split-K attention on the matrix cores (bf16) for the sequences with q_len <= split_q_max:
+// items of (row tile of <= 32 rows, split, KV head, sequence) dealt round-robin to persistent
+// waves (num_cus sizes the grid), or, for forced splits longer than 2048 keys, one 4-wave
+// workgroup per item.  `splits`: most splits of any sequence (at most 65535 for the 4-wave
+// variant).
 hipError_t launch_attn_split_mfma(const AttnArgs& a, int head_dim, int rows_per_tile,
                                   int splits, int num_cus, hipStream_t st);
 // Vector-ALU attention (fp32 and bf16), one wave per (row tile of <= 8 rows, split, KV head,
-// sequence).
+// sequence); sequences past split_q_max make one pass in split slot 0.
 hipError_t launch_attn_vec(const AttnArgs& a, int elt_bytes, int head_dim, int rows_per_tile,
                            int grid_x, hipStream_t st);
-// Prefill attention on the matrix cores (bf16): `waves` (1..12) waves x 32 rows share LDS-staged
-// K/V tiles; one workgroup per (row tile, KV head, sequence), a.row_tiles row tiles per pair.
-hipError_t launch_attn_prefill_mfma(const AttnArgs& a, int head_dim, int waves, hipStream_t st);
-// Waves per workgroup (4..12) for a prefill call: balances workgroups over the CUs.
-int prefill_waves_choice(int rows_per_pair, int pairs, int num_cus);
-// Cross-split merge of the partials written in split mode.
-hipError_t launch_attn_reduce(const AttnArgs& a, int elt_bytes, int head_dim, int max_q_len,
-                              hipStream_t st);
+// Prefill attention on the matrix cores (bf16) for the sequences with q_len > split_q_max:
+// `waves` (1..12) waves x 32 rows share LDS-staged K/V tiles; the workgroups, numbered sequence
+// by sequence (KV heads x row tiles of each prefill-class sequence), are found on the device
+// from q_lens.  `wgs`: grid size, at least the number of workgroups there are (extra ones exit).
+hipError_t launch_attn_prefill_mfma(const AttnArgs& a, int head_dim, int waves, long long wgs,
+                                    hipStream_t st);
+// Workgroups of the prefill kernel for prefill-class sequences of rows[i] = q_len * G rows each.
+long long prefill_wg_count(const int* rows, int n, int num_kv_heads, int waves);
+// Waves per workgroup (4..12) for such a set of sequences: balances workgroups over the CUs.
+int prefill_waves_choice(const int* rows, int n, int num_kv_heads, int num_cus);
+// Cross-split merge of the split-K partials: one workgroup per (partial row, q-head).
+hipError_t launch_attn_reduce(const AttnArgs& a, int elt_bytes, int head_dim, hipStream_t st);
 
 }  // namespace kvp

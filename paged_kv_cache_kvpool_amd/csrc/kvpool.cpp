@@ -70,9 +70,10 @@ int max_split_count(int split, int max_ctx) {
   return std::max(std::max(1, std::min(128, (max_ctx + 255) / 256)), (max_ctx + 2047) / 2048);
 }
 
-// Split mode serves decode and verification (few query rows per KV head): the context is cut
-// into splits so that even one sequence fills the GPU.  Longer query blocks (prefill) carry
-// enough rows to fill it without splitting.
+// The split-K path serves decode and verification (few query rows per KV head): a sequence's
+// context is cut into splits so that even one sequence fills the GPU.  A sequence whose q_len
+// times the group size exceeds this many rows (a prefill chunk) carries enough rows to fill it
+// without splitting and takes the prefill kernel.  The class depends on the sequence alone.
 constexpr int kSplitRowsMax = 128;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -363,25 +364,78 @@ int kvpool_copy_blocks(kvpool_t* pool, const int32_t* src, const int32_t* dst, i
 namespace {
 
 struct Plan {
-  bool split_mode;
-  int split;
-  int max_splits;
+  int split_q_max;    // sequences with q_len <= split_q_max take the split-K path
+  bool split_k;       // some sequence may take the split-K path with at least one row
+  bool prefill;       // some sequence may take the prefill kernel
+  int split_rows;     // rows per KV head of the longest split-K sequence (bound)
+  int split;          // fixed keys per split, or 0 for the per-length rule
+  int max_splits;     // split slots per partial row
+  int part_rows;      // partial rows: the split-K path's query tokens (or a bound of them)
+  int waves;          // prefill workgroup size
+  long long pf_wgs;   // prefill grid: its workgroups (or a bound of them)
+  size_t o_bytes;     // partial outputs, rounded up to 256 bytes
   size_t bytes;
 };
 
-Plan make_plan(const kvpool* p, int32_t num_q_heads, int32_t total_q, int32_t max_ctx_len,
-               int32_t max_q_len) {
+// The plan of one call.  With the host mirror of q_lens, the split-K rows, the prefill
+// sequences and the grids are exact; without it, they are bounds from (num_seqs, total_q,
+// max_q_len).  Either way the kernels decide each sequence's path from the device q_lens.
+Plan make_plan(const kvpool* p, int32_t num_q_heads, int32_t num_seqs, int32_t total_q,
+               int32_t max_ctx_len, int32_t max_q_len, const int32_t* q_lens_host) {
   Plan pl{};
   const int G = num_q_heads / p->num_kv_heads;
-  pl.split_mode = (long long)max_q_len * G <= kSplitRowsMax;
+  const int sqm = kSplitRowsMax / G;
+  pl.split_q_max = sqm;
   pl.split = split_tokens();
-  pl.max_splits = pl.split_mode ? max_split_count(pl.split, max_ctx_len) : 1;
-  if (pl.split_mode) {
-    // [partial outputs, fp32][partial (max, sum) pairs, fp32]
-    const size_t slots = (size_t)total_q * num_q_heads * pl.max_splits;
-    const size_t o_bytes = (slots * p->head_dim * 4 + 255) / 256 * 256;
-    pl.bytes = o_bytes + slots * 2 * 4;
+  pl.max_splits = max_split_count(pl.split, max_ctx_len);
+  std::vector<int> pf_rows;
+  if (q_lens_host) {
+    long long split_tokens_sum = 0;
+    int split_t = 0;
+    for (int s = 0; s < num_seqs; ++s) {
+      const int T = std::max(0, std::min(q_lens_host[s], max_q_len));
+      if (T <= sqm) {
+        split_tokens_sum += T;
+        split_t = std::max(split_t, T);
+      } else {
+        pf_rows.push_back(T * G);
+      }
+    }
+    pl.split_k = split_tokens_sum > 0;
+    pl.split_rows = split_t * G;
+    pl.part_rows = (int)std::min<long long>(split_tokens_sum, total_q);
+    pl.prefill = !pf_rows.empty();
+  } else {
+    pl.split_k = true;
+    pl.split_rows = std::min(max_q_len, sqm) * G;
+    pl.prefill = max_q_len > sqm;
+    // When every sequence is split-K, all query tokens are; otherwise each split-K sequence
+    // holds at most split_q_max of them.
+    pl.part_rows = pl.prefill ? (int)std::min<long long>(total_q, (long long)num_seqs * sqm) : total_q;
+    // For the workgroup size: as many sequences of max_q_len tokens as total_q allows.
+    if (pl.prefill) {
+      const int n = (int)std::min<long long>(num_seqs, (total_q + max_q_len - 1) / max_q_len);
+      pf_rows.assign(std::max(n, 1), max_q_len * G);
+    }
   }
+  if (pl.prefill) {
+    pl.waves = kvp::prefill_waves_choice(pf_rows.data(), (int)pf_rows.size(), p->num_kv_heads, p->num_cus);
+    if (const char* v = getenv("KVATTN_PREFILL_WAVES")) pl.waves = std::max(1, std::min(12, atoi(v)));  // sweeps
+    if (q_lens_host) {
+      pl.pf_wgs = kvp::prefill_wg_count(pf_rows.data(), (int)pf_rows.size(), p->num_kv_heads, pl.waves);
+    } else {
+      // n prefill sequences (at most total_q / (split_q_max + 1)) of sum(T) <= total_q hold at
+      // most (total_q * G + 31 n) / 32 row blocks, in at most (blocks + n (W - 1)) / W row
+      // tiles per KV head.
+      const long long n = std::min<long long>(num_seqs, total_q / (sqm + 1));
+      const long long blocks = ((long long)total_q * G + 31 * n) / 32;
+      pl.pf_wgs = (blocks + n * (pl.waves - 1)) / pl.waves * p->num_kv_heads;
+    }
+  }
+  // [partial outputs, fp32][partial (max, sum) pairs, fp32]
+  const size_t slots = (size_t)pl.part_rows * num_q_heads * pl.max_splits;
+  pl.o_bytes = (slots * p->head_dim * 4 + 255) / 256 * 256;
+  pl.bytes = slots ? pl.o_bytes + slots * 2 * 4 : 0;
   return pl;
 }
 
@@ -389,21 +443,22 @@ Plan make_plan(const kvpool* p, int32_t num_q_heads, int32_t total_q, int32_t ma
 
 int kvattn_workspace_size(const kvpool_t* pool, int32_t num_q_heads, int32_t num_seqs,
                           int32_t total_q, int32_t max_ctx_len, int32_t max_q_len,
-                          size_t* bytes) {
+                          const int32_t* q_lens_host, size_t* bytes) {
   if (!pool || !bytes) return fail(KV_EINVAL, "pool or bytes is NULL");
   if (num_q_heads <= 0 || num_q_heads % pool->num_kv_heads)
     return fail(KV_EINVAL, "num_q_heads must be a positive multiple of num_kv_heads");
   if (num_seqs < 0 || total_q < 0 || max_ctx_len < 0 || max_q_len < 0)
     return fail(KV_EINVAL, "negative size argument");
-  *bytes = make_plan(pool, num_q_heads, total_q, max_ctx_len, max_q_len).bytes;
+  *bytes = make_plan(pool, num_q_heads, num_seqs, total_q, max_ctx_len, max_q_len, q_lens_host).bytes;
   return ok();
 }
 
 int kvattn_forward(kvpool_t* pool, int32_t layer, const void* q, void* out, int32_t num_q_heads,
                    float scale, const int32_t* block_tables, int32_t max_blocks_per_seq,
                    const int32_t* ctx_lens, const int32_t* q_lens, int32_t num_seqs,
-                   int32_t total_q, int32_t max_ctx_len, int32_t max_q_len, void* workspace,
-                   size_t workspace_bytes, void* stream) {
+                   int32_t total_q, int32_t max_ctx_len, int32_t max_q_len,
+                   const int32_t* q_lens_host, void* workspace, size_t workspace_bytes,
+                   void* stream) {
   if (!pool) return fail(KV_EINVAL, "pool is NULL");
   if (layer < 0 || layer >= pool->num_layers) return fail(KV_EINVAL, "layer %d out of range", layer);
   if (num_q_heads <= 0 || num_q_heads % pool->num_kv_heads)
@@ -425,7 +480,7 @@ int kvattn_forward(kvpool_t* pool, int32_t layer, const void* q, void* out, int3
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   if (current_device_matches(pool) != hipSuccess)
     return fail(KV_EINVAL, "current HIP device is not the pool's device %d", pool->device);
-  const Plan pl = make_plan(pool, num_q_heads, total_q, max_ctx_len, max_q_len);
+  const Plan pl = make_plan(pool, num_q_heads, num_seqs, total_q, max_ctx_len, max_q_len, q_lens_host);
   if (pl.max_splits > 65535)
     return fail(KV_ERANGE, "%d splits per sequence exceed the launch grid (65535)", pl.max_splits);
   if ((long long)total_q * num_q_heads >= (1ll << 31))
@@ -445,6 +500,10 @@ int kvattn_forward(kvpool_t* pool, int32_t layer, const void* q, void* out, int3
     if (rc) return rc;
     rc = validate_meta(pool, m, max_blocks_per_seq, num_seqs, total_q, max_ctx_len, max_q_len);
     if (rc) return rc;
+    if (q_lens_host)
+      for (int s = 0; s < num_seqs; ++s)
+        if (q_lens_host[s] != m.ql[s])
+          return fail(KV_ERANGE, "seq %d: q_lens_host %d != q_lens %d", s, q_lens_host[s], m.ql[s]);
   }
 
   kvp::AttnArgs a;
@@ -456,11 +515,9 @@ int kvattn_forward(kvpool_t* pool, int32_t layer, const void* q, void* out, int3
   a.block_tables = block_tables;
   a.ctx_lens = ctx_lens;
   a.q_lens = q_lens;
-  const size_t slots = (size_t)total_q * num_q_heads * pl.max_splits;
   char* ws = static_cast<char*>(workspace);
   a.part_o = pl.bytes ? reinterpret_cast<float*>(ws) : nullptr;
-  a.part_ml = pl.bytes ? reinterpret_cast<float*>(ws + (slots * pool->head_dim * 4 + 255) / 256 * 256)
-                       : nullptr;
+  a.part_ml = pl.bytes ? reinterpret_cast<float*>(ws + pl.o_bytes) : nullptr;
   a.num_seqs = num_seqs;
   a.total_q = total_q;
   a.num_q_heads = num_q_heads;
@@ -472,34 +529,39 @@ int kvattn_forward(kvpool_t* pool, int32_t layer, const void* q, void* out, int3
   a.max_blocks_per_seq = max_blocks_per_seq;
   a.split_tokens = pl.split;
   a.max_splits = pl.max_splits;
-  a.split_mode = pl.split_mode ? 1 : 0;
+  a.split_q_max = pl.split_q_max;
+  a.part_rows = pl.part_rows;
   a.scale_log2 = scale * kvp::LOG2E;
 
-  const int rows = max_q_len * G;
   const int eb = elt_bytes(pool->dtype);
-  hipError_t e;
-  if (pool->dtype == KV_F32 || (pl.split_mode && max_q_len == 1 && env_flag("KVATTN_DECODE_VEC"))) {
+  hipError_t e = hipSuccess;
+  if (pool->dtype == KV_F32 || (!pl.prefill && max_q_len == 1 && env_flag("KVATTN_DECODE_VEC"))) {
+    // One launch for every sequence: split-K sequences in splits, longer ones in one pass.
     // Rows per wave: the template instance just large enough (1, 2, 4, 5 or 8).
+    const int rows = max_q_len * G;
     const int r8 = std::min(rows, 8);
     const int rpt = r8 <= 1 ? 1 : r8 <= 2 ? 2 : r8 <= 4 ? 4 : r8 <= 5 ? 5 : 8;
     a.row_tiles = (rows + rpt - 1) / rpt;
     e = timed(K_VEC, st, [&] { return kvp::launch_attn_vec(a, eb, pool->head_dim, rpt, a.row_tiles * pl.max_splits, st); });
-  } else if (pl.split_mode) {
-    const int rpt = rows <= 16 ? 16 : 32;
-    a.row_tiles = (rows + rpt - 1) / rpt;
-    e = timed(K_SPLIT_MFMA, st, [&] { return kvp::launch_attn_split_mfma(a, pool->head_dim, rpt, pl.max_splits, pool->num_cus, st); });
   } else {
-    int waves = kvp::prefill_waves_choice(rows, num_seqs * pool->num_kv_heads, pool->num_cus);
-    if (const char* v = getenv("KVATTN_PREFILL_WAVES")) waves = std::max(1, std::min(12, atoi(v)));  // sweeps
-    a.row_tiles = (rows + 32 * waves - 1) / (32 * waves);
-    e = timed(K_PREFILL_MFMA, st, [&] { return kvp::launch_attn_prefill_mfma(a, pool->head_dim, waves, st); });
+    // Split-K sequences (decode, verification) on persistent waves, then the prefill kernel
+    // for the longer query blocks of the same call.  Each kernel skips the other's sequences.
+    if (pl.split_k) {
+      const int rpt = pl.split_rows <= 16 ? 16 : 32;
+      kvp::AttnArgs as = a;
+      as.row_tiles = (pl.split_rows + rpt - 1) / rpt;
+      e = timed(K_SPLIT_MFMA, st, [&] { return kvp::launch_attn_split_mfma(as, pool->head_dim, rpt, pl.max_splits, pool->num_cus, st); });
+    }
+    if (e == hipSuccess && pl.prefill) {
+      e = timed(K_PREFILL_MFMA, st, [&] { return kvp::launch_attn_prefill_mfma(a, pool->head_dim, pl.waves, pl.pf_wgs, st); });
+    }
   }
   if (e != hipSuccess) return fail(KV_EDEVICE, "attention launch: %s", hipGetErrorString(e));
-  // Rows whose keys all fall in split 0 are finished by the attention kernel; when no sequence
+  // Rows whose keys all fall in split 0 are finished by the attention kernels; when no sequence
   // can have a second split (every split holds >= 256 keys) the reduce has nothing to do.
-  const bool need_reduce = pl.split_mode && max_ctx_len > (pl.split > 0 ? pl.split : 256);
+  const bool need_reduce = pl.split_k && max_ctx_len > (pl.split > 0 ? pl.split : 256);
   if (need_reduce) {
-    e = timed(K_REDUCE, st, [&] { return kvp::launch_attn_reduce(a, eb, pool->head_dim, max_q_len, st); });
+    e = timed(K_REDUCE, st, [&] { return kvp::launch_attn_reduce(a, eb, pool->head_dim, st); });
     if (e != hipSuccess) return fail(KV_EDEVICE, "reduce launch: %s", hipGetErrorString(e));
   }
   return ok();

@@ -227,6 +227,23 @@ def long_decode(seed: int = 4, host_pool: bool = False) -> Workload:
                 num_blocks=24576, host_pool=host_pool)
 
 
+def mixed_step(seed: int = 5, host_pool: bool = True) -> Workload:
+    """One serving step that batches every kind of sequence the pool serves: 32 decode
+    sequences (1 token, contexts uniform on [1024, 8192]), one verification of 1 + 3 draft
+    tokens over a 32768-token context and one 512-token prefill chunk over a 4096-token cached
+    prefix; 40/8 heads, D=128, bf16, B=16.  New tokens' K/V are appended first."""
+    rng = np.random.default_rng(seed)
+    ctx = list(rng.integers(1024, 8193, size=32).astype(np.int32))
+    ql = [1] * 32
+    # the verification and the prefill chunk sit between decode sequences
+    ctx[10:10] = [32768 + 4]
+    ql[10:10] = [4]
+    ctx[20:20] = [4096 + 512]
+    ql[20:20] = [512]
+    return make("mixed_step", seed=seed + 1000, dtype=BF16, num_seqs_ctx=ctx, q_lens=ql,
+                num_q_heads=40, num_kv_heads=8, head_dim=128, append=True, host_pool=host_pool)
+
+
 def random_case(seed: int, *, dtype=BF16, num_seqs=3, num_q_heads=8, num_kv_heads=2,
                 head_dim=64, block_size=16, q_len_choices=(1, 2, 4, 17), max_ctx=300,
                 extra_blocks=5, append=True) -> Workload:

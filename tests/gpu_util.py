@@ -65,11 +65,13 @@ class DeviceCase:
             self.pool.append(self.w.layer, self.k_new, self.v_new, self.tables, self.ctx, self.ql,
                              max_q_len=int(self.w.q_lens.max()))
 
-    def forward(self, q=None, out=None):
+    def forward(self, q=None, out=None, mirror=False):
+        """Attention through the library; ``mirror``: also hand it the host copy of q_lens."""
         w = self.w
         return self.pool.forward(w.layer, self.q if q is None else q, self.tables, self.ctx,
                                  self.ql, scale=w.scale, max_ctx_len=int(w.ctx_lens.max()),
-                                 max_q_len=int(w.q_lens.max()), out=out)
+                                 max_q_len=int(w.q_lens.max()), out=out,
+                                 q_lens_host=w.q_lens if mirror else None)
 
     # -- host copies for the oracle ---------------------------------------------------------
     def host_pools(self):

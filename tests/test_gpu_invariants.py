@@ -81,6 +81,32 @@ def test_batch_invariance_and_repeatability_bitwise(dtype):
         assert np.array_equal(bits(alone), bits(full[rows])), f"sequence {s}"
 
 
+@pytest.mark.parametrize("dtype", [wl.BF16, wl.F32])
+def test_mixed_batch_invariance_bitwise(dtype):
+    """Decode, verification and prefill sequences in one call give, bit for bit, what each gives
+    alone with bounds of its own (max_ctx_len, max_q_len): the kernel and the split plan follow
+    from the sequence itself, never from the rest of the batch."""
+    announce(f"mixed batch invariance {dtype}")
+    w = wl.make("mixed_inv", seed=151, dtype=dtype, num_seqs_ctx=[3000, 700, 1000, 9000, 129, 40],
+                q_lens=[1, 4, 300, 4, 129, 33], num_q_heads=40, num_kv_heads=8, head_dim=128)
+    c = DeviceCase(w)
+    c.append()
+    full = c.forward()
+    exact = c.forward(mirror=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(full), bits(exact)), "bounds vs host mirror"
+    starts = np.concatenate([[0], np.cumsum(w.q_lens)])
+    for s in range(w.num_seqs):
+        rows = slice(int(starts[s]), int(starts[s + 1]))
+        sel = torch.tensor([s], device="cuda")
+        for mirror in (None, w.q_lens[s:s + 1]):
+            alone = c.pool.forward(0, c.q[rows], c.tables[sel], c.ctx[sel], c.ql[sel],
+                                   scale=w.scale, max_ctx_len=int(w.ctx_lens[s]),
+                                   max_q_len=int(w.q_lens[s]), q_lens_host=mirror)
+            torch.cuda.synchronize()
+            assert np.array_equal(bits(alone), bits(full[rows])), f"sequence {s} mirror={mirror}"
+
+
 @pytest.mark.parametrize("dtype,bs", [(wl.BF16, 16), (wl.BF16, 64), (wl.F32, 16)])
 def test_nan_in_unread_slots(dtype, bs):
     """Pool starts all-NaN; the append writes exactly the context, so every slot past ctx_len and
@@ -216,6 +242,10 @@ def test_validation_codes(monkeypatch):
                                                  max_ctx_len=20))
     # sum(q_lens) != total_q
     _expect(kb.KV_ERANGE, lambda: c.pool.forward(0, c.q[:2], c.tables, c.ctx, c.ql, scale=w.scale))
+    # a host mirror of q_lens that differs from the device q_lens
+    _expect(kb.KV_ERANGE, lambda: c.pool.forward(0, c.q, c.tables, c.ctx, c.ql, scale=w.scale,
+                                                 q_lens_host=[1, 2]))
+    c.pool.forward(0, c.q, c.tables, c.ctx, c.ql, scale=w.scale, q_lens_host=w.q_lens)
     # two sequences writing the same block
     shared = c.tables.clone()
     shared[1, 1] = shared[0, 2]

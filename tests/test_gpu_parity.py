@@ -157,6 +157,36 @@ def test_attention_prefill_plans(plan, head_dim, monkeypatch):
     assert_close(out_f64(out), c.oracle(), wl.BF16, w.name)
 
 
+MIXED_CASES = [
+    # (dtype, Hq, Hkv, D, B): G = 4, 5, 8 and 1; both head dims and block sizes
+    (wl.BF16, 32, 8, 128, 16),
+    (wl.BF16, 40, 8, 128, 64),
+    (wl.BF16, 16, 2, 64, 16),
+    (wl.BF16, 4, 4, 64, 64),
+    (wl.F32, 10, 2, 64, 16),
+]
+
+
+@pytest.mark.parametrize("mirror", [False, True], ids=["bounds", "mirror"])
+@pytest.mark.parametrize("dtype,hq,hkv,d,bs", MIXED_CASES,
+                         ids=[f"{c[0]}_H{c[1]}x{c[2]}_D{c[3]}_B{c[4]}" for c in MIXED_CASES])
+def test_mixed_step(dtype, hq, hkv, d, bs, mirror):
+    """Decode, verification and prefill sequences in one call: each takes the kernel its own
+    q_len selects (split-K up to 128 rows per KV head, the prefill kernel past that), with
+    empty and one-key sequences between them; grids sized from the bounds, or exactly from the
+    host mirror of q_lens."""
+    announce(f"mixed step {dtype} Hq={hq} Hkv={hkv} D={d} B={bs} mirror={mirror}")
+    w = wl.make(f"mixed_{dtype}_{hq}_{d}_{bs}", seed=141 + hq + d + bs, dtype=dtype,
+                num_seqs_ctx=[3000, 700, 1000, 1, 129, 9000, 50, 300, 20],
+                q_lens=[1, 4, 300, 1, 129, 4, 0, 33, 20],
+                num_q_heads=hq, num_kv_heads=hkv, head_dim=d, block_size=bs)
+    c = DeviceCase(w)
+    c.append()
+    out = c.forward(mirror=mirror)
+    torch.cuda.synchronize()
+    assert_close(out_f64(out), c.oracle(), dtype, w.name)
+
+
 def test_decode_vec_kernel_bf16(monkeypatch):
     """The vector-ALU bf16 decode variant (selected by KVATTN_DECODE_VEC=1)."""
     monkeypatch.setenv("KVATTN_DECODE_VEC", "1")
@@ -210,6 +240,16 @@ def test_prefix_prefill_full():
     c = DeviceCase(w)
     c.append()
     out = c.forward()
+    torch.cuda.synchronize()
+    assert_close(out_f64(out), c.oracle(), wl.BF16, w.name)
+
+
+def test_mixed_step_full():
+    announce("mixed_step (32 decode + 1 verify at 32768 + 1 prefill chunk of 512 over 4096)")
+    w = wl.mixed_step()
+    c = DeviceCase(w)
+    c.append()
+    out = c.forward(mirror=True)
     torch.cuda.synchronize()
     assert_close(out_f64(out), c.oracle(), wl.BF16, w.name)
 
