@@ -23,6 +23,8 @@
 //   O^T[dim][row] += V^T . P^T   2 k-steps x D/32 MFMAs
 // The logical workgroup order is remapped so that the row tiles of one (sequence, KV head) run
 // on the same XCD (workgroups are dealt to the 8 XCDs round-robin) and share its L2.
+#include <algorithm>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -100,16 +102,17 @@ __device__ __forceinline__ void wait_vmcnt(int n) {
 }
 
 // Row tiles of one (sequence, KV head) pair of a prefill-class sequence (q_len > split_q_max):
-// its 32-row blocks dealt to workgroups of W waves; 0 for a sequence of the split-K path.
-__device__ __forceinline__ int seq_row_tiles(const AttnArgs& a, int T, int W) {
+// its 32-row blocks dealt to workgroups of R row blocks each; 0 for a sequence of the split-K
+// path.
+__device__ __forceinline__ int seq_row_tiles(const AttnArgs& a, int T, int R) {
   if (T <= a.split_q_max) return 0;
   const int nblk = (min(T, a.total_q) * a.group + 31) >> 5;  // T <= total_q for valid metadata
-  return (nblk + W - 1) / W;
+  return (nblk + R - 1) / R;
 }
 
 // Workgroups are numbered sequence by sequence: a prefill-class sequence holds num_kv_heads *
 // row tiles of them, in (KV head, row tile) order.  Total number of them (every lane).
-__device__ __forceinline__ int prefill_wg_total(const AttnArgs& a, int W) {
+__device__ __forceinline__ int prefill_wg_total(const AttnArgs& a, int R) {
   const int lane = threadIdx.x & (WAVE - 1);
   int acc = 0;
   for (int base = 0; base < a.num_seqs; base += WAVE) {  // uniform trip count
@@ -117,7 +120,7 @@ __device__ __forceinline__ int prefill_wg_total(const AttnArgs& a, int W) {
     if (j < a.num_seqs) {
       int L, T;
       seq_lens(a, j, L, T);
-      acc += seq_row_tiles(a, T, W) * a.num_kv_heads;
+      acc += seq_row_tiles(a, T, R) * a.num_kv_heads;
     }
   }
   return wave_sum_i(acc);
@@ -126,7 +129,7 @@ __device__ __forceinline__ int prefill_wg_total(const AttnArgs& a, int W) {
 // Sequence, KV head and row tile of workgroup n (in the numbering above), the sequence's row
 // tiles and the index of its first query token in q / out.  Wave-uniform; the whole wave must be
 // active.
-__device__ __forceinline__ void find_prefill_tile(const AttnArgs& a, int n, int W, int& s,
+__device__ __forceinline__ void find_prefill_tile(const AttnArgs& a, int n, int R, int& s,
                                                   int& kvh, int& rt, int& rts, int& q_start) {
   const int lane = threadIdx.x & (WAVE - 1);
   int wbase = 0, qbase = 0;
@@ -138,7 +141,7 @@ __device__ __forceinline__ void find_prefill_tile(const AttnArgs& a, int n, int 
     if (j < a.num_seqs) {
       int L, T;
       seq_lens(a, j, L, T);
-      r = seq_row_tiles(a, T, W);
+      r = seq_row_tiles(a, T, R);
       q = max(0, a.q_lens[j]);
     }
     const int wg = r * a.num_kv_heads;
@@ -164,6 +167,33 @@ __device__ __forceinline__ void find_prefill_tile(const AttnArgs& a, int n, int 
 
 }  // namespace
 
+// Issue order of one finish (the softmax and P.V of a 32-key block beside the score product of
+// the next), as chunks of at most one MFMA each.  MFMA u < D/16 is k-step u of the next block's
+// score product; u = D/16 + (D/32) j + mb is k-step j of P.V for output dims 32mb .. +32, which
+// needs the P packs 4j .. 4j+3 (made two per chunk in chunks 0-7, so j = 0 may start at chunk
+// 4 and j = 1 at chunk 8).  -1: a chunk without MFMA.  Operand loads run two MFMAs ahead.
+template <int D> struct PfSched;
+template <> struct PfSched<128> {
+  static constexpr int N = 16;
+  static constexpr int kOp[16] = {0, 1, 2, 3, 8, 4, 9, 5, 10, 6, 11, 7, 12, 13, 14, 15};
+  static constexpr int op(int ci) { return kOp[ci]; }
+  static constexpr int slot(int ci) { return ci; }
+  static constexpr int next_load(int ci) { return ci + 2 < N ? ci + 2 : -1; }
+  static constexpr int slot_of_load(int ci) { return ci; }
+};
+template <> struct PfSched<64> {
+  static constexpr int N = 10;
+  static constexpr int kOp[10] = {0, 1, 2, 3, 4, 5, -1, -1, 6, 7};
+  // MFMA chunks in order, and each chunk's index among them (operand slot)
+  static constexpr int kMf[8] = {0, 1, 2, 3, 4, 5, 8, 9};
+  static constexpr int kSlot[10] = {0, 1, 2, 3, 4, 5, 0, 0, 6, 7};
+  static constexpr int op(int ci) { return kOp[ci]; }
+  static constexpr int slot(int ci) { return kSlot[ci]; }
+  // the chunk whose operand the MFMA of chunk ci loads: the MFMA two places later
+  static constexpr int next_load(int ci) { return kSlot[ci] + 2 < 8 ? kMf[kSlot[ci] + 2] : -1; }
+  static constexpr int slot_of_load(int ci) { return kSlot[ci]; }
+};
+
 // Up to 12 waves per workgroup, 3 per SIMD: at most 168 registers per wave.
 template <int D>
 __global__ __launch_bounds__(768) __attribute__((amdgpu_waves_per_eu(3)))
@@ -179,6 +209,7 @@ void attn_prefill_mfma_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) uint16_t lds0[8][TE];
   __shared__ __attribute__((aligned(16))) uint16_t lds1[8][TE];
   __shared__ __attribute__((aligned(16))) uint16_t lds2[8][TE];
+  __shared__ __attribute__((aligned(16))) uint16_t lds3[8][TE];
   __shared__ __attribute__((aligned(16))) int s_ids[IDS];
 
   const int W = blockDim.x >> 6;
@@ -187,27 +218,39 @@ void attn_prefill_mfma_kernel(AttnArgs a) {
   const int col = lane & 31, h = lane >> 5;  // MFMA column (query row of the wave) and half
   // The grid may exceed the workgroups there are (the host sized it from bounds); the ones
   // there are get ids [0, n) and are remapped over the XCDs, the rest leave at once.
-  const int n_wg = prefill_wg_total(a, W);
+  // R row blocks per workgroup, W/2 <= R <= W: the first F = 2R - W waves own one block each,
+  // the other W - F waves pair up on the remaining blocks, the two waves of a pair taking the
+  // even and the odd 32-key blocks (merged at the end).  Waves w, w+4, w+8 share a SIMD, so
+  // with W = 12 and R = 10 every SIMD carries 2.5 blocks.
+  const int R = a.pf_rblk;
+  const int F = 2 * R - W;
+  const bool half = wave >= F;
+  const int rb = half ? F + ((wave - F) >> 1) : wave;  // the wave's row block in the workgroup
+  const int par = half ? ((wave - F) & 1) : 0;          // half waves: parity of their blocks
+  const int n_wg = prefill_wg_total(a, R);
   if ((int)blockIdx.x >= n_wg) return;
   const int logical = xcd_logical(blockIdx.x, n_wg);
   int s, kvh, rt, rts, q_start;
-  find_prefill_tile(a, logical, W, s, kvh, rt, rts, q_start);
+  find_prefill_tile(a, logical, R, s, kvh, rt, rts, q_start);
   int L, T;
   seq_lens(a, s, L, T);
+  // wave-uniform: kept in scalar registers so the per-block edge tests stay on the SALU
+  L = __builtin_amdgcn_readfirstlane(L);
+  T = __builtin_amdgcn_readfirstlane(T);
   const int G = a.group;
   const int rows = T * G;
-  // Row blocks of 32 rows are dealt to the workgroups of a (sequence, KV head) strided: wave w
-  // of row tile rt owns block rt + rts * w.  Every workgroup then holds early and late rows
-  // alike, so under the causal mask all of them carry about the same work.
+  // Row blocks of 32 rows are dealt to the workgroups of a (sequence, KV head) strided: row
+  // block k of row tile rt is block rt + rts * k of the pair.  Every workgroup then holds early
+  // and late rows alike, so under the causal mask all of them carry about the same work.
   const int nblk = (rows + 31) >> 5;
   if (rt >= nblk) return;
-  const int last_blk = rt + rts * min(W - 1, (nblk - 1 - rt) / rts);
+  const int last_blk = rt + rts * min(R - 1, (nblk - 1 - rt) / rts);
   const int ke = min(L, L - T + (min(32 * last_blk + 32, rows) - 1) / G + 1);  // keys the WG needs
   const int ntiles = (ke + 63) >> 6;
   const int npt = (ke + 15) >> 4;  // pool tiles the WG reads
-  const int rw0 = 32 * (rt + rts * wave);
-  const int kew = rw0 < rows ? min(L, L - T + (min(rw0 + 32, rows) - 1) / G + 1) : 0;
-  const int pw0 = L - T + rw0 / G;  // keys <= pw0 are visible to every row of this wave
+  const int rw0 = 32 * (rt + rts * rb);
+  const int kew = __builtin_amdgcn_readfirstlane(rw0 < rows ? min(L, L - T + (min(rw0 + 32, rows) - 1) / G + 1) : 0);
+  const int pw0 = __builtin_amdgcn_readfirstlane(L - T + rw0 / G);  // keys <= pw0: visible to every row of the wave
 
   const int32_t* tbl = a.block_tables + (size_t)s * a.max_blocks_per_seq;
   const char* kbase = reinterpret_cast<const char*>(a.k_layer);
@@ -230,8 +273,9 @@ void attn_prefill_mfma_kernel(AttnArgs a) {
   // l's 16 bytes land at base + 16*l).  Pool tiles past the context re-read the last one;
   // those keys are masked and their V zeroed.
   // The 4 block ids a stage needs (pool tiles 4j .. 4j+3, already clamped in the cache) are
-  // read from the cache with one ds_read_b128 a step ahead of their use, so the issue of a
-  // stage's DMA never waits on LDS, and its addresses are computed in scalar registers.
+  // read from the cache with one ds_read_b128 just before the issue (by the issuing waves only)
+  // and moved to scalar registers, where the addresses are computed; holding them in vector
+  // registers across a step would cost registers the compute loop needs.
   typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
   // The DMA issue goes to the waves of the least loaded SIMDs (waves are placed on the 4 SIMDs
   // round-robin, so with W % 4 != 0 the SIMDs holding wave indices >= W % 4 mod 4 carry one
@@ -246,6 +290,7 @@ void attn_prefill_mfma_kernel(AttnArgs a) {
   const int my_pieces = issue_rank < 0 ? 0 : (8 - issue_rank + nissue - 1) / nissue * TQ;
   auto read_ids = [&](int j) -> i32x4 { return *reinterpret_cast<const i32x4*>(&s_ids[4 * j - ids0]); };
   auto fetch = [&](int j, const i32x4& ids, uint16_t (&stage)[8][TE]) {
+    if (issue_rank < 0) return;  // wave-uniform
     int blk[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) blk[t] = __builtin_amdgcn_readfirstlane(ids[t]);
@@ -258,9 +303,11 @@ void attn_prefill_mfma_kernel(AttnArgs a) {
       dma_tile<TQ>((slot < 4 ? kbase : vbase) + off, lane_off, lds_address(stage[slot]));
     }
   };
+  // Three tiles in flight from the start (clamped: a short context re-reads its last tile, so
+  // every wave's count of outstanding pieces follows the same pattern).
   fetch(0, read_ids(0), lds0);
-  if (ntiles > 1) fetch(1, read_ids(1), lds1);
-  i32x4 ids_next = read_ids(min(2, ntiles - 1));  // for the fetch of step 0
+  fetch(min(1, ntiles - 1), read_ids(min(1, ntiles - 1)), lds1);
+  fetch(min(2, ntiles - 1), read_ids(min(2, ntiles - 1)), lds2);
 
   // ---- Q^T operands and per-row state ----------------------------------------------------
   // B operand of k-step k: lane (col, h) holds dims 16k + 8h .. +8 of the wave's row col.
@@ -269,9 +316,11 @@ void attn_prefill_mfma_kernel(AttnArgs a) {
   const int qi = r / G;
   const bool valid = r < rows && q_start + qi < a.total_q;
   const int prow = valid ? L - T + qi : -1;  // the row's position (keys <= prow are visible)
-  const size_t rh = valid ? (size_t)(q_start + qi) * Hq + kvh * G + r % G : 0;
+  // the row's index in q / out (recomputed for the store rather than held through the loop)
+  auto row_index = [&]() -> size_t { return valid ? (size_t)(q_start + qi) * Hq + kvh * G + r % G : 0; };
   bf16x8 qb[KS];
   {
+    const size_t rh = row_index();
     const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + rh * D + 8 * h;
 #pragma unroll
     for (int k = 0; k < KS; ++k) {
@@ -279,9 +328,10 @@ void attn_prefill_mfma_kernel(AttnArgs a) {
       qb[k] = __builtin_bit_cast(bf16x8, valid ? *reinterpret_cast<const u32x4*>(qp + 16 * k) : z);
     }
   }
-  // m_run: running row max (raw score units, the same in both lanes of a row); l_lane: this
-  // lane's share of the row sum; o: O^T, element e of block mb = dim 32mb + 8(e/4) + 4h + e%4.
-  float m_run = -INFINITY, l_lane = 0.f;
+  // msub: the running row max times c, in exp2 units (the same in both lanes of a row; -inf
+  // until the row's first key); l_lane: this lane's share of the row sum; o: O^T, element e of
+  // block mb = dim 32mb + 8(e/4) + 4h + e%4.
+  float msub = -INFINITY, l_lane = 0.f;
   floatx16 o[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
@@ -297,8 +347,8 @@ void attn_prefill_mfma_kernel(AttnArgs a) {
   // V^T: dim col of the 32-dim block, tokens 8h .. +8 of the k-step's pool tile.
   const uint32_t v_lane = (uint32_t)((col * 16 + 8 * h) * 2);  // bytes
 
-  // Tile 0 must have landed (the prologue's own waits may already have drained more).
-  __builtin_amdgcn_s_waitcnt(0x0F70);
+  // Tiles 0 and 1 must have landed (at most this wave's pieces of tile 2 outstanding).
+  wait_vmcnt(my_pieces);
   __syncthreads();
 
   // V slots of keys at or past the context (only in the last 64-key tile) may hold anything,
@@ -318,6 +368,7 @@ void attn_prefill_mfma_kernel(AttnArgs a) {
     barrier_no_fence();
   };
   zero_tail(lds0, 0);
+  zero_tail(lds1, 1);
 
   // Attention of this wave's 32 rows against one 32-key block (pool tiles 2b, 2b+1 of the
   // stage).  `edge`: the block reaches past the wave's first row (causal diagonal) or past the
@@ -336,96 +387,168 @@ void attn_prefill_mfma_kernel(AttnArgs a) {
     }
     return sc;
   };
-  // `edge`: the block reaches past the wave's first row (causal diagonal) or past the context,
-  // so its scores are masked.  Returns P (bf16 pairs, keys in PV order).
-  auto softmax = [&](floatx16 sc, int kb, bool edge, uint32_t (&pk)[8]) {
+  // Masks the scores of an edge block (past the wave's first row on the causal diagonal, or past
+  // the context), then raises the running max where a row's max grew by more than 2^8 in exp2
+  // units (lazy: P stays <= 256 and the rescale is rare).  The max is IEEE maximum (no NaN
+  // quieting needed: a masked score is -inf, never NaN).
+  auto row_max = [&](floatx16& sc, int kb, bool edge) {
     if (edge) {
+      // keys of this lane: kb + 16 (e / 8) + 8 h' + e % 8 (h' recomputed from the lane id here
+      // rather than held in a register through the loop)
+      const int hh = (__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) >> 5) & 1;
+      const int lim = min(prow, L - 1) - kb - 8 * hh;  // e is visible iff 16 (e / 8) + e % 8 <= lim
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int key = kb + 16 * (e >> 3) + 8 * h + (e & 7);
-        if (key > prow || key >= L) sc[e] = -INFINITY;
-      }
+      for (int e = 0; e < 16; ++e)
+        if (16 * (e >> 3) + (e & 7) > lim) sc[e] = -INFINITY;
     }
-    // lazy: the running max moves only when a row's max grows by more than 2^8 in exp2 units,
-    // so P stays <= 256 and the rescale is rare
-    float cmax = fmaxf(fmaxf(sc[0], sc[1]), sc[2]);
+    float cmax = __builtin_elementwise_maximum(__builtin_elementwise_maximum(sc[0], sc[1]), sc[2]);
 #pragma unroll
-    for (int e = 3; e < 15; e += 2) cmax = fmaxf(fmaxf(cmax, sc[e]), sc[e + 1]);
-    cmax = fmaxf(cmax, sc[15]);
+    for (int e = 3; e < 15; e += 2)
+      cmax = __builtin_elementwise_maximum(__builtin_elementwise_maximum(cmax, sc[e]), sc[e + 1]);
+    cmax = __builtin_elementwise_maximum(cmax, sc[15]);
     {
       float x, y;
       swap32(cmax, x, y);
-      cmax = fmaxf(x, y);
+      cmax = __builtin_elementwise_maximum(x, y);
     }
-    const bool grow = (cmax - m_run) * c > 8.f;  // false for NaN (both -inf)
+    // true on a row's first key (msub = -inf); false for a row with no key yet (NaN)
+    const float cm = cmax * c;
+    const bool grow = cm - msub > 8.f;
     if (__builtin_amdgcn_ballot_w64(grow)) {
-      const float m_new = grow ? cmax : m_run;
-      const float alpha = grow ? fast_exp2((m_run - m_new) * c) : 1.f;
+      const float m_new = grow ? cm : msub;
+      const float alpha = grow ? fast_exp2(msub - m_new) : 1.f;  // 0 on the first key
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) o[mb] *= alpha;
       l_lane *= alpha;
-      m_run = m_new;
+      msub = m_new;
     }
-    const float msub = m_run == -INFINITY ? 0.f : m_run * c;
-    float psum = 0.f;
-#pragma unroll
-    for (int e = 0; e < 16; e += 2) {
-      const float p0 = fast_exp2(sc[e] * c - msub), p1 = fast_exp2(sc[e + 1] * c - msub);
-      psum += p0 + p1;
-      pk[e >> 1] = cvt_pk_bf16(p0, p1);
-    }
-    l_lane += psum;
   };
-  // O^T += V^T P^T: k-step j takes keys 16j + 8h .. +8 (pool tile 2b + j)
-  auto pv = [&](const uint16_t (&stage)[8][TE], int b, const uint32_t (&pk)[8]) {
+  // Software pipeline over the wave's 32-key blocks: finishing block b (softmax, P.V) goes with
+  // the score product of block b+1, so each wave always has matrix work in flight beside its
+  // softmax and the waves of a SIMD need not take turns.  sc holds the scores of the block being
+  // finished.  Edge blocks (past the wave's first row or the context) take the masked path.
+  floatx16 sc;
+  // Issue order of one finish, chunk by chunk (see PfSched).
+  using Sched = PfSched<D>;
+  // finish(blk, cur, nst, stride): block blk of stage `cur`, with the score product of the
+  // wave's next block blk + stride (1 for a whole-block wave, 2 for a half wave) from `nst`.
+  auto finish = [&](int blk, const uint16_t (&cur)[8][TE], const uint16_t (&nst)[8][TE], int stride) {
+    const int kb = 32 * blk;
+    if (kb >= kew) return;  // wave-uniform
+    row_max(sc, kb, kb + 31 > pw0 || kb + 32 > L);
+    // operands: K of the next block (in the same stage or the next one; past the wave's keys
+    // its scores are never used), V^T of block blk
+    const char* kt = reinterpret_cast<const char*>(nst[2 * ((blk + stride) & 1)]) + k_lane;
+    const char* vt0 = reinterpret_cast<const char*>(cur[4 + 2 * (blk & 1)]) + v_lane;
+    const char* vt1 = reinterpret_cast<const char*>(cur[5 + 2 * (blk & 1)]) + v_lane;
+    auto load_op = [&](int u) -> u32x4 {
+      if (u < KS) return *reinterpret_cast<const u32x4*>(kt + u * 2 * 16 * 16);  // chunk 2u + h
+      const int j = (u - KS) / MB, mb = (u - KS) % MB;
+      return *reinterpret_cast<const u32x4*>((j ? vt1 : vt0) + mb * 32 * 16 * 2);
+    };
+    u32x4 ops[Sched::N];
+    ops[0] = load_op(Sched::op(0));
+    ops[1] = load_op(Sched::op(1));
+    floatx16 sn;
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pk[4 * j], pk[4 * j + 1], pk[4 * j + 2], pk[4 * j + 3]});
-      const char* vt = reinterpret_cast<const char*>(stage[4 + 2 * b + j]) + v_lane;
+    for (int e = 0; e < 16; ++e) sn[e] = 0.f;
+    uint32_t pk[8];
+    __builtin_amdgcn_sched_barrier(0);
+    // Chunks pinned in place: at most one MFMA, the operand load two MFMAs ahead, and a share
+    // of the softmax (exp2 of two scores, their bf16 pack and row sum in chunks 0-7), so the
+    // VALU and the matrix core work side by side.
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const u32x4 v = *reinterpret_cast<const u32x4*>(vt + mb * 32 * 16 * 2);
-        o[mb] = mfma32(__builtin_bit_cast(bf16x8, v), pb, o[mb]);
+    for (int ci = 0; ci < Sched::N; ++ci) {
+      const int u = Sched::op(ci);
+      if (u >= 0) {
+        const bf16x8 av = __builtin_bit_cast(bf16x8, ops[Sched::slot(ci)]);
+        if (u < KS) {
+          sn = mfma32(av, qb[u], sn);
+        } else {
+          const int j = (u - KS) / MB, mb = (u - KS) % MB;
+          const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pk[4 * j], pk[4 * j + 1], pk[4 * j + 2], pk[4 * j + 3]});
+          o[mb] = mfma32(av, pb, o[mb]);
+        }
+        const int nx = Sched::next_load(ci);
+        if (nx >= 0) ops[Sched::slot_of_load(nx)] = load_op(Sched::op(nx));
       }
+      if (ci < 8) {
+        const float p0 = fast_exp2(__builtin_fmaf(sc[2 * ci], c, -msub));
+        const float p1 = fast_exp2(__builtin_fmaf(sc[2 * ci + 1], c, -msub));
+        pk[ci] = cvt_pk_bf16(p0, p1);
+        // row sum of the fp32 values (plain adds: the bf16 dot2 would take matrix-pipe slots)
+        l_lane += p0 + p1;
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
+    sc = sn;
   };
+  if (kew > 0) sc = qk(lds0, par);  // the wave's first block: 0, or 1 for an odd half wave
 
-  // One 64-key tile: compute tile j from `cur` while tile j+2 streams into `nxt2`; tile j+1
-  // (in `nxt1`) is published at the end.
-  auto step = [&](int j, uint16_t (&cur)[8][TE], uint16_t (&nxt1)[8][TE], uint16_t (&nxt2)[8][TE]) {
-    fetch(min(j + 2, ntiles - 1), ids_next, nxt2);
-    // the ids of the next step's stage; refill the id cache first when they lie past it (rare:
-    // only past 16K keys)
-    const int jn = min(j + 3, ntiles - 1);
-    if (4 * jn + 3 - ids0 >= IDS) {
+  // One 64-key tile j (stage `cur`): tile j+3 starts streaming into `nxt3` (free: its last
+  // reader, tile j-1, was done before the barrier that ended the previous step); the blocks of
+  // tile j are finished, their successors' score products reading `nxt1` (published a step
+  // ago); then tile j+2 (in `nxt2`, issued a step ago) is waited for and published.
+  auto step = [&](int j, uint16_t (&cur)[8][TE], uint16_t (&nxt1)[8][TE], uint16_t (&nxt2)[8][TE],
+                  uint16_t (&nxt3)[8][TE]) {
+    // the ids of tile j+3; refill the id cache first when they lie past it (rare: only past
+    // 16K keys; workgroup-uniform)
+    const int jf = min(j + 3, ntiles - 1);
+    if (4 * jf + 3 - ids0 >= IDS) {
       __syncthreads();
-      ids0 = 4 * jn;
+      ids0 = 4 * jf;
       load_ids(ids0);
       __syncthreads();
     }
-    ids_next = read_ids(jn);
-    // Blocks that reach past the wave's first row (causal diagonal) or past the context take
-    // the masked path.
-    const int kb0 = 64 * j;
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const int kb = kb0 + 32 * b;
-      if (kb < kew) {
-        uint32_t p[8];
-        softmax(qk(cur, b), kb, kb + 31 > pw0 || kb + 32 > L, p);
-        pv(cur, b, p);
-      }
-    }
-    // tile j+1 (issued one step ago) has landed once at most this wave's pieces of tile j+2
-    // are outstanding; every wave's share of it is visible after the barrier
+    fetch(jf, read_ids(jf), nxt3);
+    // whole-block waves: blocks 2j and 2j+1; half waves: block 2j + parity, then the same parity
+    // in tile j+1 (wave-uniform)
+    if (!half) finish(2 * j, cur, cur, 1);
+    finish(2 * j + (half ? par : 1), cur, nxt1, half ? 2 : 1);
+    // tile j+2 has landed once at most this wave's pieces of tile j+3 are outstanding; every
+    // wave's share of it is visible after the barrier
     wait_vmcnt(my_pieces);
     barrier_no_fence();
-    zero_tail(nxt1, j + 1);
+    zero_tail(nxt2, j + 2);
   };
-  for (int j = 0; j < ntiles; j += 3) {
-    step(j, lds0, lds1, lds2);
-    if (j + 1 < ntiles) step(j + 1, lds1, lds2, lds0);
-    if (j + 2 < ntiles) step(j + 2, lds2, lds0, lds1);
+  for (int j = 0; j < ntiles; j += 4) {
+    step(j, lds0, lds1, lds2, lds3);
+    if (j + 1 < ntiles) step(j + 1, lds1, lds2, lds3, lds0);
+    if (j + 2 < ntiles) step(j + 2, lds2, lds3, lds0, lds1);
+    if (j + 3 < ntiles) step(j + 3, lds3, lds0, lds1, lds2);
+  }
+  // The last steps re-read the last tile into free stages: drain those loads before the stages
+  // are reused below or the workgroup's LDS is released.
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+
+  // ---- half pairs: the odd wave hands its (max, sum, O^T) to the even one through LDS --------
+  if (F < W) {  // workgroup-uniform
+    // every wave is done with the stages (the last step ended on a barrier); pair p uses half
+    // of stage array p / 2 for O^T (64 x 16 MB floats) and s_ids for (max, sum)
+    constexpr int OF = 16 * MB;  // O^T floats per lane
+    const int pair = half ? (wave - F) >> 1 : 0;
+    uint16_t(*st)[TE] = (pair >> 1) == 0 ? lds0 : (pair >> 1) == 1 ? lds1 : lds2;
+    float* ob = reinterpret_cast<float*>(&st[0][0]) + (pair & 1) * 64 * OF;
+    float* ml = reinterpret_cast<float*>(s_ids) + pair * 128;
+    if (half && par == 1) {
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) ob[(16 * mb + e) * 64 + lane] = o[mb][e];
+      ml[lane] = msub;
+      ml[64 + lane] = l_lane;
+    }
+    __syncthreads();
+    if (half && par == 0) {
+      const float m1 = ml[lane], l1 = ml[64 + lane];
+      const float mm = __builtin_elementwise_maximum(msub, m1);
+      const float a0 = fast_exp2(msub - mm), a1 = fast_exp2(m1 - mm);  // NaN only for rows without keys
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[mb][e] = o[mb][e] * a0 + ob[(16 * mb + e) * 64 + lane] * a1;
+      l_lane = l_lane * a0 + l1 * a1;
+    }
   }
 
   // ---- normalise and store: lane (col, h) holds dims 32mb + 8q + 4h .. +4 of its row --------
@@ -433,9 +556,9 @@ void attn_prefill_mfma_kernel(AttnArgs a) {
     float x, y;
     swap32(l_lane, x, y);
     const float lrow = x + y;
-    if (valid) {
+    if (valid && !(half && par == 1)) {  // a half pair's even wave stores the merged rows
       const float inv = 1.f / lrow;
-      uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + rh * D + 4 * h;
+      uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + row_index() * D + 4 * h;
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
@@ -449,36 +572,57 @@ void attn_prefill_mfma_kernel(AttnArgs a) {
   }
 }
 
-long long prefill_wg_count(const int* rows, int n, int num_kv_heads, int waves) {
+long long prefill_wg_count(const int* rows, int n, int num_kv_heads, int rblk) {
   long long wgs = 0;
   for (int i = 0; i < n; ++i) {
     const long long nblk = ((long long)rows[i] + 31) / 32;
-    wgs += (nblk + waves - 1) / waves * num_kv_heads;
+    wgs += (nblk + rblk - 1) / rblk * num_kv_heads;
   }
   return wgs;
 }
 
-int prefill_waves_choice(const int* rows, int n, int num_kv_heads, int num_cus) {
-  // Makespan model: one workgroup per CU at a time (LDS-bound); a workgroup of W waves of 32
-  // rows takes ceil(W/4) wave-times on its busiest SIMD.  Pick W in 4..12 minimising
-  // rounds x ceil(W/4), then the fewest idle wave slots.
-  int best = 8;
+void prefill_plan(const int* rows, int n, int num_kv_heads, int num_cus, int* waves, int* rblk) {
+  // Makespan model: one workgroup per CU at a time (LDS-bound), every workgroup streams all of
+  // its sequence's keys.  Per key tile a workgroup costs a fixed part (barrier, streaming) plus
+  // the load of its busiest SIMD: waves w, w+4, w+8 share a SIMD, a whole-block wave counts 1
+  // and a half wave 1/2 (measured on MI355X: about 1.0 + 0.45 x load microseconds per 64-key
+  // tile).  A busiest SIMD with a single wave cannot hide its own latencies (measured 25-30%
+  // slower).  Pick the (W, R), W/2 <= R <= W and at most 6 pairs, minimising rounds x tile cost,
+  // then the fewest workgroups, then the fewest waves.
+  int bw = 8, br = 8;
   double best_cost = 1e300;
   for (int w = 4; w <= 12; ++w) {
-    const long long wgs = prefill_wg_count(rows, n, num_kv_heads, w);
-    const long long rounds = (wgs + num_cus - 1) / num_cus;
-    const double cost = (double)rounds * ((w + 3) / 4) + 1e-3 * (double)rounds * w;
-    if (cost < best_cost) {
-      best_cost = cost;
-      best = w;
+    for (int r = std::max((w + 1) / 2, w - 6); r <= w; ++r) {
+      const int f = 2 * r - w;
+      double load[4] = {0, 0, 0, 0};
+      int nw[4] = {0, 0, 0, 0};
+      for (int i = 0; i < w; ++i) {
+        load[i & 3] += i < f ? 1.0 : 0.5;
+        ++nw[i & 3];
+      }
+      int bs = 0;
+      for (int k = 1; k < 4; ++k)
+        if (load[k] > load[bs] || (load[k] == load[bs] && nw[k] < nw[bs])) bs = k;
+      const long long wgs = prefill_wg_count(rows, n, num_kv_heads, r);
+      const long long rounds = (wgs + num_cus - 1) / num_cus;
+      const double tile = (1.0 + 0.45 * load[bs]) * (nw[bs] <= 1 ? 1.3 : 1.0);
+      const double cost = (double)rounds * tile + 1e-4 * (double)wgs / num_cus + 1e-6 * w;
+      if (cost < best_cost) {
+        best_cost = cost;
+        bw = w;
+        br = r;
+      }
     }
   }
-  return best;
+  *waves = bw;
+  *rblk = br;
 }
 
 hipError_t launch_attn_prefill_mfma(const AttnArgs& a, int head_dim, int waves, long long wgs,
                                     hipStream_t st) {
   if (waves < 1 || waves > 12 || wgs < 0 || wgs > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  // R row blocks with W/2 <= R <= W; at most 6 half pairs (their merge uses 3 stage arrays)
+  if (2 * a.pf_rblk < waves || a.pf_rblk > waves || waves - a.pf_rblk > 6) return hipErrorInvalidConfiguration;
   if (wgs == 0) return hipSuccess;
   const dim3 grid((unsigned)wgs);
   if (head_dim == 128)

@@ -163,6 +163,7 @@ struct AttnArgs {
   int32_t row_tiles;        // split-K and vector kernels: row tiles per (sequence, kv head)
   int32_t split_q_max;      // sequences with q_len <= split_q_max take the split-K path
   int32_t part_rows;        // rows of the partial buffers (query tokens of the split-K path)
+  int32_t pf_rblk;          // prefill kernel: 32-row blocks per workgroup
   float scale_log2;         // softmax scale * log2(e)
 };
 

@@ -44,15 +44,18 @@ hipError_t launch_attn_split_mfma(const AttnArgs& a, int head_dim, int rows_per_
 hipError_t launch_attn_vec(const AttnArgs& a, int elt_bytes, int head_dim, int rows_per_tile,
                            int grid_x, hipStream_t st);
 // Prefill attention on the matrix cores (bf16) for the sequences with q_len > split_q_max:
-// `waves` (1..12) waves x 32 rows share LDS-staged K/V tiles; the workgroups, numbered sequence
+// `waves` (1..12) waves over a.pf_rblk 32-row blocks share LDS-staged K/V tiles; the workgroups, numbered sequence
 // by sequence (KV heads x row tiles of each prefill-class sequence), are found on the device
 // from q_lens.  `wgs`: grid size, at least the number of workgroups there are (extra ones exit).
 hipError_t launch_attn_prefill_mfma(const AttnArgs& a, int head_dim, int waves, long long wgs,
                                     hipStream_t st);
-// Workgroups of the prefill kernel for prefill-class sequences of rows[i] = q_len * G rows each.
-long long prefill_wg_count(const int* rows, int n, int num_kv_heads, int waves);
-// Waves per workgroup (4..12) for such a set of sequences: balances workgroups over the CUs.
-int prefill_waves_choice(const int* rows, int n, int num_kv_heads, int num_cus);
+// Workgroups of the prefill kernel for prefill-class sequences of rows[i] = q_len * G rows each,
+// with rblk 32-row blocks per workgroup.
+long long prefill_wg_count(const int* rows, int n, int num_kv_heads, int rblk);
+// Workgroup shape for such a set of sequences: waves (4..12) and row blocks per workgroup
+// (waves/2 .. waves; the waves beyond 2*rblk - waves share a row block in pairs), balancing the
+// SIMDs and the workgroups over the CUs.
+void prefill_plan(const int* rows, int n, int num_kv_heads, int num_cus, int* waves, int* rblk);
 // Cross-split merge of the split-K partials: one workgroup per (partial row, q-head).
 hipError_t launch_attn_reduce(const AttnArgs& a, int elt_bytes, int head_dim, hipStream_t st);
 

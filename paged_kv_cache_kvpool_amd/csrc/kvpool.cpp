@@ -372,6 +372,7 @@ struct Plan {
   int max_splits;     // split slots per partial row
   int part_rows;      // partial rows: the split-K path's query tokens (or a bound of them)
   int waves;          // prefill workgroup size
+  int rblk;           // prefill 32-row blocks per workgroup
   long long pf_wgs;   // prefill grid: its workgroups (or a bound of them)
   size_t o_bytes;     // partial outputs, rounded up to 256 bytes
   size_t bytes;
@@ -419,17 +420,25 @@ Plan make_plan(const kvpool* p, int32_t num_q_heads, int32_t num_seqs, int32_t t
     }
   }
   if (pl.prefill) {
-    pl.waves = kvp::prefill_waves_choice(pf_rows.data(), (int)pf_rows.size(), p->num_kv_heads, p->num_cus);
-    if (const char* v = getenv("KVATTN_PREFILL_WAVES")) pl.waves = std::max(1, std::min(12, atoi(v)));  // sweeps
+    kvp::prefill_plan(pf_rows.data(), (int)pf_rows.size(), p->num_kv_heads, p->num_cus, &pl.waves,
+                      &pl.rblk);
+    // sweeps and tests: KVATTN_PREFILL_WAVES fixes W (then R = W unless KVATTN_PREFILL_RBLK
+    // fixes R within [W/2, W], at most 6 pairs)
+    if (const char* v = getenv("KVATTN_PREFILL_WAVES")) {
+      pl.waves = std::max(1, std::min(12, atoi(v)));
+      pl.rblk = pl.waves;
+      if (const char* r = getenv("KVATTN_PREFILL_RBLK"))
+        pl.rblk = std::max(std::max((pl.waves + 1) / 2, pl.waves - 6), std::min(pl.waves, atoi(r)));
+    }
     if (q_lens_host) {
-      pl.pf_wgs = kvp::prefill_wg_count(pf_rows.data(), (int)pf_rows.size(), p->num_kv_heads, pl.waves);
+      pl.pf_wgs = kvp::prefill_wg_count(pf_rows.data(), (int)pf_rows.size(), p->num_kv_heads, pl.rblk);
     } else {
       // n prefill sequences (at most total_q / (split_q_max + 1)) of sum(T) <= total_q hold at
-      // most (total_q * G + 31 n) / 32 row blocks, in at most (blocks + n (W - 1)) / W row
+      // most (total_q * G + 31 n) / 32 row blocks, in at most (blocks + n (R - 1)) / R row
       // tiles per KV head.
       const long long n = std::min<long long>(num_seqs, total_q / (sqm + 1));
       const long long blocks = ((long long)total_q * G + 31 * n) / 32;
-      pl.pf_wgs = (blocks + n * (pl.waves - 1)) / pl.waves * p->num_kv_heads;
+      pl.pf_wgs = (blocks + n * (pl.rblk - 1)) / pl.rblk * p->num_kv_heads;
     }
   }
   // [partial outputs, fp32][partial (max, sum) pairs, fp32]
@@ -531,6 +540,7 @@ int kvattn_forward(kvpool_t* pool, int32_t layer, const void* q, void* out, int3
   a.max_splits = pl.max_splits;
   a.split_q_max = pl.split_q_max;
   a.part_rows = pl.part_rows;
+  a.pf_rblk = pl.rblk;
   a.scale_log2 = scale * kvp::LOG2E;
 
   const int eb = elt_bytes(pool->dtype);

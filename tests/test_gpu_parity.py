@@ -140,14 +140,21 @@ def test_attention_prefill_shapes(q_len, dtype):
     assert_close(out_f64(out), c.oracle(), dtype, w.name)
 
 
-@pytest.mark.parametrize("plan", ["4", "8", "10", "12"])
+@pytest.mark.parametrize("plan", ["4", "8", "10", "12", "12:10", "12:7", "8:5", "6:3", "5:3"])
 @pytest.mark.parametrize("head_dim", [128, 64])
 def test_attention_prefill_plans(plan, head_dim, monkeypatch):
-    """Prefill workgroups of 4, 8, 10 and 12 waves (forced through KVATTN_PREFILL_WAVES), over
-    ragged sequences whose row counts leave partial row tiles and waves with no rows."""
-    monkeypatch.setenv("KVATTN_PREFILL_WAVES", plan)
+    """Prefill workgroups of W waves over R row blocks (forced through KVATTN_PREFILL_WAVES and
+    KVATTN_PREFILL_RBLK; "W" alone means R = W): whole-block waves only, or with pairs of half
+    waves that split a row block's keys by block parity and merge at the end.  Ragged sequences
+    leave partial row tiles and waves with no rows."""
+    w, _, r = plan.partition(":")
+    monkeypatch.setenv("KVATTN_PREFILL_WAVES", w)
+    if r:
+        monkeypatch.setenv("KVATTN_PREFILL_RBLK", r)
+    else:
+        monkeypatch.delenv("KVATTN_PREFILL_RBLK", raising=False)
     announce(f"prefill plan {plan} D={head_dim}")
-    w = wl.make(f"prefill_plan_{plan}_{head_dim}", seed=61, dtype=wl.BF16,
+    w = wl.make(f"prefill_plan_{plan.replace(':', 'r')}_{head_dim}", seed=61, dtype=wl.BF16,
                 num_seqs_ctx=[700, 450, 130, 1300], q_lens=[300, 450, 97, 64],
                 num_q_heads=10, num_kv_heads=2, head_dim=head_dim)
     c = DeviceCase(w)
