@@ -6,10 +6,13 @@ package imports nothing from the library or its Python binding.
 
 * ``oracle.attention`` - numpy float64 definition: explicit block-table gather, then masked
   softmax attention per q-head; pool append (scatter) and block copy as plain integer indexing.
+* ``oracle.quant``     - the int8 pool: per-(token, KV head) absmax quantisation in fp32, the int8
+  storage layout, and attention on the dequantized values (float64, via ``oracle.attention``).
 * ``oracle.brute``     - pure-Python brute force for tiny inputs (``math.fsum``, log-sum-exp
-  normalisation, element-wise scatter by the storage formula) used to pin ``oracle.attention``.
+  normalisation, element-wise scatter by the storage formula, a quantiser rounding each
+  operation to float32) used to pin ``oracle.attention`` and ``oracle.quant``.
 
 Every function is pinned by a ``-m "not gpu"`` test against something other than itself
 (brute force, closed forms, invariants).  Nothing here is "parity unpinned".
 """
-from . import attention, brute  # noqa: F401
+from . import attention, brute, quant  # noqa: F401

@@ -74,3 +74,60 @@ def bf16_to_float(bits: int) -> float:
     """Exact value of a bf16 bit pattern (the top 16 bits of a float32)."""
     import struct
     return struct.unpack("<f", struct.pack("<I", (int(bits) & 0xFFFF) << 16))[0]
+
+
+# ---- int8 pool --------------------------------------------------------------------------------
+# Offsets of the int8 storage (per layer; t = in-block token, d = dim):
+#   K: ((((b*Hkv + h)*(B/16) + t//16)*(D/16) + d//16)*16 + t%16)*16 + d%16
+#   V: ((((b*Hkv + h)*(B/16) + t//16)*4 + (t%16)//4)*16 + d%16)*(D/16)*4 + (d//16)*4 + t%4
+#   scale of (b, h, t): (b*Hkv + h)*B + t
+
+def k_offset_i8(b, h, t, d, *, num_kv_heads, block_size, head_dim):
+    tile, tt = divmod(t, 16)
+    return (((((b * num_kv_heads + h) * (block_size // 16) + tile) * (head_dim // 16) + d // 16)
+             * 16 + tt) * 16 + d % 16)
+
+
+def v_offset_i8(b, h, t, d, *, num_kv_heads, block_size, head_dim):
+    tile, tt = divmod(t, 16)
+    return (((((b * num_kv_heads + h) * (block_size // 16) + tile) * 4 + tt // 4) * 16 + d % 16)
+            * (head_dim // 16) * 4 + (d // 16) * 4 + tt % 4)
+
+
+def f32(x: float) -> float:
+    """Round a Python float to the nearest float32 (ties to even)."""
+    import struct
+    return struct.unpack("<f", struct.pack("<f", x))[0]
+
+
+def quantize_row(xs):
+    """One row of float32 values -> (codes, scale): s = absmax / 127 and q = rint(x / s), each
+    operation rounded to float32 (a float64 quotient of float32 operands, rounded once to
+    float32, is the correctly rounded float32 quotient), ties to even, clamped to +-127."""
+    absmax = max(abs(x) for x in xs)
+    s = f32(absmax / 127.0)
+    if s == 0.0:
+        return [0] * len(xs), 0.0
+    return [max(-127, min(127, round(f32(x / s)))) for x in xs], s
+
+
+def scatter_i8(k_codes, v_codes, k_scales, v_scales, tables, *, num_blocks, num_kv_heads,
+               block_size, head_dim):
+    """Flat int8 K/V storage and scale lists for one layer from dense codes k_codes[s][j][h][d]
+    and scales k_scales[s][j][h]; unwritten slots hold 0."""
+    n = num_blocks * num_kv_heads * block_size * head_dim
+    kf, vf = [0] * n, [0] * n
+    ksf = [0.0] * (num_blocks * num_kv_heads * block_size)
+    vsf = [0.0] * (num_blocks * num_kv_heads * block_size)
+    geo = dict(num_kv_heads=num_kv_heads, block_size=block_size, head_dim=head_dim)
+    for s in range(len(k_codes)):
+        for j in range(len(k_codes[s])):
+            b = tables[s][j // block_size]
+            t = j % block_size
+            for h in range(num_kv_heads):
+                ksf[(b * num_kv_heads + h) * block_size + t] = k_scales[s][j][h]
+                vsf[(b * num_kv_heads + h) * block_size + t] = v_scales[s][j][h]
+                for d in range(head_dim):
+                    kf[k_offset_i8(b, h, t, d, **geo)] = k_codes[s][j][h][d]
+                    vf[v_offset_i8(b, h, t, d, **geo)] = v_codes[s][j][h][d]
+    return kf, vf, ksf, vsf
