@@ -47,6 +47,17 @@
  * dim chunks (chunk-major, 16 tokens per chunk) and V transposed (dims-major).  One tile is
  * 4 KiB for bf16 at head_dim 128, so each tile is one coalesced read, and it can be copied
  * to LDS verbatim in the order the matrix cores consume it.
+ *
+ * int8 pools (KV_I8; the pages' int8 KV cache: NInfer serving doc, "Server options",
+ * --kv-dtype bf16|int8; sparkinfer server README, "Env", SPARKINFER_KV_INT8).  Each (token,
+ * KV head) row x of K or V is stored as codes q = rint(x / s) in [-127, 127] with one fp32
+ * scale s = absmax(x) / 127 (fp32, correctly rounded, ties to even; s = 0 and q = 0 for a zero
+ * row); it stands for q * s.  Tiles of 16 tokens, one byte per element:
+ *   K at byte  tile * 16 * head_dim + ((d / 16) * 16 + t % 16) * 16 + d % 16
+ *   V at byte  tile * 16 * head_dim + (((t % 16) / 4 * 16 + d % 16) * (head_dim / 16) + d / 16) * 4 + t % 4
+ * (V puts the 4 keys of one dim of each 16-dim group side by side).  Scales: two fp32 arrays
+ * (K, V) [num_layers][num_blocks][num_kv_heads][block_size], caller-owned like the storage.
+ * Rows appended to an int8 pool, and q / out of attention on it, are bf16.
  */
 #ifndef KVPOOL_H
 #define KVPOOL_H
@@ -75,10 +86,10 @@ typedef enum {
   KV_ENOMEM = -5         /* workspace smaller than kvattn_workspace_size() asks for         */
 } kv_status;
 
-typedef enum { KV_F32 = 0, KV_BF16 = 1 } kv_dtype;
+typedef enum { KV_F32 = 0, KV_BF16 = 1, KV_I8 = 2 } kv_dtype;
 
 /* Bytes of ONE of the two storage buffers (K or V) for this geometry, written to *bytes.
- * Supported: block_size in {16, 64}, head_dim in {64, 128}, dtype KV_F32 or KV_BF16. */
+ * Supported: block_size in {16, 64}, head_dim in {64, 128}, dtype KV_F32, KV_BF16 or KV_I8. */
 KVPOOL_API int kvpool_storage_bytes(int32_t num_layers, int32_t num_blocks, int32_t block_size,
                                     int32_t num_kv_heads, int32_t head_dim, int32_t dtype,
                                     size_t *bytes);
@@ -92,6 +103,18 @@ KVPOOL_API int kvpool_create(kvpool_t **out, int32_t num_layers, int32_t num_blo
                              int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
                              int32_t dtype, void *k_storage, void *v_storage);
 
+/* Bytes of ONE of the two scale arrays (K or V) of an int8 pool of this geometry. */
+KVPOOL_API int kvpool_scale_bytes(int32_t num_layers, int32_t num_blocks, int32_t block_size,
+                                  int32_t num_kv_heads, size_t *bytes);
+
+/* An int8 pool (the layout above) over caller-owned device storage: k_storage / v_storage of
+ * kvpool_storage_bytes(..., KV_I8) bytes and k_scales / v_scales of kvpool_scale_bytes() bytes,
+ * all 16-byte aligned.  kvpool_create refuses KV_I8 (it has no scale arrays). */
+KVPOOL_API int kvpool_create_int8(kvpool_t **out, int32_t num_layers, int32_t num_blocks,
+                                  int32_t block_size, int32_t num_kv_heads, int32_t head_dim,
+                                  void *k_storage, void *v_storage, void *k_scales,
+                                  void *v_scales);
+
 /* Frees the handle only, never the storage.  NULL is accepted. */
 KVPOOL_API int kvpool_destroy(kvpool_t *pool);
 
@@ -101,7 +124,8 @@ KVPOOL_API int kvpool_destroy(kvpool_t *pool);
  * pos % block_size.  This is how only the uncached suffix enters the pool on a prefix hit
  * (sparkinfer server README, "Automatic prefix cache").  Bit copy; every other slot keeps its
  * bits.
- *   k_new, v_new   device, [total_q][num_kv_heads][head_dim] of the pool dtype, row-major
+ *   k_new, v_new   device, [total_q][num_kv_heads][head_dim] of the pool dtype (bf16 for an
+ *                  int8 pool, quantised on the way in), row-major
  *   block_tables   device int32 [num_seqs][max_blocks_per_seq]
  *   ctx_lens       device int32 [num_seqs], length after the append (counts the new tokens)
  *   q_lens         device int32 [num_seqs], new tokens per sequence; sum == total_q
@@ -116,8 +140,8 @@ KVPOOL_API int kvpool_append(kvpool_t *pool, int32_t layer, const void *k_new,
 
 /* pool[dst[i]] <- pool[src[i]] for i < n, every layer, K and V: the copy-on-write step for a
  * shared prefix block that a sequence is about to write (blocks are shared, not copied, until
- * they diverge: sparkinfer server README, "Automatic prefix cache").  src, dst: device int32
- * [n].  dst ids must be distinct and disjoint from src ids (then the result does not depend on
+ * they diverge: sparkinfer server README, "Automatic prefix cache"); an int8 pool's scales
+ * move with their codes.  src, dst: device int32 [n].  dst ids must be distinct and disjoint from src ids (then the result does not depend on
  * order; KV_ERANGE under validation otherwise).  Bit copy. */
 KVPOOL_API int kvpool_copy_blocks(kvpool_t *pool, const int32_t *src, const int32_t *dst,
                                   int32_t n, void *stream);
@@ -139,7 +163,8 @@ KVPOOL_API int kvattn_workspace_size(const kvpool_t *pool, int32_t num_q_heads,
  * of a size set by its own ctx_len, merged in a fixed order); a longer one takes the prefill
  * kernel.  The path and the arithmetic of a sequence follow from its own lengths, so its output
  * bits do not depend on the rest of the batch or on the bounds passed here.
- *   q    device, [total_q][num_q_heads][head_dim], pool dtype, rows packed in sequence order
+ *   q    device, [total_q][num_q_heads][head_dim], pool dtype (bf16 for an int8 pool), rows
+ *        packed in sequence order
  *   out  device, same shape and dtype as q; each element is written exactly once, rounded to
  *        nearest-even from the fp32 result
  *   scale            softmax scale applied to q.k (e.g. 1/sqrt(head_dim))

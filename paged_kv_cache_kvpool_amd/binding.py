@@ -23,7 +23,7 @@ LIB_PATH = os.environ.get("KVPOOL_LIB") or os.path.join(os.path.dirname(os.path.
                                                         "libkvpool.so")
 
 KV_OK, KV_EINVAL, KV_ERANGE, KV_EUNSUPPORTED, KV_EDEVICE, KV_ENOMEM = 0, -1, -2, -3, -4, -5
-KV_F32, KV_BF16 = 0, 1
+KV_F32, KV_BF16, KV_I8 = 0, 1, 2
 STATUS_NAMES = {0: "KV_OK", -1: "KV_EINVAL", -2: "KV_ERANGE", -3: "KV_EUNSUPPORTED",
                 -4: "KV_EDEVICE", -5: "KV_ENOMEM"}
 
@@ -33,6 +33,8 @@ _i32, _f32, _sz, _vp = ctypes.c_int32, ctypes.c_float, ctypes.c_size_t, ctypes.c
 SIGNATURES = {
     "kvpool_storage_bytes": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32, ctypes.POINTER(_sz)]),
     "kvpool_create": (_i32, [ctypes.POINTER(_vp), _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp]),
+    "kvpool_scale_bytes": (_i32, [_i32, _i32, _i32, _i32, ctypes.POINTER(_sz)]),
+    "kvpool_create_int8": (_i32, [ctypes.POINTER(_vp), _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp]),
     "kvpool_destroy": (_i32, [_vp]),
     "kvpool_append": (_i32, [_vp, _i32, _vp, _vp, _vp, _i32, _vp, _vp, _i32, _i32, _i32, _vp]),
     "kvpool_copy_blocks": (_i32, [_vp, _vp, _vp, _i32, _vp]),
@@ -136,6 +138,22 @@ def kvpool_create(num_layers, num_blocks, block_size, num_kv_heads, head_dim, dt
     return h.value
 
 
+def kvpool_scale_bytes(num_layers, num_blocks, block_size, num_kv_heads) -> int:
+    out = _sz(0)
+    _check(lib().kvpool_scale_bytes(num_layers, num_blocks, block_size, num_kv_heads,
+                                    ctypes.byref(out)))
+    return out.value
+
+
+def kvpool_create_int8(num_layers, num_blocks, block_size, num_kv_heads, head_dim, k_storage,
+                       v_storage, k_scales, v_scales) -> int:
+    h = _vp(0)
+    _check(lib().kvpool_create_int8(ctypes.byref(h), num_layers, num_blocks, block_size,
+                                    num_kv_heads, head_dim, _ptr(k_storage), _ptr(v_storage),
+                                    _ptr(k_scales), _ptr(v_scales)))
+    return h.value
+
+
 def kvpool_destroy(handle) -> None:
     _check(lib().kvpool_destroy(handle))
 
@@ -184,14 +202,16 @@ def kvattn_forward(handle, layer, q, out, num_q_heads, scale, block_tables, max_
 # Convenience wrapper: owns torch storage for one pool and sizes the workspace.
 # ---------------------------------------------------------------------------------------------
 
-_TORCH_DTYPE = {KV_F32: torch.float32, KV_BF16: torch.bfloat16}
+_TORCH_DTYPE = {KV_F32: torch.float32, KV_BF16: torch.bfloat16, KV_I8: torch.int8}
 
 
 class PagedKVPool:
     """A pool whose K/V storage is a pair of torch tensors on one device.
 
     ``k_storage`` / ``v_storage`` are flat tensors of the pool dtype (see include/kvpool.h for
-    the element order).  Metadata arguments are int32 device tensors.
+    the element order); an int8 pool also owns ``k_scales`` / ``v_scales`` (float32,
+    [num_layers][num_blocks][num_kv_heads][block_size]).  Metadata arguments are int32 device
+    tensors.  q, out and appended rows are bf16 for an int8 pool.
     """
 
     def __init__(self, num_layers, num_blocks, block_size, num_kv_heads, head_dim, dtype,
@@ -205,9 +225,20 @@ class PagedKVPool:
         self.k_storage = torch.empty(n, dtype=tdt, device=device) if k_storage is None else k_storage
         self.v_storage = torch.empty(n, dtype=tdt, device=device) if v_storage is None else v_storage
         assert self.k_storage.numel() == n and self.v_storage.numel() == n
+        self.k_scales = self.v_scales = None
         with torch.cuda.device(self.k_storage.device):
-            self.handle = kvpool_create(num_layers, num_blocks, block_size, num_kv_heads,
-                                        head_dim, dtype, self.k_storage, self.v_storage)
+            if dtype == KV_I8:
+                sshape = (num_layers, num_blocks, num_kv_heads, block_size)
+                assert kvpool_scale_bytes(num_layers, num_blocks, block_size, num_kv_heads) == \
+                    4 * num_layers * num_blocks * num_kv_heads * block_size
+                self.k_scales = torch.zeros(sshape, dtype=torch.float32, device=device)
+                self.v_scales = torch.zeros(sshape, dtype=torch.float32, device=device)
+                self.handle = kvpool_create_int8(num_layers, num_blocks, block_size, num_kv_heads,
+                                                 head_dim, self.k_storage, self.v_storage,
+                                                 self.k_scales, self.v_scales)
+            else:
+                self.handle = kvpool_create(num_layers, num_blocks, block_size, num_kv_heads,
+                                            head_dim, dtype, self.k_storage, self.v_storage)
         self._ws = None
 
     def __del__(self):
@@ -219,6 +250,11 @@ class PagedKVPool:
     @property
     def torch_dtype(self):
         return _TORCH_DTYPE[self.dtype]
+
+    @property
+    def act_dtype(self):
+        """dtype of q, out and appended rows: the pool dtype, bf16 for an int8 pool."""
+        return torch.bfloat16 if self.dtype == KV_I8 else _TORCH_DTYPE[self.dtype]
 
     def block_storage(self, which="k"):
         """[num_layers, num_blocks, Hkv*block_size*head_dim] view of K or V storage."""

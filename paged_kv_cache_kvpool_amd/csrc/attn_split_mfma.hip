@@ -67,11 +67,34 @@ __device__ __forceinline__ floatx4 mfma16(bf16x8 a, bf16x8 b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-template <int D>
+template <int D, bool I8>
 struct Chunk {
   bf16x8 k[2][D / 32];  // K operand of score tile h (= pool tile h of the chunk)
   u32x2 v[2][D / 16];   // V^T operand halves: keys 4g..4g+3 of pool tile 0 and of tile 1
 };
+
+// int8 pool (tile layouts: K [d/16][t%16][d%16], V [(t%16)/4][d%16][d/16][t%4], one fp32 scale
+// per token): lane (n, g) loads K chunks 4m+g (16 dims) of key n for m < D/64 (16 bytes each,
+// two score k-steps per chunk), its V run (dims n, n+16, ... for keys 4g..4g+3: D/4 bytes) and
+// the K and V scales of keys 4g..4g+3 of each pool tile.
+template <int D>
+struct Chunk<D, true> {
+  u32x4 k[2][D / 64];
+  u32x4 v[2][D / 64];
+  floatx4 ks[2], vs[2];
+};
+
+// 8 int8 codes (two dwords) -> 8 bf16 values (exact: |code| <= 127).
+__device__ __forceinline__ bf16x8 i8x8_to_bf16(uint32_t lo, uint32_t hi) {
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const uint32_t x = i ? hi : lo;
+    w[2 * i] = cvt_pk_bf16((float)(int8_t)(x & 0xff), (float)(int8_t)((x >> 8) & 0xff));
+    w[2 * i + 1] = cvt_pk_bf16((float)(int8_t)((x >> 16) & 0xff), (float)(int8_t)(x >> 24));
+  }
+  return __builtin_bit_cast(bf16x8, u32x4{w[0], w[1], w[2], w[3]});
+}
 
 // One work item: split `sp` of sequence s for KV head kvh and row tile rt.
 struct Item {
@@ -113,7 +136,7 @@ __device__ __forceinline__ int tile_block_id(const AttnArgs& a, int s, int wb, i
 // merge through LDS (NW == 1: the wave finishes the item from registers).  RELOAD: the wave's
 // keys may span more than 128 tiles, so block ids are reloaded every 128 tiles; without it no
 // load in the chunk loop can force a wait on the chunks in flight.
-template <int D, int NT, bool RELOAD, int NW>
+template <int D, int NT, bool RELOAD, int NW, bool I8>
 __device__ __forceinline__ void run_item(const AttnArgs& a, const Item& it, int wave, int wb,
                                          int we, int ids0, int ids1) {
   constexpr int KK = D / 32;  // 32-dim steps of the score product
@@ -145,23 +168,42 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, const Item& it, int 
     const int sub = (((tile0 + ti) << 4) & bmask) >> 4;
     return block_tile_offset(blk, sub, kvh, a.block_shift, a.num_blocks, a.num_kv_heads, D);
   };
-  auto load_chunk = [&](Chunk<D>& c, int ci) {
+  auto load_chunk = [&](Chunk<D, I8>& c, int ci) {
     const size_t o0 = tile_off(2 * ci), o1 = tile_off(2 * ci + 1);
-    const uint16_t* kt[2] = {kl + o0, kl + o1};
-    const uint16_t* vt[2] = {vl + o0, vl + o1};
+    if constexpr (I8) {
+      // element offsets are byte offsets here; tile index = offset / (16 D)
+      const int8_t* k8 = reinterpret_cast<const int8_t*>(a.k_layer);
+      const int8_t* v8 = reinterpret_cast<const int8_t*>(a.v_layer);
+      const size_t oo[2] = {o0, o1};
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
+      for (int h = 0; h < 2; ++h) {
 #pragma unroll
-      for (int kk = 0; kk < KK; ++kk) c.k[h][kk] = stream16(kt[h] + ((4 * kk + g) * 16 + n) * 8);
+        for (int m = 0; m < D / 64; ++m) {
+          c.k[h][m] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(k8 + oo[h] + ((4 * m + g) * 16 + n) * 16));
+          c.v[h][m] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(v8 + oo[h] + (g * 16 + n) * (D / 4) + 16 * m));
+        }
+        const size_t si = oo[h] / D + 4 * g;  // scales of keys 4g .. 4g+3 of the tile
+        c.ks[h] = *reinterpret_cast<const floatx4*>(a.k_scale_layer + si);
+        c.vs[h] = *reinterpret_cast<const floatx4*>(a.v_scale_layer + si);
+      }
+    } else {
+      const uint16_t* kt[2] = {kl + o0, kl + o1};
+      const uint16_t* vt[2] = {vl + o0, vl + o1};
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) c.v[h][mt] = stream8(vt[h] + (16 * mt + n) * 16 + 4 * g);
+      for (int h = 0; h < 2; ++h) {
+#pragma unroll
+        for (int kk = 0; kk < KK; ++kk) c.k[h][kk] = stream16(kt[h] + ((4 * kk + g) * 16 + n) * 8);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) c.v[h][mt] = stream8(vt[h] + (16 * mt + n) * 16 + 4 * g);
+      }
     }
   };
 
-  Chunk<D> bufA, bufB;
+  Chunk<D, I8> bufA, bufB;
   if (nch) load_chunk(bufA, 0);
 
-  // Q^T as the B operand: lane (n, g) holds row n of N-tile nt, dims 32*kk + 8*g .. +8.
+  // Q^T as the B operand: lane (n, g) holds row n of N-tile nt, dims 32*kk + 8*g .. +8 (int8
+  // pools: dims 16*(4*(kk/2) + g) + 8*(kk%2) .. +8, the order of the K chunks it meets).
   const int Hq = a.num_q_heads;
   bf16x8 qb[NT][KK];
   int prow[NT];
@@ -178,7 +220,8 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, const Item& it, int 
 #pragma unroll
     for (int kk = 0; kk < KK; ++kk) {
       bf16x8 z = {};
-      qb[nt][kk] = valid ? load16(qp + 32 * kk + 8 * g) : z;
+      const int d0 = I8 ? 16 * (4 * (kk >> 1) + g) + 8 * (kk & 1) : 32 * kk + 8 * g;
+      qb[nt][kk] = valid ? load16(qp + d0) : z;
     }
   }
 
@@ -193,9 +236,25 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, const Item& it, int 
   }
   const float c = a.scale_log2;
 
-  auto compute = [&](Chunk<D>& ch, int ci) {
+  auto compute = [&](Chunk<D, I8>& ch, int ci) {
     const int c0 = wb + 32 * ci;
-    if (c0 + 32 > we) {
+    // int8: the V scales of slots at or past `we` (never written: may hold anything) zeroed so
+    // that p * scale stays 0; with two N-tiles the V^T operands are converted once for both
+    auto v_i8 = [&](int mt) {
+      return i8x8_to_bf16(ch.v[0][mt >> 2][mt & 3], ch.v[1][mt >> 2][mt & 3]);
+    };
+    bf16x8 va8[NT > 1 ? MT : 1];
+    if constexpr (I8) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          if (c0 + 16 * h + 4 * g + j >= we) ch.vs[h][j] = 0.f;
+      if constexpr (NT > 1) {
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) va8[mt] = v_i8(mt);
+      }
+    } else if (c0 + 32 > we) {
       // Last chunk: slots at or past `we` may hold anything (NaN included); zero their V so
       // that p = 0 really contributes nothing.
 #pragma unroll
@@ -216,7 +275,16 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, const Item& it, int 
       for (int h = 0; h < 2; ++h) {
         floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) acc = mfma16(ch.k[h][kk], qb[nt][kk], acc);
+        for (int kk = 0; kk < KK; ++kk) {
+          if constexpr (I8) {
+            const u32x4 w = ch.k[h][kk >> 1];
+            const bf16x8 ka = (kk & 1) ? i8x8_to_bf16(w[2], w[3]) : i8x8_to_bf16(w[0], w[1]);
+            acc = mfma16(ka, qb[nt][kk], acc);
+          } else {
+            acc = mfma16(ch.k[h][kk], qb[nt][kk], acc);
+          }
+        }
+        if constexpr (I8) acc *= ch.ks[h];  // key 4g + i of tile h: its K scale
         sc[h] = acc;
       }
       // This lane now holds row n's scores for keys c0 + 16*h + 4*g + i (j = 4*h + i).
@@ -237,18 +305,31 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, const Item& it, int 
       float psum = 0.f;
 #pragma unroll
       for (int j = 0; j < 8; j += 2) {
-        const float p0 = round_to_bf16(fast_exp2(sv[j] * c - msub));
-        const float p1 = round_to_bf16(fast_exp2(sv[j + 1] * c - msub));
-        psum += p0 + p1;
-        pk[j >> 1] = pack_exact_bf16(p0, p1);
+        if constexpr (I8) {
+          // P times the V scale of its key goes to the PV product; the row sum takes P alone
+          const float p0 = fast_exp2(sv[j] * c - msub), p1 = fast_exp2(sv[j + 1] * c - msub);
+          psum += p0 + p1;
+          pk[j >> 1] = cvt_pk_bf16(p0 * ch.vs[j >> 2][j & 3], p1 * ch.vs[j >> 2][(j & 3) + 1]);
+        } else {
+          const float p0 = round_to_bf16(fast_exp2(sv[j] * c - msub));
+          const float p1 = round_to_bf16(fast_exp2(sv[j + 1] * c - msub));
+          psum += p0 + p1;
+          pk[j >> 1] = pack_exact_bf16(p0, p1);
+        }
       }
       l_run[nt] = l_run[nt] * alpha + psum;
       m_run[nt] = m_new;
       const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const bf16x8 va = __builtin_bit_cast(
-            bf16x8, u32x4{ch.v[0][mt][0], ch.v[0][mt][1], ch.v[1][mt][0], ch.v[1][mt][1]});
+        bf16x8 va;
+        if constexpr (I8) {
+          if constexpr (NT > 1) va = va8[mt];
+          else va = v_i8(mt);
+        } else {
+          va = __builtin_bit_cast(
+              bf16x8, u32x4{ch.v[0][mt][0], ch.v[0][mt][1], ch.v[1][mt][0], ch.v[1][mt][1]});
+        }
         o[nt][mt] = mfma16(va, pb, o[nt][mt] * alpha);
       }
     }
@@ -456,8 +537,10 @@ __device__ __forceinline__ bool find_item(const AttnArgs& a, SeqGroup& gp, int t
 // Wave w of W takes items w, w + W, w + 2W, ... in increasing order.  W is what the GPU holds at
 // once, so all waves start together; a wave's next item is known in advance, and its block ids
 // are loaded before the current item's chunks.
-template <int D, int NT>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2 : 1)))
+// Two waves per SIMD for bf16 decode (NT = 1, up to 256 registers); the int8 variants convert
+// codes to bf16 in registers and need more, so they run one wave per SIMD.
+template <int D, int NT, bool I8>
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu((NT == 1 && !I8) ? 2 : 1)))
 void attn_split_persist_kernel(AttnArgs a) {
   const int W = gridDim.x;
   SeqGroup gp;
@@ -488,7 +571,7 @@ void attn_split_persist_kernel(AttnArgs a) {
     const int pt = (pe - pb + 15) >> 4;
     const int nid0 = tile_block_id(a, ps, pb, pt, pe, 0);
     const int nid1 = tile_block_id(a, ps, pb, pt, pe, 64);
-    if (cur_keys) run_item<D, NT, false, 1>(a, cur, 0, cur.kb, cur.ke, ids0, ids1);
+    if (cur_keys) run_item<D, NT, false, 1, I8>(a, cur, 0, cur.kb, cur.ke, ids0, ids1);
     if (!nhave) break;
     cur = nxt;
     cur_keys = nkeys;
@@ -499,7 +582,7 @@ void attn_split_persist_kernel(AttnArgs a) {
 
 // Forced splits longer than 2048 keys: one workgroup of 4 waves per item, on the grid
 // x = (KV head, sequence, row tile) with the KV head fastest, y = split.
-template <int D, int NT, bool RELOAD>
+template <int D, int NT, bool RELOAD, bool I8>
 __global__ __launch_bounds__(256) void attn_split_mfma_kernel(AttnArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   Item it;
@@ -521,53 +604,60 @@ __global__ __launch_bounds__(256) void attn_split_mfma_kernel(AttnArgs a) {
   // vmcnt(0) (encoding: vmcnt 0, expcnt 7, lgkmcnt 15), so the compiler knows the block ids
   // have arrived and never waits for them inside the chunk loop.
   __builtin_amdgcn_s_waitcnt(0x0F70);
-  run_item<D, NT, RELOAD, 4>(a, it, wave, wb, we, ids0, ids1);
+  run_item<D, NT, RELOAD, 4, I8>(a, it, wave, wb, we, ids0, ids1);
 }
 
 namespace {
 
 // Workgroups of the persistent kernel the GPU holds at once (per CU, from the occupancy API).
-template <int D, int NT>
+template <int D, int NT, bool I8>
 int persist_blocks_per_cu() {
   static const int n = [] {
     int b = 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-            &b, reinterpret_cast<const void*>(&attn_split_persist_kernel<D, NT>), 64, 0) != hipSuccess)
+            &b, reinterpret_cast<const void*>(&attn_split_persist_kernel<D, NT, I8>), 64, 0) != hipSuccess)
       return 0;
     return b;
   }();
   return n;
 }
 
-template <int D, int NT>
+template <int D, int NT, bool I8>
 hipError_t launch_split(const AttnArgs& a, int splits, int num_cus, hipStream_t st) {
   const bool persistent = a.split_tokens <= 2048;
   if (persistent) {
-    const int per_cu = persist_blocks_per_cu<D, NT>();
+    const int per_cu = persist_blocks_per_cu<D, NT, I8>();
     if (per_cu <= 0) return hipErrorInvalidConfiguration;
     const long long items = (long long)a.num_seqs * a.num_kv_heads * a.row_tiles * splits;
     const long long waves = std::min<long long>(items, (long long)per_cu * std::max(num_cus, 1));
-    attn_split_persist_kernel<D, NT><<<(unsigned)waves, 64, 0, st>>>(a);
+    attn_split_persist_kernel<D, NT, I8><<<(unsigned)waves, 64, 0, st>>>(a);
   } else {
     if (splits > 65535) return hipErrorInvalidConfiguration;
     const dim3 grid(a.num_kv_heads * a.num_seqs * a.row_tiles, splits, 1);
     if (a.split_tokens > 8192)
-      attn_split_mfma_kernel<D, NT, true><<<grid, 256, 0, st>>>(a);
+      attn_split_mfma_kernel<D, NT, true, I8><<<grid, 256, 0, st>>>(a);
     else
-      attn_split_mfma_kernel<D, NT, false><<<grid, 256, 0, st>>>(a);
+      attn_split_mfma_kernel<D, NT, false, I8><<<grid, 256, 0, st>>>(a);
   }
   return hipGetLastError();
+}
+
+template <bool I8>
+hipError_t launch_split_dt(const AttnArgs& a, int head_dim, int rows_per_tile, int splits,
+                           int num_cus, hipStream_t st) {
+  if (head_dim == 128)
+    return rows_per_tile <= 16 ? launch_split<128, 1, I8>(a, splits, num_cus, st)
+                               : launch_split<128, 2, I8>(a, splits, num_cus, st);
+  return rows_per_tile <= 16 ? launch_split<64, 1, I8>(a, splits, num_cus, st)
+                             : launch_split<64, 2, I8>(a, splits, num_cus, st);
 }
 
 }  // namespace
 
 hipError_t launch_attn_split_mfma(const AttnArgs& a, int head_dim, int rows_per_tile, int splits,
-                                  int num_cus, hipStream_t st) {
-  if (head_dim == 128)
-    return rows_per_tile <= 16 ? launch_split<128, 1>(a, splits, num_cus, st)
-                               : launch_split<128, 2>(a, splits, num_cus, st);
-  return rows_per_tile <= 16 ? launch_split<64, 1>(a, splits, num_cus, st)
-                             : launch_split<64, 2>(a, splits, num_cus, st);
+                                  int num_cus, bool int8_kv, hipStream_t st) {
+  return int8_kv ? launch_split_dt<true>(a, head_dim, rows_per_tile, splits, num_cus, st)
+                 : launch_split_dt<false>(a, head_dim, rows_per_tile, splits, num_cus, st);
 }
 
 }  // namespace kvp

@@ -153,6 +153,8 @@ struct AttnArgs {
   const int32_t* block_tables;
   const int32_t* ctx_lens;
   const int32_t* q_lens;
+  const float* k_scale_layer;  // int8 pools: the layer's [blocks][Hkv][block_size] scales
+  const float* v_scale_layer;
   float* part_o;            // [part_rows][Hq][max_splits][D]  split-K partial outputs
   float* part_ml;           // [part_rows][Hq][max_splits][2]  their (max, sum) pairs
   int32_t num_seqs, total_q, num_q_heads, num_kv_heads, group, block_size, num_blocks;

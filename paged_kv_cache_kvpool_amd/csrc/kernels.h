@@ -16,6 +16,8 @@ struct AppendArgs {
   const int32_t* block_tables;
   const int32_t* ctx_lens;
   const int32_t* q_lens;
+  float* k_scale_layer;  // int8 pools: per-(block, KV head, token) fp32 scales of the layer
+  float* v_scale_layer;
   int32_t num_seqs, total_q, num_kv_heads, head_dim, block_size, num_blocks;
   int32_t max_blocks_per_seq;
 };
@@ -23,12 +25,17 @@ struct AppendArgs {
 struct CopyArgs {
   void* k;
   void* v;
+  void* k_scale;  // int8 pools: scale arrays, else null
+  void* v_scale;
   const int32_t* src;
   const int32_t* dst;
   int32_t num_blocks;
-  size_t block_bytes;  // one block of one layer: Hkv * block_size * head_dim * elt
+  size_t block_bytes;        // one block of one layer: Hkv * block_size * head_dim * elt
+  size_t block_scale_bytes;  // one block of one layer of scales: Hkv * block_size * 4
 };
 
+// Append of bf16/fp32 rows into a pool of the same dtype (elt_bytes 2 or 4), or of bf16 rows
+// quantised into an int8 pool (elt_bytes 1).
 hipError_t launch_append(const AppendArgs& a, int elt_bytes, int max_q_len, hipStream_t st);
 hipError_t launch_copy_blocks(const CopyArgs& a, int n, int num_layers, hipStream_t st);
 
@@ -37,8 +44,9 @@ hipError_t launch_copy_blocks(const CopyArgs& a, int n, int num_layers, hipStrea
 // waves (num_cus sizes the grid), or, for forced splits longer than 2048 keys, one 4-wave
 // workgroup per item.  `splits`: most splits of any sequence (at most 65535 for the 4-wave
 // variant).
+// int8_kv: the pool holds int8 codes with per-token scales (a.k_scale_layer / v_scale_layer).
 hipError_t launch_attn_split_mfma(const AttnArgs& a, int head_dim, int rows_per_tile,
-                                  int splits, int num_cus, hipStream_t st);
+                                  int splits, int num_cus, bool int8_kv, hipStream_t st);
 // Vector-ALU attention (fp32 and bf16), one wave per (row tile of <= 8 rows, split, KV head,
 // sequence); sequences past split_q_max make one pass in split slot 0.
 hipError_t launch_attn_vec(const AttnArgs& a, int elt_bytes, int head_dim, int rows_per_tile,
@@ -56,6 +64,18 @@ long long prefill_wg_count(const int* rows, int n, int num_kv_heads, int rblk);
 // (waves/2 .. waves; the waves beyond 2*rblk - waves share a row block in pairs), balancing the
 // SIMDs and the workgroups over the CUs.
 void prefill_plan(const int* rows, int n, int num_kv_heads, int num_cus, int* waves, int* rblk);
+// Prefill over an int8 pool: the prefill-class sequences' tiles dequantized to bf16 into a
+// workspace pool (max_seqs sequences of blocks_per_seq 16-token blocks) and its block table
+// [num_seqs][blocks_per_seq]; wgs >= the (sequence, KV head, tile) count (extra ones exit).
+struct DequantOut {
+  uint16_t* k;
+  uint16_t* v;
+  int32_t* tables;
+  int32_t blocks_per_seq;
+  int32_t max_seqs;
+};
+hipError_t launch_dequant_prefill(const AttnArgs& a, const DequantOut& o, int head_dim,
+                                  long long wgs, hipStream_t st);
 // Cross-split merge of the split-K partials: one workgroup per (partial row, q-head).
 hipError_t launch_attn_reduce(const AttnArgs& a, int elt_bytes, int head_dim, hipStream_t st);
 

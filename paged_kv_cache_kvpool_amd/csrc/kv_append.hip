@@ -75,31 +75,115 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   }
 }
 
-// grid (n, num_layers, 2): blockIdx.z picks K or V; 16-byte copies of one block of one layer.
+// int8 pool (sparkinfer server README, "Env", SPARKINFER_KV_INT8; NInfer serving doc, "Server
+// options", --kv-dtype int8): each new (token, KV head) row of bf16 values is quantised with
+// one fp32 scale s = absmax / 127 and codes q = rint(x / s) (correctly rounded division, ties
+// to even), clamped to +-127; a zero row gets s = 0 and codes 0.  Tile layouts (16 tokens):
+//   K: [d / 16][t % 16][d % 16]                      (16-byte chunks of 16 dims)
+//   V: [(t % 16) / 4][d % 16][d / 16][t % 4]         (the 4 keys of a dim group side by side)
+// One wave per (token, KV head) row of the workgroup's 16-token tile: lane l holds dims
+// E*l .. E*l + E - 1 (E = head_dim / 64), the absolute max comes from a wave reduction, and
+// codes are stored byte by byte (K) / to their scattered V slots.
+__device__ __forceinline__ float wave_max_f(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+template <int E>
+__device__ __forceinline__ void quantise_row(const uint16_t* src, float (&q)[E], float& scale) {
+  const int lane = threadIdx.x & (WAVE - 1);
+  float x[E];
+  float m = 0.f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    x[e] = __uint_as_float((uint32_t)src[E * lane + e] << 16);
+    m = fmaxf(m, fabsf(x[e]));
+  }
+  m = wave_max_f(m);
+  scale = __fdiv_rn(m, 127.f);
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    q[e] = scale > 0.f ? fminf(fmaxf(rintf(__fdiv_rn(x[e], scale)), -127.f), 127.f) : 0.f;
+}
+
+template <int E>
+__global__ __launch_bounds__(256) void append_i8_kernel(AppendArgs a) {
+  constexpr int D = 64 * E;
+  const int s = blockIdx.z, h = blockIdx.y;
+  const int lane = threadIdx.x & (WAVE - 1), wave = threadIdx.x >> 6;
+  const int cap = a.max_blocks_per_seq * a.block_size;
+  const int L = min(max(a.ctx_lens[s], 0), cap);
+  const int T = min(max(a.q_lens[s], 0), L);
+  if (T == 0) return;
+  const int p0 = L - T;
+  const int tile_start = (p0 / TILE + (int)blockIdx.x) * TILE;
+  if (tile_start >= L) return;
+  const int lo = max(p0, tile_start), hi = min(L, tile_start + TILE);
+  const int q_start = wave_prefix_total(a.q_lens, s);
+  const int32_t* row_tbl = a.block_tables + (size_t)s * a.max_blocks_per_seq;
+  const size_t toff = tile_offset(row_tbl, tile_start, h, a.block_size, a.num_blocks,
+                                  a.num_kv_heads, D);  // bytes: one byte per element
+  int8_t* kt = reinterpret_cast<int8_t*>(a.k_layer) + toff;
+  int8_t* vt = reinterpret_cast<int8_t*>(a.v_layer) + toff;
+  float* ks = a.k_scale_layer + toff / D;  // the tile's 16 token scales
+  float* vs = a.v_scale_layer + toff / D;
+  const uint16_t* kn = reinterpret_cast<const uint16_t*>(a.k_new);
+  const uint16_t* vn = reinterpret_cast<const uint16_t*>(a.v_new);
+  for (int p = lo + wave; p < hi; p += 4) {  // wave-uniform
+    const int row = q_start + (p - p0);
+    if (row >= a.total_q) continue;
+    const int tt = p - tile_start;
+    const size_t src = ((size_t)row * a.num_kv_heads + h) * D;
+    float qk[E], qv[E], sk, sv;
+    quantise_row<E>(kn + src, qk, sk);
+    quantise_row<E>(vn + src, qv, sv);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const int d = E * lane + e;
+      kt[(d >> 4) * 256 + tt * 16 + (d & 15)] = (int8_t)(int)qk[e];
+      vt[(((tt >> 2) * 16 + (d & 15)) * (D / 16) + (d >> 4)) * 4 + (tt & 3)] = (int8_t)(int)qv[e];
+    }
+    if (lane == 0) {
+      ks[tt] = sk;
+      vs[tt] = sv;
+    }
+  }
+}
+
+// grid (n, num_layers, 2 or 4): blockIdx.z picks K or V codes, then (int8 pools) K or V
+// scales; 16-byte copies of one block of one layer.
 __global__ __launch_bounds__(256) void copy_blocks_kernel(CopyArgs a) {
-  const int i = blockIdx.x, layer = blockIdx.y;
+  const int i = blockIdx.x, layer = blockIdx.y, z = blockIdx.z;
   const int src = a.src[i], dst = a.dst[i];
   if ((unsigned)src >= (unsigned)a.num_blocks || (unsigned)dst >= (unsigned)a.num_blocks) return;
-  char* base = reinterpret_cast<char*>(blockIdx.z == 0 ? a.k : a.v);
-  const size_t layer_off = (size_t)layer * a.num_blocks * a.block_bytes;
-  const u32x4* from = reinterpret_cast<const u32x4*>(base + layer_off + (size_t)src * a.block_bytes);
-  u32x4* to = reinterpret_cast<u32x4*>(base + layer_off + (size_t)dst * a.block_bytes);
-  const int n16 = (int)(a.block_bytes / 16);
+  const size_t bb = z < 2 ? a.block_bytes : a.block_scale_bytes;
+  char* base = reinterpret_cast<char*>(z == 0 ? a.k : z == 1 ? a.v : z == 2 ? a.k_scale : a.v_scale);
+  const size_t layer_off = (size_t)layer * a.num_blocks * bb;
+  const u32x4* from = reinterpret_cast<const u32x4*>(base + layer_off + (size_t)src * bb);
+  u32x4* to = reinterpret_cast<u32x4*>(base + layer_off + (size_t)dst * bb);
+  const int n16 = (int)(bb / 16);
   for (int u = threadIdx.x; u < n16; u += blockDim.x) to[u] = from[u];
 }
 
 hipError_t launch_append(const AppendArgs& a, int elt_bytes, int max_q_len, hipStream_t st) {
   const int tiles = (max_q_len + TILE - 1) / TILE + 1;
   dim3 grid(tiles, a.num_kv_heads, a.num_seqs);
-  if (elt_bytes == 2)
+  if (elt_bytes == 1) {
+    if (a.head_dim == 128)
+      append_i8_kernel<2><<<grid, 256, 0, st>>>(a);
+    else
+      append_i8_kernel<1><<<grid, 256, 0, st>>>(a);
+  } else if (elt_bytes == 2) {
     append_kernel<uint16_t><<<grid, 256, 0, st>>>(a);
-  else
+  } else {
     append_kernel<uint32_t><<<grid, 256, 0, st>>>(a);
+  }
   return hipGetLastError();
 }
 
 hipError_t launch_copy_blocks(const CopyArgs& a, int n, int num_layers, hipStream_t st) {
-  dim3 grid(n, num_layers, 2);
+  dim3 grid(n, num_layers, a.k_scale ? 4 : 2);
   copy_blocks_kernel<<<grid, 256, 0, st>>>(a);
   return hipGetLastError();
 }

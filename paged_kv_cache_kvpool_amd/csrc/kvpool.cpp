@@ -20,6 +20,8 @@ struct kvpool {
   int32_t num_layers, num_blocks, block_size, num_kv_heads, head_dim, dtype;
   void* k;
   void* v;
+  float* k_scale;      // int8 pools: [layers][blocks][Hkv][block_size] fp32 scales, else null
+  float* v_scale;
   size_t layer_elems;  // elements of one layer of K (or V)
   int device;
   int num_cus;         // compute units of that device
@@ -44,7 +46,7 @@ int ok() {
   return KV_OK;
 }
 
-int elt_bytes(int32_t dtype) { return dtype == KV_F32 ? 4 : 2; }
+int elt_bytes(int32_t dtype) { return dtype == KV_F32 ? 4 : dtype == KV_I8 ? 1 : 2; }
 
 bool env_flag(const char* name) {
   const char* v = getenv(name);
@@ -86,8 +88,8 @@ int check_geometry(int32_t num_layers, int32_t num_blocks, int32_t block_size,
     return fail(KV_EUNSUPPORTED, "block_size %d not supported (16 or 64)", block_size);
   if (head_dim != 64 && head_dim != 128)
     return fail(KV_EUNSUPPORTED, "head_dim %d not supported (64 or 128)", head_dim);
-  if (dtype != KV_F32 && dtype != KV_BF16)
-    return fail(KV_EUNSUPPORTED, "dtype %d not supported (KV_F32 or KV_BF16)", dtype);
+  if (dtype != KV_F32 && dtype != KV_BF16 && dtype != KV_I8)
+    return fail(KV_EUNSUPPORTED, "dtype %d not supported (KV_F32, KV_BF16 or KV_I8)", dtype);
   return KV_OK;
 }
 
@@ -141,9 +143,10 @@ int validate_meta(const kvpool* p, const HostMeta& m, int32_t max_blocks, int32_
 }
 
 // Opt-in per-kernel timing: a HIP event pair around every launch, on the launch's stream.
-enum KernelId { K_APPEND, K_COPY, K_SPLIT_MFMA, K_VEC, K_PREFILL_MFMA, K_REDUCE, K_COUNT };
+enum KernelId { K_APPEND, K_COPY, K_SPLIT_MFMA, K_VEC, K_PREFILL_MFMA, K_REDUCE, K_DEQUANT, K_COUNT };
 const char* const kKernelNames[K_COUNT] = {"kv_append", "kv_copy_blocks", "attn_split_mfma",
-                                           "attn_vec", "attn_prefill_mfma", "attn_reduce"};
+                                           "attn_vec", "attn_prefill_mfma", "attn_reduce",
+                                           "kv_dequant_prefill"};
 struct ProfRec {
   int kernel;
   hipEvent_t a, b;
@@ -226,13 +229,19 @@ int kvpool_storage_bytes(int32_t num_layers, int32_t num_blocks, int32_t block_s
   return ok();
 }
 
-int kvpool_create(kvpool_t** out, int32_t num_layers, int32_t num_blocks, int32_t block_size,
-                  int32_t num_kv_heads, int32_t head_dim, int32_t dtype, void* k_storage,
-                  void* v_storage) {
+}  // extern "C"
+
+namespace {
+
+int create_pool(kvpool_t** out, int32_t num_layers, int32_t num_blocks, int32_t block_size,
+                int32_t num_kv_heads, int32_t head_dim, int32_t dtype, void* k_storage,
+                void* v_storage, void* k_scales, void* v_scales) {
   if (!out) return fail(KV_EINVAL, "out is NULL");
   *out = nullptr;
   int rc = check_geometry(num_layers, num_blocks, block_size, num_kv_heads, head_dim, dtype);
   if (rc) return rc;
+  if (dtype == KV_I8 && (!k_scales || !v_scales || !aligned16(k_scales) || !aligned16(v_scales)))
+    return fail(KV_EINVAL, "int8 pools need 16-byte aligned K and V scale arrays");
   if (!k_storage || !v_storage) return fail(KV_EINVAL, "storage pointers must not be NULL");
   if (!aligned16(k_storage) || !aligned16(v_storage))
     return fail(KV_EINVAL, "storage pointers must be 16-byte aligned");
@@ -249,6 +258,8 @@ int kvpool_create(kvpool_t** out, int32_t num_layers, int32_t num_blocks, int32_
   p->dtype = dtype;
   p->k = k_storage;
   p->v = v_storage;
+  p->k_scale = dtype == KV_I8 ? static_cast<float*>(k_scales) : nullptr;
+  p->v_scale = dtype == KV_I8 ? static_cast<float*>(v_scales) : nullptr;
   p->layer_elems = (size_t)num_blocks * num_kv_heads * block_size * head_dim;
   p->device = dev;
   p->num_cus = 256;
@@ -256,6 +267,37 @@ int kvpool_create(kvpool_t** out, int32_t num_layers, int32_t num_blocks, int32_
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0)
     p->num_cus = cus;
   *out = p;
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int kvpool_create(kvpool_t** out, int32_t num_layers, int32_t num_blocks, int32_t block_size,
+                  int32_t num_kv_heads, int32_t head_dim, int32_t dtype, void* k_storage,
+                  void* v_storage) {
+  if (dtype == KV_I8) {
+    if (out) *out = nullptr;
+    return fail(KV_EINVAL, "int8 pools are created with kvpool_create_int8 (they need scale arrays)");
+  }
+  return create_pool(out, num_layers, num_blocks, block_size, num_kv_heads, head_dim, dtype,
+                     k_storage, v_storage, nullptr, nullptr);
+}
+
+int kvpool_create_int8(kvpool_t** out, int32_t num_layers, int32_t num_blocks, int32_t block_size,
+                       int32_t num_kv_heads, int32_t head_dim, void* k_storage, void* v_storage,
+                       void* k_scales, void* v_scales) {
+  return create_pool(out, num_layers, num_blocks, block_size, num_kv_heads, head_dim, KV_I8,
+                     k_storage, v_storage, k_scales, v_scales);
+}
+
+int kvpool_scale_bytes(int32_t num_layers, int32_t num_blocks, int32_t block_size,
+                       int32_t num_kv_heads, size_t* bytes) {
+  if (!bytes) return fail(KV_EINVAL, "bytes is NULL");
+  int rc = check_geometry(num_layers, num_blocks, block_size, num_kv_heads, 64, KV_I8);
+  if (rc) return rc;
+  *bytes = (size_t)num_layers * num_blocks * num_kv_heads * block_size * sizeof(float);
   return ok();
 }
 
@@ -306,6 +348,9 @@ int kvpool_append(kvpool_t* pool, int32_t layer, const void* k_new, const void* 
   a.v_layer = static_cast<char*>(pool->v) + lo;
   a.k_new = k_new;
   a.v_new = v_new;
+  const size_t so = (size_t)layer * pool->num_blocks * pool->num_kv_heads * pool->block_size;
+  a.k_scale_layer = pool->k_scale ? pool->k_scale + so : nullptr;
+  a.v_scale_layer = pool->v_scale ? pool->v_scale + so : nullptr;
   a.block_tables = block_tables;
   a.ctx_lens = ctx_lens;
   a.q_lens = q_lens;
@@ -352,6 +397,9 @@ int kvpool_copy_blocks(kvpool_t* pool, const int32_t* src, const int32_t* dst, i
   kvp::CopyArgs a;
   a.k = pool->k;
   a.v = pool->v;
+  a.k_scale = pool->k_scale;
+  a.v_scale = pool->v_scale;
+  a.block_scale_bytes = (size_t)pool->num_kv_heads * pool->block_size * sizeof(float);
   a.src = src;
   a.dst = dst;
   a.num_blocks = pool->num_blocks;
@@ -375,6 +423,11 @@ struct Plan {
   int rblk;           // prefill 32-row blocks per workgroup
   long long pf_wgs;   // prefill grid: its workgroups (or a bound of them)
   size_t o_bytes;     // partial outputs, rounded up to 256 bytes
+  // int8 pools with prefill-class sequences: their tiles dequantized to a bf16 workspace pool
+  int dq_seqs;        // prefill sequences it holds (exact or a bound)
+  int dq_mpb;         // 16-token blocks per sequence (ceil(max_ctx_len / 16))
+  size_t dq_off;      // byte offsets in the workspace: K pool, V pool, block table
+  size_t dq_v_off, dq_tbl_off;
   size_t bytes;
 };
 
@@ -390,6 +443,7 @@ Plan make_plan(const kvpool* p, int32_t num_q_heads, int32_t num_seqs, int32_t t
   pl.split = split_tokens();
   pl.max_splits = max_split_count(pl.split, max_ctx_len);
   std::vector<int> pf_rows;
+  int n_pf_exact = 0;
   if (q_lens_host) {
     long long split_tokens_sum = 0;
     int split_t = 0;
@@ -400,6 +454,7 @@ Plan make_plan(const kvpool* p, int32_t num_q_heads, int32_t num_seqs, int32_t t
         split_t = std::max(split_t, T);
       } else {
         pf_rows.push_back(T * G);
+        ++n_pf_exact;
       }
     }
     pl.split_k = split_tokens_sum > 0;
@@ -444,7 +499,18 @@ Plan make_plan(const kvpool* p, int32_t num_q_heads, int32_t num_seqs, int32_t t
   // [partial outputs, fp32][partial (max, sum) pairs, fp32]
   const size_t slots = (size_t)pl.part_rows * num_q_heads * pl.max_splits;
   pl.o_bytes = (slots * p->head_dim * 4 + 255) / 256 * 256;
-  pl.bytes = slots ? pl.o_bytes + slots * 2 * 4 : 0;
+  pl.bytes = slots ? pl.o_bytes + (slots * 2 * 4 + 255) / 256 * 256 : 0;
+  if (p->dtype == KV_I8 && pl.prefill) {
+    // [dequantized K][dequantized V][block table], each 256-byte aligned
+    pl.dq_seqs = q_lens_host ? n_pf_exact
+                             : (int)std::min<long long>(num_seqs, total_q / (sqm + 1));
+    pl.dq_mpb = (max_ctx_len + 15) / 16;
+    const size_t pool_bytes = (size_t)pl.dq_seqs * pl.dq_mpb * p->num_kv_heads * 16 * p->head_dim * 2;
+    pl.dq_off = pl.bytes;
+    pl.dq_v_off = pl.dq_off + (pool_bytes + 255) / 256 * 256;
+    pl.dq_tbl_off = pl.dq_v_off + (pool_bytes + 255) / 256 * 256;
+    pl.bytes = pl.dq_tbl_off + ((size_t)num_seqs * pl.dq_mpb * 4 + 255) / 256 * 256;
+  }
   return pl;
 }
 
@@ -521,6 +587,9 @@ int kvattn_forward(kvpool_t* pool, int32_t layer, const void* q, void* out, int3
   a.out = out;
   a.k_layer = static_cast<const char*>(pool->k) + lo;
   a.v_layer = static_cast<const char*>(pool->v) + lo;
+  const size_t so = (size_t)layer * pool->num_blocks * pool->num_kv_heads * pool->block_size;
+  a.k_scale_layer = pool->k_scale ? pool->k_scale + so : nullptr;
+  a.v_scale_layer = pool->v_scale ? pool->v_scale + so : nullptr;
   a.block_tables = block_tables;
   a.ctx_lens = ctx_lens;
   a.q_lens = q_lens;
@@ -543,9 +612,12 @@ int kvattn_forward(kvpool_t* pool, int32_t layer, const void* q, void* out, int3
   a.pf_rblk = pl.rblk;
   a.scale_log2 = scale * kvp::LOG2E;
 
-  const int eb = elt_bytes(pool->dtype);
+  // q / out element bytes (bf16 for int8 pools)
+  const int eb = pool->dtype == KV_F32 ? 4 : 2;
+  const bool i8 = pool->dtype == KV_I8;
   hipError_t e = hipSuccess;
-  if (pool->dtype == KV_F32 || (!pl.prefill && max_q_len == 1 && env_flag("KVATTN_DECODE_VEC"))) {
+  if (pool->dtype == KV_F32 ||
+      (pool->dtype == KV_BF16 && !pl.prefill && max_q_len == 1 && env_flag("KVATTN_DECODE_VEC"))) {
     // One launch for every sequence: split-K sequences in splits, longer ones in one pass.
     // Rows per wave: the template instance just large enough (1, 2, 4, 5 or 8).
     const int rows = max_q_len * G;
@@ -560,10 +632,31 @@ int kvattn_forward(kvpool_t* pool, int32_t layer, const void* q, void* out, int3
       const int rpt = pl.split_rows <= 16 ? 16 : 32;
       kvp::AttnArgs as = a;
       as.row_tiles = (pl.split_rows + rpt - 1) / rpt;
-      e = timed(K_SPLIT_MFMA, st, [&] { return kvp::launch_attn_split_mfma(as, pool->head_dim, rpt, pl.max_splits, pool->num_cus, st); });
+      e = timed(K_SPLIT_MFMA, st, [&] { return kvp::launch_attn_split_mfma(as, pool->head_dim, rpt, pl.max_splits, pool->num_cus, i8, st); });
     }
     if (e == hipSuccess && pl.prefill) {
-      e = timed(K_PREFILL_MFMA, st, [&] { return kvp::launch_attn_prefill_mfma(a, pool->head_dim, pl.waves, pl.pf_wgs, st); });
+      kvp::AttnArgs ap = a;
+      if (i8) {
+        // dequantize the prefill sequences' tiles into the workspace pool, then run the bf16
+        // kernel on it (16-token blocks, its own block table)
+        kvp::DequantOut dq;
+        dq.k = reinterpret_cast<uint16_t*>(ws + pl.dq_off);
+        dq.v = reinterpret_cast<uint16_t*>(ws + pl.dq_v_off);
+        dq.tables = reinterpret_cast<int32_t*>(ws + pl.dq_tbl_off);
+        dq.blocks_per_seq = pl.dq_mpb;
+        dq.max_seqs = pl.dq_seqs;
+        const long long wgs = (long long)pl.dq_seqs * pool->num_kv_heads * pl.dq_mpb;
+        e = timed(K_DEQUANT, st, [&] { return kvp::launch_dequant_prefill(a, dq, pool->head_dim, wgs, st); });
+        ap.k_layer = dq.k;
+        ap.v_layer = dq.v;
+        ap.block_tables = dq.tables;
+        ap.max_blocks_per_seq = pl.dq_mpb;
+        ap.block_size = 16;
+        ap.block_shift = 4;
+        ap.num_blocks = std::max(1, pl.dq_seqs * pl.dq_mpb);
+      }
+      if (e == hipSuccess)
+        e = timed(K_PREFILL_MFMA, st, [&] { return kvp::launch_attn_prefill_mfma(ap, pool->head_dim, pl.waves, pl.pf_wgs, st); });
     }
   }
   if (e != hipSuccess) return fail(KV_EDEVICE, "attention launch: %s", hipGetErrorString(e));

@@ -18,7 +18,10 @@ Recipe (the same for every generator):
   * block tables are slices of one seeded permutation of the pool, so placement is random
     and sequences never share a block unless a test asks for it;
   * the K/V of tokens being processed (``k_new``/``v_new``) are drawn separately and are
-    written by the append call before attention.
+    written by the append call before attention;
+  * int8 pools are drawn as raw storage too: codes round(N(0,1) * 127 / 4) clipped to +-127 and
+    scales 4/127 * U(0.8, 1.2) (dequantized values roughly N(0, 1)); unreferenced blocks carry
+    NaN scales as canaries.  q and the new rows of an int8 pool are bf16.
 """
 from __future__ import annotations
 
@@ -29,6 +32,7 @@ import numpy as np
 
 F32 = "f32"
 BF16 = "bf16"
+I8 = "i8"     # int8 pool: codes and per-(token, KV head) fp32 scales; q and new rows are bf16
 
 BF16_NAN = np.uint16(0x7FC0)
 F32_NAN = np.float32(np.nan)
@@ -75,6 +79,8 @@ class Workload:
     v_new: Optional[np.ndarray] = None
     pool_seed: Optional[int] = None      # set when the pool is too large to draw on the host
     referenced: Optional[np.ndarray] = None  # bool [num_blocks]: blocks some table uses
+    k_scales: Optional[np.ndarray] = None    # int8 pools: float32 [layers][blocks][Hkv][B]
+    v_scales: Optional[np.ndarray] = None
 
     @property
     def num_seqs(self) -> int:
@@ -90,7 +96,13 @@ class Workload:
 
     @property
     def elt_bytes(self) -> int:
-        return 4 if self.dtype == F32 else 2
+        """Bytes of one pool element."""
+        return 4 if self.dtype == F32 else 1 if self.dtype == I8 else 2
+
+    @property
+    def act_dtype(self) -> str:
+        """dtype of q, out and the new rows (bf16 for an int8 pool)."""
+        return BF16 if self.dtype == I8 else self.dtype
 
 
 def _blocks_for(ctx: int, block_size: int) -> int:
@@ -115,6 +127,27 @@ def _pool(rng, dtype, num_layers, num_blocks, block_elems, referenced):
     k[:, ~referenced] = nan_fill(dtype)
     v[:, ~referenced] = nan_fill(dtype)
     return k, v
+
+
+def draw_codes(rng, shape) -> np.ndarray:
+    """int8 codes round(N(0,1) * 127 / 4), clipped to +-127."""
+    x = rng.standard_normal(size=shape, dtype=np.float32) * np.float32(127.0 / 4.0)
+    return np.clip(np.rint(x), -127, 127).astype(np.int8)
+
+
+def draw_scales(rng, shape) -> np.ndarray:
+    return (rng.uniform(0.8, 1.2, size=shape) * (4.0 / 127.0)).astype(np.float32)
+
+
+def _pool_i8(rng, num_layers, num_blocks, num_kv_heads, block_size, head_dim, referenced):
+    elems = num_kv_heads * block_size * head_dim
+    k = draw_codes(rng, (num_layers, num_blocks, elems))
+    v = draw_codes(rng, (num_layers, num_blocks, elems))
+    sshape = (num_layers, num_blocks, num_kv_heads, block_size)
+    ks, vs = draw_scales(rng, sshape), draw_scales(rng, sshape)
+    ks[:, ~referenced] = np.nan
+    vs[:, ~referenced] = np.nan
+    return k, v, ks, vs
 
 
 def _referenced(tables, ctx_lens, block_size, num_blocks):
@@ -145,16 +178,20 @@ def make(name, *, seed, dtype, num_seqs_ctx, q_lens, num_q_heads, num_kv_heads, 
     perm = rng.permutation(nb).astype(np.int32)
     tables, _ = _tables_from_perm(perm, ctx, block_size, max_blocks)
     total_q = int(ql.sum())
-    q = draw(rng, (total_q, num_q_heads, head_dim), dtype)
+    act = BF16 if dtype == I8 else dtype
+    q = draw(rng, (total_q, num_q_heads, head_dim), act)
     k_new = v_new = None
     if append:
-        k_new = draw(rng, (total_q, num_kv_heads, head_dim), dtype)
-        v_new = draw(rng, (total_q, num_kv_heads, head_dim), dtype)
+        k_new = draw(rng, (total_q, num_kv_heads, head_dim), act)
+        v_new = draw(rng, (total_q, num_kv_heads, head_dim), act)
     ref = _referenced(tables, ctx, block_size, nb)
     block_elems = num_kv_heads * block_size * head_dim
-    k_pool = v_pool = None
+    k_pool = v_pool = k_scales = v_scales = None
     pool_seed = None
-    if host_pool:
+    if host_pool and dtype == I8:
+        k_pool, v_pool, k_scales, v_scales = _pool_i8(rng, num_layers, nb, num_kv_heads,
+                                                      block_size, head_dim, ref)
+    elif host_pool:
         k_pool, v_pool = _pool(rng, dtype, num_layers, nb, block_elems, ref)
     else:
         pool_seed = int(rng.integers(0, 2**31 - 1))
@@ -164,7 +201,8 @@ def make(name, *, seed, dtype, num_seqs_ctx, q_lens, num_q_heads, num_kv_heads, 
                     block_size=block_size, num_kv_heads=num_kv_heads, num_q_heads=num_q_heads,
                     head_dim=head_dim, scale=float(scale), layer=layer, q=q, k_pool=k_pool,
                     v_pool=v_pool, block_tables=tables, ctx_lens=ctx, q_lens=ql, k_new=k_new,
-                    v_new=v_new, pool_seed=pool_seed, referenced=ref)
+                    v_new=v_new, pool_seed=pool_seed, referenced=ref, k_scales=k_scales,
+                    v_scales=v_scales)
 
 
 # ---------------------------------------------------------------------------------------
@@ -188,46 +226,49 @@ def tiny_decode(seed: int = 0) -> Workload:
                     referenced=ref)
 
 
-def batched_gqa_decode(seed: int = 1, num_seqs: int = 32, host_pool: bool = True) -> Workload:
+def batched_gqa_decode(seed: int = 1, num_seqs: int = 32, host_pool: bool = True,
+                       dtype: str = BF16) -> Workload:
     """32 sequences x 1 query token, 32 q-heads / 8 kv-heads, D=128, bf16, B=16, contexts
     uniform on [1024, 8192]; the pool is exactly the blocks the contexts need, dealt out as
     disjoint random slices of one permutation.  The current token's K/V is appended first."""
     rng = np.random.default_rng(seed)
     ctx = rng.integers(1024, 8193, size=num_seqs).astype(np.int32)
-    return make("batched_gqa_decode", seed=seed + 1000, dtype=BF16, num_seqs_ctx=ctx,
-                q_lens=np.ones(num_seqs, np.int32), num_q_heads=32, num_kv_heads=8,
-                head_dim=128, append=True, host_pool=host_pool)
+    return make("batched_gqa_decode" + ("_int8" if dtype == I8 else ""), seed=seed + 1000,
+                dtype=dtype, num_seqs_ctx=ctx, q_lens=np.ones(num_seqs, np.int32),
+                num_q_heads=32, num_kv_heads=8, head_dim=128, append=True, host_pool=host_pool)
 
 
 def spec_verify(seed: int = 2, cached: int = 32768, drafts: int = 3,
-                host_pool: bool = True) -> Workload:
+                host_pool: bool = True, dtype: str = BF16) -> Workload:
     """One sequence verifying 1 + drafts tokens (causal among themselves) over a cached
     context, 40 q-heads / 8 kv-heads, D=128, bf16, randomly permuted table; the new tokens'
     K/V are appended at positions cached .. cached+drafts."""
     t = 1 + drafts
-    return make(f"spec_verify_{cached}", seed=seed, dtype=BF16, num_seqs_ctx=[cached + t],
+    return make(f"spec_verify_{cached}" + ("_int8" if dtype == I8 else ""), seed=seed,
+                dtype=dtype, num_seqs_ctx=[cached + t],
                 q_lens=[t], num_q_heads=40, num_kv_heads=8, head_dim=128, append=True,
                 host_pool=host_pool)
 
 
 def prefix_prefill(seed: int = 3, num_seqs: int = 4, prefix: int = 4096, suffix: int = 512,
-                   host_pool: bool = True) -> Workload:
+                   host_pool: bool = True, dtype: str = BF16) -> Workload:
     """4 sequences, each a 4096-token cached prefix plus a 512-token new suffix (causal),
     40/8 heads, D=128, bf16; the suffix K/V are appended before attention."""
-    return make("prefix_prefill", seed=seed, dtype=BF16,
+    return make("prefix_prefill" + ("_int8" if dtype == I8 else ""), seed=seed, dtype=dtype,
                 num_seqs_ctx=[prefix + suffix] * num_seqs, q_lens=[suffix] * num_seqs,
                 num_q_heads=40, num_kv_heads=8, head_dim=128, append=True, host_pool=host_pool)
 
 
-def long_decode(seed: int = 4, host_pool: bool = False) -> Workload:
+def long_decode(seed: int = 4, host_pool: bool = False, dtype: str = BF16) -> Workload:
     """2 concurrent sequences at 262144 and 131072 tokens, 1 query token each, 40/8 heads,
     D=128, bf16, pool of 24576 blocks (393216 tokens) with random placement."""
-    return make("long_decode", seed=seed, dtype=BF16, num_seqs_ctx=[262144, 131072],
+    return make("long_decode" + ("_int8" if dtype == I8 else ""), seed=seed, dtype=dtype,
+                num_seqs_ctx=[262144, 131072],
                 q_lens=[1, 1], num_q_heads=40, num_kv_heads=8, head_dim=128, append=True,
                 num_blocks=24576, host_pool=host_pool)
 
 
-def mixed_step(seed: int = 5, host_pool: bool = True) -> Workload:
+def mixed_step(seed: int = 5, host_pool: bool = True, dtype: str = BF16) -> Workload:
     """One serving step that batches every kind of sequence the pool serves: 32 decode
     sequences (1 token, contexts uniform on [1024, 8192]), one verification of 1 + 3 draft
     tokens over a 32768-token context and one 512-token prefill chunk over a 4096-token cached
@@ -240,7 +281,8 @@ def mixed_step(seed: int = 5, host_pool: bool = True) -> Workload:
     ql[10:10] = [4]
     ctx[20:20] = [4096 + 512]
     ql[20:20] = [512]
-    return make("mixed_step", seed=seed + 1000, dtype=BF16, num_seqs_ctx=ctx, q_lens=ql,
+    return make("mixed_step" + ("_int8" if dtype == I8 else ""), seed=seed + 1000, dtype=dtype,
+                num_seqs_ctx=ctx, q_lens=ql,
                 num_q_heads=40, num_kv_heads=8, head_dim=128, append=True, host_pool=host_pool)
 
 

@@ -6,10 +6,15 @@ import numpy as np
 import torch
 
 from oracle import attention as ora
+from oracle import quant as oq
 from paged_kv_cache_kvpool_amd import binding as kb
 from paged_kv_cache_kvpool_amd import workloads as wl
 
-TOL = {wl.BF16: dict(max_abs=2e-2, rel_l2=5e-3), wl.F32: dict(max_abs=1e-5, rel_l2=1e-5)}
+# int8 pools: compared with the oracle run on the exactly dequantized values, at the bf16 bar
+# (q, P and out are bf16 on the GPU).
+TOL = {wl.BF16: dict(max_abs=2e-2, rel_l2=5e-3), wl.F32: dict(max_abs=1e-5, rel_l2=1e-5),
+       wl.I8: dict(max_abs=2e-2, rel_l2=5e-3)}
+KV_DTYPE = {wl.F32: kb.KV_F32, wl.BF16: kb.KV_BF16, wl.I8: kb.KV_I8}
 
 
 def to_torch(arr: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
@@ -34,11 +39,29 @@ class DeviceCase:
 
     def __init__(self, w: wl.Workload, device="cuda"):
         self.w = w
-        dt = kb.KV_BF16 if w.dtype == wl.BF16 else kb.KV_F32
         self.pool = kb.PagedKVPool(w.num_layers, w.num_blocks, w.block_size, w.num_kv_heads,
-                                   w.head_dim, dt, device=device)
+                                   w.head_dim, KV_DTYPE[w.dtype], device=device)
         kview, vview = self.pool.block_storage("k"), self.pool.block_storage("v")
-        if w.k_pool is not None:
+        if w.dtype == wl.I8 and w.k_pool is not None:
+            kview.copy_(torch.from_numpy(w.k_pool).to(device).view(kview.shape))
+            vview.copy_(torch.from_numpy(w.v_pool).to(device).view(vview.shape))
+            self.pool.k_scales.copy_(torch.from_numpy(w.k_scales).to(device))
+            self.pool.v_scales.copy_(torch.from_numpy(w.v_scales).to(device))
+        elif w.dtype == wl.I8:
+            # drawn on the device, with the generator's recipe (workloads.py): codes
+            # round(N(0,1) * 127/4) clipped to +-127, scales 4/127 * U(0.8, 1.2), NaN scales in
+            # unreferenced blocks
+            g = torch.Generator(device=device)
+            g.manual_seed(int(w.pool_seed))
+            for view in (kview, vview):
+                for layer in range(w.num_layers):
+                    x = torch.randn(view[layer].shape, generator=g, device=device) * (127.0 / 4.0)
+                    view[layer].copy_(x.round().clamp_(-127, 127).to(torch.int8))
+            for sc in (self.pool.k_scales, self.pool.v_scales):
+                sc.copy_(torch.rand(sc.shape, generator=g, device=device) * 0.4 + 0.8).mul_(4.0 / 127.0)
+                if w.referenced is not None:
+                    sc[:, torch.from_numpy(~w.referenced).to(device)] = float("nan")
+        elif w.k_pool is not None:
             kview.copy_(to_torch(w.k_pool, w.dtype, device).view(kview.shape))
             vview.copy_(to_torch(w.v_pool, w.dtype, device).view(vview.shape))
         else:
@@ -52,12 +75,13 @@ class DeviceCase:
                 if w.referenced is not None:
                     dead = torch.from_numpy(~w.referenced).to(device)
                     view[:, dead] = float("nan")
-        self.q = to_torch(w.q, w.dtype, device)
+        act = w.act_dtype
+        self.q = to_torch(w.q, act, device)
         self.tables = torch.from_numpy(w.block_tables).to(device)
         self.ctx = torch.from_numpy(w.ctx_lens).to(device)
         self.ql = torch.from_numpy(w.q_lens).to(device)
-        self.k_new = None if w.k_new is None else to_torch(w.k_new, w.dtype, device)
-        self.v_new = None if w.v_new is None else to_torch(w.v_new, w.dtype, device)
+        self.k_new = None if w.k_new is None else to_torch(w.k_new, act, device)
+        self.v_new = None if w.v_new is None else to_torch(w.v_new, act, device)
 
     # -- library --------------------------------------------------------------------------
     def append(self):
@@ -75,15 +99,35 @@ class DeviceCase:
 
     # -- host copies for the oracle ---------------------------------------------------------
     def host_pools(self):
+        """Host copies of the device pool: (K, V), or (K, V, K scales, V scales) for int8."""
         w = self.w
+        if w.dtype == wl.I8:
+            return (self.pool.block_storage("k").cpu().numpy(), self.pool.block_storage("v").cpu().numpy(),
+                    self.pool.k_scales.cpu().numpy(), self.pool.v_scales.cpu().numpy())
         k = to_numpy(self.pool.block_storage("k"), w.dtype)
         v = to_numpy(self.pool.block_storage("v"), w.dtype)
         return k, v
 
-    def oracle(self, k_pool=None, v_pool=None, seqs=None):
+    def oracle(self, k_pool=None, v_pool=None, seqs=None, scales=None):
         """Oracle output.  Pools default to the workload's own pre-append pool with the new rows
-        appended by the oracle (never the device's pool)."""
+        appended by the oracle (never the device's pool); an int8 pool also takes its scales
+        (K, V)."""
         w = self.w
+        if w.dtype == wl.I8:
+            if k_pool is None:
+                if w.k_pool is None:
+                    raise ValueError("pool drawn on the device: pass the pre-append host pool")
+                k_pool, v_pool, scales = w.k_pool, w.v_pool, (w.k_scales, w.v_scales)
+            ks, vs = scales
+            if w.k_new is not None:
+                k_pool, v_pool, ks, vs = oq.append(k_pool, v_pool, ks, vs, w.layer, w.k_new, w.v_new,
+                                                   w.block_tables, w.ctx_lens, w.q_lens,
+                                                   num_kv_heads=w.num_kv_heads,
+                                                   block_size=w.block_size, head_dim=w.head_dim)
+            return oq.paged_attention(w.q, k_pool, v_pool, ks, vs, w.layer, w.block_tables,
+                                      w.ctx_lens, w.q_lens, scale=w.scale,
+                                      num_kv_heads=w.num_kv_heads, block_size=w.block_size,
+                                      head_dim=w.head_dim, seqs=seqs)
         if k_pool is None:
             if w.k_pool is None:
                 raise ValueError("pool drawn on the device: pass the pre-append host pool")

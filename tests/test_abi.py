@@ -35,6 +35,20 @@ def test_every_declared_symbol_is_exported():
 def test_storage_bytes():
     assert kb.kvpool_storage_bytes(2, 10, 16, 8, 128, kb.KV_BF16) == 2 * 10 * 16 * 8 * 128 * 2
     assert kb.kvpool_storage_bytes(1, 3, 64, 1, 64, kb.KV_F32) == 3 * 64 * 64 * 4
+    assert kb.kvpool_storage_bytes(2, 10, 16, 8, 128, kb.KV_I8) == 2 * 10 * 16 * 8 * 128
+    assert kb.kvpool_scale_bytes(2, 10, 16, 8) == 2 * 10 * 8 * 16 * 4
+
+
+def test_int8_pool_needs_its_own_create():
+    """kvpool_create refuses KV_I8; kvpool_create_int8 refuses missing or misaligned scale arrays
+    (host-side checks, no GPU involved)."""
+    lib = kb.lib()
+    h = ctypes.c_void_p(0)
+    assert lib.kvpool_create(ctypes.byref(h), 1, 4, 16, 1, 128, kb.KV_I8, 16, 16) == kb.KV_EINVAL
+    assert lib.kvpool_create_int8(ctypes.byref(h), 1, 4, 16, 1, 128, 16, 16, None, 16) == kb.KV_EINVAL
+    assert lib.kvpool_create_int8(ctypes.byref(h), 1, 4, 16, 1, 128, 16, 16, 16, 8) == kb.KV_EINVAL
+    assert lib.kvpool_create_int8(ctypes.byref(h), 1, 4, 48, 1, 128, 16, 16, 16, 16) == kb.KV_EUNSUPPORTED
+    assert h.value is None
 
 
 @pytest.mark.parametrize("args,code", [
