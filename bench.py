@@ -46,10 +46,29 @@ WORKLOADS = {
     "mixed_step": dict(kind="hbm", desc="one call: 32 decode seqs (ctx U[1024,8192]) + 1 verify (1+3 at 32768) + "
                                         "1 prefill chunk (512 over 4096 cached), 40/8 heads, D=128, bf16"),
 }
+# The same workloads on an int8 pool (codes + one fp32 scale per token and KV head; q, out and
+# appended rows bf16).
+for _n in ("batched_gqa_decode", "spec_verify_32k", "spec_verify_128k", "prefix_prefill",
+           "long_decode", "mixed_step"):
+    WORKLOADS[_n + "_int8"] = dict(kind=WORKLOADS[_n]["kind"],
+                                   desc=WORKLOADS[_n]["desc"].replace("bf16", "int8 KV (bf16 q)"))
 
 
 def make_workload(name):
     from paged_kv_cache_kvpool_amd import workloads as wl
+    if name.endswith("_int8"):
+        base = name[:-len("_int8")]
+        kw = dict(host_pool=False, dtype=wl.I8)
+        if base == "batched_gqa_decode":
+            return wl.batched_gqa_decode(**kw)
+        if base.startswith("spec_verify_"):
+            return wl.spec_verify(cached={"32k": 32768, "128k": 131072}[base.split("_")[-1]], **kw)
+        if base == "prefix_prefill":
+            return wl.prefix_prefill(**kw)
+        if base == "long_decode":
+            return wl.long_decode(**kw)
+        if base == "mixed_step":
+            return wl.mixed_step(**kw)
     if name == "batched_gqa_decode":
         return wl.batched_gqa_decode(host_pool=False)
     if name == "tiny_decode":
@@ -75,15 +94,17 @@ SPLIT_ROWS_MAX = 128
 def algorithmic(w):
     """Per-step algorithmic bytes and flops (and attended KV tokens), from the definition, for
     the whole step and for the sequences each attention kernel serves."""
-    eb = w.elt_bytes
+    eb = w.elt_bytes                       # pool element bytes
+    ab = 4 if w.dtype == "f32" else 2      # q / out / appended row element bytes
+    sb = 2 * 4 if w.dtype == "i8" else 0   # int8 pools: K and V scale per token and KV head
     d, hq, hkv = w.head_dim, w.num_q_heads, w.num_kv_heads
     g = hq // hkv
     out = dict(kv_tokens=0, kv_bytes=0, attn_bytes=0, append_bytes=0, flops=0, pairs=0,
                split_bytes=0, split_flops=0, prefill_bytes=0, prefill_flops=0)
     for L, T in zip(w.ctx_lens.astype(np.int64), w.q_lens.astype(np.int64)):
         L, T = int(L), int(T)
-        kv = L * hkv * d * 2 * eb                       # K and V of every key, once per KV head
-        qo = 2 * T * hq * d * eb
+        kv = L * hkv * (d * 2 * eb + sb)                # K and V of every key, once per KV head
+        qo = 2 * T * hq * d * ab
         tab = (L + w.block_size - 1) // w.block_size * 4
         pairs = T * (L - T) + T * (T + 1) // 2          # row i sees L - T + i + 1 keys
         fl = 4 * d * hq * pairs
@@ -94,10 +115,10 @@ def algorithmic(w):
         out["flops"] += fl
         # a kernel's own bytes: K/V, Q and the table (its output write is small beside them)
         cls = "split" if T * g <= SPLIT_ROWS_MAX else "prefill"
-        out[cls + "_bytes"] += kv + T * hq * d * eb + tab
+        out[cls + "_bytes"] += kv + T * hq * d * ab + tab
         out[cls + "_flops"] += fl
-    if w.k_new is not None:
-        out["append_bytes"] = 2 * 2 * w.total_q * hkv * d * eb
+    if w.k_new is not None:  # read the new rows, write them (as codes and scales for int8)
+        out["append_bytes"] = 2 * w.total_q * hkv * (d * ab + d * eb + sb // 2)
     out["step_bytes"] = out["attn_bytes"] + out["append_bytes"]
     return out
 
@@ -138,28 +159,41 @@ def cpu_baseline(w, dev, kind, budget_s=15.0):
     """The float64 oracle (as it stands) on a bounded sample: whole sequences, in order, until
     about budget_s of CPU work; scaled to the metric's unit."""
     from oracle import attention as ora
+    from oracle import quant as oq
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # pragma: no cover
         threads = 1
-    k_pool, v_pool = dev.pre_append_host()
-    if w.k_new is not None:
-        k_pool, v_pool = ora.append(k_pool, v_pool, w.layer, w.k_new, w.v_new, w.block_tables,
-                                    w.ctx_lens, w.q_lens, num_kv_heads=w.num_kv_heads,
-                                    block_size=w.block_size, head_dim=w.head_dim, dtype=w.dtype)
+    geo = dict(num_kv_heads=w.num_kv_heads, block_size=w.block_size, head_dim=w.head_dim)
+    i8 = w.dtype == "i8"
+    if i8:
+        k_pool, v_pool, k_sc, v_sc = dev.pre_append_host()
+        if w.k_new is not None:
+            k_pool, v_pool, k_sc, v_sc = oq.append(k_pool, v_pool, k_sc, v_sc, w.layer, w.k_new,
+                                                   w.v_new, w.block_tables, w.ctx_lens, w.q_lens,
+                                                   **geo)
+    else:
+        k_pool, v_pool = dev.pre_append_host()
+        if w.k_new is not None:
+            k_pool, v_pool = ora.append(k_pool, v_pool, w.layer, w.k_new, w.v_new, w.block_tables,
+                                        w.ctx_lens, w.q_lens, dtype=w.dtype, **geo)
+    ab = 4 if w.dtype == "f32" else 2
+    per_key = w.num_kv_heads * (w.head_dim * 2 * w.elt_bytes + (8 if i8 else 0))
     n_done, t_used, b_done, f_done, tok_done = 0, 0.0, 0, 0, 0
     for s in range(w.num_seqs):
         t0 = time.perf_counter()
-        ora.paged_attention(w.q, k_pool, v_pool, w.layer, w.block_tables, w.ctx_lens, w.q_lens,
-                            scale=w.scale, num_kv_heads=w.num_kv_heads, block_size=w.block_size,
-                            head_dim=w.head_dim, dtype=w.dtype, seqs=[s])
+        if i8:
+            oq.paged_attention(w.q, k_pool, v_pool, k_sc, v_sc, w.layer, w.block_tables,
+                               w.ctx_lens, w.q_lens, scale=w.scale, seqs=[s], **geo)
+        else:
+            ora.paged_attention(w.q, k_pool, v_pool, w.layer, w.block_tables, w.ctx_lens,
+                                w.q_lens, scale=w.scale, dtype=w.dtype, seqs=[s], **geo)
         t_used += time.perf_counter() - t0
         L, T = int(w.ctx_lens[s]), int(w.q_lens[s])
         n_done += 1
         tok_done += L
-        b_done += (L * w.num_kv_heads * w.head_dim * 2 * w.elt_bytes
-                   + 2 * T * w.num_q_heads * w.head_dim * w.elt_bytes)
+        b_done += L * per_key + 2 * T * w.num_q_heads * w.head_dim * ab
         f_done += 4 * w.head_dim * w.num_q_heads * (T * (L - T) + T * (T + 1) // 2)
         if t_used >= budget_s:
             break
@@ -181,22 +215,41 @@ class Device:
         from paged_kv_cache_kvpool_amd import workloads as wl
         self.w = w
         self.torch = torch
-        dt = kb.KV_BF16 if w.dtype == wl.BF16 else kb.KV_F32
+        dt = {wl.BF16: kb.KV_BF16, wl.F32: kb.KV_F32, wl.I8: kb.KV_I8}[w.dtype]
         self.pool = kb.PagedKVPool(w.num_layers, w.num_blocks, w.block_size, w.num_kv_heads,
                                    w.head_dim, dt, device="cuda")
         tdt = self.pool.torch_dtype
 
-        def dev(a):
+        def dev(a, dtype):
             if a is None:
                 return None
-            if w.dtype == wl.BF16:
+            if dtype == wl.BF16:
                 return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
             return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
 
         kv, vv = self.pool.block_storage("k"), self.pool.block_storage("v")
-        if w.k_pool is not None:
-            kv.copy_(dev(w.k_pool).view(kv.shape))
-            vv.copy_(dev(w.v_pool).view(vv.shape))
+        if w.dtype == wl.I8 and w.k_pool is not None:
+            kv.copy_(torch.from_numpy(w.k_pool).cuda().view(kv.shape))
+            vv.copy_(torch.from_numpy(w.v_pool).cuda().view(vv.shape))
+            self.pool.k_scales.copy_(torch.from_numpy(w.k_scales).cuda())
+            self.pool.v_scales.copy_(torch.from_numpy(w.v_scales).cuda())
+        elif w.dtype == wl.I8:
+            # the workload generator's int8 recipe, drawn on the device: codes
+            # round(N(0,1) * 127/4) clipped to +-127, scales 4/127 * U(0.8, 1.2), NaN scales in
+            # unreferenced blocks
+            g = torch.Generator(device="cuda")
+            g.manual_seed(int(w.pool_seed))
+            for view in (kv, vv):
+                for layer in range(w.num_layers):
+                    x = torch.randn(view[layer].shape, generator=g, device="cuda") * (127.0 / 4.0)
+                    view[layer].copy_(x.round().clamp_(-127, 127).to(torch.int8))
+            dead = torch.from_numpy(~w.referenced).cuda()
+            for sc in (self.pool.k_scales, self.pool.v_scales):
+                sc.copy_(torch.rand(sc.shape, generator=g, device="cuda") * 0.4 + 0.8).mul_(4.0 / 127.0)
+                sc[:, dead] = float("nan")
+        elif w.k_pool is not None:
+            kv.copy_(dev(w.k_pool, w.dtype).view(kv.shape))
+            vv.copy_(dev(w.v_pool, w.dtype).view(vv.shape))
         else:
             g = torch.Generator(device="cuda")
             g.manual_seed(int(w.pool_seed))
@@ -206,8 +259,8 @@ class Device:
                                                   dtype=torch.float32).to(tdt))
                 view[:, torch.from_numpy(~w.referenced).cuda()] = float("nan")
         self._pre = None
-        self.q = dev(w.q)
-        self.k_new, self.v_new = dev(w.k_new), dev(w.v_new)
+        self.q = dev(w.q, w.act_dtype)
+        self.k_new, self.v_new = dev(w.k_new, w.act_dtype), dev(w.v_new, w.act_dtype)
         self.tables = torch.from_numpy(w.block_tables).cuda()
         self.ctx = torch.from_numpy(w.ctx_lens).cuda()
         self.ql = torch.from_numpy(w.q_lens).cuda()
@@ -231,6 +284,8 @@ class Device:
         for which in ("k", "v"):
             t = self.pool.block_storage(which).cpu()
             out.append(t.view(torch.int16).numpy().view(np.uint16) if self.w.dtype == wl.BF16 else t.numpy())
+        if self.w.dtype == wl.I8:
+            out += [self.pool.k_scales.cpu().numpy(), self.pool.v_scales.cpu().numpy()]
         self._pre = tuple(out)
 
     def step(self):
@@ -379,11 +434,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": w.dtype,
+        "dtype": "bf16" if w.dtype == "i8" else w.dtype,  # int8 pools: bf16 MFMA on the codes
         "data": "synthetic",
         "config": {"workload": wname, "desc": info["desc"], "kv_tokens": alg["kv_tokens"],
                    "num_seqs": w.num_seqs, "total_q": w.total_q, "block_size": w.block_size,
                    "head_dim": w.head_dim, "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
+                   "kv_dtype": {"i8": "int8", "bf16": "bf16", "f32": "f32"}[w.dtype],
                    "mall_flush": args.flush, "hip_graph": bool(args.graph)},
         "kv_tokens_per_s": alg["kv_tokens"] / (ms * 1e-3),
         "step_ms_p10_p50_p90": [float(np.percentile(step_ms, p)) for p in (10, 50, 90)],

@@ -199,8 +199,14 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, const Item& it, int 
     }
   };
 
+  // int8: a ring of four chunks, three in flight while one is computed (a chunk is half the
+  // bytes, and the wave runs alone on its SIMD, so it needs more chunks in flight to keep as
+  // many bytes coming); the ring is filled after the Q loads, so that waiting for Q never waits
+  // for the ring.  bf16: two buffers, chunk i+1 in flight while chunk i is computed (a ring
+  // measured slower there).
+  constexpr bool RING = I8;
   Chunk<D, I8> bufA, bufB;
-  if (nch) load_chunk(bufA, 0);
+  if (!RING && nch) load_chunk(bufA, 0);
 
   // Q^T as the B operand: lane (n, g) holds row n of N-tile nt, dims 32*kk + 8*g .. +8 (int8
   // pools: dims 16*(4*(kk/2) + g) + 8*(kk%2) .. +8, the order of the K chunks it meets).
@@ -244,6 +250,7 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, const Item& it, int 
       return i8x8_to_bf16(ch.v[0][mt >> 2][mt & 3], ch.v[1][mt >> 2][mt & 3]);
     };
     bf16x8 va8[NT > 1 ? MT : 1];
+    bf16x8 ka8[NT > 1 ? 2 : 1][NT > 1 ? KK : 1];
     if constexpr (I8) {
 #pragma unroll
       for (int h = 0; h < 2; ++h)
@@ -253,6 +260,13 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, const Item& it, int 
       if constexpr (NT > 1) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) va8[mt] = v_i8(mt);
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int kk = 0; kk < KK; ++kk) {
+            const u32x4 w = ch.k[h][kk >> 1];
+            ka8[h][kk] = (kk & 1) ? i8x8_to_bf16(w[2], w[3]) : i8x8_to_bf16(w[0], w[1]);
+          }
       }
     } else if (c0 + 32 > we) {
       // Last chunk: slots at or past `we` may hold anything (NaN included); zero their V so
@@ -276,7 +290,9 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, const Item& it, int 
         floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < KK; ++kk) {
-          if constexpr (I8) {
+          if constexpr (I8 && NT > 1) {
+            acc = mfma16(ka8[h][kk], qb[nt][kk], acc);
+          } else if constexpr (I8) {
             const u32x4 w = ch.k[h][kk >> 1];
             const bf16x8 ka = (kk & 1) ? i8x8_to_bf16(w[2], w[3]) : i8x8_to_bf16(w[0], w[1]);
             acc = mfma16(ka, qb[nt][kk], acc);
@@ -335,22 +351,48 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, const Item& it, int 
     }
   };
 
-  // Double-buffered walk: the loads of chunk i+1 are issued before chunk i is computed.  The
-  // last one or two chunks are peeled off, so that no load is left in flight after the walk
-  // (the registers it would land in are reused right after).
-  int ci = 0;
-  for (; ci + 2 < nch; ci += 2) {
-    load_chunk(bufB, ci + 1);
-    compute(bufA, ci);
-    load_chunk(bufA, ci + 2);
-    compute(bufB, ci + 1);
-  }
-  if (ci + 1 < nch) {
-    load_chunk(bufB, ci + 1);
-    compute(bufA, ci);
-    compute(bufB, ci + 1);
-  } else if (ci < nch) {
-    compute(bufA, ci);
+  if constexpr (RING) {
+    // Ring of four.  Loads past the last chunk re-read the item's last tile (clamped in
+    // tile_off; cache hits) and are never computed, so every load is unconditional and the
+    // waits before each compute are static.
+    if (nch) {
+      Chunk<D, I8> bufC, bufD;
+      load_chunk(bufA, 0);
+      load_chunk(bufB, 1);
+      load_chunk(bufC, 2);
+      for (int ci = 0;; ci += 4) {
+        load_chunk(bufD, ci + 3);
+        compute(bufA, ci);
+        if (ci + 1 >= nch) break;
+        load_chunk(bufA, ci + 4);
+        compute(bufB, ci + 1);
+        if (ci + 2 >= nch) break;
+        load_chunk(bufB, ci + 5);
+        compute(bufC, ci + 2);
+        if (ci + 3 >= nch) break;
+        load_chunk(bufC, ci + 6);
+        compute(bufD, ci + 3);
+        if (ci + 4 >= nch) break;
+      }
+    }
+  } else {
+    // Double-buffered walk: the loads of chunk i+1 are issued before chunk i is computed.  The
+    // last one or two chunks are peeled off, so that no load is left in flight after the walk
+    // (the registers it would land in are reused right after).
+    int ci = 0;
+    for (; ci + 2 < nch; ci += 2) {
+      load_chunk(bufB, ci + 1);
+      compute(bufA, ci);
+      load_chunk(bufA, ci + 2);
+      compute(bufB, ci + 1);
+    }
+    if (ci + 1 < nch) {
+      load_chunk(bufB, ci + 1);
+      compute(bufA, ci);
+      compute(bufB, ci + 1);
+    } else if (ci < nch) {
+      compute(bufA, ci);
+    }
   }
 
   // Adds to a row's output index (q_start + i) * Hq + head to give its partial row index
