@@ -313,10 +313,14 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, const Item& it, int 
         cmax = fmaxf(cmax, sv[j]);
       }
       cmax = xrow_max(cmax);
-      const float m_new = fmaxf(m_run[nt], cmax);
-      const bool none = (m_new == -INFINITY);
-      const float alpha = none ? 1.f : fast_exp2((m_run[nt] - m_new) * c);
-      const float msub = none ? 0.f : m_new * c;
+      // Lazy rescaling: the row's reference max moves only when the chunk's max exceeds it by
+      // more than 8 in exp2 units (so p <= 2^8), and o and l are rescaled only in a chunk where
+      // some row's reference moved; otherwise alpha = 1 and the rescale is skipped.
+      const bool grow = (cmax - m_run[nt]) * c > 8.f;  // also true for the first finite max
+      const float m_new = grow ? cmax : m_run[nt];
+      const float msub = m_new == -INFINITY ? 0.f : m_new * c;
+      const bool rescale = __builtin_amdgcn_ballot_w64(grow) != 0;  // wave-uniform
+      const float alpha = grow ? fast_exp2((m_run[nt] - m_new) * c) : 1.f;
       uint32_t pk[4];
       float psum = 0.f;
 #pragma unroll
@@ -333,8 +337,13 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, const Item& it, int 
           pk[j >> 1] = pack_exact_bf16(p0, p1);
         }
       }
-      l_run[nt] = l_run[nt] * alpha + psum;
       m_run[nt] = m_new;
+      if (rescale) {
+        l_run[nt] *= alpha;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) o[nt][mt] *= alpha;
+      }
+      l_run[nt] += psum;
       const bf16x8 pb = __builtin_bit_cast(bf16x8, u32x4{pk[0], pk[1], pk[2], pk[3]});
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
@@ -346,7 +355,7 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, const Item& it, int 
           va = __builtin_bit_cast(
               bf16x8, u32x4{ch.v[0][mt][0], ch.v[0][mt][1], ch.v[1][mt][0], ch.v[1][mt][1]});
         }
-        o[nt][mt] = mfma16(va, pb, o[nt][mt] * alpha);
+        o[nt][mt] = mfma16(va, pb, o[nt][mt]);
       }
     }
   };
