@@ -8,11 +8,13 @@ package imports nothing from the library or its Python binding.
   softmax attention per q-head; pool append (scatter) and block copy as plain integer indexing.
 * ``oracle.quant``     - the int8 pool: per-(token, KV head) absmax quantisation in fp32, the int8
   storage layout, and attention on the dequantized values (float64, via ``oracle.attention``).
+* ``oracle.sparse``    - sink + window sparse attention: each row past a length threshold reads
+  only the sequence's first positions and its latest ones (a key mask on ``oracle.attention``).
 * ``oracle.brute``     - pure-Python brute force for tiny inputs (``math.fsum``, log-sum-exp
   normalisation, element-wise scatter by the storage formula, a quantiser rounding each
-  operation to float32) used to pin ``oracle.attention`` and ``oracle.quant``.
+  operation to float32) used to pin ``oracle.attention``, ``oracle.quant`` and ``oracle.sparse``.
 
 Every function is pinned by a ``-m "not gpu"`` test against something other than itself
 (brute force, closed forms, invariants).  Nothing here is "parity unpinned".
 """
-from . import attention, brute, quant  # noqa: F401
+from . import attention, brute, quant, sparse  # noqa: F401

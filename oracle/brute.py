@@ -131,3 +131,36 @@ def scatter_i8(k_codes, v_codes, k_scales, v_scales, tables, *, num_blocks, num_
                     kf[k_offset_i8(b, h, t, d, **geo)] = k_codes[s][j][h][d]
                     vf[v_offset_i8(b, h, t, d, **geo)] = v_codes[s][j][h][d]
     return kf, vf, ksf, vsf
+
+
+def sparse_keys(p: int, *, sink: int, window: int, min_len: int):
+    """Key positions a row at absolute position p reads under sink + window sparsity, listed
+    from the two ranges (the first `sink` positions, the `window` latest up to p) once p + 1
+    reaches min_len; all of 0 .. p before that."""
+    if p + 1 < min_len:
+        return list(range(p + 1))
+    head = range(min(sink, p + 1))
+    tail = range(max(p + 1 - window, 0), p + 1)
+    return sorted(set(head) | set(tail))
+
+
+def attention_keys(q, k, v, scale, keys_of):
+    """As ``attention``, but row i (absolute position p) reads only the keys keys_of(p)."""
+    t_len, l_len = len(q), len(k)
+    hq, hkv = len(q[0]), len(k[0])
+    group = hq // hkv
+    dim = len(q[0][0])
+    out = []
+    for i in range(t_len):
+        p = l_len - t_len + i
+        keys = keys_of(p)
+        row = []
+        for h in range(hq):
+            g = h // group
+            scores = [scale * math.fsum(q[i][h][d] * k[j][g][d] for d in range(dim)) for j in keys]
+            m = max(scores)
+            lse = m + math.log(math.fsum(math.exp(sj - m) for sj in scores))
+            wts = [math.exp(sj - lse) for sj in scores]
+            row.append([math.fsum(w * v[j][g][d] for w, j in zip(wts, keys)) for d in range(dim)])
+        out.append(row)
+    return out
