@@ -189,6 +189,28 @@ KVPOOL_API int kvattn_forward(kvpool_t *pool, int32_t layer, const void *q, void
                               const int32_t *q_lens_host, void *workspace,
                               size_t workspace_bytes, void *stream);
 
+/* kvattn_forward with sink + window sparsity: a query row at absolute position p (= ctx_len -
+ * q_len + i) with p + 1 >= min_ctx_len reads only the keys j <= p with j < sink_tokens or
+ * j >= p + 1 - window_tokens; rows below the threshold read all their keys.  The pages' decode
+ * mode attends only to a sequence's first KV block and its last 4096 tokens once it holds 16384
+ * (sparkinfer server README, "Env", SPARKINFER_SPARSE_GQA6): sink_tokens = the pool's
+ * block_size, window_tokens = 4096, min_ctx_len = 16384.  The skipped keys are not read from
+ * HBM.  Arguments, workspace (kvattn_workspace_size with the same bounds is enough) and the
+ * batch-invariance guarantee are those of kvattn_forward.
+ * Errors: KV_EINVAL for sink_tokens < 0, window_tokens < 1 or min_ctx_len < 0;
+ * KV_EUNSUPPORTED for an fp32 pool, or when a sequence may be longer than the split-K path
+ * takes (q_len * num_q_heads / num_kv_heads > 128; judged from q_lens_host when given, else
+ * from max_q_len): sparse attention serves decode and verification rows only. */
+KVPOOL_API int kvattn_forward_sparse(kvpool_t *pool, int32_t layer, const void *q, void *out,
+                                     int32_t num_q_heads, float scale,
+                                     const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                     const int32_t *ctx_lens, const int32_t *q_lens,
+                                     int32_t num_seqs, int32_t total_q, int32_t max_ctx_len,
+                                     int32_t max_q_len, int32_t sink_tokens,
+                                     int32_t window_tokens, int32_t min_ctx_len,
+                                     const int32_t *q_lens_host, void *workspace,
+                                     size_t workspace_bytes, void *stream);
+
 /* Opt-in per-kernel timing for measurement.  With enable != 0, every kernel launch made by this
  * library (any pool, any thread) is bracketed by a pair of HIP events recorded on the launch's
  * stream, and earlier records are dropped; with enable == 0 recording stops (records are kept).

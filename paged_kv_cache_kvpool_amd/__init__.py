@@ -9,7 +9,8 @@ first use, importing torch); ``paged_kv_cache_kvpool_amd.workloads`` draws seede
 _BINDING_NAMES = {
     "kvpool_storage_bytes", "kvpool_scale_bytes", "kvpool_create", "kvpool_create_int8",
     "kvpool_destroy", "kvpool_append",
-    "kvpool_copy_blocks", "kvattn_workspace_size", "kvattn_forward", "kvpool_last_error",
+    "kvpool_copy_blocks", "kvattn_workspace_size", "kvattn_forward", "kvattn_forward_sparse",
+    "kvpool_last_error",
     "kvpool_profile", "kvpool_profile_kernel", "kernel_times",
     "PagedKVPool", "KVPoolError", "KV_F32", "KV_BF16", "KV_I8", "lib",
 }

@@ -41,6 +41,8 @@ SIGNATURES = {
     "kvattn_workspace_size": (_i32, [_vp, _i32, _i32, _i32, _i32, _i32, _vp, ctypes.POINTER(_sz)]),
     "kvattn_forward": (_i32, [_vp, _i32, _vp, _vp, _i32, _f32, _vp, _i32, _vp, _vp, _i32, _i32,
                               _i32, _i32, _vp, _vp, _sz, _vp]),
+    "kvattn_forward_sparse": (_i32, [_vp, _i32, _vp, _vp, _i32, _f32, _vp, _i32, _vp, _vp, _i32,
+                                     _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _sz, _vp]),
     "kvpool_last_error": (ctypes.c_char_p, []),
     "kvpool_profile": (_i32, [_i32]),
     "kvpool_profile_kernel": (_i32, [_i32, ctypes.POINTER(ctypes.c_char_p),
@@ -198,6 +200,20 @@ def kvattn_forward(handle, layer, q, out, num_q_heads, scale, block_tables, max_
     del arr
 
 
+def kvattn_forward_sparse(handle, layer, q, out, num_q_heads, scale, block_tables,
+                          max_blocks_per_seq, ctx_lens, q_lens, num_seqs, total_q, max_ctx_len,
+                          max_q_len, sink_tokens, window_tokens, min_ctx_len, workspace,
+                          workspace_bytes, stream=None, q_lens_host=None) -> None:
+    arr, addr = _host_i32(q_lens_host)
+    _check(lib().kvattn_forward_sparse(handle, layer, _ptr(q), _ptr(out), num_q_heads,
+                                       float(scale), _ptr(block_tables), max_blocks_per_seq,
+                                       _ptr(ctx_lens), _ptr(q_lens), num_seqs, total_q,
+                                       max_ctx_len, max_q_len, sink_tokens, window_tokens,
+                                       min_ctx_len, addr, _ptr(workspace), workspace_bytes,
+                                       _stream(stream)))
+    del arr
+
+
 # ---------------------------------------------------------------------------------------------
 # Convenience wrapper: owns torch storage for one pool and sizes the workspace.
 # ---------------------------------------------------------------------------------------------
@@ -292,4 +308,25 @@ class PagedKVPool:
         kvattn_forward(self.handle, layer, q, out, hq, scale, block_tables, block_tables.shape[1],
                        ctx_lens, q_lens, ctx_lens.shape[0], total_q, max_ctx_len, max_q_len,
                        ws, need, stream, q_lens_host)
+        return out
+
+    def forward_sparse(self, layer, q, block_tables, ctx_lens, q_lens, scale=None,
+                       sink_tokens=None, window_tokens=4096, min_ctx_len=16384,
+                       max_ctx_len=None, max_q_len=None, out=None, stream=None,
+                       q_lens_host=None):
+        """Sink + window sparse attention (decode and verification rows): a row at position p
+        with p + 1 >= min_ctx_len reads only keys j < sink_tokens (default: one block) or
+        j >= p + 1 - window_tokens."""
+        total_q, hq, d = q.shape
+        scale = 1.0 / math.sqrt(d) if scale is None else scale
+        sink_tokens = self.block_size if sink_tokens is None else sink_tokens
+        max_ctx_len = int(ctx_lens.max().item()) if max_ctx_len is None else max_ctx_len
+        max_q_len = int(q_lens.max().item()) if max_q_len is None else max_q_len
+        out = torch.empty_like(q) if out is None else out
+        ws, need = self.workspace(hq, ctx_lens.shape[0], total_q, max_ctx_len, max_q_len,
+                                  q_lens_host)
+        kvattn_forward_sparse(self.handle, layer, q, out, hq, scale, block_tables,
+                              block_tables.shape[1], ctx_lens, q_lens, ctx_lens.shape[0], total_q,
+                              max_ctx_len, max_q_len, sink_tokens, window_tokens, min_ctx_len,
+                              ws, need, stream, q_lens_host)
         return out

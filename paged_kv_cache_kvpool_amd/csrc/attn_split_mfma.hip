@@ -103,32 +103,41 @@ struct Item {
   int q_start;  // index of the sequence's first query token in q / out
   int p_start;  // its first row in the partial buffers
   int kb, ke;   // the item's keys [kb, ke): its split, cut at its last row's position + 1
+                // (virtual key positions: see seq_vlayout)
   int split;    // keys per split of this sequence
+  int vs1, vshift;  // the sequence's sparse key layout (identity when dense)
+  int wlo_max;      // sparse rows see keys > p - window: the largest such p - window of the
+                    // item's rows, or -1 when no row of the item is sparse
 };
 
 // Key range of an item; false if no row of the item sees a key of its split.
 template <int NT>
 __device__ __forceinline__ bool item_keys(const AttnArgs& a, Item& it) {
+  it.vs1 = it.vshift = 0;
+  it.wlo_max = -1;
   if (it.T > a.split_q_max) return false;  // a prefill-class sequence
   const int rows = it.T * a.group;
   const int r0 = it.rt * 16 * NT;
   if (r0 >= rows) return false;
   const int p_last = it.L - it.T + (min(r0 + 16 * NT, rows) - 1) / a.group;
-  it.split = seq_split(a, it.L);
+  int Lv;
+  seq_vlayout(a, it.L, it.T, Lv, it.vs1, it.vshift);
+  it.wlo_max = (a.sparse_window > 0 && p_last + 1 >= a.sparse_min) ? p_last - a.sparse_window : -1;
+  it.split = seq_split(a, Lv);
   it.kb = it.sp * it.split;
-  it.ke = min(min(it.L, p_last + 1), it.kb + it.split);
+  it.ke = min(min(Lv, virt_key(p_last, it.vs1, it.vshift) + 1), it.kb + it.split);
   return it.kb < it.ke;
 }
 
 // Block id of tile (wb/16 + base + lane) of sequence s, the tile index clamped into the wave's
 // ntile tiles and the position into the item's keys (ke >= 1), so the read is always in the
-// sequence's own table row.
+// sequence's own table row.  wb, ke: virtual key positions of the layout (vs1, vshift).
 __device__ __forceinline__ int tile_block_id(const AttnArgs& a, int s, int wb, int ntile, int ke,
-                                             int base) {
+                                             int base, int vs1, int vshift) {
   const int lane = threadIdx.x & (WAVE - 1);
   const int32_t* tbl = a.block_tables + (size_t)s * a.max_blocks_per_seq;
   const int ti = min(base + lane, max(ntile - 1, 0));
-  return tbl[min(((wb >> 4) + ti) << 4, ke - 1) >> a.block_shift];
+  return tbl[real_key(min(((wb >> 4) + ti) << 4, ke - 1), vs1, vshift) >> a.block_shift];
 }
 
 // Reduces the keys [wb, we) of item `it` for one wave.  ids0/ids1: lane i holds the block id of
@@ -160,12 +169,12 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, const Item& it, int 
     ti = min(ti, ntile - 1);  // past the end: re-read the last tile (a cache hit; masked out)
     if (RELOAD && ti - tb >= 128) {
       tb = ti & ~127;
-      ids0 = tile_block_id(a, s, wb, ntile, it.ke, tb);
-      ids1 = tile_block_id(a, s, wb, ntile, it.ke, tb + 64);
+      ids0 = tile_block_id(a, s, wb, ntile, it.ke, tb, it.vs1, it.vshift);
+      ids1 = tile_block_id(a, s, wb, ntile, it.ke, tb + 64, it.vs1, it.vshift);
     }
     const int r = ti - tb;
     const int blk = r < 64 ? __builtin_amdgcn_readlane(ids0, r) : __builtin_amdgcn_readlane(ids1, r - 64);
-    const int sub = (((tile0 + ti) << 4) & bmask) >> 4;
+    const int sub = (real_key((tile0 + ti) << 4, it.vs1, it.vshift) & bmask) >> 4;
     return block_tile_offset(blk, sub, kvh, a.block_shift, a.num_blocks, a.num_kv_heads, D);
   };
   auto load_chunk = [&](Chunk<D, I8>& c, int ci) {
@@ -212,7 +221,9 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, const Item& it, int 
   // pools: dims 16*(4*(kk/2) + g) + 8*(kk%2) .. +8, the order of the K chunks it meets).
   const int Hq = a.num_q_heads;
   bf16x8 qb[NT][KK];
-  int prow[NT];
+  int prow[NT];   // the row's real key position (-1: padding row)
+  int vprow[NT];  // its virtual position in the sequence's key layout
+  int wlo[NT];    // sparse row: keys <= wlo (and >= the sink) are not seen; else -1
   size_t rh[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
@@ -221,6 +232,9 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, const Item& it, int 
     const int grow = q_start + i;
     const bool valid = r < rows && grow < a.total_q;
     prow[nt] = valid ? L - T + i : -1;
+    vprow[nt] = virt_key(prow[nt], it.vs1, it.vshift);
+    wlo[nt] = (valid && a.sparse_window > 0 && prow[nt] + 1 >= a.sparse_min)
+                  ? prow[nt] - a.sparse_window : -1;
     rh[nt] = valid ? (size_t)grow * Hq + kvh * G + r % G : 0;
     const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + rh[nt] * D;
 #pragma unroll
@@ -243,7 +257,10 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, const Item& it, int 
   const float c = a.scale_log2;
 
   auto compute = [&](Chunk<D, I8>& ch, int ci) {
-    const int c0 = wb + 32 * ci;
+    const int c0 = wb + 32 * ci;  // virtual position of the chunk's first key
+    const int rc0 = real_key(c0, it.vs1, it.vshift);
+    // the sparse mask can remove a key of this chunk (wave-uniform)
+    const bool smask = rc0 <= it.wlo_max && rc0 + 32 > a.sparse_sink;
     // int8: the V scales of slots at or past `we` (never written: may hold anything) zeroed so
     // that p * scale stays 0; with two N-tiles the V^T operands are converted once for both
     auto v_i8 = [&](int mt) {
@@ -305,13 +322,21 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, const Item& it, int 
       }
       // This lane now holds row n's scores for keys c0 + 16*h + 4*g + i (j = 4*h + i).
       float sv[8];
-      float cmax = -INFINITY;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const int key = c0 + 16 * (j >> 2) + 4 * g + (j & 3);
-        sv[j] = (key < we && key <= prow[nt]) ? sc[j >> 2][j & 3] : -INFINITY;
-        cmax = fmaxf(cmax, sv[j]);
+        const int off = 16 * (j >> 2) + 4 * g + (j & 3);
+        sv[j] = (c0 + off < we && rc0 + off <= prow[nt]) ? sc[j >> 2][j & 3] : -INFINITY;
       }
+      if (smask) {  // sink + window: keys past the sink and at or before p - window are unseen
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int rk = rc0 + 16 * (j >> 2) + 4 * g + (j & 3);
+          if (rk >= a.sparse_sink && rk <= wlo[nt]) sv[j] = -INFINITY;
+        }
+      }
+      float cmax = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) cmax = fmaxf(cmax, sv[j]);
       cmax = xrow_max(cmax);
       // Lazy rescaling: the row's reference max moves only when the chunk's max exceeds it by
       // more than 8 in exp2 units (so p <= 2^8), and o and l are rescaled only in a chunk where
@@ -412,8 +437,8 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, const Item& it, int 
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
       const float lt = xrow_sum(l_run[nt]);
-      if (prow[nt] < kb) continue;  // padding row, or a row that sees no key of this split
-      const bool final_here = prow[nt] < split;
+      if (vprow[nt] < kb) continue;  // padding row, or a row that sees no key of this split
+      const bool final_here = vprow[nt] < split;
       if (final_here) {
         const float inv = 1.f / lt;
         uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + rh[nt] * D;
@@ -466,8 +491,8 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, const Item& it, int 
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) s_o[wave][mt][lane] = o[nt][mt] * myscale;
       __syncthreads();
-      const bool row_ok = prow[nt] >= kb;  // a real row that sees a key of this split
-      const bool final_here = prow[nt] < split;
+      const bool row_ok = vprow[nt] >= kb;  // a real row that sees a key of this split
+      const bool final_here = vprow[nt] < split;
       if (row_ok) {
         if (final_here) {
           const float inv = 1.f / Lsum;
@@ -507,8 +532,10 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, const Item& it, int 
 template <int NT>
 __device__ __forceinline__ int seq_items(const AttnArgs& a, int L, int T) {
   if (T <= 0 || T > a.split_q_max) return 0;  // no rows, or a prefill-class sequence
-  const int split = seq_split(a, L);
-  const int ns = min(L / split + (L % split != 0), a.max_splits);
+  int Lv, vs1, vshift;
+  seq_vlayout(a, L, T, Lv, vs1, vshift);
+  const int split = seq_split(a, Lv);
+  const int ns = min(Lv / split + (Lv % split != 0), a.max_splits);
   const int rts = min((T * a.group + 16 * NT - 1) / (16 * NT), a.row_tiles);
   return ns * a.num_kv_heads * rts;
 }
@@ -606,8 +633,8 @@ void attn_split_persist_kernel(AttnArgs a) {
   int ids0 = 0, ids1 = 0;
   if (have) {
     const int nt = (cur.ke - cur.kb + 15) >> 4;
-    ids0 = tile_block_id(a, cur.s, cur.kb, nt, cur.ke, 0);
-    ids1 = tile_block_id(a, cur.s, cur.kb, nt, cur.ke, 64);
+    ids0 = tile_block_id(a, cur.s, cur.kb, nt, cur.ke, 0, cur.vs1, cur.vshift);
+    ids1 = tile_block_id(a, cur.s, cur.kb, nt, cur.ke, 64, cur.vs1, cur.vshift);
   }
   while (have) {
     t += W;
@@ -619,9 +646,11 @@ void attn_split_persist_kernel(AttnArgs a) {
     const int ps = nhave ? nxt.s : cur.s;
     const int pb = nhave ? nxt.kb : cur.kb;
     const int pe = nhave ? nxt.ke : cur.ke;
+    const int pv1 = nhave ? nxt.vs1 : cur.vs1;
+    const int pvs = nhave ? nxt.vshift : cur.vshift;
     const int pt = (pe - pb + 15) >> 4;
-    const int nid0 = tile_block_id(a, ps, pb, pt, pe, 0);
-    const int nid1 = tile_block_id(a, ps, pb, pt, pe, 64);
+    const int nid0 = tile_block_id(a, ps, pb, pt, pe, 0, pv1, pvs);
+    const int nid1 = tile_block_id(a, ps, pb, pt, pe, 64, pv1, pvs);
     if (cur_keys) run_item<D, NT, false, 1, I8>(a, cur, 0, cur.kb, cur.ke, ids0, ids1);
     if (!nhave) break;
     cur = nxt;
@@ -649,8 +678,8 @@ __global__ __launch_bounds__(256) void attn_split_mfma_kernel(AttnArgs a) {
   const int wb = it.kb + wave * span;
   const int we = min(it.ke, wb + span);
   const int ntile = wb < we ? (we - wb + 15) >> 4 : 0;
-  const int ids0 = tile_block_id(a, it.s, wb, ntile, it.ke, 0);
-  const int ids1 = tile_block_id(a, it.s, wb, ntile, it.ke, 64);
+  const int ids0 = tile_block_id(a, it.s, wb, ntile, it.ke, 0, it.vs1, it.vshift);
+  const int ids1 = tile_block_id(a, it.s, wb, ntile, it.ke, 64, it.vs1, it.vshift);
   seq_starts(a, it.s, it.q_start, it.p_start);
   // vmcnt(0) (encoding: vmcnt 0, expcnt 7, lgkmcnt 15), so the compiler knows the block ids
   // have arrived and never waits for them inside the chunk loop.

@@ -166,6 +166,9 @@ struct AttnArgs {
   int32_t split_q_max;      // sequences with q_len <= split_q_max take the split-K path
   int32_t part_rows;        // rows of the partial buffers (query tokens of the split-K path)
   int32_t pf_rblk;          // prefill kernel: 32-row blocks per workgroup
+  // Sink + window sparsity (split-K path; off when sparse_window == 0): a query row at position
+  // p with p + 1 >= sparse_min reads only keys j < sparse_sink or j > p - sparse_window.
+  int32_t sparse_sink, sparse_window, sparse_min;
   float scale_log2;         // softmax scale * log2(e)
 };
 
@@ -178,6 +181,37 @@ __device__ __forceinline__ int seq_split(const AttnArgs& a, int L) {
   if (a.split_tokens > 0) return a.split_tokens;
   const int per = (L >> 7) + ((L & 127) != 0);  // ceil(L / 128) without overflow
   return min(max((per + 31) & ~31, 256), 2048);
+}
+
+// Key layout of a split-K sequence (L keys, T query rows) under sink + window sparsity.  When
+// every row of the sequence is past the threshold (L - T + 1 >= sparse_min), no row reads the
+// keys between the sink and the first row's window, so the walk skips them: virtual key
+// positions [0, vs1) are real positions [0, vs1) and virtual v >= vs1 is real v + vshift, with
+// vs1 = the sink rounded up to 32 keys and vs1 + vshift = the first row's window start rounded
+// down to 32 keys (so a 32-key chunk never straddles the gap).  Keys that the walk still reads
+// but a row must not see are masked by position.  Lv: virtual keys.  Without sparsity, or when
+// there is no gap, the layout is the identity (vs1 = vshift = 0, Lv = L).
+__device__ __forceinline__ void seq_vlayout(const AttnArgs& a, int L, int T, int& Lv, int& vs1,
+                                            int& vshift) {
+  Lv = L;
+  vs1 = 0;
+  vshift = 0;
+  if (a.sparse_window > 0 && T > 0 && L - T + 1 >= a.sparse_min) {
+    const int s1 = (min(a.sparse_sink, L) + 31) & ~31;
+    const int w0 = max(0, L - T + 1 - a.sparse_window) & ~31;
+    if (w0 > s1) {
+      vs1 = s1;
+      vshift = w0 - s1;
+      Lv = L - vshift;
+    }
+  }
+}
+// Real position of virtual key v, and virtual position of a real key that the walk reads.
+__device__ __forceinline__ int real_key(int v, int vs1, int vshift) {
+  return v >= vs1 ? v + vshift : v;
+}
+__device__ __forceinline__ int virt_key(int p, int vs1, int vshift) {
+  return p >= vs1 + vshift ? p - vshift : p;
 }
 
 // Clamped per-sequence lengths (bad metadata must never index out of bounds).

@@ -528,12 +528,21 @@ int kvattn_workspace_size(const kvpool_t* pool, int32_t num_q_heads, int32_t num
   return ok();
 }
 
-int kvattn_forward(kvpool_t* pool, int32_t layer, const void* q, void* out, int32_t num_q_heads,
-                   float scale, const int32_t* block_tables, int32_t max_blocks_per_seq,
-                   const int32_t* ctx_lens, const int32_t* q_lens, int32_t num_seqs,
-                   int32_t total_q, int32_t max_ctx_len, int32_t max_q_len,
-                   const int32_t* q_lens_host, void* workspace, size_t workspace_bytes,
-                   void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Sink + window sparsity of a call (window == 0: dense).
+struct Sparse {
+  int sink, window, min_len;
+};
+
+int forward_impl(kvpool_t* pool, int32_t layer, const void* q, void* out, int32_t num_q_heads,
+                 float scale, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                 const int32_t* ctx_lens, const int32_t* q_lens, int32_t num_seqs,
+                 int32_t total_q, int32_t max_ctx_len, int32_t max_q_len, Sparse sp,
+                 const int32_t* q_lens_host, void* workspace, size_t workspace_bytes,
+                 void* stream) {
   if (!pool) return fail(KV_EINVAL, "pool is NULL");
   if (layer < 0 || layer >= pool->num_layers) return fail(KV_EINVAL, "layer %d out of range", layer);
   if (num_q_heads <= 0 || num_q_heads % pool->num_kv_heads)
@@ -556,6 +565,17 @@ int kvattn_forward(kvpool_t* pool, int32_t layer, const void* q, void* out, int3
   if (current_device_matches(pool) != hipSuccess)
     return fail(KV_EINVAL, "current HIP device is not the pool's device %d", pool->device);
   const Plan pl = make_plan(pool, num_q_heads, num_seqs, total_q, max_ctx_len, max_q_len, q_lens_host);
+  if (sp.window > 0) {
+    // Sparse attention is a decode / verification mode: the split-K kernel serves it.
+    if (pool->dtype == KV_F32)
+      return fail(KV_EUNSUPPORTED, "sink + window sparse attention needs a bf16 or int8 pool");
+    if (pl.prefill)
+      return fail(KV_EUNSUPPORTED,
+                  "sink + window sparse attention serves decode and verification rows only "
+                  "(q_len <= %d here); %s", pl.split_q_max,
+                  q_lens_host ? "a sequence has a longer q_len"
+                              : "max_q_len allows longer ones (pass q_lens_host or a smaller max_q_len)");
+  }
   if (pl.max_splits > 65535)
     return fail(KV_ERANGE, "%d splits per sequence exceed the launch grid (65535)", pl.max_splits);
   if ((long long)total_q * num_q_heads >= (1ll << 31))
@@ -610,14 +630,17 @@ int kvattn_forward(kvpool_t* pool, int32_t layer, const void* q, void* out, int3
   a.split_q_max = pl.split_q_max;
   a.part_rows = pl.part_rows;
   a.pf_rblk = pl.rblk;
+  a.sparse_sink = sp.sink;
+  a.sparse_window = sp.window;
+  a.sparse_min = sp.min_len;
   a.scale_log2 = scale * kvp::LOG2E;
 
   // q / out element bytes (bf16 for int8 pools)
   const int eb = pool->dtype == KV_F32 ? 4 : 2;
   const bool i8 = pool->dtype == KV_I8;
   hipError_t e = hipSuccess;
-  if (pool->dtype == KV_F32 ||
-      (pool->dtype == KV_BF16 && !pl.prefill && max_q_len == 1 && env_flag("KVATTN_DECODE_VEC"))) {
+  if (pool->dtype == KV_F32 || (pool->dtype == KV_BF16 && sp.window == 0 && !pl.prefill &&
+                                 max_q_len == 1 && env_flag("KVATTN_DECODE_VEC"))) {
     // One launch for every sequence: split-K sequences in splits, longer ones in one pass.
     // Rows per wave: the template instance just large enough (1, 2, 4, 5 or 8).
     const int rows = max_q_len * G;
@@ -668,6 +691,38 @@ int kvattn_forward(kvpool_t* pool, int32_t layer, const void* q, void* out, int3
     if (e != hipSuccess) return fail(KV_EDEVICE, "reduce launch: %s", hipGetErrorString(e));
   }
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int kvattn_forward(kvpool_t* pool, int32_t layer, const void* q, void* out, int32_t num_q_heads,
+                   float scale, const int32_t* block_tables, int32_t max_blocks_per_seq,
+                   const int32_t* ctx_lens, const int32_t* q_lens, int32_t num_seqs,
+                   int32_t total_q, int32_t max_ctx_len, int32_t max_q_len,
+                   const int32_t* q_lens_host, void* workspace, size_t workspace_bytes,
+                   void* stream) {
+  return forward_impl(pool, layer, q, out, num_q_heads, scale, block_tables, max_blocks_per_seq,
+                      ctx_lens, q_lens, num_seqs, total_q, max_ctx_len, max_q_len, Sparse{0, 0, 0},
+                      q_lens_host, workspace, workspace_bytes, stream);
+}
+
+int kvattn_forward_sparse(kvpool_t* pool, int32_t layer, const void* q, void* out,
+                          int32_t num_q_heads, float scale, const int32_t* block_tables,
+                          int32_t max_blocks_per_seq, const int32_t* ctx_lens,
+                          const int32_t* q_lens, int32_t num_seqs, int32_t total_q,
+                          int32_t max_ctx_len, int32_t max_q_len, int32_t sink_tokens,
+                          int32_t window_tokens, int32_t min_ctx_len,
+                          const int32_t* q_lens_host, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  if (sink_tokens < 0 || window_tokens < 1 || min_ctx_len < 0)
+    return fail(KV_EINVAL, "sparse attention needs sink_tokens >= 0, window_tokens >= 1, "
+                "min_ctx_len >= 0 (got %d, %d, %d)", sink_tokens, window_tokens, min_ctx_len);
+  return forward_impl(pool, layer, q, out, num_q_heads, scale, block_tables, max_blocks_per_seq,
+                      ctx_lens, q_lens, num_seqs, total_q, max_ctx_len, max_q_len,
+                      Sparse{sink_tokens, window_tokens, min_ctx_len}, q_lens_host, workspace,
+                      workspace_bytes, stream);
 }
 
 const char* kvpool_last_error(void) { return g_err.c_str(); }

@@ -7,6 +7,7 @@ import torch
 
 from oracle import attention as ora
 from oracle import quant as oq
+from oracle import sparse as osp
 from paged_kv_cache_kvpool_amd import binding as kb
 from paged_kv_cache_kvpool_amd import workloads as wl
 
@@ -108,39 +109,61 @@ class DeviceCase:
         v = to_numpy(self.pool.block_storage("v"), w.dtype)
         return k, v
 
-    def oracle(self, k_pool=None, v_pool=None, seqs=None, scales=None):
-        """Oracle output.  Pools default to the workload's own pre-append pool with the new rows
-        appended by the oracle (never the device's pool); an int8 pool also takes its scales
-        (K, V)."""
+    def oracle_pools(self, k_pool=None, v_pool=None, scales=None):
+        """Host pools the oracle reads: the workload's own pre-append pool (or the given one)
+        with the new rows appended by the oracle (never the device's pool).  Returns (K, V,
+        scales); scales is (K scales, V scales) for int8 pools, else None."""
         w = self.w
-        if w.dtype == wl.I8:
-            if k_pool is None:
-                if w.k_pool is None:
-                    raise ValueError("pool drawn on the device: pass the pre-append host pool")
-                k_pool, v_pool, scales = w.k_pool, w.v_pool, (w.k_scales, w.v_scales)
-            ks, vs = scales
-            if w.k_new is not None:
-                k_pool, v_pool, ks, vs = oq.append(k_pool, v_pool, ks, vs, w.layer, w.k_new, w.v_new,
-                                                   w.block_tables, w.ctx_lens, w.q_lens,
-                                                   num_kv_heads=w.num_kv_heads,
-                                                   block_size=w.block_size, head_dim=w.head_dim)
-            return oq.paged_attention(w.q, k_pool, v_pool, ks, vs, w.layer, w.block_tables,
-                                      w.ctx_lens, w.q_lens, scale=w.scale,
-                                      num_kv_heads=w.num_kv_heads, block_size=w.block_size,
-                                      head_dim=w.head_dim, seqs=seqs)
+        geo = dict(num_kv_heads=w.num_kv_heads, block_size=w.block_size, head_dim=w.head_dim)
         if k_pool is None:
             if w.k_pool is None:
                 raise ValueError("pool drawn on the device: pass the pre-append host pool")
             k_pool, v_pool = w.k_pool, w.v_pool
+            scales = (w.k_scales, w.v_scales) if w.dtype == wl.I8 else None
+        if w.dtype == wl.I8:
+            ks, vs = scales
+            if w.k_new is not None:
+                k_pool, v_pool, ks, vs = oq.append(k_pool, v_pool, ks, vs, w.layer, w.k_new,
+                                                   w.v_new, w.block_tables, w.ctx_lens, w.q_lens,
+                                                   **geo)
+            return k_pool, v_pool, (ks, vs)
         if w.k_new is not None:
             k_pool, v_pool = ora.append(k_pool, v_pool, w.layer, w.k_new, w.v_new, w.block_tables,
-                                        w.ctx_lens, w.q_lens, num_kv_heads=w.num_kv_heads,
-                                        block_size=w.block_size, head_dim=w.head_dim,
-                                        dtype=w.dtype)
+                                        w.ctx_lens, w.q_lens, dtype=w.dtype, **geo)
+        return k_pool, v_pool, None
+
+    def oracle(self, k_pool=None, v_pool=None, seqs=None, scales=None):
+        """Oracle output on the pools of ``oracle_pools``."""
+        w = self.w
+        k_pool, v_pool, scales = self.oracle_pools(k_pool, v_pool, scales)
+        geo = dict(num_kv_heads=w.num_kv_heads, block_size=w.block_size, head_dim=w.head_dim)
+        if w.dtype == wl.I8:
+            return oq.paged_attention(w.q, k_pool, v_pool, scales[0], scales[1], w.layer,
+                                      w.block_tables, w.ctx_lens, w.q_lens, scale=w.scale,
+                                      seqs=seqs, **geo)
         return ora.paged_attention(w.q, k_pool, v_pool, w.layer, w.block_tables, w.ctx_lens,
+                                   w.q_lens, scale=w.scale, dtype=w.dtype, seqs=seqs, **geo)
+
+    def oracle_sparse(self, sink, window, min_len, k_pool=None, v_pool=None, seqs=None,
+                      scales=None):
+        """Sink + window sparse oracle output on the pools of ``oracle_pools``."""
+        w = self.w
+        k_pool, v_pool, scales = self.oracle_pools(k_pool, v_pool, scales)
+        return osp.paged_attention(w.q, k_pool, v_pool, w.layer, w.block_tables, w.ctx_lens,
                                    w.q_lens, scale=w.scale, num_kv_heads=w.num_kv_heads,
                                    block_size=w.block_size, head_dim=w.head_dim, dtype=w.dtype,
+                                   sink=sink, window=window, min_len=min_len, scales=scales,
                                    seqs=seqs)
+
+    def forward_sparse(self, sink, window, min_len, q=None, out=None, mirror=False):
+        """Sparse attention through the library (kvattn_forward_sparse)."""
+        w = self.w
+        return self.pool.forward_sparse(w.layer, self.q if q is None else q, self.tables,
+                                        self.ctx, self.ql, scale=w.scale, sink_tokens=sink,
+                                        window_tokens=window, min_ctx_len=min_len,
+                                        max_ctx_len=int(w.ctx_lens.max()),
+                                        max_q_len=int(w.q_lens.max()), out=out,
+                                        q_lens_host=w.q_lens if mirror else None)
 
 
 def errors(gpu: np.ndarray, ref: np.ndarray):
