@@ -46,10 +46,16 @@ WORKLOADS = {
     "mixed_step": dict(kind="hbm", desc="one call: 32 decode seqs (ctx U[1024,8192]) + 1 verify (1+3 at 32768) + "
                                         "1 prefill chunk (512 over 4096 cached), 40/8 heads, D=128, bf16"),
 }
+WORKLOADS["sparse_decode"] = dict(
+    kind="hbm", desc="32 seqs x 1 token, ctx U[16384,65536], 32/8 heads, D=128, bf16, B=16; sink + "
+                     "window sparse (first 16 + last 4096 keys)")
+WORKLOADS["long_decode_sparse"] = dict(
+    kind="hbm", desc="2 seqs x 1 token at 262144 and 131072, 40/8 heads, D=128, bf16; sink + window "
+                     "sparse (first 16 + last 4096 keys)")
 # The same workloads on an int8 pool (codes + one fp32 scale per token and KV head; q, out and
 # appended rows bf16).
 for _n in ("batched_gqa_decode", "spec_verify_32k", "spec_verify_128k", "prefix_prefill",
-           "long_decode", "mixed_step"):
+           "long_decode", "mixed_step", "sparse_decode"):
     WORKLOADS[_n + "_int8"] = dict(kind=WORKLOADS[_n]["kind"],
                                    desc=WORKLOADS[_n]["desc"].replace("bf16", "int8 KV (bf16 q)"))
 
@@ -69,6 +75,12 @@ def make_workload(name):
             return wl.long_decode(**kw)
         if base == "mixed_step":
             return wl.mixed_step(**kw)
+        if base == "sparse_decode":
+            return wl.sparse_decode(**kw)
+    if name == "sparse_decode":
+        return wl.sparse_decode()
+    if name == "long_decode_sparse":
+        return wl.long_decode_sparse()
     if name == "batched_gqa_decode":
         return wl.batched_gqa_decode(host_pool=False)
     if name == "tiny_decode":
@@ -91,9 +103,35 @@ def make_workload(name):
 SPLIT_ROWS_MAX = 128
 
 
+def attended(L, T, sparse):
+    """Keys of a sequence that some query row reads (their union), and the (row, key) pairs,
+    with sink + window sparsity (sink, window, min_len) or without it (None)."""
+    if sparse is None:
+        return L, T * (L - T) + T * (T + 1) // 2
+    sink, window, min_len = sparse
+    spans, pairs = [], 0
+    for i in range(T):
+        p = L - T + i
+        if p + 1 < min_len:
+            row = [(0, p + 1)]
+        else:
+            lo = max(0, p + 1 - window)
+            row = [(0, min(sink, lo)), (lo, p + 1)]
+        spans += row
+        pairs += sum(b - a for a, b in row if b > a)
+    keys, end = 0, 0
+    for a, b in sorted(spans):
+        a = max(a, end)
+        if b > a:
+            keys += b - a
+            end = b
+    return keys, pairs
+
+
 def algorithmic(w):
     """Per-step algorithmic bytes and flops (and attended KV tokens), from the definition, for
-    the whole step and for the sequences each attention kernel serves."""
+    the whole step and for the sequences each attention kernel serves.  Under sink + window
+    sparsity only the keys some row reads count."""
     eb = w.elt_bytes                       # pool element bytes
     ab = 4 if w.dtype == "f32" else 2      # q / out / appended row element bytes
     sb = 2 * 4 if w.dtype == "i8" else 0   # int8 pools: K and V scale per token and KV head
@@ -103,12 +141,12 @@ def algorithmic(w):
                split_bytes=0, split_flops=0, prefill_bytes=0, prefill_flops=0)
     for L, T in zip(w.ctx_lens.astype(np.int64), w.q_lens.astype(np.int64)):
         L, T = int(L), int(T)
-        kv = L * hkv * (d * 2 * eb + sb)                # K and V of every key, once per KV head
+        keys, pairs = attended(L, T, w.sparse)          # dense: row i sees L - T + i + 1 keys
+        kv = keys * hkv * (d * 2 * eb + sb)             # K and V of every key, once per KV head
         qo = 2 * T * hq * d * ab
-        tab = (L + w.block_size - 1) // w.block_size * 4
-        pairs = T * (L - T) + T * (T + 1) // 2          # row i sees L - T + i + 1 keys
+        tab = (keys + w.block_size - 1) // w.block_size * 4
         fl = 4 * d * hq * pairs
-        out["kv_tokens"] += L
+        out["kv_tokens"] += keys
         out["kv_bytes"] += kv
         out["attn_bytes"] += kv + qo + tab
         out["pairs"] += pairs
@@ -160,6 +198,7 @@ def cpu_baseline(w, dev, kind, budget_s=15.0):
     about budget_s of CPU work; scaled to the metric's unit."""
     from oracle import attention as ora
     from oracle import quant as oq
+    from oracle import sparse as osp
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
@@ -183,7 +222,13 @@ def cpu_baseline(w, dev, kind, budget_s=15.0):
     n_done, t_used, b_done, f_done, tok_done = 0, 0.0, 0, 0, 0
     for s in range(w.num_seqs):
         t0 = time.perf_counter()
-        if i8:
+        if w.sparse is not None:
+            sink, window, min_len = w.sparse
+            osp.paged_attention(w.q, k_pool, v_pool, w.layer, w.block_tables, w.ctx_lens,
+                                w.q_lens, scale=w.scale, dtype=w.dtype, sink=sink, window=window,
+                                min_len=min_len, scales=(k_sc, v_sc) if i8 else None, seqs=[s],
+                                **geo)
+        elif i8:
             oq.paged_attention(w.q, k_pool, v_pool, k_sc, v_sc, w.layer, w.block_tables,
                                w.ctx_lens, w.q_lens, scale=w.scale, seqs=[s], **geo)
         else:
@@ -191,10 +236,11 @@ def cpu_baseline(w, dev, kind, budget_s=15.0):
                                 w.q_lens, scale=w.scale, dtype=w.dtype, seqs=[s], **geo)
         t_used += time.perf_counter() - t0
         L, T = int(w.ctx_lens[s]), int(w.q_lens[s])
+        keys, pairs = attended(L, T, w.sparse)
         n_done += 1
-        tok_done += L
-        b_done += L * per_key + 2 * T * w.num_q_heads * w.head_dim * ab
-        f_done += 4 * w.head_dim * w.num_q_heads * (T * (L - T) + T * (T + 1) // 2)
+        tok_done += keys
+        b_done += keys * per_key + 2 * T * w.num_q_heads * w.head_dim * ab
+        f_done += 4 * w.head_dim * w.num_q_heads * pairs
         if t_used >= budget_s:
             break
     sample = (f"{n_done} of {w.num_seqs} sequences ({tok_done} KV tokens, "
@@ -293,9 +339,16 @@ class Device:
         if self.k_new is not None:
             self.pool.append(w.layer, self.k_new, self.v_new, self.tables, self.ctx, self.ql,
                              max_q_len=self.max_q)
-        self.pool.forward(w.layer, self.q, self.tables, self.ctx, self.ql, scale=w.scale,
-                          max_ctx_len=self.max_ctx, max_q_len=self.max_q, out=self.out,
-                          q_lens_host=self.ql_host)
+        if w.sparse is not None:
+            sink, window, min_len = w.sparse
+            self.pool.forward_sparse(w.layer, self.q, self.tables, self.ctx, self.ql,
+                                     scale=w.scale, sink_tokens=sink, window_tokens=window,
+                                     min_ctx_len=min_len, max_ctx_len=self.max_ctx,
+                                     max_q_len=self.max_q, out=self.out, q_lens_host=self.ql_host)
+        else:
+            self.pool.forward(w.layer, self.q, self.tables, self.ctx, self.ql, scale=w.scale,
+                              max_ctx_len=self.max_ctx, max_q_len=self.max_q, out=self.out,
+                              q_lens_host=self.ql_host)
 
 
 def main():

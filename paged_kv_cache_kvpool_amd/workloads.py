@@ -81,6 +81,7 @@ class Workload:
     referenced: Optional[np.ndarray] = None  # bool [num_blocks]: blocks some table uses
     k_scales: Optional[np.ndarray] = None    # int8 pools: float32 [layers][blocks][Hkv][B]
     v_scales: Optional[np.ndarray] = None
+    sparse: Optional[tuple] = None  # (sink, window, min_len): run as sink + window sparse attention
 
     @property
     def num_seqs(self) -> int:
@@ -284,6 +285,33 @@ def mixed_step(seed: int = 5, host_pool: bool = True, dtype: str = BF16) -> Work
     return make("mixed_step" + ("_int8" if dtype == I8 else ""), seed=seed + 1000, dtype=dtype,
                 num_seqs_ctx=ctx, q_lens=ql,
                 num_q_heads=40, num_kv_heads=8, head_dim=128, append=True, host_pool=host_pool)
+
+
+# The pages' sparse decode mode: the first KV block (16 tokens) and the last 4096 tokens once a
+# sequence holds 16384 (sparkinfer server README, "Env", SPARKINFER_SPARSE_GQA6).
+PAGES_SPARSE = (16, 4096, 16384)
+
+
+def sparse_decode(seed: int = 6, num_seqs: int = 32, host_pool: bool = False,
+                  dtype: str = BF16) -> Workload:
+    """32 sequences x 1 query token with contexts uniform on [16384, 65536], 32/8 heads, D=128,
+    bf16, B=16, in the pages' sparse mode (each reads 16 + 4096 keys); the pool holds every
+    context in full (drawn on the device)."""
+    rng = np.random.default_rng(seed)
+    ctx = rng.integers(16384, 65537, size=num_seqs).astype(np.int32)
+    w = make("sparse_decode" + ("_int8" if dtype == I8 else ""), seed=seed + 1000, dtype=dtype,
+             num_seqs_ctx=ctx, q_lens=np.ones(num_seqs, np.int32), num_q_heads=32,
+             num_kv_heads=8, head_dim=128, append=True, host_pool=host_pool)
+    w.sparse = PAGES_SPARSE
+    return w
+
+
+def long_decode_sparse(seed: int = 4, dtype: str = BF16) -> Workload:
+    """The long-context decode workload (262144 and 131072 keys) in the pages' sparse mode."""
+    w = long_decode(seed=seed, dtype=dtype)
+    w.name = "long_decode_sparse" + ("_int8" if dtype == I8 else "")
+    w.sparse = PAGES_SPARSE
+    return w
 
 
 def random_case(seed: int, *, dtype=BF16, num_seqs=3, num_q_heads=8, num_kv_heads=2,
