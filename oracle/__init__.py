@@ -10,11 +10,14 @@ package imports nothing from the library or its Python binding.
   storage layout, and attention on the dequantized values (float64, via ``oracle.attention``).
 * ``oracle.sparse``    - sink + window sparse attention: each row past a length threshold reads
   only the sequence's first positions and its latest ones (a key mask on ``oracle.attention``).
+* ``oracle.hoststore`` - the host page store for parked blocks: page bytes, the 128-bit content
+  hash that identifies equal pages, and a store model that dedups by comparing bytes.
 * ``oracle.brute``     - pure-Python brute force for tiny inputs (``math.fsum``, log-sum-exp
   normalisation, element-wise scatter by the storage formula, a quantiser rounding each
-  operation to float32) used to pin ``oracle.attention``, ``oracle.quant`` and ``oracle.sparse``.
+  operation to float32) used to pin ``oracle.attention``, ``oracle.quant``, ``oracle.sparse`` and
+  ``oracle.hoststore``.
 
 Every function is pinned by a ``-m "not gpu"`` test against something other than itself
 (brute force, closed forms, invariants).  Nothing here is "parity unpinned".
 """
-from . import attention, brute, quant, sparse  # noqa: F401
+from . import attention, brute, hoststore, quant, sparse  # noqa: F401

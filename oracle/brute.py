@@ -164,3 +164,41 @@ def attention_keys(q, k, v, scale, keys_of):
             row.append([math.fsum(w * v[j][g][d] for w, j in zip(wts, keys)) for d in range(dim)])
         out.append(row)
     return out
+
+
+def fmix64_int(k: int) -> int:
+    """MurmurHash3's 64-bit finalizer on a Python int (explicit masking to 64 bits)."""
+    mask = (1 << 64) - 1
+    k &= mask
+    k ^= k >> 33
+    k = (k * 0xFF51AFD7ED558CCD) & mask
+    k ^= k >> 33
+    k = (k * 0xC4CEB9FE1A85EC53) & mask
+    k ^= k >> 33
+    return k
+
+
+def unfmix64_int(k: int) -> int:
+    """Inverse of fmix64_int: undo each xorshift (k ^ k >> 33 is its own inverse for a 64-bit
+    word, since 2 * 33 >= 64) and each multiply (by the multiplicative inverse mod 2^64)."""
+    mask = (1 << 64) - 1
+    k ^= k >> 33
+    k = (k * pow(0xC4CEB9FE1A85EC53, -1, 1 << 64)) & mask
+    k ^= k >> 33
+    k = (k * pow(0xFF51AFD7ED558CCD, -1, 1 << 64)) & mask
+    k ^= k >> 33
+    return k
+
+
+def page_hash_bytes(data: bytes):
+    """The page hash over raw bytes, word by word with struct and Python ints:
+    h1 = sum fmix64(w_i + 0x9E3779B97F4A7C15 (i + 1)), h2 = sum fmix64(w_i ^ 0xD6E8FEB86659FD93 (i + 1))
+    mod 2^64, w_i the i-th little-endian 64-bit word."""
+    import struct
+    mask = (1 << 64) - 1
+    h1 = h2 = 0
+    for i in range(len(data) // 8):
+        (w,) = struct.unpack_from("<Q", data, 8 * i)
+        h1 = (h1 + fmix64_int((w + 0x9E3779B97F4A7C15 * (i + 1)) & mask)) & mask
+        h2 = (h2 + fmix64_int(w ^ ((0xD6E8FEB86659FD93 * (i + 1)) & mask))) & mask
+    return h1, h2
