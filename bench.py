@@ -35,6 +35,7 @@ METRIC = "decode attention achieved HBM GB/s + KV tokens/s; prefill MFMA TFLOP/s
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFLOPS = 2500.0
 FLUSH_BYTES = 1 << 30
+PCIE_PEAK_GBS = 64.0   # host link: PCIe 5.0 x16, per direction
 
 WORKLOADS = {
     "batched_gqa_decode": dict(kind="hbm", desc="32 seqs x 1 token, ctx U[1024,8192], 32/8 heads, D=128, bf16, B=16"),
@@ -52,6 +53,10 @@ WORKLOADS["sparse_decode"] = dict(
 WORKLOADS["long_decode_sparse"] = dict(
     kind="hbm", desc="2 seqs x 1 token at 262144 and 131072, 40/8 heads, D=128, bf16; sink + window "
                      "sparse (first 16 + last 4096 keys)")
+WORKLOADS["park_restore"] = dict(
+    kind="pcie", desc="16 seqs x 4096 tokens sharing a 2048-token prefix (recomputed into separate "
+                      "blocks), 8 layers, 8 KV heads, D=128, bf16, B=16 (512 KiB pages): park every "
+                      "block in the host store (equal pages once), restore every page, release")
 # The same workloads on an int8 pool (codes + one fp32 scale per token and KV head; q, out and
 # appended rows bf16).
 for _n in ("batched_gqa_decode", "spec_verify_32k", "spec_verify_128k", "prefix_prefill",
@@ -351,6 +356,123 @@ class Device:
                               q_lens_host=self.ql_host)
 
 
+def bench_park_restore(args):
+    """Park / restore over PCIe through the host page store.  One step: park the 16 sequences'
+    4096 blocks (content hashes on the GPU, 2176 distinct pages copied to pinned host memory),
+    restore all 4096 pages into spare blocks, release them.  Bytes counted: distinct pages
+    written to the host plus pages read back."""
+    import torch
+    from paged_kv_cache_kvpool_amd import binding as kb
+    torch.cuda.set_device(0)
+    layers, hkv, d, bs, seqs, per_seq, shared = 8, 8, 128, 16, 16, 256, 128
+    nb = 2 * seqs * per_seq
+    t_setup = time.perf_counter()
+    pool = kb.PagedKVPool(layers, nb, bs, hkv, d, kb.KV_BF16, device="cuda")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    for which in ("k", "v"):
+        view = pool.block_storage(which)
+        for layer in range(layers):
+            view[layer].copy_(torch.randn(view[layer].shape, generator=g, device="cuda").to(torch.bfloat16))
+    rng = np.random.default_rng(7)
+    perm = rng.permutation(nb).astype(np.int32)
+    tables = perm[:seqs * per_seq].reshape(seqs, per_seq)
+    spare = perm[seqs * per_seq:]
+    # the shared prefix: blocks 0..127 of every sequence hold sequence 0's content
+    src = np.repeat(tables[0, :shared][None], seqs - 1, 0).ravel()
+    dst = tables[1:, :shared].ravel()
+    pool.copy_blocks(torch.from_numpy(src).cuda(), torch.from_numpy(dst).cuda())
+    torch.cuda.synchronize()
+    blocks = tables.ravel()
+    store = kb.HostStore(pool, (shared + seqs * (per_seq - shared)) * 512 * 1024 + (64 << 20))
+    page = store.page_bytes
+    uniq = shared + seqs * (per_seq - shared)
+    moved = uniq * page + blocks.size * page
+    setup_s = time.perf_counter() - t_setup
+
+    def step():
+        ids = store.park(pool, blocks)
+        store.restore(pool, ids, spare[:blocks.size])
+        store.release(ids)
+        return ids
+
+    for _ in range(args.warmup):
+        ids = step()
+    assert store.stats()["pages"] == 0
+    kb.kvpool_profile(True)
+    for _ in range(args.steps):
+        ids = step()
+    torch.cuda.synchronize()
+    kb.kvpool_profile(False)
+    kt = kb.kernel_times()
+    times = []
+    torch.cuda.synchronize()
+    t_all = time.perf_counter()
+    for _ in range(args.steps):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        ids = step()
+        torch.cuda.synchronize()
+        times.append(time.perf_counter() - t0)
+    wall = time.perf_counter() - t_all
+    assert len(set(ids.tolist())) == uniq
+    ms = float(np.mean(times)) * 1e3
+    park_ms = kt["page_park"][1] / kt["page_park"][0]
+    rest_ms = kt["page_restore"][1] / kt["page_restore"][0]
+    hash_ms = kt["page_hash"][1] / kt["page_hash"][0]
+    park_gbs = uniq * page / (park_ms * 1e-3) / 1e9
+    rest_gbs = blocks.size * page / (rest_ms * 1e-3) / 1e9
+    dom, dom_ms, dom_bytes = (("page_restore", rest_ms, blocks.size * page) if rest_ms >= park_ms
+                              else ("page_park", park_ms, uniq * page))
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = park_restore_cpu(pool, blocks, spare)
+    line = {
+        "metric": METRIC, "value": moved / (ms * 1e-3) / 1e9, "unit": "GB/s (PCIe)",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "park_restore", "desc": WORKLOADS["park_restore"]["desc"],
+                   "blocks_parked": int(blocks.size), "distinct_pages": uniq, "page_bytes": page},
+        "park_gbs": park_gbs, "restore_gbs": rest_gbs, "hash_ms": hash_ms,
+        "park_ms": park_ms, "restore_ms": rest_ms,
+        "dedup_saved_bytes": (blocks.size - uniq) * page,
+        "step_ms_p10_p50_p90": [float(np.percentile(times, p)) * 1e3 for p in (10, 50, 90)],
+        "kernel_ms_per_launch": {k: v[1] / v[0] for k, v in kt.items()},
+        "roofline": {"bound": "pcie", "achieved": achieved, "peak": PCIE_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / PCIE_PEAK_GBS, "traffic": None, "kernel": dom,
+                     "kernel_ms": dom_ms},
+        "cpu_baseline": cpu, "wall_s_timed_region": wall, "setup_s": setup_s,
+        "kernel_source_sha": kernel_sha(os.path.join(ROOT, "paged_kv_cache_kvpool_amd", "csrc", "kv_host.hip")),
+    }
+    store.close()
+    print(json.dumps(line), flush=True)
+
+
+def park_restore_cpu(pool, blocks, spare, budget_s=10.0):
+    """The oracle's store model (byte comparison, Python dict) parking and restoring pages of
+    the same pool on the host: a bounded sample of blocks, scaled to GB/s of pages moved."""
+    import torch
+    from oracle import hoststore as hs
+    k = pool.block_storage("k").cpu().view(torch.int16).numpy()
+    v = pool.block_storage("v").cpu().view(torch.int16).numpy()
+    pools = (k, v)
+    n, t_used, moved = 0, 0.0, 0
+    step = 64
+    while t_used < budget_s and n < blocks.size:
+        chunk = [int(b) for b in blocks[n:n + step]]
+        t0 = time.perf_counter()
+        st = hs.Store(capacity_pages=10 ** 9)
+        ids = st.park(pools, chunk)
+        st.restore(pools, ids, [int(b) for b in spare[n:n + len(chunk)]])
+        t_used += time.perf_counter() - t0
+        moved += (len(st.pages) + len(chunk)) * hs.page_bytes(pools, chunk[0]).size
+        n += len(chunk)
+    return dict(value=moved / t_used / 1e9, unit="GB/s", cores=1, kind="oracle",
+                sample=f"{n} of {blocks.size} blocks parked and restored ({t_used:.1f} s)")
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -388,6 +510,9 @@ def main():
         return
     wname = args.workload
     info = WORKLOADS[wname]
+    if info["kind"] == "pcie":
+        bench_park_restore(args)
+        return
     t_setup = time.perf_counter()
     w = make_workload(wname)
     alg = algorithmic(w)

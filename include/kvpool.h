@@ -211,6 +211,61 @@ KVPOOL_API int kvattn_forward_sparse(kvpool_t *pool, int32_t layer, const void *
                                      const int32_t *q_lens_host, void *workspace,
                                      size_t workspace_bytes, void *stream);
 
+/* ---- host page store: park / restore pool blocks over PCIe ----------------------------------
+ * Evicted sequences can be parked in pinned host memory instead of being discarded, each taking
+ * only its real size, and computed prefixes restored over PCIe instead of being recomputed,
+ * with branches that share a prefix deduplicating against the same stored pages (NInfer serving
+ * doc, "Server options", --host-kv-cache-mib and --kv-host-cache-mib).
+ * A page is one pool block across every layer: for layer 0, 1, ...: the block's K bytes, its V
+ * bytes and, for an int8 pool, its K and V scale bytes, each in storage order.  Pages with the
+ * same content are stored once, with a reference count: content is compared through a 128-bit
+ * hash computed on the GPU (each 64-bit little-endian word w_i of the page, i = 0, 1, ...,
+ * contributes fmix64(w_i + 0x9E3779B97F4A7C15 (i + 1)) to the first half and
+ * fmix64(w_i ^ 0xD6E8FEB86659FD93 (i + 1)) to the second, sums mod 2^64; fmix64 is the
+ * MurmurHash3 finalizer), so only pages the store lacks cross PCIe.  Two different pages with
+ * equal hashes would be merged; for non-adversarial data the chance is about 2^-128 per pair.
+ * The kernels read and write the pinned store directly (no device memory is allocated).
+ * A store serves pools of the geometry (layers, block size, KV heads, head dim, dtype) it was
+ * created for.  Calls on one store are serialised by a lock; park, restore and page_hash are
+ * enqueued on `stream` and wait for it to finish before returning.  Block and page lists are
+ * host arrays. */
+typedef struct kvhost kvhost_t;
+
+/* Bytes of one page of `pool` (written to *bytes). */
+KVPOOL_API int kvhost_page_bytes(const kvpool_t *pool, size_t *bytes);
+
+/* A store holding up to budget_bytes / page slot (the page rounded up to 256 bytes) pages, in
+ * one pinned host allocation made here.  KV_EINVAL if the budget holds no page; KV_ENOMEM if the
+ * pinned allocation fails (the caller then runs without a store). */
+KVPOOL_API int kvhost_create(kvhost_t **out, const kvpool_t *pool, size_t budget_bytes);
+KVPOOL_API int kvhost_destroy(kvhost_t *store);   /* frees the pinned memory; NULL is a no-op */
+
+/* Stores pool blocks blocks[0..n) and writes their page ids to page_ids[0..n): a block whose
+ * content equals a stored page (or another block of the call) gets that page's id and adds a
+ * reference.  All or nothing: KV_ENOMEM, with nothing stored, when the distinct new pages do not
+ * fit.  KV_ERANGE for a block id outside the pool. */
+KVPOOL_API int kvhost_park(kvhost_t *store, kvpool_t *pool, const int32_t *blocks, int32_t n,
+                           int64_t *page_ids, void *stream);
+
+/* Writes page page_ids[i] into pool block dst_blocks[i], bit for bit, for i < n.  Destination
+ * blocks must be distinct; page ids must be live (KV_EINVAL otherwise, nothing written).  The
+ * references are kept (release them when the pages are no longer needed). */
+KVPOOL_API int kvhost_restore(kvhost_t *store, kvpool_t *pool, const int64_t *page_ids,
+                              const int32_t *dst_blocks, int32_t n, void *stream);
+
+/* Drops one reference per listed id; a page left with none is removed and its id goes stale
+ * (a stale id is refused, never confused with a later page).  All or nothing: KV_EINVAL, with
+ * nothing released, if an id is not live or is listed more often than it is referenced. */
+KVPOOL_API int kvhost_release(kvhost_t *store, const int64_t *page_ids, int32_t n);
+
+/* Pages stored, page capacity and live references. */
+KVPOOL_API int kvhost_stats(const kvhost_t *store, int64_t *pages, int64_t *capacity,
+                            int64_t *references);
+
+/* The 128-bit content hashes of pool blocks blocks[0..n): hashes[2i], hashes[2i + 1] (host). */
+KVPOOL_API int kvhost_page_hash(kvhost_t *store, kvpool_t *pool, const int32_t *blocks,
+                                int32_t n, uint64_t *hashes, void *stream);
+
 /* Opt-in per-kernel timing for measurement.  With enable != 0, every kernel launch made by this
  * library (any pool, any thread) is bracketed by a pair of HIP events recorded on the launch's
  * stream, and earlier records are dropped; with enable == 0 recording stops (records are kept).

@@ -12,7 +12,7 @@ _BINDING_NAMES = {
     "kvpool_copy_blocks", "kvattn_workspace_size", "kvattn_forward", "kvattn_forward_sparse",
     "kvpool_last_error",
     "kvpool_profile", "kvpool_profile_kernel", "kernel_times",
-    "PagedKVPool", "KVPoolError", "KV_F32", "KV_BF16", "KV_I8", "lib",
+    "PagedKVPool", "HostStore", "KVPoolError", "KV_F32", "KV_BF16", "KV_I8", "lib",
 }
 
 

@@ -43,6 +43,15 @@ SIGNATURES = {
                               _i32, _i32, _vp, _vp, _sz, _vp]),
     "kvattn_forward_sparse": (_i32, [_vp, _i32, _vp, _vp, _i32, _f32, _vp, _i32, _vp, _vp, _i32,
                                      _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _sz, _vp]),
+    "kvhost_page_bytes": (_i32, [_vp, ctypes.POINTER(_sz)]),
+    "kvhost_create": (_i32, [ctypes.POINTER(_vp), _vp, _sz]),
+    "kvhost_destroy": (_i32, [_vp]),
+    "kvhost_park": (_i32, [_vp, _vp, _vp, _i32, _vp, _vp]),
+    "kvhost_restore": (_i32, [_vp, _vp, _vp, _vp, _i32, _vp]),
+    "kvhost_release": (_i32, [_vp, _vp, _i32]),
+    "kvhost_stats": (_i32, [_vp, ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int64),
+                            ctypes.POINTER(ctypes.c_int64)]),
+    "kvhost_page_hash": (_i32, [_vp, _vp, _vp, _i32, _vp, _vp]),
     "kvpool_last_error": (ctypes.c_char_p, []),
     "kvpool_profile": (_i32, [_i32]),
     "kvpool_profile_kernel": (_i32, [_i32, ctypes.POINTER(ctypes.c_char_p),
@@ -329,4 +338,65 @@ class PagedKVPool:
                               block_tables.shape[1], ctx_lens, q_lens, ctx_lens.shape[0], total_q,
                               max_ctx_len, max_q_len, sink_tokens, window_tokens, min_ctx_len,
                               ws, need, stream, q_lens_host)
+        return out
+
+
+# ---------------------------------------------------------------------------------------------
+# Host page store (park / restore pool blocks over PCIe, pages with equal content stored once).
+# ---------------------------------------------------------------------------------------------
+
+class HostStore:
+    """A pinned host page store for the blocks of pools shaped like ``pool``."""
+
+    def __init__(self, pool: "PagedKVPool", budget_bytes: int):
+        h = _vp()
+        _check(lib().kvhost_create(ctypes.byref(h), pool.handle, int(budget_bytes)))
+        self.handle = h.value
+        out = _sz(0)
+        _check(lib().kvhost_page_bytes(pool.handle, ctypes.byref(out)))
+        self.page_bytes = out.value
+
+    def close(self):
+        if getattr(self, "handle", None):
+            lib().kvhost_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):  # pragma: no cover
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    @staticmethod
+    def _i32(x):
+        return np.ascontiguousarray(np.asarray(x, dtype=np.int32))
+
+    def park(self, pool, blocks, stream=None) -> np.ndarray:
+        b = self._i32(blocks)
+        ids = np.zeros(b.size, np.int64)
+        _check(lib().kvhost_park(self.handle, pool.handle, b.ctypes.data, b.size, ids.ctypes.data,
+                                 _stream(stream)))
+        return ids
+
+    def restore(self, pool, page_ids, dst_blocks, stream=None) -> None:
+        ids = np.ascontiguousarray(np.asarray(page_ids, dtype=np.int64))
+        d = self._i32(dst_blocks)
+        assert ids.size == d.size
+        _check(lib().kvhost_restore(self.handle, pool.handle, ids.ctypes.data, d.ctypes.data,
+                                    d.size, _stream(stream)))
+
+    def release(self, page_ids) -> None:
+        ids = np.ascontiguousarray(np.asarray(page_ids, dtype=np.int64))
+        _check(lib().kvhost_release(self.handle, ids.ctypes.data, ids.size))
+
+    def stats(self):
+        p, c, r = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+        _check(lib().kvhost_stats(self.handle, ctypes.byref(p), ctypes.byref(c), ctypes.byref(r)))
+        return dict(pages=p.value, capacity=c.value, references=r.value)
+
+    def page_hash(self, pool, blocks, stream=None) -> np.ndarray:
+        b = self._i32(blocks)
+        out = np.zeros((b.size, 2), np.uint64)
+        _check(lib().kvhost_page_hash(self.handle, pool.handle, b.ctypes.data, b.size,
+                                      out.ctypes.data, _stream(stream)))
         return out

@@ -20,7 +20,7 @@ LIB = os.path.join(HERE, "libkvpool.so")
 ARCH = os.environ.get("KVPOOL_ARCH", "gfx950")
 
 SOURCES = ["kvpool.cpp", "kv_append.hip", "attn_split_mfma.hip", "attn_vec.hip",
-           "attn_reduce.hip", "attn_prefill_mfma.hip", "kv_dequant.hip"]
+           "attn_reduce.hip", "attn_prefill_mfma.hip", "kv_dequant.hip", "kv_host.hip"]
 
 FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",

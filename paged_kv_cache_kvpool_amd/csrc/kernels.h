@@ -39,6 +39,29 @@ struct CopyArgs {
 hipError_t launch_append(const AppendArgs& a, int elt_bytes, int max_q_len, hipStream_t st);
 hipError_t launch_copy_blocks(const CopyArgs& a, int n, int num_layers, hipStream_t st);
 
+// Pool geometry for moving whole pages (one block across every layer: K, V and, for int8
+// pools, the K and V scales) between the pool and a pinned host page store.
+struct PageArgs {
+  void* k;
+  void* v;
+  float* k_scale;       // int8 pools, else null
+  float* v_scale;
+  int32_t num_blocks;
+  int32_t tensors;      // 2 (K, V) or 4 (K, V, K scales, V scales)
+  int32_t segs;         // segments per page: num_layers * tensors
+  size_t block_bytes;   // one block of one layer of K or V
+  size_t scale_bytes;   // one block of one layer of K or V scales
+  size_t page_stride;   // bytes between page slots in the host store
+};
+// Hash partials of pool blocks blocks[0..n): partial[2 (j * segs + seg) + {0, 1}].
+hipError_t launch_page_hash(const PageArgs& a, const int32_t* blocks, int n, uint64_t* partial,
+                            hipStream_t st);
+// pairs: [n][2] = (pool block, store slot) for park, (store slot, pool block) for restore.
+hipError_t launch_page_park(const PageArgs& a, const int32_t* pairs, int n, char* store,
+                            hipStream_t st);
+hipError_t launch_page_restore(const PageArgs& a, const int32_t* pairs, int n, const char* store,
+                               hipStream_t st);
+
 // Split-K attention on the matrix cores (bf16) for the sequences with q_len <= split_q_max:
 // items of (row tile of <= 32 rows, split, KV head, sequence) dealt round-robin to persistent
 // waves (num_cus sizes the grid), or, for forced splits longer than 2048 keys, one 4-wave

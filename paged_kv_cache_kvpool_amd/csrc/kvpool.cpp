@@ -12,6 +12,7 @@
 #include <mutex>
 #include <new>
 #include <string>
+#include <unordered_map>
 #include <vector>
 
 #include "kernels.h"
@@ -143,10 +144,14 @@ int validate_meta(const kvpool* p, const HostMeta& m, int32_t max_blocks, int32_
 }
 
 // Opt-in per-kernel timing: a HIP event pair around every launch, on the launch's stream.
-enum KernelId { K_APPEND, K_COPY, K_SPLIT_MFMA, K_VEC, K_PREFILL_MFMA, K_REDUCE, K_DEQUANT, K_COUNT };
+enum KernelId {
+  K_APPEND, K_COPY, K_SPLIT_MFMA, K_VEC, K_PREFILL_MFMA, K_REDUCE, K_DEQUANT,
+  K_PAGE_HASH, K_PAGE_PARK, K_PAGE_RESTORE, K_COUNT
+};
 const char* const kKernelNames[K_COUNT] = {"kv_append", "kv_copy_blocks", "attn_split_mfma",
                                            "attn_vec", "attn_prefill_mfma", "attn_reduce",
-                                           "kv_dequant_prefill"};
+                                           "kv_dequant_prefill", "page_hash", "page_park",
+                                           "page_restore"};
 struct ProfRec {
   int kernel;
   hipEvent_t a, b;
@@ -726,5 +731,346 @@ int kvattn_forward_sparse(kvpool_t* pool, int32_t layer, const void* q, void* ou
 }
 
 const char* kvpool_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"
+
+// ---- host page store ----------------------------------------------------------------------
+// Pinned host pages that pool blocks are parked in and restored from (park evicted sequences
+// in host RAM, restore computed prefixes over PCIe, store pages shared by several sequences
+// once: NInfer serving doc, "Server options", --host-kv-cache-mib and --kv-host-cache-mib).
+
+namespace {
+
+struct PageHash {
+  uint64_t a, b;
+  bool operator==(const PageHash& o) const { return a == o.a && b == o.b; }
+};
+struct PageHashHasher {
+  size_t operator()(const PageHash& h) const { return (size_t)(h.a ^ (h.b * 0x9E3779B97F4A7C15ull)); }
+};
+
+// Pinned host allocation mapped into the GPU's address space: *host for the host, *dev (the
+// address the device uses for it) for kernels.
+bool alloc_pinned(size_t bytes, void** host, void** dev) {
+  *host = *dev = nullptr;
+  if (hipHostMalloc(host, bytes, hipHostMallocDefault) != hipSuccess || !*host) {
+    *host = nullptr;
+    return false;
+  }
+  if (hipHostGetDevicePointer(dev, *host, 0) != hipSuccess || !*dev) {
+    hipHostFree(*host);
+    *host = *dev = nullptr;
+    return false;
+  }
+  return true;
+}
+
+// Grows a pinned host buffer to at least `bytes` (contents are not kept).
+bool grow_pinned(void** p, void** dp, size_t* cap, size_t bytes) {
+  if (*cap >= bytes) return true;
+  if (*p) hipHostFree(*p);
+  *p = *dp = nullptr;
+  *cap = 0;
+  const size_t want = std::max(bytes, (size_t)4096);
+  if (!alloc_pinned(want, p, dp)) return false;
+  *cap = want;
+  return true;
+}
+
+}  // namespace
+
+struct kvhost {
+  // geometry of the pools it serves
+  int32_t num_layers, num_blocks, block_size, num_kv_heads, head_dim, dtype;
+  size_t block_bytes, scale_bytes, page_bytes, page_stride;
+  int tensors, segs;
+  char* arena = nullptr;  // pinned: capacity page slots of page_stride bytes
+  char* arena_dev = nullptr;  // its device address
+  int64_t capacity = 0;
+  std::vector<int32_t> refs;    // per slot: references (0: free)
+  std::vector<uint32_t> gen;    // per slot: generation of the page it holds
+  std::vector<PageHash> hash_of;
+  std::vector<int32_t> free_slots;
+  std::unordered_map<PageHash, int32_t, PageHashHasher> index;
+  int64_t references = 0;
+  // pinned scratch the kernels read or write
+  void* partial = nullptr;  // hash partials
+  void* partial_dev = nullptr;
+  size_t partial_cap = 0;
+  void* ints = nullptr;     // block lists and (block, slot) pairs
+  void* ints_dev = nullptr;
+  size_t ints_cap = 0;
+  std::mutex mu;
+};
+
+namespace {
+
+int host_matches(const kvhost* h, const kvpool* p) {
+  if (!h || !p) return fail(KV_EINVAL, "store or pool is NULL");
+  if (p->num_layers != h->num_layers || p->block_size != h->block_size ||
+      p->num_kv_heads != h->num_kv_heads || p->head_dim != h->head_dim || p->dtype != h->dtype)
+    return fail(KV_EINVAL, "pool geometry differs from the store's (layers, block size, KV heads, "
+                "head dim and dtype must match)");
+  if (current_device_matches(p) != hipSuccess)
+    return fail(KV_EINVAL, "current HIP device is not the pool's device %d", p->device);
+  return KV_OK;
+}
+
+kvp::PageArgs page_args(const kvhost* h, const kvpool* p) {
+  kvp::PageArgs a;
+  a.k = p->k;
+  a.v = p->v;
+  a.k_scale = p->k_scale;
+  a.v_scale = p->v_scale;
+  a.num_blocks = p->num_blocks;
+  a.tensors = h->tensors;
+  a.segs = h->segs;
+  a.block_bytes = h->block_bytes;
+  a.scale_bytes = h->scale_bytes;
+  a.page_stride = h->page_stride;
+  return a;
+}
+
+int64_t page_id(const kvhost* h, int32_t slot) { return ((int64_t)h->gen[slot] << 32) | slot; }
+
+// Slot of a live page id, or -1.
+int32_t slot_of(const kvhost* h, int64_t id) {
+  if (id < 0) return -1;
+  const int64_t slot = id & 0xffffffffll;
+  if (slot >= h->capacity) return -1;
+  if (h->refs[slot] <= 0 || (uint32_t)(id >> 32) != h->gen[slot]) return -1;
+  return (int32_t)slot;
+}
+
+// Hashes of pool blocks blocks[0..n) (host array; validated) into out[n].
+int hash_blocks(kvhost* h, kvpool* pool, const int32_t* blocks, int32_t n, hipStream_t st,
+                std::vector<PageHash>& out) {
+  out.assign(n, PageHash{0, 0});
+  if (n == 0) return KV_OK;
+  if (!grow_pinned(&h->partial, &h->partial_dev, &h->partial_cap,
+                   (size_t)n * h->segs * 2 * sizeof(uint64_t)) ||
+      !grow_pinned(&h->ints, &h->ints_dev, &h->ints_cap, (size_t)n * 2 * sizeof(int32_t)))
+    return fail(KV_ENOMEM, "pinned host scratch for %d pages", n);
+  std::memcpy(h->ints, blocks, (size_t)n * sizeof(int32_t));
+  const kvp::PageArgs a = page_args(h, pool);
+  const int32_t* ids_dev = static_cast<const int32_t*>(h->ints_dev);
+  uint64_t* part_dev = static_cast<uint64_t*>(h->partial_dev);
+  const uint64_t* part = static_cast<const uint64_t*>(h->partial);
+  hipError_t e = timed(K_PAGE_HASH, st, [&] { return kvp::launch_page_hash(a, ids_dev, n, part_dev, st); });
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return fail(KV_EDEVICE, "page hash: %s", hipGetErrorString(e));
+  for (int32_t j = 0; j < n; ++j) {
+    uint64_t x = 0, y = 0;  // sums mod 2^64 of the page's segment partials
+    for (int g = 0; g < h->segs; ++g) {
+      x += part[2 * ((size_t)j * h->segs + g)];
+      y += part[2 * ((size_t)j * h->segs + g) + 1];
+    }
+    out[j] = PageHash{x, y};
+  }
+  return KV_OK;
+}
+
+int check_blocks(const kvpool* pool, const int32_t* blocks, int32_t n, const char* what) {
+  for (int32_t j = 0; j < n; ++j)
+    if (blocks[j] < 0 || blocks[j] >= pool->num_blocks)
+      return fail(KV_ERANGE, "%s[%d] = %d outside [0, %d)", what, j, blocks[j], pool->num_blocks);
+  return KV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int kvhost_page_bytes(const kvpool_t* pool, size_t* bytes) {
+  if (!pool || !bytes) return fail(KV_EINVAL, "pool or bytes is NULL");
+  const size_t bb = (size_t)pool->num_kv_heads * pool->block_size * pool->head_dim * elt_bytes(pool->dtype);
+  const size_t sb = pool->dtype == KV_I8 ? (size_t)pool->num_kv_heads * pool->block_size * sizeof(float) : 0;
+  *bytes = (size_t)pool->num_layers * (2 * bb + 2 * sb);
+  return ok();
+}
+
+int kvhost_create(kvhost_t** out, const kvpool_t* pool, size_t budget_bytes) {
+  if (!out) return fail(KV_EINVAL, "out is NULL");
+  *out = nullptr;
+  if (!pool) return fail(KV_EINVAL, "pool is NULL");
+  size_t pb = 0;
+  kvhost_page_bytes(pool, &pb);
+  const size_t stride = (pb + 255) / 256 * 256;
+  const int64_t cap = (int64_t)(budget_bytes / stride);
+  if (cap < 1) return fail(KV_EINVAL, "budget of %zu bytes holds no page of %zu bytes", budget_bytes, stride);
+  if (cap > 0x7fffffffll) return fail(KV_ERANGE, "budget holds more than 2^31 - 1 pages");
+  kvhost* h = new (std::nothrow) kvhost();
+  if (!h) return fail(KV_ENOMEM, "host allocation failed");
+  h->num_layers = pool->num_layers;
+  h->num_blocks = pool->num_blocks;
+  h->block_size = pool->block_size;
+  h->num_kv_heads = pool->num_kv_heads;
+  h->head_dim = pool->head_dim;
+  h->dtype = pool->dtype;
+  h->block_bytes = (size_t)pool->num_kv_heads * pool->block_size * pool->head_dim * elt_bytes(pool->dtype);
+  h->scale_bytes = pool->dtype == KV_I8 ? (size_t)pool->num_kv_heads * pool->block_size * sizeof(float) : 0;
+  h->tensors = pool->dtype == KV_I8 ? 4 : 2;
+  h->segs = pool->num_layers * h->tensors;
+  h->page_bytes = pb;
+  h->page_stride = stride;
+  void *arena = nullptr, *arena_dev = nullptr;
+  if (!alloc_pinned((size_t)cap * stride, &arena, &arena_dev)) {
+    delete h;
+    return fail(KV_ENOMEM, "pinned host allocation of %zu bytes failed", (size_t)cap * stride);
+  }
+  h->arena = static_cast<char*>(arena);
+  h->arena_dev = static_cast<char*>(arena_dev);
+  h->capacity = cap;
+  h->refs.assign(cap, 0);
+  h->gen.assign(cap, 0);
+  h->hash_of.assign(cap, PageHash{0, 0});
+  h->free_slots.reserve(cap);
+  for (int64_t i = cap - 1; i >= 0; --i) h->free_slots.push_back((int32_t)i);
+  *out = h;
+  return ok();
+}
+
+int kvhost_destroy(kvhost_t* h) {
+  if (!h) return ok();
+  if (h->arena) hipHostFree(h->arena);
+  if (h->partial) hipHostFree(h->partial);
+  if (h->ints) hipHostFree(h->ints);
+  delete h;
+  return ok();
+}
+
+int kvhost_page_hash(kvhost_t* h, kvpool_t* pool, const int32_t* blocks, int32_t n,
+                     uint64_t* hashes, void* stream) {
+  int rc = host_matches(h, pool);
+  if (rc) return rc;
+  if (n < 0 || (n > 0 && (!blocks || !hashes))) return fail(KV_EINVAL, "bad block list or output");
+  if ((rc = check_blocks(pool, blocks, n, "blocks"))) return rc;
+  std::lock_guard<std::mutex> lk(h->mu);
+  std::vector<PageHash> hv;
+  if ((rc = hash_blocks(h, pool, blocks, n, reinterpret_cast<hipStream_t>(stream), hv))) return rc;
+  for (int32_t j = 0; j < n; ++j) {
+    hashes[2 * j] = hv[j].a;
+    hashes[2 * j + 1] = hv[j].b;
+  }
+  return ok();
+}
+
+int kvhost_park(kvhost_t* h, kvpool_t* pool, const int32_t* blocks, int32_t n, int64_t* page_ids,
+                void* stream) {
+  int rc = host_matches(h, pool);
+  if (rc) return rc;
+  if (n < 0 || (n > 0 && (!blocks || !page_ids))) return fail(KV_EINVAL, "bad block list or output");
+  if ((rc = check_blocks(pool, blocks, n, "blocks"))) return rc;
+  if (n == 0) return ok();
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  std::lock_guard<std::mutex> lk(h->mu);
+  std::vector<PageHash> hv;
+  if ((rc = hash_blocks(h, pool, blocks, n, st, hv))) return rc;
+  // Distinct new pages of this call (the first block holding each), in block order.
+  std::unordered_map<PageHash, int32_t, PageHashHasher> fresh;  // hash -> index into `news`
+  std::vector<int32_t> news;
+  for (int32_t j = 0; j < n; ++j)
+    if (!h->index.count(hv[j]) && !fresh.count(hv[j])) {
+      fresh.emplace(hv[j], (int32_t)news.size());
+      news.push_back(j);
+    }
+  if ((int64_t)news.size() > (int64_t)h->free_slots.size())
+    return fail(KV_ENOMEM, "store has room for %zu more pages, %zu new ones needed (nothing parked)",
+                h->free_slots.size(), news.size());
+  std::vector<int32_t> slots(news.size());
+  int32_t* pairs = static_cast<int32_t*>(h->ints);  // hash_blocks sized it for 2n ints
+  for (size_t k = 0; k < news.size(); ++k) {
+    slots[k] = h->free_slots[h->free_slots.size() - 1 - k];
+    pairs[2 * k] = blocks[news[k]];
+    pairs[2 * k + 1] = slots[k];
+  }
+  const kvp::PageArgs a = page_args(h, pool);
+  hipError_t e = timed(K_PAGE_PARK, st, [&] {
+    return kvp::launch_page_park(a, static_cast<const int32_t*>(h->ints_dev), (int)news.size(),
+                                 h->arena_dev, st);
+  });
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return fail(KV_EDEVICE, "page park: %s", hipGetErrorString(e));
+  // The copies are done: commit.
+  h->free_slots.resize(h->free_slots.size() - news.size());
+  for (size_t k = 0; k < news.size(); ++k) {
+    const int32_t sl = slots[k];
+    h->gen[sl] += 1;
+    h->hash_of[sl] = hv[news[k]];
+    h->index.emplace(hv[news[k]], sl);
+  }
+  for (int32_t j = 0; j < n; ++j) {
+    const int32_t sl = h->index.at(hv[j]);
+    h->refs[sl] += 1;
+    page_ids[j] = page_id(h, sl);
+  }
+  h->references += n;
+  return ok();
+}
+
+int kvhost_restore(kvhost_t* h, kvpool_t* pool, const int64_t* page_ids, const int32_t* dst_blocks,
+                   int32_t n, void* stream) {
+  int rc = host_matches(h, pool);
+  if (rc) return rc;
+  if (n < 0 || (n > 0 && (!page_ids || !dst_blocks))) return fail(KV_EINVAL, "bad page or block list");
+  if ((rc = check_blocks(pool, dst_blocks, n, "dst_blocks"))) return rc;
+  if (n == 0) return ok();
+  std::vector<char> seen(pool->num_blocks, 0);
+  for (int32_t j = 0; j < n; ++j) {
+    if (seen[dst_blocks[j]]) return fail(KV_EINVAL, "dst_blocks[%d] = %d appears twice", j, dst_blocks[j]);
+    seen[dst_blocks[j]] = 1;
+  }
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  std::lock_guard<std::mutex> lk(h->mu);
+  if (!grow_pinned(&h->ints, &h->ints_dev, &h->ints_cap, (size_t)n * 2 * sizeof(int32_t)))
+    return fail(KV_ENOMEM, "pinned host scratch for %d pages", n);
+  int32_t* pairs = static_cast<int32_t*>(h->ints);
+  for (int32_t j = 0; j < n; ++j) {
+    const int32_t sl = slot_of(h, page_ids[j]);
+    if (sl < 0) return fail(KV_EINVAL, "page_ids[%d] = %lld is not a live page", j, (long long)page_ids[j]);
+    pairs[2 * j] = sl;
+    pairs[2 * j + 1] = dst_blocks[j];
+  }
+  const kvp::PageArgs a = page_args(h, pool);
+  hipError_t e = timed(K_PAGE_RESTORE, st, [&] {
+    return kvp::launch_page_restore(a, static_cast<const int32_t*>(h->ints_dev), n, h->arena_dev,
+                                    st);
+  });
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return fail(KV_EDEVICE, "page restore: %s", hipGetErrorString(e));
+  return ok();
+}
+
+int kvhost_release(kvhost_t* h, const int64_t* page_ids, int32_t n) {
+  if (!h) return fail(KV_EINVAL, "store is NULL");
+  if (n < 0 || (n > 0 && !page_ids)) return fail(KV_EINVAL, "bad page list");
+  std::lock_guard<std::mutex> lk(h->mu);
+  std::unordered_map<int32_t, int32_t> drop;  // slot -> references dropped by this call
+  for (int32_t j = 0; j < n; ++j) {
+    const int32_t sl = slot_of(h, page_ids[j]);
+    if (sl < 0 || ++drop[sl] > h->refs[sl])
+      return fail(KV_EINVAL, "page_ids[%d] = %lld is not a live reference (nothing released)", j,
+                  (long long)page_ids[j]);
+  }
+  for (const auto& d : drop) {
+    const int32_t sl = d.first;
+    h->refs[sl] -= d.second;
+    if (h->refs[sl] == 0) {
+      h->index.erase(h->hash_of[sl]);
+      h->free_slots.push_back(sl);
+    }
+  }
+  h->references -= n;
+  return ok();
+}
+
+int kvhost_stats(const kvhost_t* h, int64_t* pages, int64_t* capacity, int64_t* references) {
+  if (!h || !pages || !capacity || !references) return fail(KV_EINVAL, "NULL argument");
+  std::lock_guard<std::mutex> lk(const_cast<kvhost*>(h)->mu);
+  *pages = h->capacity - (int64_t)h->free_slots.size();
+  *capacity = h->capacity;
+  *references = h->references;
+  return ok();
+}
 
 }  // extern "C"

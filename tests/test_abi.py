@@ -96,3 +96,21 @@ def test_sparse_rejects_bad_parameters(sink, window, min_len):
     assert lib.kvattn_forward_sparse(None, 0, None, None, 8, 1.0, None, 1, None, None, 1, 1, 1, 1,
                                      sink, window, min_len, None, None, 0, None) == kb.KV_EINVAL
     assert "sparse" in kb.kvpool_last_error()
+
+
+def test_host_store_null_arguments():
+    """The host page store's entry points refuse NULL handles before any device call."""
+    lib = kb.lib()
+    h = ctypes.c_void_p(0)
+    assert lib.kvhost_create(None, None, 1 << 20) == kb.KV_EINVAL
+    assert lib.kvhost_create(ctypes.byref(h), None, 1 << 20) == kb.KV_EINVAL
+    assert h.value is None
+    assert lib.kvhost_destroy(None) == kb.KV_OK
+    assert lib.kvhost_park(None, None, None, 1, None, None) == kb.KV_EINVAL
+    assert lib.kvhost_restore(None, None, None, None, 1, None) == kb.KV_EINVAL
+    assert lib.kvhost_release(None, None, 1) == kb.KV_EINVAL
+    assert lib.kvhost_page_hash(None, None, None, 1, None, None) == kb.KV_EINVAL
+    sz = ctypes.c_size_t(0)
+    assert lib.kvhost_page_bytes(None, ctypes.byref(sz)) == kb.KV_EINVAL
+    a = ctypes.c_int64()
+    assert lib.kvhost_stats(None, ctypes.byref(a), ctypes.byref(a), ctypes.byref(a)) == kb.KV_EINVAL
