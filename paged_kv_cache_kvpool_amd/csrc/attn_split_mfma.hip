@@ -63,6 +63,21 @@ __device__ __forceinline__ u32x2 stream8(const uint16_t* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
 }
 
+// Buffer resource over `bytes` bytes at p (raw, no stride): loads at offsets past `bytes` return
+// zero without touching memory, so a load that must be issued but is not needed fetches nothing.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const void* p, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), 0, bytes, 0x00020000);
+}
+constexpr int kBufNT = 2;  // buffer load cache policy: nontemporal (streamed once)
+
+typedef int int4v __attribute__((ext_vector_type(4)));
+// 16x16x64 int8 product with int32 accumulation (exact).  The k order inside a lane does not
+// matter as long as A and B use the same one: lane (n, g) holds 16 consecutive dims of row /
+// column n, the group g of each 64-dim step.
+__device__ __forceinline__ int4v mfma16_i8(int4v a, int4v b, int4v c) {
+  return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
+}
+
 __device__ __forceinline__ floatx4 mfma16(bf16x8 a, bf16x8 b, floatx4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -166,7 +181,7 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, const Item& it, int 
 
   int tb = 0;
   auto tile_off = [&](int ti) -> size_t {
-    ti = min(ti, ntile - 1);  // past the end: re-read the last tile (a cache hit; masked out)
+    ti = min(ti, ntile - 1);  // past the end: the last tile's address (never computed)
     if (RELOAD && ti - tb >= 128) {
       tb = ti & ~127;
       ids0 = tile_block_id(a, s, wb, ntile, it.ke, tb, it.vs1, it.vshift);
@@ -180,20 +195,27 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, const Item& it, int 
   auto load_chunk = [&](Chunk<D, I8>& c, int ci) {
     const size_t o0 = tile_off(2 * ci), o1 = tile_off(2 * ci + 1);
     if constexpr (I8) {
-      // element offsets are byte offsets here; tile index = offset / (16 D)
+      // Byte offsets here (tile index = offset / (16 D)).  Buffer loads over the tile: a tile
+      // past the walk (the ring runs up to three chunks ahead of the last one) gets a zero-size
+      // resource, so its loads are issued but fetch nothing.
       const int8_t* k8 = reinterpret_cast<const int8_t*>(a.k_layer);
       const int8_t* v8 = reinterpret_cast<const int8_t*>(a.v_layer);
       const size_t oo[2] = {o0, o1};
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
+        const bool live = 2 * ci + h < ntile;  // wave-uniform
+        const auto rk = tile_rsrc(k8 + oo[h], live ? 16 * D : 0);
+        const auto rv = tile_rsrc(v8 + oo[h], live ? 16 * D : 0);
 #pragma unroll
         for (int m = 0; m < D / 64; ++m) {
-          c.k[h][m] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(k8 + oo[h] + ((4 * m + g) * 16 + n) * 16));
-          c.v[h][m] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(v8 + oo[h] + (g * 16 + n) * (D / 4) + 16 * m));
+          c.k[h][m] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rk, ((4 * m + g) * 16 + n) * 16, 0, kBufNT));
+          c.v[h][m] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rv, (g * 16 + n) * (D / 4) + 16 * m, 0, kBufNT));
         }
-        const size_t si = oo[h] / D + 4 * g;  // scales of keys 4g .. 4g+3 of the tile
-        c.ks[h] = *reinterpret_cast<const floatx4*>(a.k_scale_layer + si);
-        c.vs[h] = *reinterpret_cast<const floatx4*>(a.v_scale_layer + si);
+        // the 16 K and V scales of the tile; lane (n, g) takes those of keys 4g .. 4g+3
+        const auto rks = tile_rsrc(a.k_scale_layer + oo[h] / D, live ? 64 : 0);
+        const auto rvs = tile_rsrc(a.v_scale_layer + oo[h] / D, live ? 64 : 0);
+        c.ks[h] = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(rks, 16 * g, 0, 0));
+        c.vs[h] = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(rvs, 16 * g, 0, 0));
       }
     } else {
       const uint16_t* kt[2] = {kl + o0, kl + o1};
@@ -245,6 +267,51 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, const Item& it, int 
     }
   }
 
+  // int8 pools: the q row as a 15-bit fixed-point value with a per-row power-of-two scale,
+  // q ~ (256 hi + lo) * qs with hi in [-64, 64] and lo in [-128, 127], so that q.k of the int8
+  // codes is two exact int8 products (scores then carry a relative error of about 2^-15 of the
+  // row's largest |q|, far below the bf16 rounding of P).  Lane (n, g) holds dims
+  // 16 (4 m + g) .. + 16 of row n for 64-dim step m, in the order of its K codes.
+  int4v qhi[I8 ? NT : 1][I8 ? D / 64 : 1], qlo[I8 ? NT : 1][I8 ? D / 64 : 1];
+  float qs[NT];
+  if constexpr (I8) {
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      float qm = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < KK; ++kk)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qm = fmaxf(qm, fabsf((float)qb[nt][kk][e]));
+      qm = xrow_max(qm);  // the row's lanes n, n + 16, n + 32, n + 48
+      int ex = 0;
+      (void)frexpf(qm, &ex);  // qm < 2^ex
+      const int sh = qm > 0.f ? 14 - ex : 0;
+      qs[nt] = qm > 0.f ? __builtin_amdgcn_ldexpf(1.f, -sh) : 0.f;
+#pragma unroll
+      for (int m = 0; m < D / 64; ++m) {
+        uint32_t hw[4], lw[4];
+#pragma unroll
+        for (int w4 = 0; w4 < 4; ++w4) {
+          uint32_t hv = 0, lv = 0;
+#pragma unroll
+          for (int b = 0; b < 4; ++b) {
+            const int j = 4 * w4 + b;  // dim 16 (4 m + g) + j
+            const float x = (float)qb[nt][2 * m + (j >> 3)][j & 7];
+            const int q16 = (int)rintf(__builtin_amdgcn_ldexpf(x, sh));  // |q16| <= 2^14
+            const int lo = ((q16 + 128) & 255) - 128;
+            const int hi = (q16 - lo) >> 8;
+            hv |= (uint32_t)(hi & 255) << (8 * b);
+            lv |= (uint32_t)(lo & 255) << (8 * b);
+          }
+          hw[w4] = hv;
+          lw[w4] = lv;
+        }
+        qhi[nt][m] = int4v{(int)hw[0], (int)hw[1], (int)hw[2], (int)hw[3]};
+        qlo[nt][m] = int4v{(int)lw[0], (int)lw[1], (int)lw[2], (int)lw[3]};
+      }
+    }
+  }
+
   float m_run[NT], l_run[NT];
   floatx4 o[NT][MT];
 #pragma unroll
@@ -267,7 +334,6 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, const Item& it, int 
       return i8x8_to_bf16(ch.v[0][mt >> 2][mt & 3], ch.v[1][mt >> 2][mt & 3]);
     };
     bf16x8 va8[NT > 1 ? MT : 1];
-    bf16x8 ka8[NT > 1 ? 2 : 1][NT > 1 ? KK : 1];
     if constexpr (I8) {
 #pragma unroll
       for (int h = 0; h < 2; ++h)
@@ -277,13 +343,6 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, const Item& it, int 
       if constexpr (NT > 1) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) va8[mt] = v_i8(mt);
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-          for (int kk = 0; kk < KK; ++kk) {
-            const u32x4 w = ch.k[h][kk >> 1];
-            ka8[h][kk] = (kk & 1) ? i8x8_to_bf16(w[2], w[3]) : i8x8_to_bf16(w[0], w[1]);
-          }
       }
     } else if (c0 + 32 > we) {
       // Last chunk: slots at or past `we` may hold anything (NaN included); zero their V so
@@ -304,21 +363,24 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, const Item& it, int 
       floatx4 sc[2];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+        if constexpr (I8) {
+          // exact int32 dot products of the codes with the two halves of the fixed-point q
+          int4v ah = {0, 0, 0, 0}, al = {0, 0, 0, 0};
 #pragma unroll
-        for (int kk = 0; kk < KK; ++kk) {
-          if constexpr (I8 && NT > 1) {
-            acc = mfma16(ka8[h][kk], qb[nt][kk], acc);
-          } else if constexpr (I8) {
-            const u32x4 w = ch.k[h][kk >> 1];
-            const bf16x8 ka = (kk & 1) ? i8x8_to_bf16(w[2], w[3]) : i8x8_to_bf16(w[0], w[1]);
-            acc = mfma16(ka, qb[nt][kk], acc);
-          } else {
-            acc = mfma16(ch.k[h][kk], qb[nt][kk], acc);
+          for (int m = 0; m < D / 64; ++m) {
+            const int4v ka = __builtin_bit_cast(int4v, ch.k[h][m]);
+            ah = mfma16_i8(ka, qhi[nt][m], ah);
+            al = mfma16_i8(ka, qlo[nt][m], al);
           }
+          const floatx4 ksq = ch.ks[h] * qs[nt];  // key 4g + i of tile h: K scale times q scale
+#pragma unroll
+          for (int i = 0; i < 4; ++i) sc[h][i] = (float)(ah[i] * 256 + al[i]) * ksq[i];
+        } else {
+          floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int kk = 0; kk < KK; ++kk) acc = mfma16(ch.k[h][kk], qb[nt][kk], acc);
+          sc[h] = acc;
         }
-        if constexpr (I8) acc *= ch.ks[h];  // key 4g + i of tile h: its K scale
-        sc[h] = acc;
       }
       // This lane now holds row n's scores for keys c0 + 16*h + 4*g + i (j = 4*h + i).
       float sv[8];
@@ -386,9 +448,9 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, const Item& it, int 
   };
 
   if constexpr (RING) {
-    // Ring of four.  Loads past the last chunk re-read the item's last tile (clamped in
-    // tile_off; cache hits) and are never computed, so every load is unconditional and the
-    // waits before each compute are static.
+    // Ring of four.  Loads past the last chunk are issued with zero-size buffer resources
+    // (nothing is fetched) and never computed, so every load is unconditional and the waits
+    // before each compute are static.
     if (nch) {
       Chunk<D, I8> bufC, bufD;
       load_chunk(bufA, 0);
