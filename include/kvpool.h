@@ -31,11 +31,12 @@
  *     KVPOOL_VALIDATE=1 is set, in which case it is copied to the host (synchronising the
  *     stream) and every violation returns KV_ERANGE.  Without validation, kernels clamp ids and
  *     lengths into range so that bad metadata gives wrong values, never an out-of-bounds access.
- *   - Determinism: no float atomics.  The split of a sequence's keys depends only on that
- *     sequence's own length, so a sequence's output is bitwise independent of the rest of the
- *     batch and of where its blocks sit in the pool (the pages' decode path has no float
- *     atomics and a deterministic mode is batch-invariant: sparkinfer server README,
- *     "Determinism").
+ *   - Determinism: no float atomics, so every call is bitwise reproducible.  The split of a
+ *     decode or verification sequence's keys depends only on that sequence's own length, so its
+ *     output is bitwise independent of the rest of the batch and of where its blocks sit in the
+ *     pool.  Prefill-class sequences are batch-invariant too with KVATTN_DETERMINISTIC=1 (see
+ *     kvattn_forward); the pages' decode path has no float atomics and their deterministic mode
+ *     is batch-invariant (sparkinfer server README, "Determinism").
  *
  * Pool storage layout (K and V are separate buffers of identical size).  Element type: fp32
  * or bf16; X = 16 bytes / element size (4 for fp32, 8 for bf16).  For layer l, block b,
@@ -161,8 +162,15 @@ KVPOOL_API int kvattn_workspace_size(const kvpool_t *pool, int32_t num_q_heads,
  * sparkinfer server README, "Request isolation & continuous batching").  A sequence with
  * q_len * (num_q_heads / num_kv_heads) <= 128 takes the split-K kernel (its keys cut into splits
  * of a size set by its own ctx_len, merged in a fixed order); a longer one takes the prefill
- * kernel.  The path and the arithmetic of a sequence follow from its own lengths, so its output
- * bits do not depend on the rest of the batch or on the bounds passed here.
+ * kernel.  Decode and verification sequences: the path and the arithmetic follow from the
+ * sequence's own lengths, so their output bits never depend on the rest of the batch or on the
+ * bounds passed here.  Prefill-class sequences: the workgroup plan follows the call (for speed,
+ * a row block may be split between two waves whose partial results are merged), so their bits
+ * may differ from batch to batch, within the same tolerance; with the environment variable
+ * KVATTN_DETERMINISTIC=1 every row block is reduced by one wave in key order and their bits,
+ * too, depend on the sequence alone (the pages' servers likewise offer bit-reproducible,
+ * batch-invariant output as a mode that costs prefill time: sparkinfer server README,
+ * "Determinism").
  *   q    device, [total_q][num_q_heads][head_dim], pool dtype (bf16 for an int8 pool), rows
  *        packed in sequence order
  *   out  device, same shape and dtype as q; each element is written exactly once, rounded to

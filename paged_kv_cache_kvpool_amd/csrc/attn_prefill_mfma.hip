@@ -439,6 +439,10 @@ void attn_prefill_mfma_kernel(AttnArgs a) {
     const int kb = 32 * blk;
     if (kb >= kew) return;  // wave-uniform
     row_max(sc, kb, kb + 31 > pw0 || kb + 32 > L);
+    // A row without a visible key yet (possible in a half wave: its first block may lie wholly
+    // past the row's position) keeps msub = -inf; subtract 0 for it, so that its masked scores
+    // give p = 0 rather than exp2(-inf + inf) = NaN.
+    const float nms = msub > -INFINITY ? -msub : 0.f;
     // operands: K of the next block (in the same stage or the next one; past the wave's keys
     // its scores are never used), V^T of block blk
     const char* kt = reinterpret_cast<const char*>(nst[2 * ((blk + stride) & 1)]) + k_lane;
@@ -476,8 +480,8 @@ void attn_prefill_mfma_kernel(AttnArgs a) {
         if (nx >= 0) ops[Sched::slot_of_load(nx)] = load_op(Sched::op(nx));
       }
       if (ci < 8) {
-        const float p0 = fast_exp2(__builtin_fmaf(sc[2 * ci], c, -msub));
-        const float p1 = fast_exp2(__builtin_fmaf(sc[2 * ci + 1], c, -msub));
+        const float p0 = fast_exp2(__builtin_fmaf(sc[2 * ci], c, nms));
+        const float p1 = fast_exp2(__builtin_fmaf(sc[2 * ci + 1], c, nms));
         pk[ci] = cvt_pk_bf16(p0, p1);
         // row sum of the fp32 values (plain adds: the bf16 dot2 would take matrix-pipe slots)
         l_lane += p0 + p1;
@@ -545,7 +549,9 @@ void attn_prefill_mfma_kernel(AttnArgs a) {
     if (half && par == 0) {
       const float m1 = ml[lane], l1 = ml[64 + lane];
       const float mm = __builtin_elementwise_maximum(msub, m1);
-      const float a0 = fast_exp2(msub - mm), a1 = fast_exp2(m1 - mm);  // NaN only for rows without keys
+      // the even wave always holds a row's key 0, so mm is finite; a1 = 0 for a row with no key
+      // in the odd wave's blocks (whose o and l are then 0)
+      const float a0 = fast_exp2(msub - mm), a1 = fast_exp2(m1 - mm);
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
@@ -584,18 +590,20 @@ long long prefill_wg_count(const int* rows, int n, int num_kv_heads, int rblk) {
   return wgs;
 }
 
-void prefill_plan(const int* rows, int n, int num_kv_heads, int num_cus, int* waves, int* rblk) {
+void prefill_plan(const int* rows, int n, int num_kv_heads, int num_cus, bool whole_only,
+                  int* waves, int* rblk) {
   // Makespan model: one workgroup per CU at a time (LDS-bound), every workgroup streams all of
   // its sequence's keys.  Per key tile a workgroup costs a fixed part (barrier, streaming) plus
   // the load of its busiest SIMD: waves w, w+4, w+8 share a SIMD, a whole-block wave counts 1
   // and a half wave 1/2 (measured on MI355X: about 1.0 + 0.45 x load microseconds per 64-key
   // tile).  A busiest SIMD with a single wave cannot hide its own latencies (measured 25-30%
   // slower).  Pick the (W, R), W/2 <= R <= W and at most 6 pairs, minimising rounds x tile cost,
-  // then the fewest workgroups, then the fewest waves.
+  // then the fewest workgroups, then the fewest waves.  whole_only: R = W (every row block one
+  // wave), the plans whose arithmetic per row block does not depend on (W, R).
   int bw = 8, br = 8;
   double best_cost = 1e300;
   for (int w = 4; w <= 12; ++w) {
-    for (int r = std::max((w + 1) / 2, w - 6); r <= w; ++r) {
+    for (int r = whole_only ? w : std::max((w + 1) / 2, w - 6); r <= w; ++r) {
       const int f = 2 * r - w;
       double load[4] = {0, 0, 0, 0};
       int nw[4] = {0, 0, 0, 0};

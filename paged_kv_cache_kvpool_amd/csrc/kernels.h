@@ -85,8 +85,9 @@ hipError_t launch_attn_prefill_mfma(const AttnArgs& a, int head_dim, int waves, 
 long long prefill_wg_count(const int* rows, int n, int num_kv_heads, int rblk);
 // Workgroup shape for such a set of sequences: waves (4..12) and row blocks per workgroup
 // (waves/2 .. waves; the waves beyond 2*rblk - waves share a row block in pairs), balancing the
-// SIMDs and the workgroups over the CUs.
-void prefill_plan(const int* rows, int n, int num_kv_heads, int num_cus, int* waves, int* rblk);
+// SIMDs and the workgroups over the CUs.  whole_only: rblk = waves (no pairs).
+void prefill_plan(const int* rows, int n, int num_kv_heads, int num_cus, bool whole_only,
+                  int* waves, int* rblk);
 // Prefill over an int8 pool: the prefill-class sequences' tiles dequantized to bf16 into a
 // workspace pool (max_seqs sequences of blocks_per_seq 16-token blocks) and its block table
 // [num_seqs][blocks_per_seq]; wgs >= the (sequence, KV head, tile) count (extra ones exit).

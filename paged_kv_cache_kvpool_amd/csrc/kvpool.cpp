@@ -480,8 +480,14 @@ Plan make_plan(const kvpool* p, int32_t num_q_heads, int32_t num_seqs, int32_t t
     }
   }
   if (pl.prefill) {
-    kvp::prefill_plan(pf_rows.data(), (int)pf_rows.size(), p->num_kv_heads, p->num_cus, &pl.waves,
-                      &pl.rblk);
+    // Deterministic mode (KVATTN_DETERMINISTIC=1): whole-block plans only.  A row block is then
+    // always reduced by one wave over its keys in key order, whatever (W, R) the batch leads to,
+    // so a prefill-class sequence's output bits no longer depend on the rest of the batch.  By
+    // default a row block may also be split between a pair of half waves (even and odd key
+    // blocks, merged at the end): faster when the batch is small, but the merge rounds
+    // differently, so the bits follow the plan.
+    kvp::prefill_plan(pf_rows.data(), (int)pf_rows.size(), p->num_kv_heads, p->num_cus,
+                      env_flag("KVATTN_DETERMINISTIC"), &pl.waves, &pl.rblk);
     // sweeps and tests: KVATTN_PREFILL_WAVES fixes W (then R = W unless KVATTN_PREFILL_RBLK
     // fixes R within [W/2, W], at most 6 pairs)
     if (const char* v = getenv("KVATTN_PREFILL_WAVES")) {

@@ -82,10 +82,13 @@ def test_batch_invariance_and_repeatability_bitwise(dtype):
 
 
 @pytest.mark.parametrize("dtype", [wl.BF16, wl.F32])
-def test_mixed_batch_invariance_bitwise(dtype):
-    """Decode, verification and prefill sequences in one call give, bit for bit, what each gives
-    alone with bounds of its own (max_ctx_len, max_q_len): the kernel and the split plan follow
-    from the sequence itself, never from the rest of the batch."""
+def test_mixed_batch_invariance_bitwise(dtype, monkeypatch):
+    """In deterministic mode (KVATTN_DETERMINISTIC=1, as the pages' servers offer bit-reproducible,
+    batch-invariant output as a mode: sparkinfer server README, "Determinism"), decode,
+    verification and prefill sequences in one call give, bit for bit, what each gives alone with
+    bounds of its own (max_ctx_len, max_q_len): the kernel and the split plan follow from the
+    sequence itself, and prefill row blocks are always reduced by one wave in key order."""
+    monkeypatch.setenv("KVATTN_DETERMINISTIC", "1")
     announce(f"mixed batch invariance {dtype}")
     w = wl.make("mixed_inv", seed=151, dtype=dtype, num_seqs_ctx=[3000, 700, 1000, 9000, 129, 40],
                 q_lens=[1, 4, 300, 4, 129, 33], num_q_heads=40, num_kv_heads=8, head_dim=128)
@@ -313,3 +316,31 @@ def test_graph_replay_matches_eager(mode):
         g.replay()
         torch.cuda.synchronize()
         assert np.array_equal(bits(out), bits(eager)), f"replay {i}"
+
+
+@pytest.mark.parametrize("dtype", [wl.BF16, wl.F32])
+def test_default_mode_decode_rows_batch_invariant(dtype, monkeypatch):
+    """Without deterministic mode the prefill plan follows the batch, but decode and verification
+    rows (the split-K path: no plan choice) still give each sequence's bits alone; every row
+    stays within tolerance of the oracle."""
+    monkeypatch.delenv("KVATTN_DETERMINISTIC", raising=False)
+    announce(f"default-mode invariance of split-K rows {dtype}")
+    w = wl.make("mixed_inv_default", seed=152, dtype=dtype,
+                num_seqs_ctx=[3000, 700, 1000, 9000, 129, 40, 5000],
+                q_lens=[1, 4, 300, 4, 129, 33, 1], num_q_heads=40, num_kv_heads=8, head_dim=128)
+    c = DeviceCase(w)
+    c.append()
+    full = c.forward()
+    torch.cuda.synchronize()
+    assert_close(out_f64(full), c.oracle(), dtype, w.name)
+    starts = np.concatenate([[0], np.cumsum(w.q_lens)])
+    G = w.num_q_heads // w.num_kv_heads
+    for s in range(w.num_seqs):
+        if w.q_lens[s] * G > 128:
+            continue  # a prefill-class sequence: its plan follows the batch in this mode
+        rows = slice(int(starts[s]), int(starts[s + 1]))
+        sel = torch.tensor([s], device="cuda")
+        alone = c.pool.forward(0, c.q[rows], c.tables[sel], c.ctx[sel], c.ql[sel], scale=w.scale,
+                               max_ctx_len=int(w.ctx_lens[s]), max_q_len=int(w.q_lens[s]))
+        torch.cuda.synchronize()
+        assert np.array_equal(bits(alone), bits(full[rows])), f"sequence {s}"
