@@ -4,30 +4,28 @@
 // "Determinism").  Rows whose keys all fall in split 0 were finished by the attention kernel.
 //
 // One 256-thread workgroup per (row of the partial buffers, q-head); the row's sequence is
-// found from the per-sequence counts of split-K tokens.  The weights 2^{(m_i - M)c} are computed
-// once into LDS; then thread t accumulates dims 4*(t % (D/4)) .. +4 over splits
-// t / (D/4), + 256/(D/4), ..., so each pass over the partials reads whole rows of D floats
-// with 16-byte loads; the split groups are summed in LDS in a fixed order at the end.
+// found from the per-sequence counts of split-K tokens.  Thread t owns dims 4 (t % (D/4)) .. +4
+// and the splits t / (D/4), + 256/(D/4), ...; it merges them in split order with a running max
+// (each partial's m, l and o loaded together, so the loads of all its splits are independent
+// and go out at once: one memory round trip), and the split groups are merged in LDS in a fixed
+// order at the end.
 #include "common.h"
 #include "kernels.h"
 
 namespace kvp {
 
 namespace {
-constexpr int RT = 256;            // threads per workgroup
-constexpr int WMAX = 4096;         // split weights held in LDS per pass
+constexpr int RT = 256;  // threads per workgroup
 }  // namespace
 
 template <typename E, int D>
 __global__ __launch_bounds__(256) void attn_reduce_kernel(AttnArgs a) {
-  constexpr int DQ = D / 4;        // float4 columns
-  constexpr int SG = RT / DQ;      // split groups
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int DQ = D / 4;    // float4 columns
+  constexpr int SG = RT / DQ;  // split groups
+  const int tid = threadIdx.x;
   const int r = blockIdx.x, hh = blockIdx.y;
-  int s, i, q_start;
-  if (!find_split_row(a, r, s, i, q_start)) return;
-  int L, T;
-  seq_lens(a, s, L, T);
+  int s, i, q_start, L, T;
+  if (!find_split_row(a, r, s, i, q_start, L, T)) return;
   int Lv, vs1, vshift;
   seq_vlayout(a, L, T, Lv, vs1, vshift);  // the splits cut the sequence's virtual key positions
   const int p = virt_key(L - T + i, vs1, vshift);
@@ -38,47 +36,59 @@ __global__ __launch_bounds__(256) void attn_reduce_kernel(AttnArgs a) {
   const size_t slot0 = ((size_t)r * a.num_q_heads + hh) * a.max_splits;
   const float c = a.scale_log2;
 
-  __shared__ float s_w[WMAX];
-  __shared__ float s_red[RT / 64];
+  __shared__ float s_m[SG], s_l[SG];
   __shared__ floatx4 s_acc[SG][DQ];
 
-  // M = max_i m_i
-  float M = -INFINITY;
-  for (int k = tid; k < ns; k += RT) M = fmaxf(M, a.part_ml[2 * (slot0 + k)]);
-  M = xrow_max(row_max(M));
-  if (lane == 0) s_red[wave] = M;
-  __syncthreads();
-  M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
-  __syncthreads();
-
+  // Running merge over this thread's splits, in split order: mt is the largest m seen so far
+  // (-inf before any split with a key), lt and acc the sums scaled to it.  A split with no key
+  // for this row (m = -inf, l = 0, o = 0) contributes nothing.  Splits go in batches of 8 whose
+  // loads are all issued before any is used (indices clamped, no branches around them).
   const int dq = tid % DQ, sg = tid / DQ;
+  float mt = -INFINITY, lt = 0.f;
   floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-  float den = 0.f;
-  for (int k0 = 0; k0 < ns; k0 += WMAX) {
-    const int kn = min(ns - k0, WMAX);
-    for (int k = tid; k < kn; k += RT) {
-      const float m = a.part_ml[2 * (slot0 + k0 + k)];
-      const float w = fast_exp2((m - M) * c);
-      s_w[k] = w;
-      den = fmaf(w, a.part_ml[2 * (slot0 + k0 + k) + 1], den);
+  const float2* pml = reinterpret_cast<const float2*>(a.part_ml) + slot0;
+  const floatx4* po = reinterpret_cast<const floatx4*>(a.part_o + slot0 * D) + dq;
+  constexpr int NB = 8;
+  for (int k0 = sg; k0 < ns; k0 += NB * SG) {
+    float2 ml[NB];
+    floatx4 ok[NB];
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      const int k = min(k0 + u * SG, ns - 1);
+      ml[u] = pml[k];
+      ok[u] = po[(size_t)k * DQ];
     }
-    __syncthreads();
-    const floatx4* po = reinterpret_cast<const floatx4*>(a.part_o + (slot0 + k0) * D) + dq;
-    int k = sg;
-#pragma unroll 4
-    for (; k < kn; k += SG) acc += s_w[k] * po[(size_t)k * DQ];
-    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      const bool has = k0 + u * SG < ns && ml[u].x != -INFINITY;
+      const float mn = has ? fmaxf(mt, ml[u].x) : mt;
+      const float sc = mn == mt ? 1.f : fast_exp2((mt - mn) * c);  // 0 while mt is -inf
+      const float w = has ? fast_exp2((ml[u].x - mn) * c) : 0.f;
+      acc = acc * sc + w * ok[u];
+      lt = fmaf(w, ml[u].y, lt * sc);
+      mt = mn;
+    }
   }
   s_acc[sg][dq] = acc;
-  den = xrow_sum(row_sum(den));
-  if (lane == 0) s_red[wave] = den;
+  if (dq == 0) {
+    s_m[sg] = mt;
+    s_l[sg] = lt;
+  }
   __syncthreads();
   if (tid < DQ) {
-    floatx4 v = s_acc[0][tid];
+    float M = s_m[0];
 #pragma unroll
-    for (int g2 = 1; g2 < SG; ++g2) v += s_acc[g2][tid];
-    const float inv = 1.f / ((s_red[0] + s_red[1]) + (s_red[2] + s_red[3]));
-    v *= inv;
+    for (int g2 = 1; g2 < SG; ++g2) M = fmaxf(M, s_m[g2]);
+    floatx4 v = {0.f, 0.f, 0.f, 0.f};
+    float den = 0.f;
+#pragma unroll
+    for (int g2 = 0; g2 < SG; ++g2) {
+      const float mg = s_m[g2];
+      const float w = mg == -INFINITY ? 0.f : fast_exp2((mg - M) * c);
+      v += w * s_acc[g2][tid];
+      den = fmaf(w, s_l[g2], den);
+    }
+    v *= 1.f / den;
     const size_t ob = ((size_t)grow * a.num_q_heads + hh) * D + 4 * tid;
     if constexpr (sizeof(E) == 2) {
       const uint32_t w0 = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);

@@ -155,14 +155,81 @@ __device__ __forceinline__ int tile_block_id(const AttnArgs& a, int s, int wb, i
   return tbl[real_key(min(((wb >> 4) + ti) << 4, ke - 1), vs1, vshift) >> a.block_shift];
 }
 
+// Element offset of tile ti (clamped to the walk's ntile tiles) of a walk starting at tile
+// tile0, whose block ids for tiles tb .. tb + 127 are in ids0 / ids1 (lane i: tile tb + i / 64 +
+// i).  The tile past the end gets the last tile's address (loaded, never computed).
+template <int D>
+__device__ __forceinline__ size_t walk_tile_off(const AttnArgs& a, int kvh, int tile0, int ntile,
+                                                int vs1, int vshift, int ids0, int ids1, int tb,
+                                                int ti) {
+  ti = min(ti, ntile - 1);
+  const int r = ti - tb;
+  const int blk = r < 64 ? __builtin_amdgcn_readlane(ids0, r) : __builtin_amdgcn_readlane(ids1, r - 64);
+  const int sub = (real_key((tile0 + ti) << 4, vs1, vshift) & (a.block_size - 1)) >> 4;
+  return block_tile_offset(blk, sub, kvh, a.block_shift, a.num_blocks, a.num_kv_heads, D);
+}
+
+// bf16 pool: the K and V operands of one 32-key chunk, pool tiles at element offsets o0, o1.
+template <int D>
+__device__ __forceinline__ void load_chunk_bf16(const AttnArgs& a, Chunk<D, false>& c, size_t o0,
+                                                size_t o1) {
+  const int lane = threadIdx.x & (WAVE - 1);
+  const int n = lane & 15, g = lane >> 4;
+  const uint16_t* kl = reinterpret_cast<const uint16_t*>(a.k_layer);
+  const uint16_t* vl = reinterpret_cast<const uint16_t*>(a.v_layer);
+  const uint16_t* kt[2] = {kl + o0, kl + o1};
+  const uint16_t* vt[2] = {vl + o0, vl + o1};
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) c.k[h][kk] = stream16(kt[h] + ((4 * kk + g) * 16 + n) * 8);
+#pragma unroll
+    for (int mt = 0; mt < D / 16; ++mt) c.v[h][mt] = stream8(vt[h] + (16 * mt + n) * 16 + 4 * g);
+  }
+}
+
+// Row r0 + 16 nt + n of an item (n = lane % 16): its index in q / out and whether it exists.
+__device__ __forceinline__ bool item_row(const AttnArgs& a, const Item& it, int r, size_t& rh) {
+  const int G = a.group;
+  const int i = r / G;
+  const int grow = it.q_start + i;
+  const bool valid = r < it.T * G && grow < a.total_q;
+  rh = valid ? (size_t)grow * a.num_q_heads + it.kvh * G + r % G : 0;
+  return valid;
+}
+
+// Q^T of an item's rows as the B operand of the score product: lane (n, g) holds row n of N-tile
+// nt, dims 32 kk + 8 g .. +8 (int8 pools: dims 16 (4 (kk / 2) + g) + 8 (kk % 2) .. +8, the order
+// of the K codes it meets); zero for rows that do not exist.
+template <int D, int NT, bool I8>
+__device__ __forceinline__ void load_q(const AttnArgs& a, const Item& it, bf16x8 (&qb)[NT][D / 32]) {
+  const int lane = threadIdx.x & (WAVE - 1);
+  const int n = lane & 15, g = lane >> 4;
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    size_t rh;
+    const bool valid = item_row(a, it, it.rt * 16 * NT + 16 * nt + n, rh);
+    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + rh * D;
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) {
+      bf16x8 z = {};
+      const int d0 = I8 ? 16 * (4 * (kk >> 1) + g) + 8 * (kk & 1) : 32 * kk + 8 * g;
+      qb[nt][kk] = valid ? load16(qp + d0) : z;
+    }
+  }
+}
+
 // Reduces the keys [wb, we) of item `it` for one wave.  ids0/ids1: lane i holds the block id of
 // the wave's tile i / 64 + i (from tile_block_id).  NW: waves sharing the item, whose partials
 // merge through LDS (NW == 1: the wave finishes the item from registers).  RELOAD: the wave's
 // keys may span more than 128 tiles, so block ids are reloaded every 128 tiles; without it no
 // load in the chunk loop can force a wait on the chunks in flight.
-template <int D, int NT, bool RELOAD, int NW, bool I8>
-__device__ __forceinline__ void run_item(const AttnArgs& a, const Item& it, int wave, int wb,
-                                         int we, int ids0, int ids1) {
+// keys: false for an item none of whose rows sees a key of its split (one wave per item only):
+// then nothing is computed or stored.  end_walk() (bf16 walks): called on every path once every
+// load of the walk has been consumed, before the stores (see attn_split_persist_kernel).
+template <int D, int NT, bool RELOAD, int NW, bool I8, typename EndWalk>
+__device__ __forceinline__ void run_item(const AttnArgs& a, const Item& it, bool keys, int wave,
+                                         int wb, int we, int ids0, int ids1, EndWalk&& end_walk) {
   constexpr int KK = D / 32;  // 32-dim steps of the score product
   constexpr int MT = D / 16;  // 16-dim tiles of the output
   const int lane = threadIdx.x & (WAVE - 1);
@@ -172,7 +239,7 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, const Item& it, int 
   const int G = a.group;
   const int rows = T * G;
   const int r0 = it.rt * 16 * NT;
-  const int nch = wb < we ? (we - wb + 31) >> 5 : 0;
+  const int nch = keys && wb < we ? (we - wb + 31) >> 5 : 0;
   const int ntile = wb < we ? (we - wb + 15) >> 4 : 0;
   const int tile0 = wb >> 4;
   const uint16_t* kl = reinterpret_cast<const uint16_t*>(a.k_layer);
@@ -187,10 +254,7 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, const Item& it, int 
       ids0 = tile_block_id(a, s, wb, ntile, it.ke, tb, it.vs1, it.vshift);
       ids1 = tile_block_id(a, s, wb, ntile, it.ke, tb + 64, it.vs1, it.vshift);
     }
-    const int r = ti - tb;
-    const int blk = r < 64 ? __builtin_amdgcn_readlane(ids0, r) : __builtin_amdgcn_readlane(ids1, r - 64);
-    const int sub = (real_key((tile0 + ti) << 4, it.vs1, it.vshift) & bmask) >> 4;
-    return block_tile_offset(blk, sub, kvh, a.block_shift, a.num_blocks, a.num_kv_heads, D);
+    return walk_tile_off<D>(a, kvh, tile0, ntile, it.vs1, it.vshift, ids0, ids1, tb, ti);
   };
   auto load_chunk = [&](Chunk<D, I8>& c, int ci) {
     const size_t o0 = tile_off(2 * ci), o1 = tile_off(2 * ci + 1);
@@ -218,15 +282,7 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, const Item& it, int 
         c.vs[h] = __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(rvs, 16 * g, 0, 0));
       }
     } else {
-      const uint16_t* kt[2] = {kl + o0, kl + o1};
-      const uint16_t* vt[2] = {vl + o0, vl + o1};
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-#pragma unroll
-        for (int kk = 0; kk < KK; ++kk) c.k[h][kk] = stream16(kt[h] + ((4 * kk + g) * 16 + n) * 8);
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) c.v[h][mt] = stream8(vt[h] + (16 * mt + n) * 16 + 4 * g);
-      }
+      load_chunk_bf16<D>(a, c, o0, o1);
     }
   };
 
@@ -243,6 +299,7 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, const Item& it, int 
   // pools: dims 16*(4*(kk/2) + g) + 8*(kk%2) .. +8, the order of the K chunks it meets).
   const int Hq = a.num_q_heads;
   bf16x8 qb[NT][KK];
+  load_q<D, NT, I8>(a, it, qb);
   int prow[NT];   // the row's real key position (-1: padding row)
   int vprow[NT];  // its virtual position in the sequence's key layout
   int wlo[NT];    // sparse row: keys <= wlo (and >= the sink) are not seen; else -1
@@ -250,21 +307,11 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, const Item& it, int 
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     const int r = r0 + 16 * nt + n;
-    const int i = r / G;
-    const int grow = q_start + i;
-    const bool valid = r < rows && grow < a.total_q;
-    prow[nt] = valid ? L - T + i : -1;
+    const bool valid = item_row(a, it, r, rh[nt]);
+    prow[nt] = valid ? L - T + r / G : -1;
     vprow[nt] = virt_key(prow[nt], it.vs1, it.vshift);
     wlo[nt] = (valid && a.sparse_window > 0 && prow[nt] + 1 >= a.sparse_min)
                   ? prow[nt] - a.sparse_window : -1;
-    rh[nt] = valid ? (size_t)grow * Hq + kvh * G + r % G : 0;
-    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + rh[nt] * D;
-#pragma unroll
-    for (int kk = 0; kk < KK; ++kk) {
-      bf16x8 z = {};
-      const int d0 = I8 ? 16 * (4 * (kk >> 1) + g) + 8 * (kk & 1) : 32 * kk + 8 * g;
-      qb[nt][kk] = valid ? load16(qp + d0) : z;
-    }
   }
 
   // int8 pools: the q row as a 15-bit fixed-point value with a per-row power-of-two scale,
@@ -489,7 +536,14 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, const Item& it, int 
     } else if (ci < nch) {
       compute(bufA, ci);
     }
+    // Every load of the walk has been consumed.  With 32-row tiles, saying so here and having
+    // end_walk read the next item's block ids (loaded before this item's chunks) tells the
+    // compiler they have arrived, so the next item does not wait for them, and behind them for
+    // the stores below, before its first loads.
+    if constexpr (NT == 2) __builtin_amdgcn_s_waitcnt(0x0F70);
+    end_walk();
   }
+  if (!keys) return;  // wave-uniform
 
   // Adds to a row's output index (q_start + i) * Hq + head to give its partial row index
   // (p_start + i) * Hq + head (modulo 2^64: the sum is never negative).
@@ -676,7 +730,9 @@ __device__ __forceinline__ bool find_item(const AttnArgs& a, SeqGroup& gp, int t
 
 // Wave w of W takes items w, w + W, w + 2W, ... in increasing order.  W is what the GPU holds at
 // once, so all waves start together; a wave's next item is known in advance, and its block ids
-// are loaded before the current item's chunks.
+// are loaded before the current item's chunks.  (Holding the next item's first chunk in
+// registers across an item's end does not fit the 256 registers of two waves per SIMD: the
+// compiler spills.)
 // Two waves per SIMD for bf16 decode (NT = 1, up to 256 registers); the int8 variants convert
 // codes to bf16 in registers and need more, so they run one wave per SIMD.
 template <int D, int NT, bool I8>
@@ -698,9 +754,22 @@ void attn_split_persist_kernel(AttnArgs a) {
     ids0 = tile_block_id(a, cur.s, cur.kb, nt, cur.ke, 0, cur.vs1, cur.vshift);
     ids1 = tile_block_id(a, cur.s, cur.kb, nt, cur.ke, 64, cur.vs1, cur.vshift);
   }
+  // Block ids at item starts (32-row tiles).  The compiler tracks loads per register and, where
+  // paths merge, assumes the worst: the ids copied in at the loop's end look outstanding at the
+  // next item's first block-id read, which then waits for every older memory operation, the
+  // next item's own id loads and the last item's stores included (a full memory latency per
+  // item).  Waiting for the first item's ids here and marking the next item's ids as arrived
+  // at the end of each walk (run_item) removes that wait: verification of 4 drafts over 32K
+  // keys, one item per wave, measured 34.7 -> 32 us.  With 16-row tiles (two waves per SIMD,
+  // where the other wave covers the wait) the same change measured about 1% slower, so it is
+  // left out there.
+  if constexpr (NT == 2) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    asm volatile("" ::"v"(ids0), "v"(ids1));
+  }
   while (have) {
     t += W;
-    Item nxt;
+    Item nxt = cur;
     const bool nhave = t < (1 << 30) && find_item<NT>(a, gp, t, nxt);
     const bool nkeys = nhave && item_keys<NT>(a, nxt);
     // Unconditional loads (the current item's ids again when there is no next item), so that
@@ -713,7 +782,9 @@ void attn_split_persist_kernel(AttnArgs a) {
     const int pt = (pe - pb + 15) >> 4;
     const int nid0 = tile_block_id(a, ps, pb, pt, pe, 0, pv1, pvs);
     const int nid1 = tile_block_id(a, ps, pb, pt, pe, 64, pv1, pvs);
-    if (cur_keys) run_item<D, NT, false, 1, I8>(a, cur, 0, cur.kb, cur.ke, ids0, ids1);
+    run_item<D, NT, false, 1, I8>(a, cur, cur_keys, 0, cur.kb, cur.ke, ids0, ids1, [&]() {
+      if constexpr (NT == 2) asm volatile("" ::"v"(nid0), "v"(nid1));
+    });
     if (!nhave) break;
     cur = nxt;
     cur_keys = nkeys;
@@ -746,7 +817,7 @@ __global__ __launch_bounds__(256) void attn_split_mfma_kernel(AttnArgs a) {
   // vmcnt(0) (encoding: vmcnt 0, expcnt 7, lgkmcnt 15), so the compiler knows the block ids
   // have arrived and never waits for them inside the chunk loop.
   __builtin_amdgcn_s_waitcnt(0x0F70);
-  run_item<D, NT, RELOAD, 4, I8>(a, it, wave, wb, we, ids0, ids1);
+  run_item<D, NT, RELOAD, 4, I8>(a, it, true, wave, wb, we, ids0, ids1, []() {});
 }
 
 namespace {

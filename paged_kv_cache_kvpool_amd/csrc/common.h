@@ -251,13 +251,19 @@ __device__ __forceinline__ void seq_starts(const AttnArgs& a, int s, int& q_star
 // sequence order), and the sequence's first row in q / out.  False if r is past the last one.
 // Wave-uniform; the whole wave must be active.
 __device__ __forceinline__ bool find_split_row(const AttnArgs& a, int r, int& s, int& i,
-                                               int& q_start) {
+                                               int& q_start, int& L, int& T) {
   const int lane = threadIdx.x & (WAVE - 1);
   int pbase = 0, qbase = 0;
   for (int base = 0; base < a.num_seqs; base += WAVE) {
     const int j = base + lane;
-    const int pr = j < a.num_seqs ? split_rows_of(a, j) : 0;
-    const int q = j < a.num_seqs ? max(0, a.q_lens[j]) : 0;
+    int Lj = 0, Tj = 0, q = 0;
+    if (j < a.num_seqs) {  // seq_lens(a, j, Lj, Tj), reading q_lens[j] once
+      const int ql = a.q_lens[j];
+      Lj = min(max(a.ctx_lens[j], 0), a.max_blocks_per_seq * a.block_size);
+      Tj = min(max(ql, 0), Lj);
+      q = max(0, ql);
+    }
+    const int pr = Tj <= a.split_q_max ? Tj : 0;  // split_rows_of(a, j)
     const int pin = wave_incl_scan(pr);
     const int qin = wave_incl_scan(q);
     const int ptot = __builtin_amdgcn_readlane(pin, WAVE - 1);
@@ -268,12 +274,19 @@ __device__ __forceinline__ bool find_split_row(const AttnArgs& a, int r, int& s,
       s = base + k;
       i = rr - (__builtin_amdgcn_readlane(pin, k) - __builtin_amdgcn_readlane(pr, k));
       q_start = qbase + __builtin_amdgcn_readlane(qin, k) - __builtin_amdgcn_readlane(q, k);
+      L = __builtin_amdgcn_readlane(Lj, k);
+      T = __builtin_amdgcn_readlane(Tj, k);
       return true;
     }
     pbase += ptot;
     qbase += __builtin_amdgcn_readlane(qin, WAVE - 1);
   }
   return false;
+}
+__device__ __forceinline__ bool find_split_row(const AttnArgs& a, int r, int& s, int& i,
+                                               int& q_start) {
+  int L, T;
+  return find_split_row(a, r, s, i, q_start, L, T);
 }
 
 // Element offset of the 16-token tile holding logical position `pos` of sequence s for KV head
