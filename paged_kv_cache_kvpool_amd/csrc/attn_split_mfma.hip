@@ -240,7 +240,7 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, const Item& it, bool
   const int rows = T * G;
   const int r0 = it.rt * 16 * NT;
   const int nch = keys && wb < we ? (we - wb + 31) >> 5 : 0;
-  const int ntile = wb < we ? (we - wb + 15) >> 4 : 0;
+  const int ntile = keys && wb < we ? (we - wb + 15) >> 4 : 0;
   const int tile0 = wb >> 4;
   const uint16_t* kl = reinterpret_cast<const uint16_t*>(a.k_layer);
   const uint16_t* vl = reinterpret_cast<const uint16_t*>(a.v_layer);
@@ -288,11 +288,11 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, const Item& it, bool
 
   // int8: a ring of four chunks, three in flight while one is computed (a chunk is half the
   // bytes, and the wave runs alone on its SIMD, so it needs more chunks in flight to keep as
-  // many bytes coming); the ring is filled after the Q loads, so that waiting for Q never waits
-  // for the ring.  bf16: two buffers, chunk i+1 in flight while chunk i is computed (a ring
-  // measured slower there).
+  // many bytes coming); the ring is filled right after the Q loads, before Q is converted, so
+  // that the wait for Q has three chunks in flight behind it and never waits for them.  bf16:
+  // two buffers, chunk i+1 in flight while chunk i is computed (a ring measured slower there).
   constexpr bool RING = I8;
-  Chunk<D, I8> bufA, bufB;
+  Chunk<D, I8> bufA, bufB, bufC, bufD;
   if (!RING && nch) load_chunk(bufA, 0);
 
   // Q^T as the B operand: lane (n, g) holds row n of N-tile nt, dims 32*kk + 8*g .. +8 (int8
@@ -300,6 +300,13 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, const Item& it, bool
   const int Hq = a.num_q_heads;
   bf16x8 qb[NT][KK];
   load_q<D, NT, I8>(a, it, qb);
+  if constexpr (RING) {
+    // Unconditional (a wave without keys has ntile = 0: zero-size loads that fetch nothing), so
+    // the compiler's count of loads in flight is exact at the wait for Q.
+    load_chunk(bufA, 0);
+    load_chunk(bufB, 1);
+    load_chunk(bufC, 2);
+  }
   int prow[NT];   // the row's real key position (-1: padding row)
   int vprow[NT];  // its virtual position in the sequence's key layout
   int wlo[NT];    // sparse row: keys <= wlo (and >= the sink) are not seen; else -1
@@ -499,10 +506,6 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, const Item& it, bool
     // (nothing is fetched) and never computed, so every load is unconditional and the waits
     // before each compute are static.
     if (nch) {
-      Chunk<D, I8> bufC, bufD;
-      load_chunk(bufA, 0);
-      load_chunk(bufB, 1);
-      load_chunk(bufC, 2);
       for (int ci = 0;; ci += 4) {
         load_chunk(bufD, ci + 3);
         compute(bufA, ci);
@@ -518,6 +521,10 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, const Item& it, bool
         if (ci + 4 >= nch) break;
       }
     }
+    // Only the ring's loads past the end (zero-size) may be outstanding: as in the bf16 walk
+    // below, this lets the next item start without waiting for its ids behind the stores.
+    __builtin_amdgcn_s_waitcnt(0x0F70);
+    end_walk();
   } else {
     // Double-buffered walk: the loads of chunk i+1 are issued before chunk i is computed.  The
     // last one or two chunks are peeled off, so that no load is left in flight after the walk
@@ -763,7 +770,7 @@ void attn_split_persist_kernel(AttnArgs a) {
   // keys, one item per wave, measured 34.7 -> 32 us.  With 16-row tiles (two waves per SIMD,
   // where the other wave covers the wait) the same change measured about 1% slower, so it is
   // left out there.
-  if constexpr (NT == 2) {
+  if constexpr (NT == 2 || I8) {
     __builtin_amdgcn_s_waitcnt(0x0F70);
     asm volatile("" ::"v"(ids0), "v"(ids1));
   }
@@ -783,7 +790,7 @@ void attn_split_persist_kernel(AttnArgs a) {
     const int nid0 = tile_block_id(a, ps, pb, pt, pe, 0, pv1, pvs);
     const int nid1 = tile_block_id(a, ps, pb, pt, pe, 64, pv1, pvs);
     run_item<D, NT, false, 1, I8>(a, cur, cur_keys, 0, cur.kb, cur.ke, ids0, ids1, [&]() {
-      if constexpr (NT == 2) asm volatile("" ::"v"(nid0), "v"(nid1));
+      if constexpr (NT == 2 || I8) asm volatile("" ::"v"(nid0), "v"(nid1));
     });
     if (!nhave) break;
     cur = nxt;
