@@ -286,13 +286,18 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, const Item& it, bool
     }
   };
 
-  // int8: a ring of four chunks, three in flight while one is computed (a chunk is half the
-  // bytes, and the wave runs alone on its SIMD, so it needs more chunks in flight to keep as
-  // many bytes coming); the ring is filled right after the Q loads, before Q is converted, so
-  // that the wait for Q has three chunks in flight behind it and never waits for them.  bf16:
-  // two buffers, chunk i+1 in flight while chunk i is computed (a ring measured slower there).
+  // int8: a ring of RN chunks, RN - 1 in flight while one is computed.  16-row tiles: three,
+  // at two waves per SIMD (250 registers); 32-row tiles: four, at one wave per SIMD (a chunk
+  // is half the bytes, so the lone wave needs more of them in flight).  Measured on batched
+  // decode: ring of three at two waves per SIMD 71 us, ring of four at one wave 81 us, ring of
+  // six at one wave 90 us (each item ends with RN - 1 chunks of zero-size loads).  The ring is
+  // filled right after the Q loads, before Q is converted, so that the wait for Q has the ring
+  // in flight behind it and never waits for it.  bf16: two buffers, chunk i+1 in flight while
+  // chunk i is computed (a ring measured slower there).
   constexpr bool RING = I8;
-  Chunk<D, I8> bufA, bufB, bufC, bufD;
+  constexpr int RN = NT == 1 ? 3 : 4;
+  Chunk<D, I8> bufA, bufB;
+  Chunk<D, I8> rb[RING ? RN : 1];
   if (!RING && nch) load_chunk(bufA, 0);
 
   // Q^T as the B operand: lane (n, g) holds row n of N-tile nt, dims 32*kk + 8*g .. +8 (int8
@@ -303,9 +308,8 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, const Item& it, bool
   if constexpr (RING) {
     // Unconditional (a wave without keys has ntile = 0: zero-size loads that fetch nothing), so
     // the compiler's count of loads in flight is exact at the wait for Q.
-    load_chunk(bufA, 0);
-    load_chunk(bufB, 1);
-    load_chunk(bufC, 2);
+#pragma unroll
+    for (int j = 0; j + 1 < RN; ++j) load_chunk(rb[j], j);
   }
   int prow[NT];   // the row's real key position (-1: padding row)
   int vprow[NT];  // its virtual position in the sequence's key layout
@@ -502,23 +506,23 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, const Item& it, bool
   };
 
   if constexpr (RING) {
-    // Ring of four.  Loads past the last chunk are issued with zero-size buffer resources
-    // (nothing is fetched) and never computed, so every load is unconditional and the waits
-    // before each compute are static.
+    // Chunk ci sits in rb[ci % RN]; chunk ci + RN - 1 goes into the slot chunk ci - 1 left,
+    // before chunk ci is computed.  Loads past the last chunk are issued with zero-size buffer
+    // resources (nothing is fetched) and never computed, so every load is unconditional and the
+    // waits before each compute are static.
     if (nch) {
-      for (int ci = 0;; ci += 4) {
-        load_chunk(bufD, ci + 3);
-        compute(bufA, ci);
-        if (ci + 1 >= nch) break;
-        load_chunk(bufA, ci + 4);
-        compute(bufB, ci + 1);
-        if (ci + 2 >= nch) break;
-        load_chunk(bufB, ci + 5);
-        compute(bufC, ci + 2);
-        if (ci + 3 >= nch) break;
-        load_chunk(bufC, ci + 6);
-        compute(bufD, ci + 3);
-        if (ci + 4 >= nch) break;
+      for (int ci = 0;; ci += RN) {
+        bool done = false;
+#pragma unroll
+        for (int j = 0; j < RN; ++j) {
+          load_chunk(rb[(j + RN - 1) % RN], ci + j + RN - 1);
+          compute(rb[j], ci + j);
+          if (ci + j + 1 >= nch) {
+            done = true;
+            break;
+          }
+        }
+        if (done) break;
       }
     }
     // Only the ring's loads past the end (zero-size) may be outstanding: as in the bf16 walk
@@ -740,10 +744,9 @@ __device__ __forceinline__ bool find_item(const AttnArgs& a, SeqGroup& gp, int t
 // are loaded before the current item's chunks.  (Holding the next item's first chunk in
 // registers across an item's end does not fit the 256 registers of two waves per SIMD: the
 // compiler spills.)
-// Two waves per SIMD for bf16 decode (NT = 1, up to 256 registers); the int8 variants convert
-// codes to bf16 in registers and need more, so they run one wave per SIMD.
+// Two waves per SIMD for 16-row tiles (NT = 1, up to 256 registers), one for 32-row tiles.
 template <int D, int NT, bool I8>
-__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu((NT == 1 && !I8) ? 2 : 1)))
+__global__ __launch_bounds__(64) __attribute__((amdgpu_waves_per_eu(NT == 1 ? 2 : 1)))
 void attn_split_persist_kernel(AttnArgs a) {
   const int W = gridDim.x;
   SeqGroup gp;
