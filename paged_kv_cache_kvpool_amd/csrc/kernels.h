@@ -90,7 +90,7 @@ void prefill_plan(const int* rows, int n, int num_kv_heads, int num_cus, bool wh
                   int* waves, int* rblk);
 // Prefill over an int8 pool: the prefill-class sequences' tiles dequantized to bf16 into a
 // workspace pool (max_seqs sequences of blocks_per_seq 16-token blocks) and its block table
-// [num_seqs][blocks_per_seq]; wgs >= the (sequence, KV head, tile) count (extra ones exit).
+// [num_seqs][blocks_per_seq]; the grid covers max_seqs sequences of blocks_per_seq tiles.
 struct DequantOut {
   uint16_t* k;
   uint16_t* v;
@@ -99,7 +99,7 @@ struct DequantOut {
   int32_t max_seqs;
 };
 hipError_t launch_dequant_prefill(const AttnArgs& a, const DequantOut& o, int head_dim,
-                                  long long wgs, hipStream_t st);
+                                  hipStream_t st);
 // Cross-split merge of the split-K partials: one workgroup per (partial row, q-head).
 hipError_t launch_attn_reduce(const AttnArgs& a, int elt_bytes, int head_dim, hipStream_t st);
 

@@ -679,8 +679,7 @@ int forward_impl(kvpool_t* pool, int32_t layer, const void* q, void* out, int32_
         dq.tables = reinterpret_cast<int32_t*>(ws + pl.dq_tbl_off);
         dq.blocks_per_seq = pl.dq_mpb;
         dq.max_seqs = pl.dq_seqs;
-        const long long wgs = (long long)pl.dq_seqs * pool->num_kv_heads * pl.dq_mpb;
-        e = timed(K_DEQUANT, st, [&] { return kvp::launch_dequant_prefill(a, dq, pool->head_dim, wgs, st); });
+        e = timed(K_DEQUANT, st, [&] { return kvp::launch_dequant_prefill(a, dq, pool->head_dim, st); });
         ap.k_layer = dq.k;
         ap.v_layer = dq.v;
         ap.block_tables = dq.tables;
