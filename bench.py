@@ -53,6 +53,9 @@ WORKLOADS["sparse_decode"] = dict(
 WORKLOADS["long_decode_sparse"] = dict(
     kind="hbm", desc="2 seqs x 1 token at 262144 and 131072, 40/8 heads, D=128, bf16; sink + window "
                      "sparse (first 16 + last 4096 keys)")
+WORKLOADS["long_prefix_chunk"] = dict(
+    kind="mfma", desc="1 seq x (32768 cached + 512 new causal): one chunked-prefill step of a long "
+                      "prompt, 40/8 heads, D=128, bf16")
 WORKLOADS["park_restore"] = dict(
     kind="pcie", desc="16 seqs x 4096 tokens sharing a 2048-token prefix (recomputed into separate "
                       "blocks), 8 layers, 8 KV heads, D=128, bf16, B=16 (512 KiB pages): park every "
@@ -100,6 +103,8 @@ def make_workload(name):
         return wl.long_decode(host_pool=False)
     if name == "mixed_step":
         return wl.mixed_step(host_pool=False)
+    if name == "long_prefix_chunk":
+        return wl.long_prefix_chunk(host_pool=False)
     raise SystemExit(f"unknown workload {name}")
 
 

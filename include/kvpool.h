@@ -165,10 +165,12 @@ KVPOOL_API int kvattn_workspace_size(const kvpool_t *pool, int32_t num_q_heads,
  * kernel.  Decode and verification sequences: the path and the arithmetic follow from the
  * sequence's own lengths, so their output bits never depend on the rest of the batch or on the
  * bounds passed here.  Prefill-class sequences: the workgroup plan follows the call (for speed,
- * a row block may be split between two waves whose partial results are merged), so their bits
- * may differ from batch to batch, within the same tolerance; with the environment variable
- * KVATTN_DETERMINISTIC=1 every row block is reduced by one wave in key order and their bits,
- * too, depend on the sequence alone (the pages' servers likewise offer bit-reproducible,
+ * a row block may be split between two waves whose partial results are merged, and when the
+ * call's prefill row tiles leave CUs idle each row tile's keys are cut into ranges whose
+ * partials a second launch merges in range order), so their bits may differ from batch to
+ * batch, within the same tolerance; with the environment variable KVATTN_DETERMINISTIC=1
+ * every row block is reduced by one wave in key order and their bits, too, depend on the
+ * sequence alone (the pages' servers likewise offer bit-reproducible,
  * batch-invariant output as a mode that costs prefill time: sparkinfer server README,
  * "Determinism").
  *   q    device, [total_q][num_q_heads][head_dim], pool dtype (bf16 for an int8 pool), rows

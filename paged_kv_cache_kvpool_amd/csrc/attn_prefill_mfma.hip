@@ -23,6 +23,10 @@
 //   O^T[dim][row] += V^T . P^T   2 k-steps x D/32 MFMAs
 // The logical workgroup order is remapped so that the row tiles of one (sequence, KV head) run
 // on the same XCD (workgroups are dealt to the 8 XCDs round-robin) and share its L2.
+// When the row tiles alone leave CUs idle (a single prefill chunk, or one beside decode rows),
+// each row tile's keys are cut into pf_ksplit ranges of whole 64-key tiles, one workgroup per
+// range; such a workgroup stores its rows' unnormalised partials, merged in range order by
+// attn_reduce_prefill (as split-K decode merges its splits).
 #include <algorithm>
 
 #include "common.h"
@@ -227,11 +231,18 @@ void attn_prefill_mfma_kernel(AttnArgs a) {
   const bool half = wave >= F;
   const int rb = half ? F + ((wave - F) >> 1) : wave;  // the wave's row block in the workgroup
   const int par = half ? ((wave - F) & 1) : 0;          // half waves: parity of their blocks
-  const int n_wg = prefill_wg_total(a, R);
+  const int NKR = a.pf_ksplit;  // key ranges per row tile
+  const int n_base = prefill_wg_total(a, R);  // row tiles of every (sequence, KV head)
+  const int n_wg = n_base * NKR;
   if ((int)blockIdx.x >= n_wg) return;
+  // logical = key range * n_base + row tile: the row tiles of one key range of a (sequence, KV
+  // head) stay next to each other, on one XCD
   const int logical = xcd_logical(blockIdx.x, n_wg);
+  // (wave-uniform values from divisions come out of vector registers: readfirstlane keeps them
+  // in scalar ones, as the register budget of three waves per SIMD needs)
+  const int kj = __builtin_amdgcn_readfirstlane(logical / n_base);
   int s, kvh, rt, rts, q_start;
-  find_prefill_tile(a, logical, R, s, kvh, rt, rts, q_start);
+  find_prefill_tile(a, logical - kj * n_base, R, s, kvh, rt, rts, q_start);
   int L, T;
   seq_lens(a, s, L, T);
   // wave-uniform: kept in scalar registers so the per-block edge tests stay on the SALU
@@ -245,11 +256,20 @@ void attn_prefill_mfma_kernel(AttnArgs a) {
   const int nblk = (rows + 31) >> 5;
   if (rt >= nblk) return;
   const int last_blk = rt + rts * min(R - 1, (nblk - 1 - rt) / rts);
-  const int ke = min(L, L - T + (min(32 * last_blk + 32, rows) - 1) / G + 1);  // keys the WG needs
+  const int ke = __builtin_amdgcn_readfirstlane(
+      min(L, L - T + (min(32 * last_blk + 32, rows) - 1) / G + 1));  // keys the WG needs
   const int ntiles = (ke + 63) >> 6;
   const int npt = (ke + 15) >> 4;  // pool tiles the WG reads
+  // This workgroup's 64-key tiles [jt0, jt1): key range kj of the sequence's tiles (the same cut
+  // for every row tile), within the tiles the workgroup needs.  An empty range still stores
+  // (empty) partials for its rows.
+  const int tpk = __builtin_amdgcn_readfirstlane((((L + 63) >> 6) + NKR - 1) / NKR);
+  const int jt0 = __builtin_amdgcn_readfirstlane(min(kj * tpk, ntiles));
+  const int jt1 = __builtin_amdgcn_readfirstlane(min(jt0 + tpk, ntiles));
   const int rw0 = 32 * (rt + rts * rb);
-  const int kew = __builtin_amdgcn_readfirstlane(rw0 < rows ? min(L, L - T + (min(rw0 + 32, rows) - 1) / G + 1) : 0);
+  // the wave's keys end at the last key its rows see, and at the range's end
+  const int kew = __builtin_amdgcn_readfirstlane(
+      rw0 < rows ? min(64 * jt1, min(L, L - T + (min(rw0 + 32, rows) - 1) / G + 1)) : 0);
   const int pw0 = __builtin_amdgcn_readfirstlane(L - T + rw0 / G);  // keys <= pw0: visible to every row of the wave
 
   const int32_t* tbl = a.block_tables + (size_t)s * a.max_blocks_per_seq;
@@ -258,14 +278,17 @@ void attn_prefill_mfma_kernel(AttnArgs a) {
   const int bmask = a.block_size - 1;
 
   // Block ids of pool tiles [ids0, ids0 + IDS) of this sequence, in LDS.
-  int ids0 = 0;
   auto load_ids = [&](int base) {
     for (int i = tid; i < IDS; i += blockDim.x) {
       const int pt = min(base + i, npt - 1);
       s_ids[i] = tbl[(pt << 4) >> a.block_shift];
     }
   };
-  load_ids(0);
+  // Fetches are clamped into [jb, jlast] (for an empty range: its base tile, never computed).
+  const int jb = __builtin_amdgcn_readfirstlane(min(jt0, ntiles - 1));
+  const int jlast = __builtin_amdgcn_readfirstlane(max(min(jt1, ntiles) - 1, jb));
+  int ids0 = 4 * jb;
+  load_ids(ids0);
   __syncthreads();
 
   // ---- K/V staging: the 8 pool tiles of a stage ([K0..K3, V0..V3] of a 64-key tile) are dealt
@@ -308,9 +331,9 @@ void attn_prefill_mfma_kernel(AttnArgs a) {
   };
   // Three tiles in flight from the start (clamped: a short context re-reads its last tile, so
   // every wave's count of outstanding pieces follows the same pattern).
-  fetch(0, read_ids(0), lds0);
-  fetch(min(1, ntiles - 1), read_ids(min(1, ntiles - 1)), lds1);
-  fetch(min(2, ntiles - 1), read_ids(min(2, ntiles - 1)), lds2);
+  fetch(jb, read_ids(jb), lds0);
+  fetch(min(jt0 + 1, jlast), read_ids(min(jt0 + 1, jlast)), lds1);
+  fetch(min(jt0 + 2, jlast), read_ids(min(jt0 + 2, jlast)), lds2);
 
   // ---- Q^T operands and per-row state ----------------------------------------------------
   // B operand of k-step k: lane (col, h) holds dims 16k + 8h .. +8 of the wave's row col.
@@ -370,8 +393,8 @@ void attn_prefill_mfma_kernel(AttnArgs a) {
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this thread's LDS writes are done
     barrier_no_fence();
   };
-  zero_tail(lds0, 0);
-  zero_tail(lds1, 1);
+  zero_tail(lds0, jt0);
+  zero_tail(lds1, jt0 + 1);
 
   // Attention of this wave's 32 rows against one 32-key block (pool tiles 2b, 2b+1 of the
   // stage).  `edge`: the block reaches past the wave's first row (causal diagonal) or past the
@@ -490,7 +513,8 @@ void attn_prefill_mfma_kernel(AttnArgs a) {
     }
     sc = sn;
   };
-  if (kew > 0) sc = qk(lds0, par);  // the wave's first block: 0, or 1 for an odd half wave
+  // the wave's first block: the range's first, or its second for an odd half wave
+  if (kew > 64 * jt0) sc = qk(lds0, par);
 
   // One 64-key tile j (stage `cur`): tile j+3 starts streaming into `nxt3` (free: its last
   // reader, tile j-1, was done before the barrier that ended the previous step); the blocks of
@@ -500,7 +524,7 @@ void attn_prefill_mfma_kernel(AttnArgs a) {
                   uint16_t (&nxt3)[8][TE]) {
     // the ids of tile j+3; refill the id cache first when they lie past it (rare: only past
     // 16K keys; workgroup-uniform)
-    const int jf = min(j + 3, ntiles - 1);
+    const int jf = min(j + 3, jlast);
     if (4 * jf + 3 - ids0 >= IDS) {
       __syncthreads();
       ids0 = 4 * jf;
@@ -518,11 +542,11 @@ void attn_prefill_mfma_kernel(AttnArgs a) {
     barrier_no_fence();
     zero_tail(nxt2, j + 2);
   };
-  for (int j = 0; j < ntiles; j += 4) {
+  for (int j = jt0; j < jt1; j += 4) {
     step(j, lds0, lds1, lds2, lds3);
-    if (j + 1 < ntiles) step(j + 1, lds1, lds2, lds3, lds0);
-    if (j + 2 < ntiles) step(j + 2, lds2, lds3, lds0, lds1);
-    if (j + 3 < ntiles) step(j + 3, lds3, lds0, lds1, lds2);
+    if (j + 1 < jt1) step(j + 1, lds1, lds2, lds3, lds0);
+    if (j + 2 < jt1) step(j + 2, lds2, lds3, lds0, lds1);
+    if (j + 3 < jt1) step(j + 3, lds3, lds0, lds1, lds2);
   }
   // The last steps re-read the last tile into free stages: drain those loads before the stages
   // are reused below or the workgroup's LDS is released.
@@ -549,14 +573,16 @@ void attn_prefill_mfma_kernel(AttnArgs a) {
     if (half && par == 0) {
       const float m1 = ml[lane], l1 = ml[64 + lane];
       const float mm = __builtin_elementwise_maximum(msub, m1);
-      // the even wave always holds a row's key 0, so mm is finite; a1 = 0 for a row with no key
-      // in the odd wave's blocks (whose o and l are then 0)
-      const float a0 = fast_exp2(msub - mm), a1 = fast_exp2(m1 - mm);
+      // a wave with no key of the row (msub or m1 = -inf, its o and l 0) weighs 0; under key
+      // ranges neither wave may have one (mm = -inf: the row's partial stays empty)
+      const float a0 = msub == -INFINITY ? 0.f : fast_exp2(msub - mm);
+      const float a1 = m1 == -INFINITY ? 0.f : fast_exp2(m1 - mm);
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) o[mb][e] = o[mb][e] * a0 + ob[(16 * mb + e) * 64 + lane] * a1;
       l_lane = l_lane * a0 + l1 * a1;
+      msub = mm;
     }
   }
 
@@ -565,7 +591,21 @@ void attn_prefill_mfma_kernel(AttnArgs a) {
     float x, y;
     swap32(l_lane, x, y);
     const float lrow = x + y;
-    if (valid && !(half && par == 1)) {  // a half pair's even wave stores the merged rows
+    if (NKR > 1) {
+      // key range kj of a split row tile: the row's unnormalised partial, relative to its max
+      // (exp2 units; -inf when the range holds none of the row's keys)
+      if (valid && !(half && par == 1)) {
+        const size_t slot = row_index() * NKR + kj;
+        float* po = a.pf_part_o + slot * D + 4 * h;
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            *reinterpret_cast<floatx4*>(po + 32 * mb + 8 * q) =
+                floatx4{o[mb][4 * q], o[mb][4 * q + 1], o[mb][4 * q + 2], o[mb][4 * q + 3]};
+        if (h == 0) *reinterpret_cast<float2*>(a.pf_part_ml + 2 * slot) = make_float2(msub, lrow);
+      }
+    } else if (valid && !(half && par == 1)) {  // a half pair's even wave stores the merged rows
       const float inv = 1.f / lrow;
       uint16_t* op = reinterpret_cast<uint16_t*>(a.out) + row_index() * D + 4 * h;
 #pragma unroll
@@ -629,13 +669,37 @@ void prefill_plan(const int* rows, int n, int num_kv_heads, int num_cus, bool wh
   *rblk = br;
 }
 
+int prefill_ksplit(long long wgs, int num_cus, int max_ctx, bool deterministic) {
+  // Cost in 64-key tile times (measured on MI355X: a workgroup over n tiles takes about n + 8.5
+  // of them, the 8.5 being its start and drain; the merge launch about 7): k ranges make
+  // rounds(k) = ceil(k wgs / CUs) rounds of workgroups over n/k tiles each.  A 512-token chunk
+  // over a 32K prefix (160 workgroups of 520 tiles) measured 598 us at k = 1, 442 us at k = 3;
+  // over a 4K prefix (72 tiles) k = 3 and k = 1 measured the same.
+  if (deterministic || wgs <= 0 || num_cus <= 0) return 1;
+  const double n = (double)((max_ctx + 63) / 64);
+  const int kmax = std::max(1, std::min(8, (int)(n / 4)));
+  int best_k = 1;
+  double best = n + 8.5;
+  for (int k = 2; k <= kmax; ++k) {
+    const long long rounds = (wgs * k + num_cus - 1) / num_cus;
+    const double cost = (double)rounds * (n / k + 8.5) + 7.0;
+    if (cost < best - 1e-9) {
+      best = cost;
+      best_k = k;
+    }
+  }
+  return best_k;
+}
+
 hipError_t launch_attn_prefill_mfma(const AttnArgs& a, int head_dim, int waves, long long wgs,
                                     hipStream_t st) {
   if (waves < 1 || waves > 12 || wgs < 0 || wgs > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   // R row blocks with W/2 <= R <= W; at most 6 half pairs (their merge uses 3 stage arrays)
   if (2 * a.pf_rblk < waves || a.pf_rblk > waves || waves - a.pf_rblk > 6) return hipErrorInvalidConfiguration;
   if (wgs == 0) return hipSuccess;
-  const dim3 grid((unsigned)wgs);
+  if (a.pf_ksplit < 1 || a.pf_ksplit > 8 || wgs * a.pf_ksplit > 0x7fffffffLL)
+    return hipErrorInvalidConfiguration;
+  const dim3 grid((unsigned)(wgs * a.pf_ksplit));
   if (head_dim == 128)
     attn_prefill_mfma_kernel<128><<<grid, 64 * waves, 0, st>>>(a);
   else

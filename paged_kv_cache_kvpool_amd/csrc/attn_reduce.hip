@@ -100,6 +100,109 @@ __global__ __launch_bounds__(256) void attn_reduce_kernel(AttnArgs a) {
   }
 }
 
+// ---- prefill key ranges ----------------------------------------------------------------
+// Sequence s of query token grow (q_lens prefix sums, 64 sequences per step), the token's index
+// i in it and the sequence's lengths.  False past the last token.
+__device__ __forceinline__ bool find_token(const AttnArgs& a, int grow, int& s, int& i, int& L,
+                                           int& T) {
+  const int lane = threadIdx.x & (WAVE - 1);
+  int qbase = 0;
+  for (int base = 0; base < a.num_seqs; base += WAVE) {
+    const int j = base + lane;
+    int Lj = 0, Tj = 0, q = 0;
+    if (j < a.num_seqs) {
+      const int ql = a.q_lens[j];
+      Lj = min(max(a.ctx_lens[j], 0), a.max_blocks_per_seq * a.block_size);
+      Tj = min(max(ql, 0), Lj);
+      q = max(0, ql);
+    }
+    const int qin = wave_incl_scan(q);
+    const int tot = __builtin_amdgcn_readlane(qin, WAVE - 1);
+    const int g = grow - qbase;
+    if (g < tot) {
+      const int k = __builtin_popcountll(__builtin_amdgcn_ballot_w64(qin <= g));
+      s = base + k;
+      i = g - (__builtin_amdgcn_readlane(qin, k) - __builtin_amdgcn_readlane(q, k));
+      L = __builtin_amdgcn_readlane(Lj, k);
+      T = __builtin_amdgcn_readlane(Tj, k);
+      return true;
+    }
+    qbase += tot;
+  }
+  return false;
+}
+
+// Merge of the pf_ksplit (= KR) key-range partials of the prefill rows of one query token:
+// out = sum_k 2^{m_k - M} o_k / sum_k 2^{m_k - M} l_k, M = max_k m_k (m in exp2 units), summed
+// in range order.  Grid (token, slice group): thread t of workgroup y takes the (q-head, 4 dims)
+// slice 256 y + t and loads its KR partials at once; tokens of split-K sequences leave at once.
+constexpr int kMaxKSplit = 8;
+template <typename E, int D, int KR>
+__global__ __launch_bounds__(256) void attn_reduce_prefill_kernel(AttnArgs a) {
+  constexpr int DQ = D / 4;
+  const int grow = blockIdx.x;
+  const int Hq = a.num_q_heads;
+  const int u = blockIdx.y * RT + threadIdx.x;  // (q-head, 4-dim) slice
+  int s, i, L, T;
+  if (!find_token(a, grow, s, i, L, T)) return;
+  if (T <= a.split_q_max || i >= T) return;  // not a row the prefill kernel computed
+  if (u >= Hq * DQ) return;
+  const int hh = u / DQ, dq = u % DQ;
+  const size_t slot0 = ((size_t)grow * Hq + hh) * KR;
+  const float2* pml = reinterpret_cast<const float2*>(a.pf_part_ml) + slot0;
+  const floatx4* po = reinterpret_cast<const floatx4*>(a.pf_part_o) + slot0 * DQ + dq;
+  float2 ml[KR];
+  floatx4 ok[KR];
+#pragma unroll
+  for (int k = 0; k < KR; ++k) {
+    ml[k] = pml[k];
+    ok[k] = po[(size_t)k * DQ];
+  }
+  float M = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < KR; ++k) M = fmaxf(M, ml[k].x);
+  floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+  float den = 0.f;
+#pragma unroll
+  for (int k = 0; k < KR; ++k) {
+    if (ml[k].x == -INFINITY) continue;  // an empty range adds nothing
+    const float w = fast_exp2(ml[k].x - M);
+    acc += w * ok[k];
+    den = fmaf(w, ml[k].y, den);
+  }
+  const floatx4 v = acc * (1.f / den);
+  const size_t ob = ((size_t)grow * Hq + hh) * D + 4 * dq;
+  if constexpr (sizeof(E) == 2) {
+    const uint32_t w0 = f32_to_bf16_bits(v[0]) | (f32_to_bf16_bits(v[1]) << 16);
+    const uint32_t w1 = f32_to_bf16_bits(v[2]) | (f32_to_bf16_bits(v[3]) << 16);
+    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(a.out) + ob) = make_uint2(w0, w1);
+  } else {
+    *reinterpret_cast<floatx4*>(reinterpret_cast<float*>(a.out) + ob) = v;
+  }
+}
+
+template <typename E, int D, int KR>
+hipError_t launch_reduce_pf(const AttnArgs& a, hipStream_t st) {
+  if constexpr (KR > kMaxKSplit) {
+    return hipErrorInvalidConfiguration;
+  } else if (a.pf_ksplit != KR) {
+    return launch_reduce_pf<E, D, KR + 1>(a, st);
+  } else {
+    const dim3 grid(a.total_q, (a.num_q_heads * (D / 4) + RT - 1) / RT);
+    attn_reduce_prefill_kernel<E, D, KR><<<grid, RT, 0, st>>>(a);
+    return hipGetLastError();
+  }
+}
+
+hipError_t launch_attn_reduce_prefill(const AttnArgs& a, int elt_bytes, int head_dim,
+                                      hipStream_t st) {
+  if (a.pf_ksplit <= 1 || a.total_q <= 0) return hipSuccess;
+  if (a.pf_ksplit > kMaxKSplit) return hipErrorInvalidConfiguration;
+  if (elt_bytes == 2)
+    return head_dim == 128 ? launch_reduce_pf<uint16_t, 128, 2>(a, st) : launch_reduce_pf<uint16_t, 64, 2>(a, st);
+  return head_dim == 128 ? launch_reduce_pf<float, 128, 2>(a, st) : launch_reduce_pf<float, 64, 2>(a, st);
+}
+
 hipError_t launch_attn_reduce(const AttnArgs& a, int elt_bytes, int head_dim, hipStream_t st) {
   if (a.part_rows <= 0) return hipSuccess;
   dim3 grid(a.part_rows, a.num_q_heads);

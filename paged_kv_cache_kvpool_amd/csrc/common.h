@@ -166,6 +166,12 @@ struct AttnArgs {
   int32_t split_q_max;      // sequences with q_len <= split_q_max take the split-K path
   int32_t part_rows;        // rows of the partial buffers (query tokens of the split-K path)
   int32_t pf_rblk;          // prefill kernel: 32-row blocks per workgroup
+  // Prefill key splits (pf_ksplit > 1): each row tile's keys are cut into pf_ksplit ranges of
+  // whole 64-key tiles, reduced by separate workgroups into partials [total_q][Hq][pf_ksplit]
+  // ([D] outputs, (max, sum) pairs) that attn_reduce_prefill merges in range order.
+  int32_t pf_ksplit;
+  float* pf_part_o;
+  float* pf_part_ml;
   // Sink + window sparsity (split-K path; off when sparse_window == 0): a query row at position
   // p with p + 1 >= sparse_min reads only keys j < sparse_sink or j > p - sparse_window.
   int32_t sparse_sink, sparse_window, sparse_min;

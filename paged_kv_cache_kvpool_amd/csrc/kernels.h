@@ -83,6 +83,10 @@ hipError_t launch_attn_prefill_mfma(const AttnArgs& a, int head_dim, int waves, 
 // Workgroups of the prefill kernel for prefill-class sequences of rows[i] = q_len * G rows each,
 // with rblk 32-row blocks per workgroup.
 long long prefill_wg_count(const int* rows, int n, int num_kv_heads, int rblk);
+// Key ranges per prefill row tile (1..8): more when the row tiles alone, wgs of them, leave
+// CUs idle; 1 in deterministic mode.  max_ctx: the longest context (ranges of whole 64-key
+// tiles, at least 4 each).
+int prefill_ksplit(long long wgs, int num_cus, int max_ctx, bool deterministic);
 // Workgroup shape for such a set of sequences: waves (4..12) and row blocks per workgroup
 // (waves/2 .. waves; the waves beyond 2*rblk - waves share a row block in pairs), balancing the
 // SIMDs and the workgroups over the CUs.  whole_only: rblk = waves (no pairs).
@@ -102,5 +106,9 @@ hipError_t launch_dequant_prefill(const AttnArgs& a, const DequantOut& o, int he
                                   hipStream_t st);
 // Cross-split merge of the split-K partials: one workgroup per (partial row, q-head).
 hipError_t launch_attn_reduce(const AttnArgs& a, int elt_bytes, int head_dim, hipStream_t st);
+// Merge of the prefill kernel's key-range partials (a.pf_ksplit > 1, at most 8): one workgroup
+// per query token.
+hipError_t launch_attn_reduce_prefill(const AttnArgs& a, int elt_bytes, int head_dim,
+                                      hipStream_t st);
 
 }  // namespace kvp

@@ -146,12 +146,12 @@ int validate_meta(const kvpool* p, const HostMeta& m, int32_t max_blocks, int32_
 // Opt-in per-kernel timing: a HIP event pair around every launch, on the launch's stream.
 enum KernelId {
   K_APPEND, K_COPY, K_SPLIT_MFMA, K_VEC, K_PREFILL_MFMA, K_REDUCE, K_DEQUANT,
-  K_PAGE_HASH, K_PAGE_PARK, K_PAGE_RESTORE, K_COUNT
+  K_PAGE_HASH, K_PAGE_PARK, K_PAGE_RESTORE, K_REDUCE_PF, K_COUNT
 };
 const char* const kKernelNames[K_COUNT] = {"kv_append", "kv_copy_blocks", "attn_split_mfma",
                                            "attn_vec", "attn_prefill_mfma", "attn_reduce",
                                            "kv_dequant_prefill", "page_hash", "page_park",
-                                           "page_restore"};
+                                           "page_restore", "attn_reduce_prefill"};
 struct ProfRec {
   int kernel;
   hipEvent_t a, b;
@@ -427,6 +427,8 @@ struct Plan {
   int waves;          // prefill workgroup size
   int rblk;           // prefill 32-row blocks per workgroup
   long long pf_wgs;   // prefill grid: its workgroups (or a bound of them)
+  int pf_ks;          // prefill key ranges per row tile (1: no partials)
+  size_t pf_o_off, pf_ml_off;  // their partials in the workspace
   size_t o_bytes;     // partial outputs, rounded up to 256 bytes
   // int8 pools with prefill-class sequences: their tiles dequantized to a bf16 workspace pool
   int dq_seqs;        // prefill sequences it holds (exact or a bound)
@@ -511,6 +513,22 @@ Plan make_plan(const kvpool* p, int32_t num_q_heads, int32_t num_seqs, int32_t t
   const size_t slots = (size_t)pl.part_rows * num_q_heads * pl.max_splits;
   pl.o_bytes = (slots * p->head_dim * 4 + 255) / 256 * 256;
   pl.bytes = slots ? pl.o_bytes + (slots * 2 * 4 + 255) / 256 * 256 : 0;
+  // Prefill key ranges when the row tiles alone leave CUs idle (never in deterministic mode:
+  // the ranges follow the batch); KVATTN_PREFILL_KSPLIT fixes their number (tests, sweeps).
+  // Partials [total_q][Hq][ranges] of D floats and of (max, sum) pairs.
+  pl.pf_ks = 1;
+  if (pl.prefill && p->dtype != KV_F32) {  // (fp32 pools run every sequence in attn_vec)
+    const bool det = env_flag("KVATTN_DETERMINISTIC");
+    pl.pf_ks = kvp::prefill_ksplit(pl.pf_wgs, p->num_cus, max_ctx_len, det);
+    if (const char* v = getenv("KVATTN_PREFILL_KSPLIT")) pl.pf_ks = std::max(1, std::min(8, atoi(v)));
+    if (det) pl.pf_ks = 1;
+  }
+  if (pl.pf_ks > 1) {
+    const size_t pslots = (size_t)total_q * num_q_heads * pl.pf_ks;
+    pl.pf_o_off = pl.bytes;
+    pl.pf_ml_off = pl.pf_o_off + (pslots * p->head_dim * 4 + 255) / 256 * 256;
+    pl.bytes = pl.pf_ml_off + (pslots * 2 * 4 + 255) / 256 * 256;
+  }
   if (p->dtype == KV_I8 && pl.prefill) {
     // [dequantized K][dequantized V][block table], each 256-byte aligned
     pl.dq_seqs = q_lens_host ? n_pf_exact
@@ -641,6 +659,9 @@ int forward_impl(kvpool_t* pool, int32_t layer, const void* q, void* out, int32_
   a.split_q_max = pl.split_q_max;
   a.part_rows = pl.part_rows;
   a.pf_rblk = pl.rblk;
+  a.pf_ksplit = pl.pf_ks;
+  a.pf_part_o = pl.pf_ks > 1 ? reinterpret_cast<float*>(ws + pl.pf_o_off) : nullptr;
+  a.pf_part_ml = pl.pf_ks > 1 ? reinterpret_cast<float*>(ws + pl.pf_ml_off) : nullptr;
   a.sparse_sink = sp.sink;
   a.sparse_window = sp.window;
   a.sparse_min = sp.min_len;
@@ -690,6 +711,8 @@ int forward_impl(kvpool_t* pool, int32_t layer, const void* q, void* out, int32_
       }
       if (e == hipSuccess)
         e = timed(K_PREFILL_MFMA, st, [&] { return kvp::launch_attn_prefill_mfma(ap, pool->head_dim, pl.waves, pl.pf_wgs, st); });
+      if (e == hipSuccess && pl.pf_ks > 1)
+        e = timed(K_REDUCE_PF, st, [&] { return kvp::launch_attn_reduce_prefill(ap, eb, pool->head_dim, st); });
     }
   }
   if (e != hipSuccess) return fail(KV_EDEVICE, "attention launch: %s", hipGetErrorString(e));

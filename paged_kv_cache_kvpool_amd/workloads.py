@@ -260,6 +260,16 @@ def prefix_prefill(seed: int = 3, num_seqs: int = 4, prefix: int = 4096, suffix:
                 num_q_heads=40, num_kv_heads=8, head_dim=128, append=True, host_pool=host_pool)
 
 
+def long_prefix_chunk(seed: int = 7, prefix: int = 32768, suffix: int = 512,
+                      host_pool: bool = True, dtype: str = BF16) -> Workload:
+    """One chunked-prefill step of a long prompt: a 512-token chunk over a 32768-token cached
+    prefix (causal), 40/8 heads, D=128, bf16.  Its row tiles alone fill under two thirds of the
+    GPU, so each row tile's keys are cut into ranges."""
+    return make("long_prefix_chunk" + ("_int8" if dtype == I8 else ""), seed=seed, dtype=dtype,
+                num_seqs_ctx=[prefix + suffix], q_lens=[suffix], num_q_heads=40, num_kv_heads=8,
+                head_dim=128, append=True, host_pool=host_pool)
+
+
 def long_decode(seed: int = 4, host_pool: bool = False, dtype: str = BF16) -> Workload:
     """2 concurrent sequences at 262144 and 131072 tokens, 1 query token each, 40/8 heads,
     D=128, bf16, pool of 24576 blocks (393216 tokens) with random placement."""
