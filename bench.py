@@ -344,8 +344,17 @@ class Device:
             out += [self.pool.k_scales.cpu().numpy(), self.pool.v_scales.cpu().numpy()]
         self._pre = tuple(out)
 
+    # kvattn_append_forward for dense steps with new tokens (the split-K kernel appends them
+    # itself when every sequence takes it); False: kvpool_append, then kvattn_forward.
+    fused_append = True
+
     def step(self):
         w = self.w
+        if self.k_new is not None and w.sparse is None and self.fused_append:
+            self.pool.append_forward(w.layer, self.k_new, self.v_new, self.q, self.tables, self.ctx,
+                                     self.ql, scale=w.scale, max_ctx_len=self.max_ctx,
+                                     max_q_len=self.max_q, out=self.out, q_lens_host=self.ql_host)
+            return
         if self.k_new is not None:
             self.pool.append(w.layer, self.k_new, self.v_new, self.tables, self.ctx, self.ql,
                              max_q_len=self.max_q)
@@ -490,6 +499,9 @@ def main():
                          "slower than eager launches on this ROCm); 0: eager launches")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (scale for HBM counters)")
+    ap.add_argument("--separate-append", action="store_true",
+                    help="append with kvpool_append, then kvattn_forward (default: one "
+                         "kvattn_append_forward call)")
     ap.add_argument("--flush", default="read", choices=["read", "write", "none"],
                     help="evict MALL and L2 between steps by reading (default) or writing 1 GiB")
     args = ap.parse_args()
@@ -522,6 +534,7 @@ def main():
     w = make_workload(wname)
     alg = algorithmic(w)
     dev = Device(w)
+    dev.fused_append = not args.separate_append
     want_cpu = not args.no_cpu_baseline
     dev.snapshot_pre_append(want_cpu)
     scratch = torch.zeros(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
@@ -623,7 +636,8 @@ def main():
                    "num_seqs": w.num_seqs, "total_q": w.total_q, "block_size": w.block_size,
                    "head_dim": w.head_dim, "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
                    "kv_dtype": {"i8": "int8", "bf16": "bf16", "f32": "f32"}[w.dtype],
-                   "mall_flush": args.flush, "hip_graph": bool(args.graph)},
+                   "mall_flush": args.flush, "hip_graph": bool(args.graph),
+                   "append": "separate" if args.separate_append else "fused call"},
         "kv_tokens_per_s": alg["kv_tokens"] / (ms * 1e-3),
         "step_ms_p10_p50_p90": [float(np.percentile(step_ms, p)) for p in (10, 50, 90)],
         "kernel_ms_per_launch": {k: v[1] / v[0] for k, v in ktimes.items()},

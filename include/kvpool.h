@@ -199,6 +199,26 @@ KVPOOL_API int kvattn_forward(kvpool_t *pool, int32_t layer, const void *q, void
                               const int32_t *q_lens_host, void *workspace,
                               size_t workspace_bytes, void *stream);
 
+/* kvpool_append followed by kvattn_forward, in one call: the new tokens' K/V rows (k_new,
+ * v_new, as for kvpool_append) are written into the pool, then every sequence attends as in
+ * kvattn_forward (the pages' serving step appends a layer's new K/V and attends over the pool:
+ * NInfer serving doc, "Execution behavior").  The result, pool and output, is bit for bit that
+ * of the two calls.  When every sequence takes the split-K kernel (decode and verification
+ * rows only, judged from q_lens_host when given, else from max_q_len), that kernel writes each
+ * new token itself, in the work item whose keys hold it, before reading it: one launch fewer
+ * per step.  Otherwise the append kernel runs first.  Arguments: those of both calls, with
+ * max_q_len bounding q_lens for both; each call's argument errors and (KVPOOL_VALIDATE)
+ * metadata checks apply, and a nonzero return enqueues no work.  The workspace is
+ * kvattn_workspace_size's. */
+KVPOOL_API int kvattn_append_forward(kvpool_t *pool, int32_t layer, const void *k_new,
+                                     const void *v_new, const void *q, void *out,
+                                     int32_t num_q_heads, float scale,
+                                     const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                     const int32_t *ctx_lens, const int32_t *q_lens,
+                                     int32_t num_seqs, int32_t total_q, int32_t max_ctx_len,
+                                     int32_t max_q_len, const int32_t *q_lens_host,
+                                     void *workspace, size_t workspace_bytes, void *stream);
+
 /* kvattn_forward with sink + window sparsity: a query row at absolute position p (= ctx_len -
  * q_len + i) with p + 1 >= min_ctx_len reads only the keys j <= p with j < sink_tokens or
  * j >= p + 1 - window_tokens; rows below the threshold read all their keys.  The pages' decode

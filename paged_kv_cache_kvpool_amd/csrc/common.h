@@ -176,6 +176,11 @@ struct AttnArgs {
   // p with p + 1 >= sparse_min reads only keys j < sparse_sink or j > p - sparse_window.
   int32_t sparse_sink, sparse_window, sparse_min;
   float scale_log2;         // softmax scale * log2(e)
+  // Fused append (kvattn_append_forward; split-K calls only): the new tokens' rows
+  // [total_q][Hkv][D] (bf16), written into the pool by the split-K item whose keys hold them
+  // before it reads them; null otherwise.
+  const void* k_new;
+  const void* v_new;
 };
 
 // Keys per split of a sequence with L keys on the split-K path: a fixed count if the caller set one,
@@ -315,6 +320,62 @@ __device__ __forceinline__ size_t block_tile_offset(int blk, int sub, int h, int
   blk = ((unsigned)blk < (unsigned)num_blocks) ? blk : 0;
   const size_t tile = (((size_t)blk * num_kv_heads + h) << (block_shift - 4)) + sub;
   return tile * (size_t)(TILE * head_dim);
+}
+
+// int8 pool (sparkinfer server README, "Env", SPARKINFER_KV_INT8; NInfer serving doc, "Server
+// options", --kv-dtype int8): each new (token, KV head) row of bf16 values is quantised with
+// one fp32 scale s = absmax / 127 and codes q = rint(x / s) (correctly rounded division, ties
+// to even), clamped to +-127; a zero row gets s = 0 and codes 0.  Tile layouts (16 tokens):
+//   K: [d / 16][t % 16][d % 16]                      (16-byte chunks of 16 dims)
+//   V: [(t % 16) / 4][d % 16][d / 16][t % 4]         (the 4 keys of a dim group side by side)
+// One wave per (token, KV head) row: lane l holds dims E*l .. E*l + E - 1 (E = head_dim / 64),
+// the absolute max comes from a wave reduction, and codes are stored byte by byte (K) / to
+// their scattered V slots.  The append kernel and the split-K kernel's fused append both store
+// rows through append_row_i8, so their bits are the same.
+__device__ __forceinline__ float wave_max_f(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+
+template <int E>
+__device__ __forceinline__ void quantise_row(const uint16_t* src, float (&q)[E], float& scale) {
+  const int lane = threadIdx.x & (WAVE - 1);
+  float x[E];
+  float m = 0.f;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    x[e] = __uint_as_float((uint32_t)src[E * lane + e] << 16);
+    m = fmaxf(m, fabsf(x[e]));
+  }
+  m = wave_max_f(m);
+  scale = __fdiv_rn(m, 127.f);
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    q[e] = scale > 0.f ? fminf(fmaxf(rintf(__fdiv_rn(x[e], scale)), -127.f), 127.f) : 0.f;
+}
+
+// Quantises the bf16 rows krow / vrow (head_dim 64 E) of token slot tt of a 16-token tile and
+// stores codes and scales into the tile (kt, vt: the tile's codes; ks, vs: its 16 scales).
+// The whole wave takes part (wave reductions).
+template <int E>
+__device__ __forceinline__ void append_row_i8(int8_t* kt, int8_t* vt, float* ks, float* vs,
+                                              const uint16_t* krow, const uint16_t* vrow, int tt) {
+  constexpr int D = 64 * E;
+  const int lane = threadIdx.x & (WAVE - 1);
+  float qk[E], qv[E], sk, sv;
+  quantise_row<E>(krow, qk, sk);
+  quantise_row<E>(vrow, qv, sv);
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int d = E * lane + e;
+    kt[(d >> 4) * 256 + tt * 16 + (d & 15)] = (int8_t)(int)qk[e];
+    vt[(((tt >> 2) * 16 + (d & 15)) * (D / 16) + (d >> 4)) * 4 + (tt & 3)] = (int8_t)(int)qv[e];
+  }
+  if (lane == 0) {
+    ks[tt] = sk;
+    vs[tt] = sv;
+  }
 }
 
 }  // namespace kvp

@@ -75,38 +75,8 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   }
 }
 
-// int8 pool (sparkinfer server README, "Env", SPARKINFER_KV_INT8; NInfer serving doc, "Server
-// options", --kv-dtype int8): each new (token, KV head) row of bf16 values is quantised with
-// one fp32 scale s = absmax / 127 and codes q = rint(x / s) (correctly rounded division, ties
-// to even), clamped to +-127; a zero row gets s = 0 and codes 0.  Tile layouts (16 tokens):
-//   K: [d / 16][t % 16][d % 16]                      (16-byte chunks of 16 dims)
-//   V: [(t % 16) / 4][d % 16][d / 16][t % 4]         (the 4 keys of a dim group side by side)
-// One wave per (token, KV head) row of the workgroup's 16-token tile: lane l holds dims
-// E*l .. E*l + E - 1 (E = head_dim / 64), the absolute max comes from a wave reduction, and
-// codes are stored byte by byte (K) / to their scattered V slots.
-__device__ __forceinline__ float wave_max_f(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
-}
-
-template <int E>
-__device__ __forceinline__ void quantise_row(const uint16_t* src, float (&q)[E], float& scale) {
-  const int lane = threadIdx.x & (WAVE - 1);
-  float x[E];
-  float m = 0.f;
-#pragma unroll
-  for (int e = 0; e < E; ++e) {
-    x[e] = __uint_as_float((uint32_t)src[E * lane + e] << 16);
-    m = fmaxf(m, fabsf(x[e]));
-  }
-  m = wave_max_f(m);
-  scale = __fdiv_rn(m, 127.f);
-#pragma unroll
-  for (int e = 0; e < E; ++e)
-    q[e] = scale > 0.f ? fminf(fmaxf(rintf(__fdiv_rn(x[e], scale)), -127.f), 127.f) : 0.f;
-}
-
+// int8 pools: each new (token, KV head) row is quantised and stored by append_row_i8 (common.h),
+// one wave per row of the workgroup's 16-token tile.
 template <int E>
 __global__ __launch_bounds__(256) void append_i8_kernel(AppendArgs a) {
   constexpr int D = 64 * E;
@@ -135,19 +105,7 @@ __global__ __launch_bounds__(256) void append_i8_kernel(AppendArgs a) {
     if (row >= a.total_q) continue;
     const int tt = p - tile_start;
     const size_t src = ((size_t)row * a.num_kv_heads + h) * D;
-    float qk[E], qv[E], sk, sv;
-    quantise_row<E>(kn + src, qk, sk);
-    quantise_row<E>(vn + src, qv, sv);
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      const int d = E * lane + e;
-      kt[(d >> 4) * 256 + tt * 16 + (d & 15)] = (int8_t)(int)qk[e];
-      vt[(((tt >> 2) * 16 + (d & 15)) * (D / 16) + (d >> 4)) * 4 + (tt & 3)] = (int8_t)(int)qv[e];
-    }
-    if (lane == 0) {
-      ks[tt] = sk;
-      vs[tt] = sv;
-    }
+    append_row_i8<E>(kt, vt, ks, vs, kn + src, vn + src, tt);
   }
 }
 

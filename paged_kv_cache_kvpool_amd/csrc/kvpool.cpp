@@ -277,6 +277,83 @@ int create_pool(kvpool_t** out, int32_t num_layers, int32_t num_blocks, int32_t 
 
 }  // namespace
 
+namespace {
+
+// Checks (and, under KVPOOL_VALIDATE, validates) an append; *nothing = true when there is no
+// row to write.  Shared by kvpool_append and kvattn_append_forward.
+int append_check(kvpool_t* pool, int32_t layer, const void* k_new, const void* v_new,
+                 const int32_t* block_tables, int32_t max_blocks_per_seq, const int32_t* ctx_lens,
+                 const int32_t* q_lens, int32_t num_seqs, int32_t total_q, int32_t max_q_len,
+                 hipStream_t st, bool* nothing) {
+  *nothing = false;
+  if (!pool) return fail(KV_EINVAL, "pool is NULL");
+  if (layer < 0 || layer >= pool->num_layers) return fail(KV_EINVAL, "layer %d out of range", layer);
+  if (num_seqs < 0 || total_q < 0 || max_q_len < 0 || max_blocks_per_seq < 0)
+    return fail(KV_EINVAL, "negative size argument");
+  if (num_seqs > 65535) return fail(KV_EUNSUPPORTED, "num_seqs %d > 65535", num_seqs);
+  if (num_seqs == 0 || total_q == 0 || max_q_len == 0) {
+    *nothing = true;
+    return ok();
+  }
+  if (!k_new || !v_new || !block_tables || !ctx_lens || !q_lens)
+    return fail(KV_EINVAL, "NULL device pointer");
+  if (!aligned16(k_new) || !aligned16(v_new)) return fail(KV_EINVAL, "k_new/v_new must be 16-byte aligned");
+  if (current_device_matches(pool) != hipSuccess)
+    return fail(KV_EINVAL, "current HIP device is not the pool's device %d", pool->device);
+  if (env_flag("KVPOOL_VALIDATE")) {
+    HostMeta m;
+    int rc = fetch_meta(block_tables, max_blocks_per_seq, ctx_lens, q_lens, num_seqs, st, m);
+    if (rc) return rc;
+    rc = validate_meta(pool, m, max_blocks_per_seq, num_seqs, total_q, INT32_MAX, max_q_len);
+    if (rc) return rc;
+    // Blocks being written must belong to exactly one sequence of this call.
+    std::vector<int> owner(pool->num_blocks, -1);
+    for (int s = 0; s < num_seqs; ++s) {
+      const int nb = (m.ctx[s] + pool->block_size - 1) / pool->block_size;
+      for (int b = 0; b < nb; ++b) {
+        const int id = m.tables[(size_t)s * max_blocks_per_seq + b];
+        if (owner[id] >= 0 && owner[id] != s) {
+          const int first_new = (m.ctx[s] - m.ql[s]) / pool->block_size;
+          if (b >= first_new) return fail(KV_ERANGE, "seq %d writes block %d shared with seq %d", s, id, owner[id]);
+        }
+        owner[id] = s;
+      }
+    }
+  }
+  return ok();
+}
+
+// The append kernel's launch (arguments already checked).
+int append_launch(kvpool_t* pool, int32_t layer, const void* k_new, const void* v_new,
+                  const int32_t* block_tables, int32_t max_blocks_per_seq,
+                  const int32_t* ctx_lens, const int32_t* q_lens, int32_t num_seqs,
+                  int32_t total_q, int32_t max_q_len, hipStream_t st) {
+  kvp::AppendArgs a;
+  const size_t lo = (size_t)layer * pool->layer_elems * elt_bytes(pool->dtype);
+  a.k_layer = static_cast<char*>(pool->k) + lo;
+  a.v_layer = static_cast<char*>(pool->v) + lo;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  const size_t so = (size_t)layer * pool->num_blocks * pool->num_kv_heads * pool->block_size;
+  a.k_scale_layer = pool->k_scale ? pool->k_scale + so : nullptr;
+  a.v_scale_layer = pool->v_scale ? pool->v_scale + so : nullptr;
+  a.block_tables = block_tables;
+  a.ctx_lens = ctx_lens;
+  a.q_lens = q_lens;
+  a.num_seqs = num_seqs;
+  a.total_q = total_q;
+  a.num_kv_heads = pool->num_kv_heads;
+  a.head_dim = pool->head_dim;
+  a.block_size = pool->block_size;
+  a.num_blocks = pool->num_blocks;
+  a.max_blocks_per_seq = max_blocks_per_seq;
+  hipError_t e = timed(K_APPEND, st, [&] { return kvp::launch_append(a, elt_bytes(pool->dtype), max_q_len, st); });
+  if (e != hipSuccess) return fail(KV_EDEVICE, "append launch: %s", hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
 extern "C" {
 
 int kvpool_create(kvpool_t** out, int32_t num_layers, int32_t num_blocks, int32_t block_size,
@@ -315,60 +392,14 @@ int kvpool_append(kvpool_t* pool, int32_t layer, const void* k_new, const void* 
                   const int32_t* block_tables, int32_t max_blocks_per_seq,
                   const int32_t* ctx_lens, const int32_t* q_lens, int32_t num_seqs,
                   int32_t total_q, int32_t max_q_len, void* stream) {
-  if (!pool) return fail(KV_EINVAL, "pool is NULL");
-  if (layer < 0 || layer >= pool->num_layers) return fail(KV_EINVAL, "layer %d out of range", layer);
-  if (num_seqs < 0 || total_q < 0 || max_q_len < 0 || max_blocks_per_seq < 0)
-    return fail(KV_EINVAL, "negative size argument");
-  if (num_seqs > 65535) return fail(KV_EUNSUPPORTED, "num_seqs %d > 65535", num_seqs);
-  if (num_seqs == 0 || total_q == 0 || max_q_len == 0) return ok();
-  if (!k_new || !v_new || !block_tables || !ctx_lens || !q_lens)
-    return fail(KV_EINVAL, "NULL device pointer");
-  if (!aligned16(k_new) || !aligned16(v_new)) return fail(KV_EINVAL, "k_new/v_new must be 16-byte aligned");
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
-  if (current_device_matches(pool) != hipSuccess)
-    return fail(KV_EINVAL, "current HIP device is not the pool's device %d", pool->device);
-  if (env_flag("KVPOOL_VALIDATE")) {
-    HostMeta m;
-    int rc = fetch_meta(block_tables, max_blocks_per_seq, ctx_lens, q_lens, num_seqs, st, m);
-    if (rc) return rc;
-    rc = validate_meta(pool, m, max_blocks_per_seq, num_seqs, total_q, INT32_MAX, max_q_len);
-    if (rc) return rc;
-    // Blocks being written must belong to exactly one sequence of this call.
-    std::vector<int> owner(pool->num_blocks, -1);
-    for (int s = 0; s < num_seqs; ++s) {
-      const int nb = (m.ctx[s] + pool->block_size - 1) / pool->block_size;
-      for (int b = 0; b < nb; ++b) {
-        const int id = m.tables[(size_t)s * max_blocks_per_seq + b];
-        if (owner[id] >= 0 && owner[id] != s) {
-          const int first_new = (m.ctx[s] - m.ql[s]) / pool->block_size;
-          if (b >= first_new) return fail(KV_ERANGE, "seq %d writes block %d shared with seq %d", s, id, owner[id]);
-        }
-        owner[id] = s;
-      }
-    }
-  }
-  kvp::AppendArgs a;
-  const size_t lo = (size_t)layer * pool->layer_elems * elt_bytes(pool->dtype);
-  a.k_layer = static_cast<char*>(pool->k) + lo;
-  a.v_layer = static_cast<char*>(pool->v) + lo;
-  a.k_new = k_new;
-  a.v_new = v_new;
-  const size_t so = (size_t)layer * pool->num_blocks * pool->num_kv_heads * pool->block_size;
-  a.k_scale_layer = pool->k_scale ? pool->k_scale + so : nullptr;
-  a.v_scale_layer = pool->v_scale ? pool->v_scale + so : nullptr;
-  a.block_tables = block_tables;
-  a.ctx_lens = ctx_lens;
-  a.q_lens = q_lens;
-  a.num_seqs = num_seqs;
-  a.total_q = total_q;
-  a.num_kv_heads = pool->num_kv_heads;
-  a.head_dim = pool->head_dim;
-  a.block_size = pool->block_size;
-  a.num_blocks = pool->num_blocks;
-  a.max_blocks_per_seq = max_blocks_per_seq;
-  hipError_t e = timed(K_APPEND, st, [&] { return kvp::launch_append(a, elt_bytes(pool->dtype), max_q_len, st); });
-  if (e != hipSuccess) return fail(KV_EDEVICE, "append launch: %s", hipGetErrorString(e));
-  return ok();
+  bool nothing = false;
+  if (int rc = append_check(pool, layer, k_new, v_new, block_tables, max_blocks_per_seq, ctx_lens,
+                            q_lens, num_seqs, total_q, max_q_len, st, &nothing))
+    return rc;
+  if (nothing) return ok();
+  return append_launch(pool, layer, k_new, v_new, block_tables, max_blocks_per_seq, ctx_lens,
+                       q_lens, num_seqs, total_q, max_q_len, st);
 }
 
 int kvpool_copy_blocks(kvpool_t* pool, const int32_t* src, const int32_t* dst, int32_t n,
@@ -566,12 +597,14 @@ struct Sparse {
   int sink, window, min_len;
 };
 
+// k_new / v_new (kvattn_append_forward, arguments already checked by append_check): the new
+// tokens' rows to append first; null for a plain forward.
 int forward_impl(kvpool_t* pool, int32_t layer, const void* q, void* out, int32_t num_q_heads,
                  float scale, const int32_t* block_tables, int32_t max_blocks_per_seq,
                  const int32_t* ctx_lens, const int32_t* q_lens, int32_t num_seqs,
                  int32_t total_q, int32_t max_ctx_len, int32_t max_q_len, Sparse sp,
                  const int32_t* q_lens_host, void* workspace, size_t workspace_bytes,
-                 void* stream) {
+                 void* stream, const void* k_new = nullptr, const void* v_new = nullptr) {
   if (!pool) return fail(KV_EINVAL, "pool is NULL");
   if (layer < 0 || layer >= pool->num_layers) return fail(KV_EINVAL, "layer %d out of range", layer);
   if (num_q_heads <= 0 || num_q_heads % pool->num_kv_heads)
@@ -666,13 +699,29 @@ int forward_impl(kvpool_t* pool, int32_t layer, const void* q, void* out, int32_
   a.sparse_window = sp.window;
   a.sparse_min = sp.min_len;
   a.scale_log2 = scale * kvp::LOG2E;
+  a.k_new = nullptr;
+  a.v_new = nullptr;
 
   // q / out element bytes (bf16 for int8 pools)
   const int eb = pool->dtype == KV_F32 ? 4 : 2;
   const bool i8 = pool->dtype == KV_I8;
   hipError_t e = hipSuccess;
-  if (pool->dtype == KV_F32 || (pool->dtype == KV_BF16 && sp.window == 0 && !pl.prefill &&
-                                 max_q_len == 1 && env_flag("KVATTN_DECODE_VEC"))) {
+  const bool vec = pool->dtype == KV_F32 || (pool->dtype == KV_BF16 && sp.window == 0 && !pl.prefill &&
+                                              max_q_len == 1 && env_flag("KVATTN_DECODE_VEC"));
+  if (k_new) {
+    // Append inside the split-K kernel when every sequence takes it on persistent waves;
+    // otherwise the append kernel runs first, as kvpool_append would.
+    const bool fuse = !vec && !pl.prefill && pl.split_k && sp.window == 0 &&
+                      (pl.split == 0 || pl.split <= 2048);
+    if (fuse) {
+      a.k_new = k_new;
+      a.v_new = v_new;
+    } else if (int rc = append_launch(pool, layer, k_new, v_new, block_tables, max_blocks_per_seq,
+                                      ctx_lens, q_lens, num_seqs, total_q, max_q_len, st)) {
+      return rc;
+    }
+  }
+  if (vec) {
     // One launch for every sequence: split-K sequences in splits, longer ones in one pass.
     // Rows per wave: the template instance just large enough (1, 2, 4, 5 or 8).
     const int rows = max_q_len * G;
@@ -739,6 +788,30 @@ int kvattn_forward(kvpool_t* pool, int32_t layer, const void* q, void* out, int3
   return forward_impl(pool, layer, q, out, num_q_heads, scale, block_tables, max_blocks_per_seq,
                       ctx_lens, q_lens, num_seqs, total_q, max_ctx_len, max_q_len, Sparse{0, 0, 0},
                       q_lens_host, workspace, workspace_bytes, stream);
+}
+
+int kvattn_append_forward(kvpool_t* pool, int32_t layer, const void* k_new, const void* v_new,
+                          const void* q, void* out, int32_t num_q_heads, float scale,
+                          const int32_t* block_tables, int32_t max_blocks_per_seq,
+                          const int32_t* ctx_lens, const int32_t* q_lens, int32_t num_seqs,
+                          int32_t total_q, int32_t max_ctx_len, int32_t max_q_len,
+                          const int32_t* q_lens_host, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+  bool nothing = false;
+  if (int rc = append_check(pool, layer, k_new, v_new, block_tables, max_blocks_per_seq, ctx_lens,
+                            q_lens, num_seqs, total_q, max_q_len, st, &nothing))
+    return rc;
+  if (nothing)
+    return forward_impl(pool, layer, q, out, num_q_heads, scale, block_tables, max_blocks_per_seq,
+                        ctx_lens, q_lens, num_seqs, total_q, max_ctx_len, max_q_len,
+                        Sparse{0, 0, 0}, q_lens_host, workspace, workspace_bytes, stream);
+  // (forward_impl returns before its launches only when it has no row: then nothing may be
+  // appended either, which these bounds guarantee)
+  if (max_ctx_len < max_q_len) return fail(KV_EINVAL, "max_q_len > max_ctx_len");
+  return forward_impl(pool, layer, q, out, num_q_heads, scale, block_tables, max_blocks_per_seq,
+                      ctx_lens, q_lens, num_seqs, total_q, max_ctx_len, max_q_len, Sparse{0, 0, 0},
+                      q_lens_host, workspace, workspace_bytes, stream, k_new, v_new);
 }
 
 int kvattn_forward_sparse(kvpool_t* pool, int32_t layer, const void* q, void* out,

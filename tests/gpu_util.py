@@ -98,6 +98,15 @@ class DeviceCase:
                                  max_q_len=int(w.q_lens.max()), out=out,
                                  q_lens_host=w.q_lens if mirror else None)
 
+    def append_forward(self, out=None, mirror=False):
+        """Append and attention in one call (kvattn_append_forward)."""
+        w = self.w
+        return self.pool.append_forward(w.layer, self.k_new, self.v_new, self.q, self.tables,
+                                        self.ctx, self.ql, scale=w.scale,
+                                        max_ctx_len=int(w.ctx_lens.max()),
+                                        max_q_len=int(w.q_lens.max()), out=out,
+                                        q_lens_host=w.q_lens if mirror else None)
+
     # -- host copies for the oracle ---------------------------------------------------------
     def host_pools(self):
         """Host copies of the device pool: (K, V), or (K, V, K scales, V scales) for int8."""

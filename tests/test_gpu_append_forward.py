@@ -1,0 +1,103 @@
+"""GPU parity of kvattn_append_forward (append and attention in one call): the output and the
+whole pool after the call equal, bit for bit, those of kvpool_append followed by kvattn_forward
+on an identical second pool, and the output matches the oracle.  Split-K calls (decode,
+verification, many sequences, int8 pools, new tokens on both sides of a split boundary) append
+inside the split-K kernel; calls with prefill chunks, fp32 pools and the vector path fall back to
+the append kernel.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from paged_kv_cache_kvpool_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover
+    pytest.skip("no GPU", allow_module_level=True)
+
+from tests.gpu_util import DeviceCase, assert_close, out_f64  # noqa: E402
+
+
+def announce(msg):
+    print(f"\n[case] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+def raw(t):
+    return t.detach().contiguous().view(torch.uint8).cpu().numpy()
+
+
+CASES = {
+    "decode": dict(num_seqs_ctx=[3000, 700, 40, 9000, 17, 256, 257], q_lens=[1] * 7,
+                   num_q_heads=32, num_kv_heads=8),
+    "verify": dict(num_seqs_ctx=[32772, 2050, 4], q_lens=[4, 4, 4], num_q_heads=40, num_kv_heads=8),
+    "many": dict(num_seqs_ctx=list(range(300, 300 + 97 * 37, 37)), q_lens=[1, 2, 1, 4] * 24 + [1],
+                 num_q_heads=16, num_kv_heads=4),
+    "mixed": dict(num_seqs_ctx=[3000, 700, 900, 5000], q_lens=[1, 4, 300, 1], num_q_heads=40,
+                  num_kv_heads=8),
+    "wide_rows": dict(num_seqs_ctx=[5000, 1300], q_lens=[8, 5], num_q_heads=64, num_kv_heads=8),
+}
+
+
+def pair(name, dtype, seed):
+    cfg = CASES[name]
+    w = wl.make(f"af_{name}_{dtype}", seed=seed, dtype=dtype, head_dim=128, **cfg)
+    return w, DeviceCase(w), DeviceCase(w)
+
+
+def check(name, dtype, seed=601, mirror=True):
+    announce(f"append_forward {name} {dtype} mirror={mirror}")
+    w, a, b = pair(name, dtype, seed)
+    a.append()
+    ref = a.forward(mirror=mirror)
+    got = b.append_forward(mirror=mirror)
+    torch.cuda.synchronize()
+    assert np.array_equal(raw(got), raw(ref)), "output differs from append + forward"
+    for x, y in zip(a.host_pools(), b.host_pools()):
+        assert np.array_equal(np.asarray(x).view(np.uint8), np.asarray(y).view(np.uint8)), \
+            "pool differs from append + forward"
+    assert_close(out_f64(got), b.oracle(), dtype, w.name)
+
+
+@pytest.mark.parametrize("name", ["decode", "verify", "many", "wide_rows", "mixed"])
+@pytest.mark.parametrize("dtype", [wl.BF16, wl.I8])
+def test_append_forward(name, dtype):
+    check(name, dtype)
+
+
+def test_append_forward_without_mirror():
+    check("verify", wl.BF16, mirror=False)
+    check("decode", wl.I8, mirror=False)
+
+
+@pytest.mark.parametrize("split", ["256", "512"])
+def test_new_tokens_across_a_split_boundary(split, monkeypatch):
+    """Fixed splits put a verification's new tokens on both sides of a split boundary: each
+    split's item writes its own."""
+    monkeypatch.setenv("KVATTN_SPLIT_TOKENS", split)
+    announce(f"append_forward across a split boundary ({split})")
+    w = wl.make("af_boundary", seed=602, dtype=wl.BF16, num_seqs_ctx=[2 * int(split) + 2, 1026],
+                q_lens=[4, 4], num_q_heads=40, num_kv_heads=8, head_dim=128)
+    a, b = DeviceCase(w), DeviceCase(w)
+    a.append()
+    ref = a.forward(mirror=True)
+    got = b.append_forward(mirror=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(raw(got), raw(ref))
+    for x, y in zip(a.host_pools(), b.host_pools()):
+        assert np.array_equal(np.asarray(x).view(np.uint8), np.asarray(y).view(np.uint8))
+
+
+def test_fp32_pool_falls_back():
+    announce("append_forward fp32")
+    w = wl.make("af_fp32", seed=603, dtype=wl.F32, num_seqs_ctx=[300, 700], q_lens=[1, 1],
+                num_q_heads=8, num_kv_heads=8, head_dim=64)
+    a, b = DeviceCase(w), DeviceCase(w)
+    a.append()
+    ref = a.forward(mirror=True)
+    got = b.append_forward(mirror=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(raw(got), raw(ref))
