@@ -203,10 +203,11 @@ KVPOOL_API int kvattn_forward(kvpool_t *pool, int32_t layer, const void *q, void
  * v_new, as for kvpool_append) are written into the pool, then every sequence attends as in
  * kvattn_forward (the pages' serving step appends a layer's new K/V and attends over the pool:
  * NInfer serving doc, "Execution behavior").  The result, pool and output, is bit for bit that
- * of the two calls.  When every sequence takes the split-K kernel (decode and verification
- * rows only, judged from q_lens_host when given, else from max_q_len), that kernel writes each
- * new token itself, in the work item whose keys hold it, before reading it: one launch fewer
- * per step.  Otherwise the append kernel runs first.  Arguments: those of both calls, with
+ * of the two calls.  On a bf16 pool, when every sequence takes the split-K kernel (decode and
+ * verification rows only, judged from q_lens_host when given, else from max_q_len), that
+ * kernel writes each new token itself, in the work item whose keys hold it, before reading it:
+ * one launch fewer per step.  Otherwise (int8 and fp32 pools, prefill chunks) the append
+ * kernel runs first.  Arguments: those of both calls, with
  * max_q_len bounding q_lens for both; each call's argument errors and (KVPOOL_VALIDATE)
  * metadata checks apply, and a nonzero return enqueues no work.  The workspace is
  * kvattn_workspace_size's. */

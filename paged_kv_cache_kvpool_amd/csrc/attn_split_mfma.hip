@@ -257,15 +257,16 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, const Item& it, bool
     return walk_tile_off<D>(a, kvh, tile0, ntile, it.vs1, it.vshift, ids0, ids1, tb, ti);
   };
   // Fused append (kvattn_append_forward): the new tokens whose keys fall in this item's range
-  // are written for its KV head (bit copies for bf16, append_row_i8 for int8: the same bits as
-  // the append kernel) just before the loads of the first chunk that holds one, so the walk's
+  // are written for its KV head (bit copies: the same bits as the append kernel) just before the loads of the first chunk that holds one, so the walk's
   // earlier chunks never queue behind the stores.  The wave's later loads of those bytes see
   // them without a wait: a wave's vector memory operations to one address are performed in
   // order (the compiler relies on the same for any thread's store-then-load); the empty asm
   // only keeps the compiler from moving loads above the stores.  Items of other row tiles of
   // the same split write the same bytes.
+  // (bf16 pools only: in the int8 kernel at two waves per SIMD the code would cost registers
+  // the walk needs, and int8 calls append with the append kernel.)
   const int p_new = L - T;  // the first new token (dense layout: virtual = real position)
-  const int c_new = (NW == 1 && a.k_new != nullptr && nch > 0 && p_new < we && L > wb)
+  const int c_new = (!I8 && NW == 1 && a.k_new != nullptr && nch > 0 && p_new < we && L > wb)
                         ? (max(p_new, wb) - wb) >> 5 : -1;  // wave-uniform
   auto append_new = [&]() {
     const uint16_t* kn = reinterpret_cast<const uint16_t*>(a.k_new);
@@ -276,12 +277,7 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, const Item& it, bool
       const size_t off = tile_off((p >> 4) - tile0);  // elements of the pool tile
       const int tt = p & 15;
       const size_t src = ((size_t)row * a.num_kv_heads + kvh) * D;
-      if constexpr (I8) {
-        int8_t* k8 = const_cast<int8_t*>(reinterpret_cast<const int8_t*>(a.k_layer));
-        int8_t* v8 = const_cast<int8_t*>(reinterpret_cast<const int8_t*>(a.v_layer));
-        append_row_i8<D / 64>(k8 + off, v8 + off, const_cast<float*>(a.k_scale_layer) + off / D,
-                              const_cast<float*>(a.v_scale_layer) + off / D, kn + src, vn + src, tt);
-      } else {
+      if constexpr (!I8) {
         uint16_t* kt = const_cast<uint16_t*>(kl) + off;
         uint16_t* vt = const_cast<uint16_t*>(vl) + off;
         if (lane < D / 8)  // K: 8-dim chunk `lane` of the token
@@ -295,7 +291,9 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, const Item& it, bool
   };
 
   auto load_chunk = [&](Chunk<D, I8>& c, int ci) {
-    if (ci == c_new) append_new();  // wave-uniform; once, before the chunk's own loads
+    if constexpr (!I8) {
+      if (ci == c_new) append_new();  // wave-uniform; once, before the chunk's own loads
+    }
     const size_t o0 = tile_off(2 * ci), o1 = tile_off(2 * ci + 1);
     if constexpr (I8) {
       // Byte offsets here (tile index = offset / (16 D)).  Buffer loads over the tile: a tile

@@ -709,10 +709,10 @@ int forward_impl(kvpool_t* pool, int32_t layer, const void* q, void* out, int32_
   const bool vec = pool->dtype == KV_F32 || (pool->dtype == KV_BF16 && sp.window == 0 && !pl.prefill &&
                                               max_q_len == 1 && env_flag("KVATTN_DECODE_VEC"));
   if (k_new) {
-    // Append inside the split-K kernel when every sequence takes it on persistent waves;
-    // otherwise the append kernel runs first, as kvpool_append would.
-    const bool fuse = !vec && !pl.prefill && pl.split_k && sp.window == 0 &&
-                      (pl.split == 0 || pl.split <= 2048);
+    // Append inside the split-K kernel when every sequence takes it on persistent waves (bf16
+    // pools); otherwise the append kernel runs first, as kvpool_append would.
+    const bool fuse = pool->dtype == KV_BF16 && !vec && !pl.prefill && pl.split_k &&
+                      sp.window == 0 && (pl.split == 0 || pl.split <= 2048);
     if (fuse) {
       a.k_new = k_new;
       a.v_new = v_new;
