@@ -344,30 +344,27 @@ class Device:
             out += [self.pool.k_scales.cpu().numpy(), self.pool.v_scales.cpu().numpy()]
         self._pre = tuple(out)
 
-    # kvattn_append_forward for dense steps with new tokens (the split-K kernel appends them
-    # itself when every sequence takes it); False: kvpool_append, then kvattn_forward.
+    # kvattn_append_forward(_sparse) for steps with new tokens (the split-K kernel appends them
+    # itself when every sequence takes it); False: kvpool_append, then the attention call.
     fused_append = True
 
     def step(self):
         w = self.w
-        if self.k_new is not None and w.sparse is None and self.fused_append:
-            self.pool.append_forward(w.layer, self.k_new, self.v_new, self.q, self.tables, self.ctx,
-                                     self.ql, scale=w.scale, max_ctx_len=self.max_ctx,
-                                     max_q_len=self.max_q, out=self.out, q_lens_host=self.ql_host)
+        common = dict(scale=w.scale, max_ctx_len=self.max_ctx, max_q_len=self.max_q, out=self.out,
+                      q_lens_host=self.ql_host)
+        sp = {} if w.sparse is None else dict(zip(("sink_tokens", "window_tokens", "min_ctx_len"),
+                                                  w.sparse))
+        args = (w.layer,)
+        if self.k_new is not None and self.fused_append:
+            call = self.pool.append_forward_sparse if sp else self.pool.append_forward
+            call(*args, self.k_new, self.v_new, self.q, self.tables, self.ctx, self.ql, **sp,
+                 **common)
             return
         if self.k_new is not None:
             self.pool.append(w.layer, self.k_new, self.v_new, self.tables, self.ctx, self.ql,
                              max_q_len=self.max_q)
-        if w.sparse is not None:
-            sink, window, min_len = w.sparse
-            self.pool.forward_sparse(w.layer, self.q, self.tables, self.ctx, self.ql,
-                                     scale=w.scale, sink_tokens=sink, window_tokens=window,
-                                     min_ctx_len=min_len, max_ctx_len=self.max_ctx,
-                                     max_q_len=self.max_q, out=self.out, q_lens_host=self.ql_host)
-        else:
-            self.pool.forward(w.layer, self.q, self.tables, self.ctx, self.ql, scale=w.scale,
-                              max_ctx_len=self.max_ctx, max_q_len=self.max_q, out=self.out,
-                              q_lens_host=self.ql_host)
+        call = self.pool.forward_sparse if sp else self.pool.forward
+        call(*args, self.q, self.tables, self.ctx, self.ql, **sp, **common)
 
 
 def bench_park_restore(args):
@@ -500,8 +497,8 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (scale for HBM counters)")
     ap.add_argument("--separate-append", action="store_true",
-                    help="append with kvpool_append, then kvattn_forward (default: one "
-                         "kvattn_append_forward call)")
+                    help="append with kvpool_append, then the attention call (default: one "
+                         "kvattn_append_forward(_sparse) call)")
     ap.add_argument("--flush", default="read", choices=["read", "write", "none"],
                     help="evict MALL and L2 between steps by reading (default) or writing 1 GiB")
     args = ap.parse_args()

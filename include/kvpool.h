@@ -242,6 +242,25 @@ KVPOOL_API int kvattn_forward_sparse(kvpool_t *pool, int32_t layer, const void *
                                      const int32_t *q_lens_host, void *workspace,
                                      size_t workspace_bytes, void *stream);
 
+/* kvpool_append followed by kvattn_forward_sparse, in one call (the sparse decode step of the
+ * same serving loop as kvattn_append_forward).  The result, pool and output, is bit for bit that
+ * of the two calls.  On a bf16 pool the split-K kernel writes each new token itself, in the work
+ * item whose (sparse) key range holds it: new tokens are the last q_len positions, which every
+ * row's window holds, so they always lie past the keys that sparsity skips.  On an int8 pool the
+ * append kernel runs first.  Arguments and errors: those of both calls (the sparse parameter
+ * checks come first); a nonzero return enqueues no work. */
+KVPOOL_API int kvattn_append_forward_sparse(kvpool_t *pool, int32_t layer, const void *k_new,
+                                            const void *v_new, const void *q, void *out,
+                                            int32_t num_q_heads, float scale,
+                                            const int32_t *block_tables,
+                                            int32_t max_blocks_per_seq, const int32_t *ctx_lens,
+                                            const int32_t *q_lens, int32_t num_seqs,
+                                            int32_t total_q, int32_t max_ctx_len,
+                                            int32_t max_q_len, int32_t sink_tokens,
+                                            int32_t window_tokens, int32_t min_ctx_len,
+                                            const int32_t *q_lens_host, void *workspace,
+                                            size_t workspace_bytes, void *stream);
+
 /* ---- host page store: park / restore pool blocks over PCIe ----------------------------------
  * Evicted sequences can be parked in pinned host memory instead of being discarded, each taking
  * only its real size, and computed prefixes restored over PCIe instead of being recomputed,

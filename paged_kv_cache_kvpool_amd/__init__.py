@@ -10,7 +10,7 @@ _BINDING_NAMES = {
     "kvpool_storage_bytes", "kvpool_scale_bytes", "kvpool_create", "kvpool_create_int8",
     "kvpool_destroy", "kvpool_append",
     "kvpool_copy_blocks", "kvattn_workspace_size", "kvattn_forward", "kvattn_forward_sparse",
-    "kvattn_append_forward",
+    "kvattn_append_forward", "kvattn_append_forward_sparse",
     "kvpool_last_error",
     "kvpool_profile", "kvpool_profile_kernel", "kernel_times",
     "PagedKVPool", "HostStore", "KVPoolError", "KV_F32", "KV_BF16", "KV_I8", "lib",

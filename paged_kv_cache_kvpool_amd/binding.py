@@ -45,6 +45,9 @@ SIGNATURES = {
                                      _vp, _i32, _i32, _i32, _i32, _vp, _vp, _sz, _vp]),
     "kvattn_forward_sparse": (_i32, [_vp, _i32, _vp, _vp, _i32, _f32, _vp, _i32, _vp, _vp, _i32,
                                      _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _sz, _vp]),
+    "kvattn_append_forward_sparse": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _i32, _f32, _vp, _i32,
+                                            _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
+                                            _vp, _vp, _sz, _vp]),
     "kvhost_page_bytes": (_i32, [_vp, ctypes.POINTER(_sz)]),
     "kvhost_create": (_i32, [ctypes.POINTER(_vp), _vp, _sz]),
     "kvhost_destroy": (_i32, [_vp]),
@@ -238,6 +241,20 @@ def kvattn_forward_sparse(handle, layer, q, out, num_q_heads, scale, block_table
     del arr
 
 
+def kvattn_append_forward_sparse(handle, layer, k_new, v_new, q, out, num_q_heads, scale,
+                                 block_tables, max_blocks_per_seq, ctx_lens, q_lens, num_seqs,
+                                 total_q, max_ctx_len, max_q_len, sink_tokens, window_tokens,
+                                 min_ctx_len, workspace, workspace_bytes, stream=None,
+                                 q_lens_host=None) -> None:
+    arr, addr = _host_i32(q_lens_host)
+    _check(lib().kvattn_append_forward_sparse(
+        handle, layer, _ptr(k_new), _ptr(v_new), _ptr(q), _ptr(out), num_q_heads, float(scale),
+        _ptr(block_tables), max_blocks_per_seq, _ptr(ctx_lens), _ptr(q_lens), num_seqs, total_q,
+        max_ctx_len, max_q_len, sink_tokens, window_tokens, min_ctx_len, addr, _ptr(workspace),
+        workspace_bytes, _stream(stream)))
+    del arr
+
+
 # ---------------------------------------------------------------------------------------------
 # Convenience wrapper: owns torch storage for one pool and sizes the workspace.
 # ---------------------------------------------------------------------------------------------
@@ -369,6 +386,26 @@ class PagedKVPool:
                               block_tables.shape[1], ctx_lens, q_lens, ctx_lens.shape[0], total_q,
                               max_ctx_len, max_q_len, sink_tokens, window_tokens, min_ctx_len,
                               ws, need, stream, q_lens_host)
+        return out
+
+    def append_forward_sparse(self, layer, k_new, v_new, q, block_tables, ctx_lens, q_lens,
+                              scale=None, sink_tokens=None, window_tokens=4096,
+                              min_ctx_len=16384, max_ctx_len=None, max_q_len=None, out=None,
+                              stream=None, q_lens_host=None):
+        """append(k_new, v_new) then forward_sparse(q) in one call."""
+        total_q, hq, d = q.shape
+        scale = 1.0 / math.sqrt(d) if scale is None else scale
+        sink_tokens = self.block_size if sink_tokens is None else sink_tokens
+        max_ctx_len = int(ctx_lens.max().item()) if max_ctx_len is None else max_ctx_len
+        max_q_len = int(q_lens.max().item()) if max_q_len is None else max_q_len
+        out = torch.empty_like(q) if out is None else out
+        ws, need = self.workspace(hq, ctx_lens.shape[0], total_q, max_ctx_len, max_q_len,
+                                  q_lens_host)
+        kvattn_append_forward_sparse(self.handle, layer, k_new, v_new, q, out, hq, scale,
+                                     block_tables, block_tables.shape[1], ctx_lens, q_lens,
+                                     ctx_lens.shape[0], total_q, max_ctx_len, max_q_len,
+                                     sink_tokens, window_tokens, min_ctx_len, ws, need, stream,
+                                     q_lens_host)
         return out
 
 

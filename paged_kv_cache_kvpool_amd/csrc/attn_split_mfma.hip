@@ -265,16 +265,21 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, const Item& it, bool
   // the same split write the same bytes.
   // (bf16 pools only: in the int8 kernel at two waves per SIMD the code would cost registers
   // the walk needs, and int8 calls append with the append kernel.)
-  const int p_new = L - T;  // the first new token (dense layout: virtual = real position)
-  const int c_new = (!I8 && NW == 1 && a.k_new != nullptr && nch > 0 && p_new < we && L > wb)
-                        ? (max(p_new, wb) - wb) >> 5 : -1;  // wave-uniform
+  // New tokens are the last T real positions; under sparsity they sit past the layout's gap
+  // (the window always holds them), so their virtual positions are contiguous too.
+  const int p_new = L - T;
+  const int v_new = virt_key(p_new, it.vs1, it.vshift);  // virtual position of the first
+  const int v_end = v_new + T;
+  const int c_new = (!I8 && NW == 1 && a.k_new != nullptr && nch > 0 && v_new < we && v_end > wb)
+                        ? (max(v_new, wb) - wb) >> 5 : -1;  // wave-uniform
   auto append_new = [&]() {
     const uint16_t* kn = reinterpret_cast<const uint16_t*>(a.k_new);
     const uint16_t* vn = reinterpret_cast<const uint16_t*>(a.v_new);
-    for (int p = max(p_new, wb); p < min(L, we); ++p) {
+    for (int vp = max(v_new, wb); vp < min(v_end, we); ++vp) {
+      const int p = p_new + (vp - v_new);  // real position
       const int row = q_start + (p - p_new);
       if (row >= a.total_q) continue;
-      const size_t off = tile_off((p >> 4) - tile0);  // elements of the pool tile
+      const size_t off = tile_off((vp >> 4) - tile0);  // elements of the pool tile
       const int tt = p & 15;
       const size_t src = ((size_t)row * a.num_kv_heads + kvh) * D;
       if constexpr (!I8) {

@@ -712,7 +712,7 @@ int forward_impl(kvpool_t* pool, int32_t layer, const void* q, void* out, int32_
     // Append inside the split-K kernel when every sequence takes it on persistent waves (bf16
     // pools); otherwise the append kernel runs first, as kvpool_append would.
     const bool fuse = pool->dtype == KV_BF16 && !vec && !pl.prefill && pl.split_k &&
-                      sp.window == 0 && (pl.split == 0 || pl.split <= 2048);
+                      (pl.split == 0 || pl.split <= 2048);
     if (fuse) {
       a.k_new = k_new;
       a.v_new = v_new;
@@ -790,13 +790,16 @@ int kvattn_forward(kvpool_t* pool, int32_t layer, const void* q, void* out, int3
                       q_lens_host, workspace, workspace_bytes, stream);
 }
 
-int kvattn_append_forward(kvpool_t* pool, int32_t layer, const void* k_new, const void* v_new,
-                          const void* q, void* out, int32_t num_q_heads, float scale,
-                          const int32_t* block_tables, int32_t max_blocks_per_seq,
-                          const int32_t* ctx_lens, const int32_t* q_lens, int32_t num_seqs,
-                          int32_t total_q, int32_t max_ctx_len, int32_t max_q_len,
-                          const int32_t* q_lens_host, void* workspace, size_t workspace_bytes,
-                          void* stream) {
+}  // extern "C"
+
+namespace {
+int append_forward_impl(kvpool_t* pool, int32_t layer, const void* k_new, const void* v_new,
+                        const void* q, void* out, int32_t num_q_heads, float scale,
+                        const int32_t* block_tables, int32_t max_blocks_per_seq,
+                        const int32_t* ctx_lens, const int32_t* q_lens, int32_t num_seqs,
+                        int32_t total_q, int32_t max_ctx_len, int32_t max_q_len, Sparse sp,
+                        const int32_t* q_lens_host, void* workspace, size_t workspace_bytes,
+                        void* stream) {
   hipStream_t st = reinterpret_cast<hipStream_t>(stream);
   bool nothing = false;
   if (int rc = append_check(pool, layer, k_new, v_new, block_tables, max_blocks_per_seq, ctx_lens,
@@ -804,14 +807,48 @@ int kvattn_append_forward(kvpool_t* pool, int32_t layer, const void* k_new, cons
     return rc;
   if (nothing)
     return forward_impl(pool, layer, q, out, num_q_heads, scale, block_tables, max_blocks_per_seq,
-                        ctx_lens, q_lens, num_seqs, total_q, max_ctx_len, max_q_len,
-                        Sparse{0, 0, 0}, q_lens_host, workspace, workspace_bytes, stream);
+                        ctx_lens, q_lens, num_seqs, total_q, max_ctx_len, max_q_len, sp,
+                        q_lens_host, workspace, workspace_bytes, stream);
   // (forward_impl returns before its launches only when it has no row: then nothing may be
   // appended either, which these bounds guarantee)
   if (max_ctx_len < max_q_len) return fail(KV_EINVAL, "max_q_len > max_ctx_len");
   return forward_impl(pool, layer, q, out, num_q_heads, scale, block_tables, max_blocks_per_seq,
-                      ctx_lens, q_lens, num_seqs, total_q, max_ctx_len, max_q_len, Sparse{0, 0, 0},
+                      ctx_lens, q_lens, num_seqs, total_q, max_ctx_len, max_q_len, sp,
                       q_lens_host, workspace, workspace_bytes, stream, k_new, v_new);
+}
+}  // namespace
+
+extern "C" {
+
+int kvattn_append_forward(kvpool_t* pool, int32_t layer, const void* k_new, const void* v_new,
+                          const void* q, void* out, int32_t num_q_heads, float scale,
+                          const int32_t* block_tables, int32_t max_blocks_per_seq,
+                          const int32_t* ctx_lens, const int32_t* q_lens, int32_t num_seqs,
+                          int32_t total_q, int32_t max_ctx_len, int32_t max_q_len,
+                          const int32_t* q_lens_host, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  return append_forward_impl(pool, layer, k_new, v_new, q, out, num_q_heads, scale, block_tables,
+                             max_blocks_per_seq, ctx_lens, q_lens, num_seqs, total_q, max_ctx_len,
+                             max_q_len, Sparse{0, 0, 0}, q_lens_host, workspace, workspace_bytes,
+                             stream);
+}
+
+int kvattn_append_forward_sparse(kvpool_t* pool, int32_t layer, const void* k_new,
+                                 const void* v_new, const void* q, void* out,
+                                 int32_t num_q_heads, float scale, const int32_t* block_tables,
+                                 int32_t max_blocks_per_seq, const int32_t* ctx_lens,
+                                 const int32_t* q_lens, int32_t num_seqs, int32_t total_q,
+                                 int32_t max_ctx_len, int32_t max_q_len, int32_t sink_tokens,
+                                 int32_t window_tokens, int32_t min_ctx_len,
+                                 const int32_t* q_lens_host, void* workspace,
+                                 size_t workspace_bytes, void* stream) {
+  if (sink_tokens < 0 || window_tokens < 1 || min_ctx_len < 0)
+    return fail(KV_EINVAL, "sparse attention needs sink_tokens >= 0, window_tokens >= 1, "
+                "min_ctx_len >= 0 (got %d, %d, %d)", sink_tokens, window_tokens, min_ctx_len);
+  return append_forward_impl(pool, layer, k_new, v_new, q, out, num_q_heads, scale, block_tables,
+                             max_blocks_per_seq, ctx_lens, q_lens, num_seqs, total_q, max_ctx_len,
+                             max_q_len, Sparse{sink_tokens, window_tokens, min_ctx_len},
+                             q_lens_host, workspace, workspace_bytes, stream);
 }
 
 int kvattn_forward_sparse(kvpool_t* pool, int32_t layer, const void* q, void* out,

@@ -107,6 +107,17 @@ class DeviceCase:
                                         max_q_len=int(w.q_lens.max()), out=out,
                                         q_lens_host=w.q_lens if mirror else None)
 
+    def append_forward_sparse(self, sink, window, min_len, out=None, mirror=False):
+        """Append and sparse attention in one call (kvattn_append_forward_sparse)."""
+        w = self.w
+        return self.pool.append_forward_sparse(w.layer, self.k_new, self.v_new, self.q,
+                                               self.tables, self.ctx, self.ql, scale=w.scale,
+                                               sink_tokens=sink, window_tokens=window,
+                                               min_ctx_len=min_len,
+                                               max_ctx_len=int(w.ctx_lens.max()),
+                                               max_q_len=int(w.q_lens.max()), out=out,
+                                               q_lens_host=w.q_lens if mirror else None)
+
     # -- host copies for the oracle ---------------------------------------------------------
     def host_pools(self):
         """Host copies of the device pool: (K, V), or (K, V, K scales, V scales) for int8."""

@@ -85,6 +85,9 @@ def test_null_handles():
     assert lib.kvpool_append(None, 0, None, None, None, 1, None, None, 1, 1, 1, None) == kb.KV_EINVAL
     assert lib.kvattn_append_forward(None, 0, None, None, None, None, 8, 1.0, None, 1, None, None,
                                      1, 1, 1, 1, None, None, 0, None) == kb.KV_EINVAL
+    assert lib.kvattn_append_forward_sparse(None, 0, None, None, None, None, 8, 1.0, None, 1,
+                                            None, None, 1, 1, 1, 1, 16, 4096, 16384, None, None,
+                                            0, None) == kb.KV_EINVAL
     assert lib.kvpool_copy_blocks(None, None, None, 1, None) == kb.KV_EINVAL
     sz = ctypes.c_size_t(0)
     assert lib.kvattn_workspace_size(None, 8, 1, 1, 1, 1, None, ctypes.byref(sz)) == kb.KV_EINVAL
@@ -97,6 +100,10 @@ def test_sparse_rejects_bad_parameters(sink, window, min_len):
     lib = kb.lib()
     assert lib.kvattn_forward_sparse(None, 0, None, None, 8, 1.0, None, 1, None, None, 1, 1, 1, 1,
                                      sink, window, min_len, None, None, 0, None) == kb.KV_EINVAL
+    assert "sparse" in kb.kvpool_last_error()
+    assert lib.kvattn_append_forward_sparse(None, 0, None, None, None, None, 8, 1.0, None, 1,
+                                            None, None, 1, 1, 1, 1, sink, window, min_len, None,
+                                            None, 0, None) == kb.KV_EINVAL
     assert "sparse" in kb.kvpool_last_error()
 
 

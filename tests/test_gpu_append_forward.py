@@ -3,7 +3,9 @@ whole pool after the call equal, bit for bit, those of kvpool_append followed by
 on an identical second pool, and the output matches the oracle.  Split-K calls (decode,
 verification, many sequences, int8 pools, new tokens on both sides of a split boundary) append
 inside the split-K kernel; calls with prefill chunks, fp32 pools and the vector path fall back to
-the append kernel.
+the append kernel.  kvattn_append_forward_sparse is held to the same bar against kvpool_append
+followed by kvattn_forward_sparse (sequences below and above the sparse threshold, new tokens
+past the skipped keys, fixed splits that cut the window) and against the sparse oracle.
 """
 import sys
 
@@ -101,3 +103,47 @@ def test_fp32_pool_falls_back():
     got = b.append_forward(mirror=True)
     torch.cuda.synchronize()
     assert np.array_equal(raw(got), raw(ref))
+
+
+SPARSE = {  # (workload arguments, sink, window, min_len)
+    "pages": (dict(num_seqs_ctx=[16383, 16384, 16385, 20000, 40000, 1000, 16400], q_lens=[1] * 7,
+                   num_q_heads=32, num_kv_heads=8), 16, 4096, 16384),
+    "verify": (dict(num_seqs_ctx=[16385, 16387, 16390, 30000, 16384], q_lens=[4] * 5,
+                    num_q_heads=40, num_kv_heads=8), 16, 4096, 16384),
+    "small": (dict(num_seqs_ctx=[700, 301, 1500, 90, 2222], q_lens=[1, 4, 2, 1, 3],
+                   num_q_heads=8, num_kv_heads=2), 5, 100, 300),
+}
+
+
+def check_sparse(name, dtype, seed=611, mirror=True):
+    cfg, sink, window, min_len = SPARSE[name]
+    announce(f"append_forward_sparse {name} {dtype} mirror={mirror}")
+    w = wl.make(f"afs_{name}_{dtype}", seed=seed, dtype=dtype, head_dim=128, **cfg)
+    a, b = DeviceCase(w), DeviceCase(w)
+    a.append()
+    ref = a.forward_sparse(sink, window, min_len, mirror=mirror)
+    got = b.append_forward_sparse(sink, window, min_len, mirror=mirror)
+    torch.cuda.synchronize()
+    assert np.array_equal(raw(got), raw(ref)), "output differs from append + forward_sparse"
+    for x, y in zip(a.host_pools(), b.host_pools()):
+        assert np.array_equal(np.asarray(x).view(np.uint8), np.asarray(y).view(np.uint8)), \
+            "pool differs from append + forward_sparse"
+    assert_close(out_f64(got), b.oracle_sparse(sink, window, min_len), dtype, w.name)
+
+
+@pytest.mark.parametrize("name", ["pages", "verify", "small"])
+@pytest.mark.parametrize("dtype", [wl.BF16, wl.I8])
+def test_append_forward_sparse(name, dtype):
+    check_sparse(name, dtype)
+
+
+def test_append_forward_sparse_without_mirror():
+    check_sparse("verify", wl.BF16, mirror=False)
+
+
+@pytest.mark.parametrize("split", ["256", "1024"])
+def test_sparse_new_tokens_with_fixed_splits(split, monkeypatch):
+    """Fixed splits cut the sparse key range (sink, then the window) into several items; the
+    new tokens sit in the last one or straddle two."""
+    monkeypatch.setenv("KVATTN_SPLIT_TOKENS", split)
+    check_sparse("verify", wl.BF16, seed=612)
