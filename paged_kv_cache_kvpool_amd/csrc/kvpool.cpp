@@ -54,10 +54,11 @@ bool env_flag(const char* name) {
   return v && *v && strcmp(v, "0") != 0;
 }
 
-// Keys per split in split mode: 0 selects the per-length rule the kernels apply to each
-// sequence (a power of two in [256, 2048], about L/128), KVATTN_SPLIT_TOKENS fixes a count for
-// tuning sweeps.  Neither depends on the rest of the batch, so each sequence's reduction order
-// is a function of its own length only.
+// Keys per split in split mode: 0 selects the per-sequence rule the kernels apply (about L/128
+// rounded up to 32 keys, within [512, 2048] for sequences whose rows per KV head fit one 16-row
+// tile and [256, 2048] otherwise), KVATTN_SPLIT_TOKENS fixes a count for tuning sweeps.  Neither
+// depends on the rest of the batch, so each sequence's reduction order is a function of its own
+// length and row count only.
 int split_tokens() {
   const char* v = getenv("KVATTN_SPLIT_TOKENS");
   if (!v || !*v) return 0;
@@ -68,7 +69,7 @@ int split_tokens() {
 // Upper bound of a sequence's split count over all lengths <= max_ctx.
 int max_split_count(int split, int max_ctx) {
   if (split > 0) return std::max(1, (max_ctx + split - 1) / split);
-  // The rule (ceil(L/128) rounded up to 32, within [256, 2048]) gives at most
+  // The rule (ceil(L/128) rounded up to 32, within [256 or 512, 2048]) gives at most
   // min(128, ceil(L/256)) splits up to 262144 keys and ceil(L/2048) past that.
   return std::max(std::max(1, std::min(128, (max_ctx + 255) / 256)), (max_ctx + 2047) / 2048);
 }
