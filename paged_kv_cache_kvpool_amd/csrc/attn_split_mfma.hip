@@ -132,6 +132,7 @@ __device__ __forceinline__ bool item_keys(const AttnArgs& a, Item& it) {
   it.wlo_max = -1;
   if (it.T > a.split_q_max) return false;  // a prefill-class sequence
   const int rows = it.T * a.group;
+  if (rows <= a.split_rows_lo || rows > a.split_rows_hi) return false;  // another launch's
   const int r0 = it.rt * 16 * NT;
   if (r0 >= rows) return false;
   const int p_last = it.L - it.T + (min(r0 + 16 * NT, rows) - 1) / a.group;
@@ -701,6 +702,7 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, const Item& it, bool
 template <int NT>
 __device__ __forceinline__ int seq_items(const AttnArgs& a, int L, int T) {
   if (T <= 0 || T > a.split_q_max) return 0;  // no rows, or a prefill-class sequence
+  if (T * a.group <= a.split_rows_lo || T * a.group > a.split_rows_hi) return 0;  // another launch's
   int Lv, vs1, vshift;
   seq_vlayout(a, L, T, Lv, vs1, vshift);
   const int split = seq_split(a, Lv, T);

@@ -164,6 +164,8 @@ struct AttnArgs {
   int32_t max_splits;       // splits per partial row in the workspace
   int32_t row_tiles;        // split-K and vector kernels: row tiles per (sequence, kv head)
   int32_t split_q_max;      // sequences with q_len <= split_q_max take the split-K path
+  int32_t split_rows_lo;    // split-K kernels: only sequences with lo < q_len * group <= hi
+  int32_t split_rows_hi;    // (a call may run its short and long sequences in two launches)
   int32_t part_rows;        // rows of the partial buffers (query tokens of the split-K path)
   int32_t pf_rblk;          // prefill kernel: 32-row blocks per workgroup
   // Prefill key splits (pf_ksplit > 1): each row tile's keys are cut into pf_ksplit ranges of

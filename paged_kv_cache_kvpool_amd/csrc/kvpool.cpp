@@ -453,6 +453,7 @@ struct Plan {
   bool split_k;       // some sequence may take the split-K path with at least one row
   bool prefill;       // some sequence may take the prefill kernel
   int split_rows;     // rows per KV head of the longest split-K sequence (bound)
+  int split_rows_min; // rows per KV head of the shortest split-K sequence with rows (0: unknown)
   int split;          // fixed keys per split, or 0 for the per-length rule
   int max_splits;     // split slots per partial row
   int part_rows;      // partial rows: the split-K path's query tokens (or a bound of them)
@@ -485,12 +486,13 @@ Plan make_plan(const kvpool* p, int32_t num_q_heads, int32_t num_seqs, int32_t t
   int n_pf_exact = 0;
   if (q_lens_host) {
     long long split_tokens_sum = 0;
-    int split_t = 0;
+    int split_t = 0, split_t_min = 0;
     for (int s = 0; s < num_seqs; ++s) {
       const int T = std::max(0, std::min(q_lens_host[s], max_q_len));
       if (T <= sqm) {
         split_tokens_sum += T;
         split_t = std::max(split_t, T);
+        if (T > 0) split_t_min = split_t_min ? std::min(split_t_min, T) : T;
       } else {
         pf_rows.push_back(T * G);
         ++n_pf_exact;
@@ -498,11 +500,13 @@ Plan make_plan(const kvpool* p, int32_t num_q_heads, int32_t num_seqs, int32_t t
     }
     pl.split_k = split_tokens_sum > 0;
     pl.split_rows = split_t * G;
+    pl.split_rows_min = split_t_min * G;
     pl.part_rows = (int)std::min<long long>(split_tokens_sum, total_q);
     pl.prefill = !pf_rows.empty();
   } else {
     pl.split_k = true;
     pl.split_rows = std::min(max_q_len, sqm) * G;
+    pl.split_rows_min = 0;
     pl.prefill = max_q_len > sqm;
     // When every sequence is split-K, all query tokens are; otherwise each split-K sequence
     // holds at most split_q_max of them.
@@ -665,6 +669,8 @@ int forward_impl(kvpool_t* pool, int32_t layer, const void* q, void* out, int32_
   }
 
   kvp::AttnArgs a;
+  a.split_rows_lo = 0;
+  a.split_rows_hi = INT32_MAX;
   const size_t lo = (size_t)layer * pool->layer_elems * elt_bytes(pool->dtype);
   a.q = q;
   a.out = out;
@@ -734,10 +740,26 @@ int forward_impl(kvpool_t* pool, int32_t layer, const void* q, void* out, int32_
     // Split-K sequences (decode, verification) on persistent waves, then the prefill kernel
     // for the longer query blocks of the same call.  Each kernel skips the other's sequences.
     if (pl.split_k) {
-      const int rpt = pl.split_rows <= 16 ? 16 : 32;
-      kvp::AttnArgs as = a;
-      as.row_tiles = (pl.split_rows + rpt - 1) / rpt;
-      e = timed(K_SPLIT_MFMA, st, [&] { return kvp::launch_attn_split_mfma(as, pool->head_dim, rpt, pl.max_splits, pool->num_cus, i8, st); });
+      // Sequences with rows per KV head in (lo, hi], in 16- or 32-row tiles.
+      auto split_launch = [&](int rows, int lo_rows, int hi_rows) {
+        const int rpt = rows <= 16 ? 16 : 32;
+        kvp::AttnArgs as = a;
+        as.row_tiles = (rows + rpt - 1) / rpt;
+        as.split_rows_lo = lo_rows;
+        as.split_rows_hi = hi_rows;
+        return kvp::launch_attn_split_mfma(as, pool->head_dim, rpt, pl.max_splits, pool->num_cus,
+                                           i8, st);
+      };
+      // When the host's q_lens show sequences of at most 16 rows per KV head (decode) beside
+      // longer ones (verification), the short ones take the 16-row kernel, which runs twice the
+      // waves, and the others the 32-row kernel, one launch after the other.  (One 32-row launch
+      // for all would leave most of a decode item's tile empty.)  Timed as one stage.
+      const bool two = pl.split_rows > 16 && pl.split_rows_min > 0 && pl.split_rows_min <= 16;
+      e = timed(K_SPLIT_MFMA, st, [&] {
+        if (!two) return split_launch(pl.split_rows, 0, INT32_MAX);
+        hipError_t r = split_launch(16, 0, 16);
+        return r == hipSuccess ? split_launch(pl.split_rows, 16, INT32_MAX) : r;
+      });
     }
     if (e == hipSuccess && pl.prefill) {
       kvp::AttnArgs ap = a;

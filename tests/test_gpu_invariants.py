@@ -110,6 +110,26 @@ def test_mixed_batch_invariance_bitwise(dtype, monkeypatch):
             assert np.array_equal(bits(alone), bits(full[rows])), f"sequence {s} mirror={mirror}"
 
 
+@pytest.mark.parametrize("dtype", [wl.BF16, wl.I8])
+def test_decode_beside_verification_two_launches(dtype):
+    """Decode sequences (5 rows per KV head) beside verifications (20 rows) in one call: with the
+    host's q_lens the decode sequences take the 16-row kernel and the verifications the 32-row
+    one (two launches); from the bounds alone, one 32-row launch serves all.  Both plans give
+    the same bits (a row's arithmetic does not depend on the tile it shares), and they match
+    the oracle."""
+    announce(f"decode beside verification, two launches, {dtype}")
+    w = wl.make(f"two_launch_{dtype}", seed=152, dtype=dtype,
+                num_seqs_ctx=[3000, 32772, 700, 9000, 5000, 2050, 17, 4100],
+                q_lens=[1, 4, 1, 1, 4, 4, 1, 1], num_q_heads=40, num_kv_heads=8, head_dim=128)
+    c = DeviceCase(w)
+    c.append()
+    one = c.forward()
+    two = c.forward(mirror=True)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(one), bits(two)), "one launch vs two"
+    assert_close(out_f64(two), c.oracle(), dtype, w.name)
+
+
 @pytest.mark.parametrize("dtype,bs", [(wl.BF16, 16), (wl.BF16, 64), (wl.F32, 16)])
 def test_nan_in_unread_slots(dtype, bs):
     """Pool starts all-NaN; the append writes exactly the context, so every slot past ctx_len and
