@@ -29,7 +29,7 @@ __global__ __launch_bounds__(256) void attn_reduce_kernel(AttnArgs a) {
   int Lv, vs1, vshift;
   seq_vlayout(a, L, T, Lv, vs1, vshift);  // the splits cut the sequence's virtual key positions
   const int p = virt_key(L - T + i, vs1, vshift);
-  const int ns = min(a.max_splits, p / seq_split(a, Lv, T) + 1);
+  const int ns = min(a.max_splits, p / seq_split(a, Lv, T, vshift > 0) + 1);
   if (ns <= 1) return;
   const int grow = q_start + i;
   if (grow >= a.total_q) return;

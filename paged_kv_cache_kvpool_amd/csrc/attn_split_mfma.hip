@@ -139,7 +139,7 @@ __device__ __forceinline__ bool item_keys(const AttnArgs& a, Item& it) {
   int Lv;
   seq_vlayout(a, it.L, it.T, Lv, it.vs1, it.vshift);
   it.wlo_max = (a.sparse_window > 0 && p_last + 1 >= a.sparse_min) ? p_last - a.sparse_window : -1;
-  it.split = seq_split(a, Lv, it.T);
+  it.split = seq_split(a, Lv, it.T, it.vshift > 0);
   it.kb = it.sp * it.split;
   it.ke = min(min(Lv, virt_key(p_last, it.vs1, it.vshift) + 1), it.kb + it.split);
   return it.kb < it.ke;
@@ -705,7 +705,7 @@ __device__ __forceinline__ int seq_items(const AttnArgs& a, int L, int T) {
   if (T * a.group <= a.split_rows_lo || T * a.group > a.split_rows_hi) return 0;  // another launch's
   int Lv, vs1, vshift;
   seq_vlayout(a, L, T, Lv, vs1, vshift);
-  const int split = seq_split(a, Lv, T);
+  const int split = seq_split(a, Lv, T, vshift > 0);
   const int ns = min(Lv / split + (Lv % split != 0), a.max_splits);
   const int rts = min((T * a.group + 16 * NT - 1) / (16 * NT), a.row_tiles);
   return ns * a.num_kv_heads * rts;

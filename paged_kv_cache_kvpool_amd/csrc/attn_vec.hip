@@ -63,7 +63,7 @@ __global__ __launch_bounds__(64) void attn_vec_kernel(AttnArgs a) {
   // make one pass over all their keys, in split slot 0.
   const bool split_k = T <= a.split_q_max;
   if (!split_k && sp > 0) return;
-  const int split = split_k ? seq_split(a, L, T) : L;
+  const int split = split_k ? seq_split(a, L, T, false) : L;
   const int kb = split_k ? sp * split : 0;
   const int ke = min(min(L, p_last + 1), kb + split);
   if (kb >= ke) return;

@@ -185,19 +185,21 @@ struct AttnArgs {
   const void* v_new;
 };
 
-// Keys per split of a sequence with L keys and T query rows on the split-K path: a fixed count
-// if the caller set one, else ceil(L/128) rounded up to a multiple of 32 and clamped to
-// [lo, 2048], where lo = 512 when the sequence's rows per KV head (T times the group size) fit
-// one 16-row tile and 256 otherwise.  That gives at most 128 splits up to 262144 keys (so one
-// long sequence's splits fit the GPU in one pass, with no sliver of a split left over).  Short
-// single-tile sequences come in batches, where the wider floor halves their items and partials
-// (measured: 32 decode sequences of 1-8K keys 4% faster in bf16, 8% in int8); a verification's
-// two-tile items gain nothing from it (32K keys: 6% slower).  The split depends on the
-// sequence's own length and row count only, so its reduction order does too.
-__device__ __forceinline__ int seq_split(const AttnArgs& a, int L, int T) {
+// Keys per split of a sequence with L (virtual) keys and T query rows on the split-K path: a
+// fixed count if the caller set one, else ceil(L/128) rounded up to a multiple of 32 and clamped
+// to [lo, 2048], where lo = 512 when the sequence's rows per KV head (T times the group size)
+// fit one 16-row tile and its keys have no sparse gap (gapped: vshift > 0), and 256 otherwise.
+// That gives at most 128 splits up to 262144 keys (so one long sequence's splits fit the GPU in
+// one pass, with no sliver of a split left over).  Short single-tile sequences come in batches,
+// where the wider floor halves their items and partials (measured: 32 decode sequences of 1-8K
+// keys 4% faster in bf16, 8% in int8); a verification's two-tile items gain nothing from it
+// (32K keys: 6% slower), nor does a sparse walk of one window, whose few items bound its
+// latency (two 4K-key windows: 14 -> 20 us).  The split depends on the sequence alone, so its
+// reduction order does too.
+__device__ __forceinline__ int seq_split(const AttnArgs& a, int L, int T, bool gapped) {
   if (a.split_tokens > 0) return a.split_tokens;
   const int per = (L >> 7) + ((L & 127) != 0);  // ceil(L / 128) without overflow
-  const int lo = T * a.group <= 16 ? 512 : 256;
+  const int lo = T * a.group <= 16 && !gapped ? 512 : 256;
   return min(max((per + 31) & ~31, lo), 2048);
 }
 
