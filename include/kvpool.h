@@ -32,7 +32,7 @@
  *     stream) and every violation returns KV_ERANGE.  Without validation, kernels clamp ids and
  *     lengths into range so that bad metadata gives wrong values, never an out-of-bounds access.
  *   - Determinism: no float atomics, so every call is bitwise reproducible.  The split of a
- *     decode or verification sequence's keys depends only on that sequence's own length, so its
+ *     decode or verification sequence's keys depends only on that sequence's own lengths, so its
  *     output is bitwise independent of the rest of the batch and of where its blocks sit in the
  *     pool.  Prefill-class sequences are batch-invariant too with KVATTN_DETERMINISTIC=1 (see
  *     kvattn_forward); the pages' decode path has no float atomics and their deterministic mode
@@ -161,7 +161,9 @@ KVPOOL_API int kvattn_workspace_size(const kvpool_t *pool, int32_t num_q_heads,
  * step packs every ready request into one batch (NInfer serving doc, "Execution behavior";
  * sparkinfer server README, "Request isolation & continuous batching").  A sequence with
  * q_len * (num_q_heads / num_kv_heads) <= 128 takes the split-K kernel (its keys cut into splits
- * of a size set by its own ctx_len, merged in a fixed order); a longer one takes the prefill
+ * of a size set by its own ctx_len and q_len, merged in a fixed order; when q_lens_host shows
+ * sequences of at most 16 rows per KV head beside longer ones, the two kinds run in two
+ * launches of 16- and 32-row tiles, with the same bits as one); a longer one takes the prefill
  * kernel.  Decode and verification sequences: the path and the arithmetic follow from the
  * sequence's own lengths, so their output bits never depend on the rest of the batch or on the
  * bounds passed here.  Prefill-class sequences: the workgroup plan follows the call (for speed,
