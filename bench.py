@@ -503,7 +503,7 @@ def main():
                     help="evict MALL and L2 between steps by reading (default) or writing 1 GiB")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
               f"(asked for --gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
 
