@@ -130,6 +130,22 @@ def test_decode_beside_verification_two_launches(dtype):
     assert_close(out_f64(two), c.oracle(), dtype, w.name)
 
 
+@pytest.mark.parametrize("dtype", [wl.BF16, wl.I8, wl.F32])
+@pytest.mark.parametrize("mirror", [False, True], ids=["bounds", "mirror"])
+def test_short_decode_without_reduce(dtype, mirror):
+    """Decode sequences of at most 512 keys (single-tile rows take 512-key splits): the call
+    skips the reduce launch, and every row still matches the oracle."""
+    announce(f"short decode without reduce {dtype} mirror={mirror}")
+    w = wl.make(f"short_dec_{dtype}", seed=153, dtype=dtype,
+                num_seqs_ctx=[300, 400, 512, 257, 511, 33], q_lens=[1] * 6, num_q_heads=32,
+                num_kv_heads=8, head_dim=128)
+    c = DeviceCase(w)
+    c.append()
+    out = c.forward(mirror=mirror)
+    torch.cuda.synchronize()
+    assert_close(out_f64(out), c.oracle(), dtype, w.name)
+
+
 @pytest.mark.parametrize("dtype,bs", [(wl.BF16, 16), (wl.BF16, 64), (wl.F32, 16)])
 def test_nan_in_unread_slots(dtype, bs):
     """Pool starts all-NaN; the append writes exactly the context, so every slot past ctx_len and
