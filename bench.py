@@ -2,6 +2,12 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 
+Without --workload the run measures every configuration of the hot path in one process: the
+batched GQA decode (32 sequences, 1-8K keys) as the top-level fields, and the tiny fp32 decode,
+the two speculative verifications (32K and 128K keys), the prefix-reuse chunked prefill and
+the long-context decode (262144 + 131072 keys) under "configs", each with its own step time,
+roofline (kernel and step fraction, target and whether it is met), traffic and CPU baseline.
+
 One step is one pass of the hot path over one batch: append the new tokens' K/V into their
 pool blocks (kvpool_append), then attention against the paged pool (kvattn_forward: the split
 attention kernel or the prefill kernel, plus the cross-split reduce in split mode).  Inputs are
@@ -190,30 +196,33 @@ def kernel_sha(path):
 
 def load_traffic(workload, kernel):
     """Per-launch HBM bytes from the committed rocprofv3 FETCH_SIZE/WRITE_SIZE summary, or None
-    when it is missing or was taken on a different kernel source."""
+    when it is missing or was taken on different sources (the kernel's own file, the shared
+    device helpers or the dispatcher)."""
     p = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(p) as f:
             t = json.load(f)[workload]
     except (OSError, KeyError, ValueError):
         return None
-    src = os.path.join(ROOT, "paged_kv_cache_kvpool_amd", "csrc", t.get("source", ""))
-    if t.get("kernel") != kernel or not os.path.exists(src) or kernel_sha(src) != t.get("source_sha"):
+    src = KERNEL_SOURCES.get(kernel)
+    if t.get("kernel") != kernel or src is None or t.get("source") != src:
+        return None
+    try:
+        if source_sha(src) != t.get("sources_sha"):
+            return None
+    except OSError:
         return None
     return t.get("bytes_per_launch")
 
 
 def cpu_baseline(w, dev, kind, budget_s=15.0):
     """The float64 oracle (as it stands) on a bounded sample: whole sequences, in order, until
-    about budget_s of CPU work; scaled to the metric's unit."""
+    about budget_s of CPU work; scaled to the metric's unit.  `cores`: the BLAS threads the
+    oracle's matrix products ran on."""
     from oracle import attention as ora
     from oracle import quant as oq
     from oracle import sparse as osp
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = 1
+    threads = blas_threads()
     geo = dict(num_kv_heads=w.num_kv_heads, block_size=w.block_size, head_dim=w.head_dim)
     i8 = w.dtype == "i8"
     if i8:
@@ -484,57 +493,74 @@ def park_restore_cpu(pool, blocks, spare, budget_s=10.0):
                 sample=f"{n} of {blocks.size} blocks parked and restored ({t_used:.1f} s)")
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="batched_gqa_decode", choices=sorted(WORKLOADS))
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--graph", type=int, default=0,
-                    help="1: time the step as a captured HIP graph replay (as a serving loop would; "
-                         "slower than eager launches on this ROCm); 0: eager launches")
-    ap.add_argument("--calibrate-copy", action="store_true",
-                    help="only run a plain 1 GiB device-to-device copy (scale for HBM counters)")
-    ap.add_argument("--separate-append", action="store_true",
-                    help="append with kvpool_append, then the attention call (default: one "
-                         "kvattn_append_forward(_sparse) call)")
-    ap.add_argument("--flush", default="read", choices=["read", "write", "none"],
-                    help="evict MALL and L2 between steps by reading (default) or writing 1 GiB")
-    args = ap.parse_args()
-    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU only: the library has no multi-GPU path "
-              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
-        sys.exit(2)
+# The BASELINE configurations the default run measures: the headline (batched GQA decode) as
+# the top-level fields, every other configuration under "configs".  Targets: decode at >= 70% of
+# HBM peak, chunked prefill at >= 50% of bf16 MFMA peak; verification is reported against 70%;
+# the tiny fp32 decode is a latency row (microseconds).
+HEADLINE = "batched_gqa_decode"
+DEFAULT_CONFIGS = ["tiny_decode", "spec_verify_32k", "spec_verify_128k", "prefix_prefill",
+                   "long_decode"]
+TARGETS = {"batched_gqa_decode": ("hbm", 0.70, "target"), "spec_verify_32k": ("hbm", 0.70, "aim"),
+           "spec_verify_128k": ("hbm", 0.70, "aim"), "prefix_prefill": ("mfma", 0.50, "target"),
+           "long_decode": ("hbm", 0.70, "target"), "tiny_decode": ("latency", None, "report us")}
 
+# Sources whose change changes what a kernel does (its own file, the shared device helpers and
+# the dispatcher that plans and launches it): the committed traffic counters of a workload count
+# only while all of them hash as they did when the counters were taken.
+KERNEL_SOURCES = {"attn_split_mfma": "attn_split_mfma.hip", "attn_vec": "attn_vec.hip",
+                  "attn_prefill_mfma": "attn_prefill_mfma.hip"}
+SHARED_SOURCES = ["common.h", "kernels.h", "kvpool.cpp"]
+
+
+def source_sha(kernel_src):
+    """sha256[:16] over the kernel's source and the sources it shares with the dispatcher."""
+    h = hashlib.sha256()
+    for f in [kernel_src] + SHARED_SOURCES:
+        with open(os.path.join(ROOT, "paged_kv_cache_kvpool_amd", "csrc", f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def cpu_info():
+    """Host facts recorded beside the oracle's timing."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        affinity = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        affinity = os.cpu_count()
+    return {"cpu_model": model, "affinity_cores": affinity,
+            "omp_num_threads": os.environ.get("OMP_NUM_THREADS")}
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        return 1
+
+
+def run_workload(wname, args, scratch, want_cpu, cpu_budget_s, single_core=False):
+    """One workload: warm-up, a profiled pass (the library's HIP-event pair around every launch),
+    then exactly args.steps timed steps.  Returns the JSON record (not printed)."""
     import torch
     from paged_kv_cache_kvpool_amd import binding as kb
 
-    assert torch.cuda.is_available(), "bench.py needs a GPU"
-    torch.cuda.set_device(0)
-    if args.calibrate_copy:
-        # A plain copy of known size: reads and writes exactly 1 GiB per launch.
-        src = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(max(1, args.steps)):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"calibrate_copy_bytes": FLUSH_BYTES, "launches": max(1, args.steps)}),
-              flush=True)
-        return
-    wname = args.workload
     info = WORKLOADS[wname]
-    if info["kind"] == "pcie":
-        bench_park_restore(args)
-        return
     t_setup = time.perf_counter()
     w = make_workload(wname)
     alg = algorithmic(w)
     dev = Device(w)
     dev.fused_append = not args.separate_append
-    want_cpu = not args.no_cpu_baseline
     dev.snapshot_pre_append(want_cpu)
-    scratch = torch.zeros(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t_setup
 
@@ -599,36 +625,49 @@ def main():
     kind = info["kind"]
     if kind == "mfma":
         value, unit = alg["flops"] / (ms * 1e-3) / 1e12, "TFLOP/s"
+        step_frac = value / MFMA_BF16_PEAK_TFLOPS
     else:
         value, unit = alg["step_bytes"] / (ms * 1e-3) / 1e9, "GB/s"
+        step_frac = value / HBM_PEAK_GBS
     roof = kernel_roofline(dom, alg, dom_ms)
     dom_bytes = alg["prefill_bytes"] if dom == "attn_prefill_mfma" else alg["split_bytes"]
-    src = {"attn_split_mfma": "attn_split_mfma.hip", "attn_vec": "attn_vec.hip",
-           "attn_prefill_mfma": "attn_prefill_mfma.hip"}[dom]
     roof["kernel"] = dom
     roof["kernel_ms"] = dom_ms
     roof["traffic"] = load_traffic(wname, dom)
+    roof["step_frac"] = step_frac
+    tgt = TARGETS.get(wname)
+    if tgt and tgt[1] is not None:
+        roof["target_frac"] = tgt[1]
+        roof["target_kind"] = tgt[2]
+        roof["met_kernel"] = bool(roof["frac"] >= tgt[1])
+        roof["met_step"] = bool(step_frac >= tgt[1])
     # every attention kernel of the step (more than one when a call mixes sequence kinds)
     rooflines = {k: dict(kernel_roofline(k, alg, ktimes[k][1] / ktimes[k][0]),
                          kernel_ms=ktimes[k][1] / ktimes[k][0]) for k in attn_kernels}
 
     cpu = None
     if want_cpu:
-        cpu = cpu_baseline(w, dev, kind)
+        cpu = cpu_baseline(w, dev, kind, budget_s=cpu_budget_s)
+        cpu.update(cpu_info())
+        if single_core:
+            try:
+                from threadpoolctl import threadpool_limits
+                with threadpool_limits(limits=1):
+                    one = cpu_baseline(w, dev, kind, budget_s=max(2.0, cpu_budget_s / 3))
+                cpu["single_core"] = {"value": one["value"], "unit": one["unit"],
+                                      "sample": one["sample"]}
+            except Exception as e:  # pragma: no cover
+                cpu["single_core"] = {"error": str(e)}
 
-    line = {
+    rec = {
         "metric": METRIC,
         "value": value,
         "unit": unit,
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
         "ms_per_step": ms,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16" if w.dtype == "i8" else w.dtype,  # int8 pools: bf16 MFMA on the codes
-        "data": "synthetic",
+        # arithmetic types of the path: fp32 pools compute in fp32; bf16 pools on bf16 MFMA with
+        # fp32 accumulation; int8 pools take q.k on the int8 matrix cores (int32 accumulation)
+        # and P.V on bf16 MFMA
+        "dtype": {"i8": "i8/bf16", "bf16": "bf16", "f32": "f32"}[w.dtype],
         "config": {"workload": wname, "desc": info["desc"], "kv_tokens": alg["kv_tokens"],
                    "num_seqs": w.num_seqs, "total_q": w.total_q, "block_size": w.block_size,
                    "head_dim": w.head_dim, "q_heads": w.num_q_heads, "kv_heads": w.num_kv_heads,
@@ -645,8 +684,92 @@ def main():
         "cpu_baseline": cpu,
         "wall_s_timed_region": wall,
         "setup_s": setup_s,
-        "kernel_source_sha": kernel_sha(os.path.join(ROOT, "paged_kv_cache_kvpool_amd", "csrc", src)),
+        "kernel_source_sha": source_sha(KERNEL_SOURCES[dom]),
     }
+    if kind == "latency":
+        rec["latency_us"] = ms * 1e3
+    del dev
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return rec
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=None, choices=sorted(WORKLOADS),
+                    help="measure this workload alone (default: the headline batched GQA decode "
+                         "with every other BASELINE configuration under \"configs\")")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=None,
+                    help="seconds of oracle time per configuration (default 15 alone, 6 each in "
+                         "the all-configuration run)")
+    ap.add_argument("--graph", type=int, default=0,
+                    help="1: time the step as a captured HIP graph replay (as a serving loop would; "
+                         "slower than eager launches on this ROCm); 0: eager launches")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (scale for HBM counters)")
+    ap.add_argument("--separate-append", action="store_true",
+                    help="append with kvpool_append, then the attention call (default: one "
+                         "kvattn_append_forward(_sparse) call)")
+    ap.add_argument("--flush", default="read", choices=["read", "write", "none"],
+                    help="evict MALL and L2 between steps by reading (default) or writing 1 GiB")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        # A plain copy of known size: reads and writes exactly 1 GiB per launch.
+        src = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(max(1, args.steps)):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": FLUSH_BYTES, "launches": max(1, args.steps)}),
+              flush=True)
+        return
+    want_cpu = not args.no_cpu_baseline
+    single = args.workload is None
+    wname = args.workload or HEADLINE
+    if WORKLOADS[wname]["kind"] == "pcie":
+        bench_park_restore(args)
+        return
+    scratch = torch.zeros(FLUSH_BYTES, dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    budget = args.cpu_budget if args.cpu_budget is not None else (6.0 if single else 15.0)
+    t_all = time.perf_counter()
+    rec = run_workload(wname, args, scratch, want_cpu, budget, single_core=single)
+    line = {"metric": rec["metric"], "value": rec["value"], "unit": rec["unit"], "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": rec["ms_per_step"],
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": rec["dtype"], "data": "synthetic"}
+    line.update({k: v for k, v in rec.items() if k not in line})
+    if single:
+        # every other BASELINE configuration, measured in the same process the same way
+        configs = {}
+        for name in DEFAULT_CONFIGS:
+            r = run_workload(name, args, scratch, want_cpu, budget)
+            print(f"[bench] {name}: {r['value']:.4g} {r['unit']}, {r['ms_per_step'] * 1e3:.1f} us/step, "
+                  f"kernel frac {r['roofline']['frac']:.3f}", file=sys.stderr, flush=True)
+            configs[name] = {k: r[k] for k in ("value", "unit", "ms_per_step", "dtype", "config",
+                                               "kv_tokens_per_s", "step_ms_p10_p50_p90",
+                                               "kernel_ms_per_launch", "algorithmic", "roofline",
+                                               "rooflines", "cpu_baseline", "wall_s_timed_region")}
+            if "latency_us" in r:
+                configs[name]["latency_us"] = r["latency_us"]
+        line["configs"] = configs
+        line["targets_met"] = {n: (c["roofline"].get("met_kernel"), c["roofline"].get("met_step"))
+                               for n, c in [(wname, line)] + list(configs.items())
+                               if "met_kernel" in c["roofline"]}
+    line["wall_s_all_configs"] = time.perf_counter() - t_all
     print(json.dumps(line), flush=True)
 
 

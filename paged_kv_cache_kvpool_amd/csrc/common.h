@@ -196,10 +196,17 @@ struct AttnArgs {
 // (32K keys: 6% slower), nor does a sparse walk of one window, whose few items bound its
 // latency (two 4K-key windows: 14 -> 20 us).  The split depends on the sequence alone, so its
 // reduction order does too.
+// The floor of that rule, shared by the kernels (per sequence: its rows per KV head and whether
+// its keys have a sparse gap) and the host (for a whole call: the largest rows per KV head of its
+// split-K sequences and whether any may be gapped), so that the host's decision to skip the
+// reduce launch (no sequence can have a second split) always agrees with the kernels' splits.
+__host__ __device__ __forceinline__ int split_floor(int rows_per_kv_head, bool gapped) {
+  return rows_per_kv_head <= 16 && !gapped ? 512 : 256;
+}
 __device__ __forceinline__ int seq_split(const AttnArgs& a, int L, int T, bool gapped) {
   if (a.split_tokens > 0) return a.split_tokens;
   const int per = (L >> 7) + ((L & 127) != 0);  // ceil(L / 128) without overflow
-  const int lo = T * a.group <= 16 && !gapped ? 512 : 256;
+  const int lo = split_floor(T * a.group, gapped);
   return min(max((per + 31) & ~31, lo), 2048);
 }
 

@@ -789,9 +789,9 @@ int forward_impl(kvpool_t* pool, int32_t layer, const void* q, void* out, int32_
   }
   if (e != hipSuccess) return fail(KV_EDEVICE, "attention launch: %s", hipGetErrorString(e));
   // Rows whose keys all fall in split 0 are finished by the attention kernels; when no sequence
-  // can have a second split the reduce has nothing to do.  Every split holds >= 256 keys, and
-  // >= 512 when every split-K sequence has at most 16 rows per KV head and no sparse gap.
-  const int min_split = pl.split > 0 ? pl.split : (pl.split_rows <= 16 && sp.window == 0 ? 512 : 256);
+  // can have a second split the reduce has nothing to do.  Every split holds at least the rule's
+  // floor for the call's longest split-K rows per KV head (a sparse call may have a gap).
+  const int min_split = pl.split > 0 ? pl.split : kvp::split_floor(pl.split_rows, sp.window > 0);
   const bool need_reduce = pl.split_k && max_ctx_len > min_split;
   if (need_reduce) {
     e = timed(K_REDUCE, st, [&] { return kvp::launch_attn_reduce(a, eb, pool->head_dim, st); });

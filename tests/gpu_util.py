@@ -194,11 +194,54 @@ def errors(gpu: np.ndarray, ref: np.ndarray):
     return max_abs, rel_l2
 
 
-def assert_close(gpu: np.ndarray, ref: np.ndarray, dtype: str, what=""):
+# A single (row, q-head) output vector may not be off by more than this many times the
+# whole-tensor rel-L2 bar: the tensor bar alone would let a few wrong vectors of a large output
+# pass (one vector 20% off among 32 x 32 changes the tensor's rel-L2 by about 0.006).
+VECTOR_FACTOR = 4.0
+
+
+def vector_errors(gpu: np.ndarray, ref: np.ndarray):
+    """Per-(row, q-head) rel-L2 of [rows, heads, D] outputs: (worst rel-L2, its (row, head),
+    the rel-L2 array).  A vector's denominator is floored at 5% of the median vector norm, so a
+    near-zero reference vector cannot inflate the ratio by itself."""
+    g = gpu.reshape(-1, gpu.shape[-2], gpu.shape[-1]) if gpu.ndim >= 3 else gpu.reshape(-1, 1, gpu.shape[-1])
+    r = ref.reshape(g.shape)
+    ok = ~np.isnan(r)
+    d = np.where(ok, g - r, 0.0)
+    rn = np.sqrt(np.sum(np.where(ok, r, 0.0) ** 2, axis=-1))
+    dn = np.sqrt(np.sum(d ** 2, axis=-1))
+    floor = 0.05 * float(np.median(rn)) if rn.size else 0.0
+    rel = dn / np.maximum(rn, max(floor, 1e-300))
+    if rel.size == 0:
+        return 0.0, (0, 0), rel
+    idx = np.unravel_index(int(np.argmax(rel)), rel.shape)
+    return float(rel[idx]), (int(idx[0]), int(idx[1])), rel
+
+
+def row_owner(row: int, q_lens):
+    """(sequence, token index within it) of packed query row `row`."""
+    c = np.cumsum(np.asarray(q_lens, dtype=np.int64))
+    s = int(np.searchsorted(c, row, side="right"))
+    return s, int(row - (c[s - 1] if s else 0))
+
+
+def assert_close(gpu: np.ndarray, ref: np.ndarray, dtype: str, what="", q_lens=None):
+    """Whole-tensor max-abs and rel-L2 at the bar, and every (row, q-head) vector within
+    VECTOR_FACTOR times the rel-L2 bar.  Prints the worst vector (with its sequence and token
+    when q_lens is given)."""
     assert gpu.shape == ref.shape
     assert np.all(np.isfinite(gpu[~np.isnan(ref)])), f"{what}: non-finite output"
     max_abs, rel_l2 = errors(gpu, ref)
     tol = TOL[dtype]
+    worst, (wr, wh), _ = vector_errors(gpu, ref)
+    where = f"row {wr}, q-head {wh}"
+    if q_lens is not None:
+        s, i = row_owner(wr, q_lens)
+        where += f" (sequence {s}, token {i})"
+    print(f"[parity] {what}: max_abs={max_abs:.3e} rel_l2={rel_l2:.3e} worst vector rel_l2="
+          f"{worst:.3e} at {where}", flush=True)
     assert max_abs <= tol["max_abs"] and rel_l2 <= tol["rel_l2"], \
         f"{what}: max_abs={max_abs:.3e} rel_l2={rel_l2:.3e} (tol {tol})"
+    assert worst <= VECTOR_FACTOR * tol["rel_l2"], \
+        f"{what}: vector at {where} has rel_l2={worst:.3e} > {VECTOR_FACTOR} x {tol['rel_l2']}"
     return max_abs, rel_l2

@@ -61,7 +61,7 @@ def check(name, dtype, seed=601, mirror=True):
     for x, y in zip(a.host_pools(), b.host_pools()):
         assert np.array_equal(np.asarray(x).view(np.uint8), np.asarray(y).view(np.uint8)), \
             "pool differs from append + forward"
-    assert_close(out_f64(got), b.oracle(), dtype, w.name)
+    assert_close(out_f64(got), b.oracle(), dtype, w.name, q_lens=w.q_lens)
 
 
 @pytest.mark.parametrize("name", ["decode", "verify", "many", "wide_rows", "mixed"])
@@ -128,7 +128,7 @@ def check_sparse(name, dtype, seed=611, mirror=True):
     for x, y in zip(a.host_pools(), b.host_pools()):
         assert np.array_equal(np.asarray(x).view(np.uint8), np.asarray(y).view(np.uint8)), \
             "pool differs from append + forward_sparse"
-    assert_close(out_f64(got), b.oracle_sparse(sink, window, min_len), dtype, w.name)
+    assert_close(out_f64(got), b.oracle_sparse(sink, window, min_len), dtype, w.name, q_lens=w.q_lens)
 
 
 @pytest.mark.parametrize("name", ["pages", "verify", "small"])

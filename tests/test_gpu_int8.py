@@ -87,7 +87,7 @@ def test_attention_int8_random(seed, hq, hkv, bs, d):
     c.append()
     out = c.forward()
     torch.cuda.synchronize()
-    assert_close(out_f64(out), c.oracle(), wl.I8, w.name)
+    assert_close(out_f64(out), c.oracle(), wl.I8, w.name, q_lens=w.q_lens)
 
 
 @pytest.mark.parametrize("prompt", [1500, 2000, 2047, 2048, 2049, 2100, 3000, 4000])
@@ -101,7 +101,7 @@ def test_int8_prefill_lengths(prompt):
     c.append()
     out = c.forward(mirror=True)
     torch.cuda.synchronize()
-    assert_close(out_f64(out), c.oracle(), wl.I8, w.name)
+    assert_close(out_f64(out), c.oracle(), wl.I8, w.name, q_lens=w.q_lens)
 
 
 @pytest.mark.parametrize("mirror", [False, True], ids=["bounds", "mirror"])
@@ -116,7 +116,7 @@ def test_mixed_step_int8(hq, hkv, d, bs, mirror):
     c.append()
     out = c.forward(mirror=mirror)
     torch.cuda.synchronize()
-    assert_close(out_f64(out), c.oracle(), wl.I8, w.name)
+    assert_close(out_f64(out), c.oracle(), wl.I8, w.name, q_lens=w.q_lens)
 
 
 def test_int8_batch_invariance_bitwise(monkeypatch):
@@ -151,7 +151,7 @@ def test_batched_gqa_decode_int8_full():
     c.append()
     out = c.forward(mirror=True)
     torch.cuda.synchronize()
-    assert_close(out_f64(out), c.oracle(), wl.I8, w.name)
+    assert_close(out_f64(out), c.oracle(), wl.I8, w.name, q_lens=w.q_lens)
 
 
 @pytest.mark.parametrize("cached", [32768, 131072])
@@ -162,7 +162,7 @@ def test_spec_verify_int8_full(cached):
     c.append()
     out = c.forward(mirror=True)
     torch.cuda.synchronize()
-    assert_close(out_f64(out), c.oracle(), wl.I8, w.name)
+    assert_close(out_f64(out), c.oracle(), wl.I8, w.name, q_lens=w.q_lens)
 
 
 def test_prefix_prefill_int8_full():
@@ -172,7 +172,7 @@ def test_prefix_prefill_int8_full():
     c.append()
     out = c.forward(mirror=True)
     torch.cuda.synchronize()
-    assert_close(out_f64(out), c.oracle(), wl.I8, w.name)
+    assert_close(out_f64(out), c.oracle(), wl.I8, w.name, q_lens=w.q_lens)
 
 
 def test_long_decode_int8_full():
@@ -193,4 +193,4 @@ def test_mixed_step_int8_full():
     c.append()
     out = c.forward(mirror=True)
     torch.cuda.synchronize()
-    assert_close(out_f64(out), c.oracle(), wl.I8, w.name)
+    assert_close(out_f64(out), c.oracle(), wl.I8, w.name, q_lens=w.q_lens)

@@ -127,7 +127,7 @@ def test_decode_beside_verification_two_launches(dtype):
     two = c.forward(mirror=True)
     torch.cuda.synchronize()
     assert np.array_equal(bits(one), bits(two)), "one launch vs two"
-    assert_close(out_f64(two), c.oracle(), dtype, w.name)
+    assert_close(out_f64(two), c.oracle(), dtype, w.name, q_lens=w.q_lens)
 
 
 @pytest.mark.parametrize("dtype", [wl.BF16, wl.I8, wl.F32])
@@ -141,9 +141,46 @@ def test_short_decode_without_reduce(dtype, mirror):
                 num_kv_heads=8, head_dim=128)
     c = DeviceCase(w)
     c.append()
+    kb.kvpool_profile(True)
     out = c.forward(mirror=mirror)
     torch.cuda.synchronize()
-    assert_close(out_f64(out), c.oracle(), dtype, w.name)
+    kb.kvpool_profile(False)
+    assert "attn_reduce" not in kb.kernel_times(), "a call with no second split ran the reduce"
+    assert_close(out_f64(out), c.oracle(), dtype, w.name, q_lens=w.q_lens)
+
+
+# (context lengths, q_lens, q-heads, sparse parameters or None, reduce launches expected).  The
+# reduce runs exactly when the shared split floor lets some sequence have a second split: 512
+# keys for single-tile rows (q_len * G <= 16, no sparse gap), 256 otherwise; a sparse call may
+# have a gap, so its host bound is 256.
+REDUCE_CASES = [
+    ([512, 300], [1, 1], 32, None, 0),        # G = 4: 4 rows per KV head, 512-key splits
+    ([513, 300], [1, 1], 32, None, 1),        # 513 keys: a second split
+    ([300, 200], [4, 1], 32, None, 0),        # T*G = 16: still one tile, 512-key floor
+    ([300, 200], [5, 1], 32, None, 1),        # T*G = 20: 256-key floor, 300 keys = 2 splits
+    ([256, 100], [5, 2], 32, None, 0),        # 256-key floor but nobody past 256 keys
+    ([400, 300], [1, 1], 32, (16, 64, 10**6), 1),  # sparse, below threshold: host bound 256
+]
+
+
+@pytest.mark.parametrize("case", range(len(REDUCE_CASES)))
+def test_reduce_launch_follows_split_floor(case):
+    """The host launches the reduce only when some sequence can have a second split, by the
+    same floor the kernels split with; every row still matches the oracle."""
+    ctx, ql, hq, sparse, expect = REDUCE_CASES[case]
+    announce(f"reduce launch case {case}: ctx={ctx} q_lens={ql} sparse={sparse}")
+    w = wl.make(f"reduce_case_{case}", seed=170 + case, dtype=wl.BF16, num_seqs_ctx=ctx,
+                q_lens=ql, num_q_heads=hq, num_kv_heads=8, head_dim=128)
+    c = DeviceCase(w)
+    c.append()
+    kb.kvpool_profile(True)
+    out = c.forward(mirror=True) if sparse is None else c.forward_sparse(*sparse, mirror=True)
+    torch.cuda.synchronize()
+    kb.kvpool_profile(False)
+    got = kb.kernel_times().get("attn_reduce", (0, 0.0))[0]
+    assert got == expect, f"reduce launches {got}, expected {expect}"
+    ref = c.oracle() if sparse is None else c.oracle_sparse(*sparse)
+    assert_close(out_f64(out), ref, wl.BF16, w.name, q_lens=w.q_lens)
 
 
 @pytest.mark.parametrize("dtype,bs", [(wl.BF16, 16), (wl.BF16, 64), (wl.F32, 16)])
@@ -215,7 +252,7 @@ def test_forced_split_sizes(monkeypatch, split):
     c.append()
     out = c.forward()
     torch.cuda.synchronize()
-    assert_close(out_f64(out), c.oracle(), wl.BF16, w.name)
+    assert_close(out_f64(out), c.oracle(), wl.BF16, w.name, q_lens=w.q_lens)
 
 
 @pytest.mark.parametrize("hq,hkv,d,bs", [(16, 1, 64, 64), (1, 1, 128, 16), (12, 4, 128, 64)])
@@ -228,7 +265,7 @@ def test_edge_shapes(hq, hkv, d, bs):
     c.append()
     out = c.forward()
     torch.cuda.synchronize()
-    assert_close(out_f64(out), c.oracle(), wl.BF16, w.name)
+    assert_close(out_f64(out), c.oracle(), wl.BF16, w.name, q_lens=w.q_lens)
 
 
 def test_empty_batch_is_a_noop():
@@ -368,7 +405,7 @@ def test_default_mode_decode_rows_batch_invariant(dtype, monkeypatch):
     c.append()
     full = c.forward()
     torch.cuda.synchronize()
-    assert_close(out_f64(full), c.oracle(), dtype, w.name)
+    assert_close(out_f64(full), c.oracle(), dtype, w.name, q_lens=w.q_lens)
     starts = np.concatenate([[0], np.cumsum(w.q_lens)])
     G = w.num_q_heads // w.num_kv_heads
     for s in range(w.num_seqs):

@@ -43,7 +43,7 @@ def test_many_sequences_decode(dtype):
     c.append()
     out = c.forward()
     torch.cuda.synchronize()
-    assert_close(out_f64(out), c.oracle(), dtype, w.name)
+    assert_close(out_f64(out), c.oracle(), dtype, w.name, q_lens=w.q_lens)
 
 
 @pytest.mark.parametrize("mirror", [False, True], ids=["bounds", "mirror"])
@@ -56,7 +56,7 @@ def test_many_sequences_mixed(mirror):
     c.append()
     out = c.forward(mirror=mirror)
     torch.cuda.synchronize()
-    assert_close(out_f64(out), c.oracle(), wl.BF16, w.name)
+    assert_close(out_f64(out), c.oracle(), wl.BF16, w.name, q_lens=w.q_lens)
 
 
 def test_many_sequences_sparse():
@@ -70,7 +70,7 @@ def test_many_sequences_sparse():
     c.append()
     out = c.forward_sparse(16, 500, 1000)
     torch.cuda.synchronize()
-    assert_close(out_f64(out), c.oracle_sparse(16, 500, 1000), wl.BF16, w.name)
+    assert_close(out_f64(out), c.oracle_sparse(16, 500, 1000), wl.BF16, w.name, q_lens=w.q_lens)
 
 
 def test_many_sequences_batch_invariance(monkeypatch):
@@ -112,4 +112,4 @@ def test_prefill_short_prefix_half_pairs(plan, monkeypatch):
     c.append()
     out = c.forward(mirror=True)
     torch.cuda.synchronize()
-    assert_close(out_f64(out), c.oracle(), wl.BF16, w.name)
+    assert_close(out_f64(out), c.oracle(), wl.BF16, w.name, q_lens=w.q_lens)

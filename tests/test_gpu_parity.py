@@ -122,7 +122,7 @@ def test_attention_random(seed, dtype, hq, hkv, bs, d):
     c.append()
     out = c.forward()
     torch.cuda.synchronize()
-    assert_close(out_f64(out), c.oracle(), dtype, w.name)
+    assert_close(out_f64(out), c.oracle(), dtype, w.name, q_lens=w.q_lens)
 
 
 @pytest.mark.parametrize("q_len", [33, 128, 200])
@@ -137,7 +137,7 @@ def test_attention_prefill_shapes(q_len, dtype):
     c.append()
     out = c.forward()
     torch.cuda.synchronize()
-    assert_close(out_f64(out), c.oracle(), dtype, w.name)
+    assert_close(out_f64(out), c.oracle(), dtype, w.name, q_lens=w.q_lens)
 
 
 @pytest.mark.parametrize("plan", ["4", "8", "10", "12", "12:10", "12:7", "8:5", "6:3", "5:3"])
@@ -161,7 +161,7 @@ def test_attention_prefill_plans(plan, head_dim, monkeypatch):
     c.append()
     out = c.forward()
     torch.cuda.synchronize()
-    assert_close(out_f64(out), c.oracle(), wl.BF16, w.name)
+    assert_close(out_f64(out), c.oracle(), wl.BF16, w.name, q_lens=w.q_lens)
 
 
 MIXED_CASES = [
@@ -191,7 +191,7 @@ def test_mixed_step(dtype, hq, hkv, d, bs, mirror):
     c.append()
     out = c.forward(mirror=mirror)
     torch.cuda.synchronize()
-    assert_close(out_f64(out), c.oracle(), dtype, w.name)
+    assert_close(out_f64(out), c.oracle(), dtype, w.name, q_lens=w.q_lens)
 
 
 def test_decode_vec_kernel_bf16(monkeypatch):
@@ -204,7 +204,7 @@ def test_decode_vec_kernel_bf16(monkeypatch):
     c.append()
     out = c.forward()
     torch.cuda.synchronize()
-    assert_close(out_f64(out), c.oracle(), wl.BF16, w.name)
+    assert_close(out_f64(out), c.oracle(), wl.BF16, w.name, q_lens=w.q_lens)
 
 
 # ---------------------------------------------------------------------------------------------
@@ -217,7 +217,7 @@ def test_tiny_decode_fp32():
     c = DeviceCase(w)
     out = c.forward()
     torch.cuda.synchronize()
-    assert_close(out_f64(out), c.oracle(), wl.F32, w.name)
+    assert_close(out_f64(out), c.oracle(), wl.F32, w.name, q_lens=w.q_lens)
 
 
 def test_batched_gqa_decode_full():
@@ -227,7 +227,7 @@ def test_batched_gqa_decode_full():
     c.append()
     out = c.forward()
     torch.cuda.synchronize()
-    assert_close(out_f64(out), c.oracle(), wl.BF16, w.name)
+    assert_close(out_f64(out), c.oracle(), wl.BF16, w.name, q_lens=w.q_lens)
 
 
 @pytest.mark.parametrize("cached", [32768, 131072])
@@ -238,7 +238,7 @@ def test_spec_verify_full(cached):
     c.append()
     out = c.forward()
     torch.cuda.synchronize()
-    assert_close(out_f64(out), c.oracle(), wl.BF16, w.name)
+    assert_close(out_f64(out), c.oracle(), wl.BF16, w.name, q_lens=w.q_lens)
 
 
 def test_prefix_prefill_full():
@@ -248,7 +248,7 @@ def test_prefix_prefill_full():
     c.append()
     out = c.forward()
     torch.cuda.synchronize()
-    assert_close(out_f64(out), c.oracle(), wl.BF16, w.name)
+    assert_close(out_f64(out), c.oracle(), wl.BF16, w.name, q_lens=w.q_lens)
 
 
 def test_mixed_step_full():
@@ -258,7 +258,7 @@ def test_mixed_step_full():
     c.append()
     out = c.forward(mirror=True)
     torch.cuda.synchronize()
-    assert_close(out_f64(out), c.oracle(), wl.BF16, w.name)
+    assert_close(out_f64(out), c.oracle(), wl.BF16, w.name, q_lens=w.q_lens)
 
 
 def test_long_decode_full():
@@ -269,4 +269,4 @@ def test_long_decode_full():
     c.append()
     out = c.forward()
     torch.cuda.synchronize()
-    assert_close(out_f64(out), c.oracle(kh, vh), wl.BF16, w.name)
+    assert_close(out_f64(out), c.oracle(kh, vh), wl.BF16, w.name, q_lens=w.q_lens)

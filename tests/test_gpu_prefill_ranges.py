@@ -52,7 +52,7 @@ def run_case(name, dtype, ks, plan=None, monkeypatch=None, seed=501, mirror=True
     c.append()
     out = c.forward(mirror=mirror)
     torch.cuda.synchronize()
-    assert_close(out_f64(out), c.oracle(), dtype, w.name)
+    assert_close(out_f64(out), c.oracle(), dtype, w.name, q_lens=w.q_lens)
     return c, out
 
 
@@ -96,4 +96,4 @@ def test_automatic_choice(monkeypatch):
     c.append()
     out = c.forward(mirror=True)
     torch.cuda.synchronize()
-    assert_close(out_f64(out), c.oracle(), wl.BF16, w.name)
+    assert_close(out_f64(out), c.oracle(), wl.BF16, w.name, q_lens=w.q_lens)

@@ -47,7 +47,7 @@ def test_sparse_decode_pages_parameters(dtype, mirror):
     c.append()
     out = c.forward_sparse(mirror=mirror, **PAGES)
     torch.cuda.synchronize()
-    assert_close(out_f64(out), c.oracle_sparse(**PAGES), dtype, w.name)
+    assert_close(out_f64(out), c.oracle_sparse(**PAGES), dtype, w.name, q_lens=w.q_lens)
 
 
 @pytest.mark.parametrize("dtype", [wl.BF16, wl.I8])
@@ -62,7 +62,7 @@ def test_sparse_verify_around_threshold(dtype):
     c.append()
     out = c.forward_sparse(**PAGES)
     torch.cuda.synchronize()
-    assert_close(out_f64(out), c.oracle_sparse(**PAGES), dtype, w.name)
+    assert_close(out_f64(out), c.oracle_sparse(**PAGES), dtype, w.name, q_lens=w.q_lens)
 
 
 SMALL = [  # (seed, dtype, hq, hkv, d, bs, sink, window, min_len)
@@ -92,7 +92,7 @@ def test_sparse_small_parameters(case):
     c.append()
     out = c.forward_sparse(sink, window, min_len)
     torch.cuda.synchronize()
-    assert_close(out_f64(out), c.oracle_sparse(sink, window, min_len), dtype, w.name)
+    assert_close(out_f64(out), c.oracle_sparse(sink, window, min_len), dtype, w.name, q_lens=w.q_lens)
 
 
 @pytest.mark.parametrize("split", ["64", "96", "4096", "12288"])
@@ -108,7 +108,7 @@ def test_sparse_forced_splits(split, monkeypatch):
     c.append()
     out = c.forward_sparse(16, 2000, 5000)
     torch.cuda.synchronize()
-    assert_close(out_f64(out), c.oracle_sparse(16, 2000, 5000), wl.BF16, w.name)
+    assert_close(out_f64(out), c.oracle_sparse(16, 2000, 5000), wl.BF16, w.name, q_lens=w.q_lens)
 
 
 def test_sparse_without_effect_is_dense_bitwise():
