@@ -17,8 +17,10 @@
  *
  * Conventions shared by every entry point
  *   - Ownership: the caller owns every device buffer (pool storage, q, out, metadata,
- *     workspace).  The library allocates no device memory and keeps no pointer beyond
- *     kvpool_create's storage pointers.
+ *     workspace).  No call allocates device memory and the library keeps no pointer beyond
+ *     kvpool_create's storage pointers; its one piece of device memory is the static scratch of
+ *     kvattn_forward_noalloc (KVATTN_NOALLOC_SCRATCH_BYTES on each GPU that loads the library,
+ *     placed there by the runtime with the library's code).
  *   - Asynchrony: work is enqueued on `stream` (a hipStream_t; NULL = the null stream) with no
  *     host synchronisation, so calls can be captured in a HIP graph.  Faults inside kernels
  *     surface at the caller's next synchronisation.
@@ -200,6 +202,28 @@ KVPOOL_API int kvattn_forward(kvpool_t *pool, int32_t layer, const void *q, void
                               int32_t max_ctx_len, int32_t max_q_len,
                               const int32_t *q_lens_host, void *workspace,
                               size_t workspace_bytes, void *stream);
+
+/* kvattn_forward for callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  It takes no workspace: the library keeps
+ * one static scratch buffer of KVATTN_NOALLOC_SCRATCH_BYTES per GPU, which each GPU that loads
+ * the library holds until the process ends; its device address is taken once per device by
+ * kvpool_create.  The call allocates nothing (no hipMalloc or hipFree, no events: with
+ * kvpool_profile enabled its launches are not timed) and makes no host synchronisation unless
+ * KVPOOL_VALIDATE=1.  Arguments, outputs and bits: those of kvattn_forward with the same
+ * arguments.  Errors: those of kvattn_forward; KV_ENOMEM when the call needs more scratch than
+ * the buffer holds (kvattn_workspace_size with the same bounds tells how much; use
+ * kvattn_forward then); KV_EDEVICE when the buffer's address could not be taken on the pool's
+ * device.  Every call on one GPU shares that GPU's buffer, which keeps the last call's partial
+ * results (no kernel needs it cleared on entry): calls ordered on one stream are safe, calls
+ * that may overlap on one GPU (several streams or threads) race and must not be made. */
+#define KVATTN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+KVPOOL_API int kvattn_forward_noalloc(kvpool_t *pool, int32_t layer, const void *q, void *out,
+                                      int32_t num_q_heads, float scale,
+                                      const int32_t *block_tables, int32_t max_blocks_per_seq,
+                                      const int32_t *ctx_lens, const int32_t *q_lens,
+                                      int32_t num_seqs, int32_t total_q, int32_t max_ctx_len,
+                                      int32_t max_q_len, const int32_t *q_lens_host,
+                                      void *stream);
 
 /* kvpool_append followed by kvattn_forward, in one call: the new tokens' K/V rows (k_new,
  * v_new, as for kvpool_append) are written into the pool, then every sequence attends as in

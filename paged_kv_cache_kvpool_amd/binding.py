@@ -41,6 +41,8 @@ SIGNATURES = {
     "kvattn_workspace_size": (_i32, [_vp, _i32, _i32, _i32, _i32, _i32, _vp, ctypes.POINTER(_sz)]),
     "kvattn_forward": (_i32, [_vp, _i32, _vp, _vp, _i32, _f32, _vp, _i32, _vp, _vp, _i32, _i32,
                               _i32, _i32, _vp, _vp, _sz, _vp]),
+    "kvattn_forward_noalloc": (_i32, [_vp, _i32, _vp, _vp, _i32, _f32, _vp, _i32, _vp, _vp, _i32,
+                                      _i32, _i32, _i32, _vp, _vp]),
     "kvattn_append_forward": (_i32, [_vp, _i32, _vp, _vp, _vp, _vp, _i32, _f32, _vp, _i32, _vp,
                                      _vp, _i32, _i32, _i32, _i32, _vp, _vp, _sz, _vp]),
     "kvattn_forward_sparse": (_i32, [_vp, _i32, _vp, _vp, _i32, _f32, _vp, _i32, _vp, _vp, _i32,
@@ -214,6 +216,21 @@ def kvattn_forward(handle, layer, q, out, num_q_heads, scale, block_tables, max_
     del arr
 
 
+def kvattn_forward_noalloc(handle, layer, q, out, num_q_heads, scale, block_tables,
+                           max_blocks_per_seq, ctx_lens, q_lens, num_seqs, total_q, max_ctx_len,
+                           max_q_len, stream=None, q_lens_host=None) -> None:
+    """kvattn_forward on the library's static per-GPU scratch (no workspace, no allocation)."""
+    arr, addr = _host_i32(q_lens_host)
+    _check(lib().kvattn_forward_noalloc(handle, layer, _ptr(q), _ptr(out), num_q_heads,
+                                        float(scale), _ptr(block_tables), max_blocks_per_seq,
+                                        _ptr(ctx_lens), _ptr(q_lens), num_seqs, total_q,
+                                        max_ctx_len, max_q_len, addr, _stream(stream)))
+    del arr
+
+
+KVATTN_NOALLOC_SCRATCH_BYTES = 64 << 20  # include/kvpool.h
+
+
 def kvattn_append_forward(handle, layer, k_new, v_new, q, out, num_q_heads, scale, block_tables,
                           max_blocks_per_seq, ctx_lens, q_lens, num_seqs, total_q, max_ctx_len,
                           max_q_len, workspace, workspace_bytes, stream=None,
@@ -349,6 +366,17 @@ class PagedKVPool:
         kvattn_forward(self.handle, layer, q, out, hq, scale, block_tables, block_tables.shape[1],
                        ctx_lens, q_lens, ctx_lens.shape[0], total_q, max_ctx_len, max_q_len,
                        ws, need, stream, q_lens_host)
+        return out
+
+    def forward_noalloc(self, layer, q, block_tables, ctx_lens, q_lens, max_ctx_len, max_q_len,
+                        out, scale=None, stream=None, q_lens_host=None):
+        """forward() through kvattn_forward_noalloc: the library's static scratch instead of a
+        workspace.  The caller supplies `out` and the bounds, so nothing here allocates either."""
+        total_q, hq, d = q.shape
+        scale = 1.0 / math.sqrt(d) if scale is None else scale
+        kvattn_forward_noalloc(self.handle, layer, q, out, hq, scale, block_tables,
+                               block_tables.shape[1], ctx_lens, q_lens, ctx_lens.shape[0], total_q,
+                               max_ctx_len, max_q_len, stream, q_lens_host)
         return out
 
     def append_forward(self, layer, k_new, v_new, q, block_tables, ctx_lens, q_lens, scale=None,

@@ -173,10 +173,15 @@ hipEvent_t prof_event() {
   return e;
 }
 
+// Set for the duration of an allocation-free call (kvattn_forward_noalloc): its launches are
+// never bracketed by events, which the runtime may allocate.
+thread_local bool g_no_events = false;
+
 template <class F>
 hipError_t timed(int kernel, hipStream_t st, F launch) {
   std::unique_lock<std::mutex> lk(g_prof_mu);
-  if (!g_prof_on) {
+  if (!g_prof_on || g_no_events) {
+
     lk.unlock();
     return launch();
   }
@@ -237,9 +242,43 @@ int kvpool_storage_bytes(int32_t num_layers, int32_t num_blocks, int32_t block_s
 
 }  // extern "C"
 
+// ---- scratch of the allocation-free entry point ----------------------------------------------
+// The workspace of kvattn_forward_noalloc.  Every GPU that loads this library's code holds its
+// own copy, zero at load, until the process ends.  In host code this name stands for a host-side
+// shadow, not for device memory: its device address on each GPU is taken once with
+// hipGetSymbolAddress (scratch_setup) and only that address is ever handed to a kernel.
+static __device__ __align__(256) unsigned char scratch[KVATTN_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
-int create_pool(kvpool_t** out, int32_t num_layers, int32_t num_blocks, int32_t block_size,
+constexpr int kMaxDevices = 64;
+struct ScratchSlot {
+  bool done;
+  hipError_t err;
+  void* ptr;  // device address of `scratch` on this device
+};
+std::mutex g_scratch_mu;
+ScratchSlot g_scratch[kMaxDevices];
+
+// Takes the scratch array's device address on device `dev`, which must be current (called by
+// kvpool_create, the library's set-up call).  Once per device; a failure is recorded and reported
+// by kvattn_forward_noalloc, never by the pool's other entry points.
+void scratch_setup(int dev) {
+  if (dev < 0 || dev >= kMaxDevices) return;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  ScratchSlot& sl = g_scratch[dev];
+  if (sl.done) return;
+  void* p = nullptr;
+  sl.err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  sl.ptr = sl.err == hipSuccess ? p : nullptr;
+  sl.done = true;
+}
+
+}  // namespace
+
+namespace {
+
+int create_pool(kvpool_t** out, int32_t num_layers, int32_t num_blocks,  int32_t num_layers, int32_t num_blocks, int32_t block_size,
                 int32_t num_kv_heads, int32_t head_dim, int32_t dtype, void* k_storage,
                 void* v_storage, void* k_scales, void* v_scales) {
   if (!out) return fail(KV_EINVAL, "out is NULL");
@@ -268,6 +307,7 @@ int create_pool(kvpool_t** out, int32_t num_layers, int32_t num_blocks, int32_t 
   p->v_scale = dtype == KV_I8 ? static_cast<float*>(v_scales) : nullptr;
   p->layer_elems = (size_t)num_blocks * num_kv_heads * block_size * head_dim;
   p->device = dev;
+  scratch_setup(dev);
   p->num_cus = 256;
   int cus = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && cus > 0)
@@ -649,8 +689,16 @@ int forward_impl(kvpool_t* pool, int32_t layer, const void* q, void* out, int32_
     return fail(KV_ERANGE, "total_q * num_q_heads must stay below 2^31");
   if ((long long)num_seqs * pool->num_kv_heads * 8 * pl.max_splits >= (1ll << 30))
     return fail(KV_ERANGE, "too many work items (splits x KV heads x row tiles) in one call");
+  if (g_no_events && pl.bytes > workspace_bytes)
+    return fail(KV_ENOMEM,
+                "this call needs %zu bytes of scratch; the static buffer of the allocation-free "
+                "entry point holds %zu (call kvattn_forward with a workspace instead)",
+                pl.bytes, workspace_bytes);
   if (pl.bytes) {
     if (!workspace) return fail(KV_ENOMEM, "workspace of %zu bytes required", pl.bytes);
+    if (workspace_bytes < pl.bytes)
+      return fail(KV_ENOMEM, "workspace has %zu bytes, %zu required", workspace_bytes, pl.bytes);
+
     if (workspace_bytes < pl.bytes)
       return fail(KV_ENOMEM, "workspace has %zu bytes, %zu required", workspace_bytes, pl.bytes);
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
@@ -813,6 +861,30 @@ int kvattn_forward(kvpool_t* pool, int32_t layer, const void* q, void* out, int3
   return forward_impl(pool, layer, q, out, num_q_heads, scale, block_tables, max_blocks_per_seq,
                       ctx_lens, q_lens, num_seqs, total_q, max_ctx_len, max_q_len, Sparse{0, 0, 0},
                       q_lens_host, workspace, workspace_bytes, stream);
+}
+
+int kvattn_forward_noalloc(kvpool_t* pool, int32_t layer, const void* q, void* out,
+                           int32_t num_q_heads, float scale, const int32_t* block_tables,
+                           int32_t max_blocks_per_seq, const int32_t* ctx_lens,
+                           const int32_t* q_lens, int32_t num_seqs, int32_t total_q,
+                           int32_t max_ctx_len, int32_t max_q_len, const int32_t* q_lens_host,
+                           void* stream) {
+  if (!pool) return fail(KV_EINVAL, "pool is NULL");
+  ScratchSlot sl{false, hipSuccess, nullptr};
+  if (pool->device >= 0 && pool->device < kMaxDevices) {
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    sl = g_scratch[pool->device];
+  }
+  if (!sl.done || sl.err != hipSuccess || !sl.ptr)
+    return fail(KV_EDEVICE, "no static scratch on device %d: %s", pool->device,
+                sl.done ? hipGetErrorString(sl.err) : "not set up (device id out of range)");
+  g_no_events = true;
+  const int rc = forward_impl(pool, layer, q, out, num_q_heads, scale, block_tables,
+                              max_blocks_per_seq, ctx_lens, q_lens, num_seqs, total_q, max_ctx_len,
+                              max_q_len, Sparse{0, 0, 0}, q_lens_host, sl.ptr,
+                              KVATTN_NOALLOC_SCRATCH_BYTES, stream);
+  g_no_events = false;
+  return rc;
 }
 
 }  // extern "C"
