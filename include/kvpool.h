@@ -294,12 +294,14 @@ KVPOOL_API int kvattn_append_forward_sparse(kvpool_t *pool, int32_t layer, const
  * doc, "Server options", --host-kv-cache-mib and --kv-host-cache-mib).
  * A page is one pool block across every layer: for layer 0, 1, ...: the block's K bytes, its V
  * bytes and, for an int8 pool, its K and V scale bytes, each in storage order.  Pages with the
- * same content are stored once, with a reference count: content is compared through a 128-bit
- * hash computed on the GPU (each 64-bit little-endian word w_i of the page, i = 0, 1, ...,
- * contributes fmix64(w_i + 0x9E3779B97F4A7C15 (i + 1)) to the first half and
- * fmix64(w_i ^ 0xD6E8FEB86659FD93 (i + 1)) to the second, sums mod 2^64; fmix64 is the
- * MurmurHash3 finalizer), so only pages the store lacks cross PCIe.  Two different pages with
- * equal hashes would be merged; for non-adversarial data the chance is about 2^-128 per pair.
+ * same content are stored once, with a reference count, so only pages the store lacks are
+ * written over PCIe.  A 128-bit hash computed on the GPU nominates the candidates (each 64-bit
+ * little-endian word w_i of the page, i = 0, 1, ..., contributes fmix64(w_i + 0x9E3779B97F4A7C15
+ * (i + 1)) to the first half and fmix64(w_i ^ 0xD6E8FEB86659FD93 (i + 1)) to the second, sums
+ * mod 2^64; fmix64 is the MurmurHash3 finalizer) and the bytes decide: before a block shares a
+ * page, the GPU compares it with that page (a stored page is read back over PCIe, a page new in
+ * the same call is read from the pool), so pages with equal hashes but different bytes, whether
+ * by chance or crafted, are stored apart.
  * The kernels read and write the pinned store directly (no device memory is allocated).
  * A store serves pools of the geometry (layers, block size, KV heads, head dim, dtype) it was
  * created for.  Calls on one store are serialised by a lock; park, restore and page_hash are

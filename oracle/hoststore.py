@@ -16,10 +16,11 @@ Readings taken (the pages give no format):
   stores nothing (the caller falls back to recomputing, as the pages' servers do);
 * restoring a page writes its bytes back into a pool block, bit for bit.
 
-The store model below decides "same page" by comparing bytes.  The library compares a 128-bit
-content hash instead, defined in ``page_hash`` (each 64-bit little-endian word w_i of the page,
-i = 0, 1, ..., is keyed by its position and passed through the 64-bit finalizer of MurmurHash3;
-the two hash halves are the sums, mod 2^64, of two differently keyed mixes).
+The store model below decides "same page" by comparing bytes, as the library does after its
+128-bit content hash, defined in ``page_hash``, has nominated a candidate (each 64-bit
+little-endian word w_i of the page, i = 0, 1, ..., is keyed by its position and passed through
+the 64-bit finalizer of MurmurHash3; the two hash halves are the sums, mod 2^64, of two
+differently keyed mixes).
 """
 from __future__ import annotations
 

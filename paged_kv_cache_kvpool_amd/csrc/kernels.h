@@ -61,6 +61,11 @@ hipError_t launch_page_park(const PageArgs& a, const int32_t* pairs, int n, char
                             hipStream_t st);
 hipError_t launch_page_restore(const PageArgs& a, const int32_t* pairs, int n, const char* store,
                                hipStream_t st);
+// Byte comparison of n page pairs: triples[3j] = pool block, triples[3j + 1] = 0 (the other page
+// is store slot triples[3j + 2]) or 1 (pool block triples[3j + 2]); diff[j * segs + seg] = 1 when
+// that segment differs, else 0.
+hipError_t launch_page_compare(const PageArgs& a, const int32_t* triples, int n, const char* store,
+                               uint32_t* diff, hipStream_t st);
 
 // Split-K attention on the matrix cores (bf16) for the sequences with q_len <= split_q_max:
 // items of (row tile of <= 32 rows, split, KV head, sequence) dealt round-robin to persistent

@@ -130,7 +130,46 @@ __global__ __launch_bounds__(256) void page_restore_kernel(PageArgs a, const int
   for (; u < n16; u += 256) d[u] = s[u];
 }
 
+// triples[3j] = pool block; triples[3j + 1] = 0: compare with store slot triples[3j + 2] (read
+// over PCIe), 1: with pool block triples[3j + 2].  diff[(j, seg)] = 1 when the segment differs.
+// Dedup merges two pages only when every segment compares equal (a hash only nominates them).
+__global__ __launch_bounds__(256) void page_compare_kernel(PageArgs a, const int32_t* triples,
+                                                           const char* store, uint32_t* diff) {
+  const int j = blockIdx.x / a.segs, seg = blockIdx.x - j * a.segs;
+  const int b = triples[3 * j], kind = triples[3 * j + 1], other = triples[3 * j + 2];
+  const char* src;
+  size_t off, bytes;
+  segment(a, b, seg, src, off, bytes);
+  const u32x4* x = reinterpret_cast<const u32x4*>(src);
+  const u32x4* y;
+  if (kind == 0) {
+    y = reinterpret_cast<const u32x4*>(store + (size_t)other * a.page_stride + off);
+  } else {
+    const char* src2;
+    size_t off2, bytes2;
+    segment(a, other, seg, src2, off2, bytes2);
+    y = reinterpret_cast<const u32x4*>(src2);
+  }
+  const int n16 = (int)(bytes / 16);
+  uint32_t d = 0;
+  for (int u = threadIdx.x; u < n16; u += 256) {
+    const u32x4 p = x[u], q = y[u];
+    d |= (p[0] ^ q[0]) | (p[1] ^ q[1]) | (p[2] ^ q[2]) | (p[3] ^ q[3]);
+  }
+  const int any = __syncthreads_or(d != 0u);
+  if (threadIdx.x == 0) diff[blockIdx.x] = any ? 1u : 0u;
+}
+
 }  // namespace
+
+hipError_t launch_page_compare(const PageArgs& a, const int32_t* triples, int n, const char* store,
+                               uint32_t* diff, hipStream_t st) {
+  const long long wgs = (long long)n * a.segs;
+  if (wgs <= 0) return hipSuccess;
+  if (wgs > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  page_compare_kernel<<<(unsigned)wgs, 256, 0, st>>>(a, triples, store, diff);
+  return hipGetLastError();
+}
 
 hipError_t launch_page_hash(const PageArgs& a, const int32_t* blocks, int n, uint64_t* partial,
                             hipStream_t st) {

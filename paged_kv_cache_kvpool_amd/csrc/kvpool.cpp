@@ -15,6 +15,7 @@
 #include <unordered_map>
 #include <vector>
 
+#include "host_dedup.h"
 #include "kernels.h"
 
 struct kvpool {
@@ -147,12 +148,13 @@ int validate_meta(const kvpool* p, const HostMeta& m, int32_t max_blocks, int32_
 // Opt-in per-kernel timing: a HIP event pair around every launch, on the launch's stream.
 enum KernelId {
   K_APPEND, K_COPY, K_SPLIT_MFMA, K_VEC, K_PREFILL_MFMA, K_REDUCE, K_DEQUANT,
-  K_PAGE_HASH, K_PAGE_PARK, K_PAGE_RESTORE, K_REDUCE_PF, K_COUNT
+  K_PAGE_HASH, K_PAGE_PARK, K_PAGE_RESTORE, K_REDUCE_PF, K_PAGE_COMPARE, K_COUNT
 };
 const char* const kKernelNames[K_COUNT] = {"kv_append", "kv_copy_blocks", "attn_split_mfma",
                                            "attn_vec", "attn_prefill_mfma", "attn_reduce",
                                            "kv_dequant_prefill", "page_hash", "page_park",
-                                           "page_restore", "attn_reduce_prefill"};
+                                           "page_restore", "attn_reduce_prefill",
+                                           "page_compare"};
 struct ProfRec {
   int kernel;
   hipEvent_t a, b;
@@ -181,7 +183,6 @@ template <class F>
 hipError_t timed(int kernel, hipStream_t st, F launch) {
   std::unique_lock<std::mutex> lk(g_prof_mu);
   if (!g_prof_on || g_no_events) {
-
     lk.unlock();
     return launch();
   }
@@ -278,7 +279,7 @@ void scratch_setup(int dev) {
 
 namespace {
 
-int create_pool(kvpool_t** out, int32_t num_layers, int32_t num_blocks,  int32_t num_layers, int32_t num_blocks, int32_t block_size,
+int create_pool(kvpool_t** out, int32_t num_layers, int32_t num_blocks, int32_t block_size,
                 int32_t num_kv_heads, int32_t head_dim, int32_t dtype, void* k_storage,
                 void* v_storage, void* k_scales, void* v_scales) {
   if (!out) return fail(KV_EINVAL, "out is NULL");
@@ -698,9 +699,6 @@ int forward_impl(kvpool_t* pool, int32_t layer, const void* q, void* out, int32_
     if (!workspace) return fail(KV_ENOMEM, "workspace of %zu bytes required", pl.bytes);
     if (workspace_bytes < pl.bytes)
       return fail(KV_ENOMEM, "workspace has %zu bytes, %zu required", workspace_bytes, pl.bytes);
-
-    if (workspace_bytes < pl.bytes)
-      return fail(KV_ENOMEM, "workspace has %zu bytes, %zu required", workspace_bytes, pl.bytes);
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
       return fail(KV_EINVAL, "workspace must be 256-byte aligned");
   }
@@ -976,13 +974,8 @@ const char* kvpool_last_error(void) { return g_err.c_str(); }
 
 namespace {
 
-struct PageHash {
-  uint64_t a, b;
-  bool operator==(const PageHash& o) const { return a == o.a && b == o.b; }
-};
-struct PageHashHasher {
-  size_t operator()(const PageHash& h) const { return (size_t)(h.a ^ (h.b * 0x9E3779B97F4A7C15ull)); }
-};
+using kvp::PageHash;
+using kvp::PageHashHasher;
 
 // Pinned host allocation mapped into the GPU's address space: *host for the host, *dev (the
 // address the device uses for it) for kernels.
@@ -1026,13 +1019,13 @@ struct kvhost {
   std::vector<uint32_t> gen;    // per slot: generation of the page it holds
   std::vector<PageHash> hash_of;
   std::vector<int32_t> free_slots;
-  std::unordered_map<PageHash, int32_t, PageHashHasher> index;
+  kvp::PageIndex index;  // stored pages by content hash (several slots only after a collision)
   int64_t references = 0;
   // pinned scratch the kernels read or write
   void* partial = nullptr;  // hash partials
   void* partial_dev = nullptr;
   size_t partial_cap = 0;
-  void* ints = nullptr;     // block lists and (block, slot) pairs
+  void* ints = nullptr;     // block lists, (block, slot) pairs and comparison triples
   void* ints_dev = nullptr;
   size_t ints_cap = 0;
   std::mutex mu;
@@ -1102,13 +1095,56 @@ int hash_blocks(kvhost* h, kvpool* pool, const int32_t* blocks, int32_t n, hipSt
     }
     out[j] = PageHash{x, y};
   }
+  // Test knob: KVHOST_HASH_BITS=k keeps only the low k bits of the hash (k = 0: every page has
+  // the same hash), so that distinct pages collide and only the byte comparison tells them apart.
+  if (const char* v = getenv("KVHOST_HASH_BITS")) {
+    const int k = std::max(0, std::min(64, atoi(v)));
+    const uint64_t mask = k >= 64 ? ~0ull : ((1ull << k) - 1);
+    for (auto& hh : out) hh = PageHash{hh.a & mask, 0};
+  }
   return KV_OK;
 }
+
+// Byte comparison of the pairs of one dedup round on the GPU: block pairs[k].block of the call
+// (pool block blocks[...]) against a stored page (read from the pinned store over PCIe) or
+// against another pool block (read from HBM).  equal[k] = 1 when every segment is the same.
+int compare_pages(kvhost* h, kvpool* pool, const int32_t* blocks,
+                  const std::vector<kvp::DedupPair>& pairs, std::vector<char>& equal,
+                  hipStream_t st);
 
 int check_blocks(const kvpool* pool, const int32_t* blocks, int32_t n, const char* what) {
   for (int32_t j = 0; j < n; ++j)
     if (blocks[j] < 0 || blocks[j] >= pool->num_blocks)
       return fail(KV_ERANGE, "%s[%d] = %d outside [0, %d)", what, j, blocks[j], pool->num_blocks);
+  return KV_OK;
+}
+
+int compare_pages(kvhost* h, kvpool* pool, const int32_t* blocks,
+                  const std::vector<kvp::DedupPair>& pairs, std::vector<char>& equal,
+                  hipStream_t st) {
+  const size_t m = pairs.size();
+  if (!grow_pinned(&h->partial, &h->partial_dev, &h->partial_cap, m * h->segs * sizeof(uint32_t)) ||
+      !grow_pinned(&h->ints, &h->ints_dev, &h->ints_cap, m * 3 * sizeof(int32_t)))
+    return fail(KV_ENOMEM, "pinned host scratch for %zu page comparisons", m);
+  int32_t* tri = static_cast<int32_t*>(h->ints);
+  for (size_t k = 0; k < m; ++k) {
+    tri[3 * k] = blocks[pairs[k].block];
+    tri[3 * k + 1] = pairs[k].stored ? 0 : 1;
+    tri[3 * k + 2] = pairs[k].stored ? pairs[k].id : blocks[pairs[k].id];
+  }
+  const kvp::PageArgs a = page_args(h, pool);
+  hipError_t e = timed(K_PAGE_COMPARE, st, [&] {
+    return kvp::launch_page_compare(a, static_cast<const int32_t*>(h->ints_dev), (int)m,
+                                    h->arena_dev, static_cast<uint32_t*>(h->partial_dev), st);
+  });
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  if (e != hipSuccess) return fail(KV_EDEVICE, "page compare: %s", hipGetErrorString(e));
+  const uint32_t* diff = static_cast<const uint32_t*>(h->partial);
+  for (size_t k = 0; k < m; ++k) {
+    uint32_t d = 0;
+    for (int g = 0; g < h->segs; ++g) d |= diff[k * h->segs + g];
+    equal[k] = d == 0;
+  }
   return KV_OK;
 }
 
@@ -1201,21 +1237,29 @@ int kvhost_park(kvhost_t* h, kvpool_t* pool, const int32_t* blocks, int32_t n, i
   std::lock_guard<std::mutex> lk(h->mu);
   std::vector<PageHash> hv;
   if ((rc = hash_blocks(h, pool, blocks, n, st, hv))) return rc;
+  // Which stored page, or which new page of this call, each block holds: equal hashes only
+  // nominate candidates, bytes decide (compared on the GPU).
+  std::vector<kvp::DedupRef> ref;
+  rc = kvp::dedup_resolve(hv, h->index, [&](const std::vector<kvp::DedupPair>& pairs,
+                                            std::vector<char>& equal) {
+    return compare_pages(h, pool, blocks, pairs, equal, st);
+  }, ref);
+  if (rc) return rc;
   // Distinct new pages of this call (the first block holding each), in block order.
-  std::unordered_map<PageHash, int32_t, PageHashHasher> fresh;  // hash -> index into `news`
   std::vector<int32_t> news;
   for (int32_t j = 0; j < n; ++j)
-    if (!h->index.count(hv[j]) && !fresh.count(hv[j])) {
-      fresh.emplace(hv[j], (int32_t)news.size());
-      news.push_back(j);
-    }
+    if (!ref[j].stored && ref[j].id == j) news.push_back(j);
   if ((int64_t)news.size() > (int64_t)h->free_slots.size())
     return fail(KV_ENOMEM, "store has room for %zu more pages, %zu new ones needed (nothing parked)",
                 h->free_slots.size(), news.size());
+  if (!grow_pinned(&h->ints, &h->ints_dev, &h->ints_cap, news.size() * 2 * sizeof(int32_t)))
+    return fail(KV_ENOMEM, "pinned host scratch for %zu pages", news.size());
   std::vector<int32_t> slots(news.size());
-  int32_t* pairs = static_cast<int32_t*>(h->ints);  // hash_blocks sized it for 2n ints
+  std::vector<int32_t> slot_of_rep(n, -1);
+  int32_t* pairs = static_cast<int32_t*>(h->ints);
   for (size_t k = 0; k < news.size(); ++k) {
     slots[k] = h->free_slots[h->free_slots.size() - 1 - k];
+    slot_of_rep[news[k]] = slots[k];
     pairs[2 * k] = blocks[news[k]];
     pairs[2 * k + 1] = slots[k];
   }
@@ -1232,10 +1276,10 @@ int kvhost_park(kvhost_t* h, kvpool_t* pool, const int32_t* blocks, int32_t n, i
     const int32_t sl = slots[k];
     h->gen[sl] += 1;
     h->hash_of[sl] = hv[news[k]];
-    h->index.emplace(hv[news[k]], sl);
+    h->index[hv[news[k]]].push_back(sl);
   }
   for (int32_t j = 0; j < n; ++j) {
-    const int32_t sl = h->index.at(hv[j]);
+    const int32_t sl = ref[j].stored ? ref[j].id : slot_of_rep[ref[j].id];
     h->refs[sl] += 1;
     page_ids[j] = page_id(h, sl);
   }
@@ -1291,7 +1335,12 @@ int kvhost_release(kvhost_t* h, const int64_t* page_ids, int32_t n) {
     const int32_t sl = d.first;
     h->refs[sl] -= d.second;
     if (h->refs[sl] == 0) {
-      h->index.erase(h->hash_of[sl]);
+      auto it = h->index.find(h->hash_of[sl]);
+      if (it != h->index.end()) {
+        std::vector<int32_t>& v = it->second;
+        v.erase(std::remove(v.begin(), v.end(), sl), v.end());
+        if (v.empty()) h->index.erase(it);
+      }
       h->free_slots.push_back(sl);
     }
   }

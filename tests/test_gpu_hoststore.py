@@ -94,6 +94,34 @@ def test_park_restore_round_trip(dtype):
     store.close()
 
 
+@pytest.mark.parametrize("bits", [0, 2])
+def test_forced_hash_collisions_keep_pages_apart(bits, monkeypatch):
+    """With the hash cut to `bits` bits (a test knob of the library), distinct pages collide; the
+    GPU byte comparison must still keep them apart, across two park calls (the second call's
+    blocks meet stored pages), and restores must be bit exact."""
+    announce(f"forced hash collisions, {bits} hash bits")
+    monkeypatch.setenv("KVHOST_HASH_BITS", str(bits))
+    w, blocks, spare = shared_case(wl.BF16, layers=2)
+    c = DeviceCase(w)
+    store = kb.HostStore(c.pool, 64 << 20)
+    pools = host_pools_of(w)
+    model = hs.Store(capacity_pages=10 ** 6)
+    half = len(blocks) // 2
+    ids = list(store.park(c.pool, blocks[:half])) + list(store.park(c.pool, blocks[half:]))
+    mids = model.park(pools, blocks[:half]) + model.park(pools, blocks[half:])
+    for i in range(len(blocks)):
+        for j in range(len(blocks)):
+            assert (ids[i] == ids[j]) == (mids[i] == mids[j]), (i, j)
+    assert store.stats()["pages"] == len(model.pages)
+    dst = spare[:len(blocks)]
+    store.restore(c.pool, np.array(ids, dtype=np.int64), dst)
+    torch.cuda.synchronize()
+    want = model.restore(pools, mids, dst)
+    for g, x in zip(c.host_pools(), want):
+        assert np.array_equal(np.asarray(g).view(np.uint8), np.asarray(x).view(np.uint8))
+    store.close()
+
+
 def test_restore_into_another_pool():
     """Pages parked from one pool restore into another pool of the same geometry."""
     announce("restore into another pool")
