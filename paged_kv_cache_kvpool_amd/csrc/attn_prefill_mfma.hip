@@ -179,8 +179,14 @@ __device__ __forceinline__ void find_prefill_tile(const AttnArgs& a, int n, int 
 template <int D> struct PfSched;
 template <> struct PfSched<128> {
   static constexpr int N = 16;
+  // MFMA of each chunk (all 16 chunks carry one): score k-steps 0-3, then P.V k-step 0 (u 8-11)
+  // interleaved with score k-steps 4-7, then P.V k-step 1 (u 12-15)
   static constexpr int kOp[16] = {0, 1, 2, 3, 8, 4, 9, 5, 10, 6, 11, 7, 12, 13, 14, 15};
+  // exp2 pair (P pack) made in each chunk: packs 0-3 before P.V k-step 0 starts (chunk 4), packs
+  // 4-7 one every other chunk beside the MFMAs of chunks 4-11, before P.V k-step 1 (chunk 12)
+  static constexpr int kExp[16] = {0, 1, 2, 3, -1, 4, -1, 5, -1, 6, -1, 7, -1, -1, -1, -1};
   static constexpr int op(int ci) { return kOp[ci]; }
+  static constexpr int exp_pair(int ci) { return kExp[ci]; }
   static constexpr int slot(int ci) { return ci; }
   static constexpr int next_load(int ci) { return ci + 2 < N ? ci + 2 : -1; }
   static constexpr int slot_of_load(int ci) { return ci; }
@@ -188,10 +194,12 @@ template <> struct PfSched<128> {
 template <> struct PfSched<64> {
   static constexpr int N = 10;
   static constexpr int kOp[10] = {0, 1, 2, 3, 4, 5, -1, -1, 6, 7};
+  static constexpr int kExp[10] = {0, 1, 2, 3, 4, 5, 6, 7, -1, -1};
   // MFMA chunks in order, and each chunk's index among them (operand slot)
   static constexpr int kMf[8] = {0, 1, 2, 3, 4, 5, 8, 9};
   static constexpr int kSlot[10] = {0, 1, 2, 3, 4, 5, 0, 0, 6, 7};
   static constexpr int op(int ci) { return kOp[ci]; }
+  static constexpr int exp_pair(int ci) { return kExp[ci]; }
   static constexpr int slot(int ci) { return kSlot[ci]; }
   // the chunk whose operand the MFMA of chunk ci loads: the MFMA two places later
   static constexpr int next_load(int ci) { return kSlot[ci] + 2 < 8 ? kMf[kSlot[ci] + 2] : -1; }
@@ -453,15 +461,16 @@ void attn_prefill_mfma_kernel(AttnArgs a) {
   // the score product of block b+1, so each wave always has matrix work in flight beside its
   // softmax and the waves of a SIMD need not take turns.  sc holds the scores of the block being
   // finished.  Edge blocks (past the wave's first row or the context) take the masked path.
-  floatx16 sc;
   // Issue order of one finish, chunk by chunk (see PfSched).
   using Sched = PfSched<D>;
-  // finish(blk, cur, nst, stride): block blk of stage `cur`, with the score product of the
-  // wave's next block blk + stride (1 for a whole-block wave, 2 for a half wave) from `nst`.
-  auto finish = [&](int blk, const uint16_t (&cur)[8][TE], const uint16_t (&nst)[8][TE], int stride) {
+  // finish(blk, cur, nst, stride, sc, sn): block blk of stage `cur` (its scores in sc, already
+  // masked, with the running max raised for them), with the score product of the wave's next
+  // block blk + stride (1 for a whole-block wave, 2 for a half wave) from `nst` into sn; then
+  // that next block's mask and row max, issued behind the last P.V MFMAs so that they overlap.
+  auto finish = [&](int blk, const uint16_t (&cur)[8][TE], const uint16_t (&nst)[8][TE], int stride,
+                    const floatx16& sc, floatx16& sn) {
     const int kb = 32 * blk;
     if (kb >= kew) return;  // wave-uniform
-    row_max(sc, kb, kb + 31 > pw0 || kb + 32 > L);
     // A row without a visible key yet (possible in a half wave: its first block may lie wholly
     // past the row's position) keeps msub = -inf; subtract 0 for it, so that its masked scores
     // give p = 0 rather than exp2(-inf + inf) = NaN.
@@ -479,14 +488,13 @@ void attn_prefill_mfma_kernel(AttnArgs a) {
     u32x4 ops[Sched::N];
     ops[0] = load_op(Sched::op(0));
     ops[1] = load_op(Sched::op(1));
-    floatx16 sn;
 #pragma unroll
     for (int e = 0; e < 16; ++e) sn[e] = 0.f;
     uint32_t pk[8];
     __builtin_amdgcn_sched_barrier(0);
-    // Chunks pinned in place: at most one MFMA, the operand load two MFMAs ahead, and a share
-    // of the softmax (exp2 of two scores, their bf16 pack and row sum in chunks 0-7), so the
-    // VALU and the matrix core work side by side.
+    // Chunks pinned in place: at most one MFMA, the operand load two MFMAs ahead, and at most one
+    // exp2 pair of the softmax (the two scores' exp2, their bf16 pack and row sum), spread so
+    // that the VALU work stays under the matrix core's.
 #pragma unroll
     for (int ci = 0; ci < Sched::N; ++ci) {
       const int u = Sched::op(ci);
@@ -502,19 +510,29 @@ void attn_prefill_mfma_kernel(AttnArgs a) {
         const int nx = Sched::next_load(ci);
         if (nx >= 0) ops[Sched::slot_of_load(nx)] = load_op(Sched::op(nx));
       }
-      if (ci < 8) {
-        const float p0 = fast_exp2(__builtin_fmaf(sc[2 * ci], c, nms));
-        const float p1 = fast_exp2(__builtin_fmaf(sc[2 * ci + 1], c, nms));
-        pk[ci] = cvt_pk_bf16(p0, p1);
+      const int ep = Sched::exp_pair(ci);
+      if (ep >= 0) {
+        const float p0 = fast_exp2(__builtin_fmaf(sc[2 * ep], c, nms));
+        const float p1 = fast_exp2(__builtin_fmaf(sc[2 * ep + 1], c, nms));
+        pk[ep] = cvt_pk_bf16(p0, p1);
         // row sum of the fp32 values (plain adds: the bf16 dot2 would take matrix-pipe slots)
         l_lane += p0 + p1;
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    sc = sn;
+    const int kn = 32 * (blk + stride);
+    if (kn < kew) row_max(sn, kn, kn + 31 > pw0 || kn + 32 > L);  // wave-uniform
   };
-  // the wave's first block: the range's first, or its second for an odd half wave
-  if (kew > 64 * jt0) sc = qk(lds0, par);
+  // the wave's first block: the range's first, or its second for an odd half wave; whole-block
+  // waves alternate their scores between sa and sb, half waves keep theirs in sa
+  floatx16 sa, sb;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) sa[e] = sb[e] = 0.f;
+  if (kew > 64 * jt0 + 32 * par) {
+    sa = qk(lds0, par);
+    const int k0 = 64 * jt0 + 32 * par;
+    row_max(sa, k0, k0 + 31 > pw0 || k0 + 32 > L);
+  }
 
   // One 64-key tile j (stage `cur`): tile j+3 starts streaming into `nxt3` (free: its last
   // reader, tile j-1, was done before the barrier that ended the previous step); the blocks of
@@ -534,8 +552,12 @@ void attn_prefill_mfma_kernel(AttnArgs a) {
     fetch(jf, read_ids(jf), nxt3);
     // whole-block waves: blocks 2j and 2j+1; half waves: block 2j + parity, then the same parity
     // in tile j+1 (wave-uniform)
-    if (!half) finish(2 * j, cur, cur, 1);
-    finish(2 * j + (half ? par : 1), cur, nxt1, half ? 2 : 1);
+    if (!half) {
+      finish(2 * j, cur, cur, 1, sa, sb);
+      sa = sb;
+    }
+    finish(2 * j + (half ? par : 1), cur, nxt1, half ? 2 : 1, sa, sb);
+    sa = sb;
     // tile j+2 has landed once at most this wave's pieces of tile j+3 are outstanding; every
     // wave's share of it is visible after the barrier
     wait_vmcnt(my_pieces);
