@@ -187,26 +187,35 @@ struct AttnArgs {
 
 // Keys per split of a sequence with L (virtual) keys and T query rows on the split-K path: a
 // fixed count if the caller set one, else ceil(L/128) rounded up to a multiple of 32 and clamped
-// to [lo, 2048], where lo = 512 when the sequence's rows per KV head (T times the group size)
-// fit one 16-row tile and its keys have no sparse gap (gapped: vshift > 0), and 256 otherwise.
-// That gives at most 128 splits up to 262144 keys (so one long sequence's splits fit the GPU in
-// one pass, with no sliver of a split left over).  Short single-tile sequences come in batches,
-// where the wider floor halves their items and partials (measured: 32 decode sequences of 1-8K
-// keys 4% faster in bf16, 8% in int8); a verification's two-tile items gain nothing from it
-// (32K keys: 6% slower), nor does a sparse walk of one window, whose few items bound its
-// latency (two 4K-key windows: 14 -> 20 us).  The split depends on the sequence alone, so its
-// reduction order does too.
-// The floor of that rule, shared by the kernels (per sequence: its rows per KV head and whether
-// its keys have a sparse gap) and the host (for a whole call: the largest rows per KV head of its
-// split-K sequences and whether any may be gapped), so that the host's decision to skip the
-// reduce launch (no sequence can have a second split) always agrees with the kernels' splits.
-__host__ __device__ __forceinline__ int split_floor(int rows_per_kv_head, bool gapped) {
-  return rows_per_kv_head <= 16 && !gapped ? 512 : 256;
+// to [lo, 2048] with lo = split_floor(...).  That gives at most 128 splits up to 262144 keys (so
+// one long sequence's splits fit the GPU in one pass, with no sliver of a split left over).  The
+// split depends on the sequence and the pool alone, so its reduction order does too.
+//
+// The floor: 512 keys when the sequence's rows per KV head (T times the group size) fit one
+// 16-row tile and its keys have no sparse gap (gapped: vshift > 0); otherwise 352 on bf16 / fp32
+// pools and 256 on int8 pools, and 256 for a gapped walk.  Measured (step time, one MI355X):
+//  - short single-tile sequences come in batches, where the wider floor halves their items and
+//    partials (32 decode sequences of 1-8K keys 4% faster in bf16, 8% in int8 at 512 than 256);
+//  - a verification of 1 + 3 drafts over 32K keys (two 16-row tiles per KV head) takes 41.0 us at
+//    288-key splits, 37.8 at 352, 37.9 at 384 and 43.0 at 512 on a bf16 pool; on an int8 pool,
+//    whose chunks are half the bytes, 40.6 at 288 and 42.2 at 352;
+//  - a sparse walk of one window has few items, which bound its latency (two 4K-key windows:
+//    14 -> 20 us with the 512 floor).
+// Shared by the kernels (per sequence: its rows per KV head, whether its keys have a sparse gap)
+// and the host (for a whole call: the largest rows per KV head of its split-K sequences and
+// whether any may be gapped; the result is the smallest floor of the call), so the host's
+// decision to skip the reduce launch (no sequence can have a second split) always agrees with the
+// kernels' splits.
+__host__ __device__ __forceinline__ int split_floor(int rows_per_kv_head, bool gapped, bool int8) {
+  if (gapped) return 256;
+  if (rows_per_kv_head <= 16) return 512;
+  return int8 ? 256 : 352;
 }
+// k_scale_layer is set exactly for int8 pools.
 __device__ __forceinline__ int seq_split(const AttnArgs& a, int L, int T, bool gapped) {
   if (a.split_tokens > 0) return a.split_tokens;
   const int per = (L >> 7) + ((L & 127) != 0);  // ceil(L / 128) without overflow
-  const int lo = split_floor(T * a.group, gapped);
+  const int lo = split_floor(T * a.group, gapped, a.k_scale_layer != nullptr);
   return min(max((per + 31) & ~31, lo), 2048);
 }
 

@@ -56,8 +56,8 @@ bool env_flag(const char* name) {
 }
 
 // Keys per split in split mode: 0 selects the per-sequence rule the kernels apply (about L/128
-// rounded up to 32 keys, within [512, 2048] for sequences whose rows per KV head fit one 16-row
-// tile and [256, 2048] otherwise), KVATTN_SPLIT_TOKENS fixes a count for tuning sweeps.  Neither
+// rounded up to 32 keys, within [split_floor, 2048]), KVATTN_SPLIT_TOKENS fixes a count for
+// tuning sweeps.  Neither
 // depends on the rest of the batch, so each sequence's reduction order is a function of its own
 // length and row count only.
 int split_tokens() {
@@ -837,7 +837,8 @@ int forward_impl(kvpool_t* pool, int32_t layer, const void* q, void* out, int32_
   // Rows whose keys all fall in split 0 are finished by the attention kernels; when no sequence
   // can have a second split the reduce has nothing to do.  Every split holds at least the rule's
   // floor for the call's longest split-K rows per KV head (a sparse call may have a gap).
-  const int min_split = pl.split > 0 ? pl.split : kvp::split_floor(pl.split_rows, sp.window > 0);
+  const int min_split = pl.split > 0 ? pl.split
+                                     : kvp::split_floor(pl.split_rows, sp.window > 0, i8);
   const bool need_reduce = pl.split_k && max_ctx_len > min_split;
   if (need_reduce) {
     e = timed(K_REDUCE, st, [&] { return kvp::launch_attn_reduce(a, eb, pool->head_dim, st); });

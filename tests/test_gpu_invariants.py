@@ -149,17 +149,19 @@ def test_short_decode_without_reduce(dtype, mirror):
     assert_close(out_f64(out), c.oracle(), dtype, w.name, q_lens=w.q_lens)
 
 
-# (context lengths, q_lens, q-heads, sparse parameters or None, reduce launches expected).  The
-# reduce runs exactly when the shared split floor lets some sequence have a second split: 512
-# keys for single-tile rows (q_len * G <= 16, no sparse gap), 256 otherwise; a sparse call may
-# have a gap, so its host bound is 256.
+# (context lengths, q_lens, q-heads, sparse parameters or None, pool dtype, reduce launches
+# expected).  The reduce runs exactly when the shared split floor lets some sequence have a
+# second split: 512 keys for single-tile rows (q_len * G <= 16, no sparse gap), otherwise 352 on
+# bf16 pools and 256 on int8 pools; a sparse call may have a gap, so its host bound is 256.
 REDUCE_CASES = [
-    ([512, 300], [1, 1], 32, None, 0),        # G = 4: 4 rows per KV head, 512-key splits
-    ([513, 300], [1, 1], 32, None, 1),        # 513 keys: a second split
-    ([300, 200], [4, 1], 32, None, 0),        # T*G = 16: still one tile, 512-key floor
-    ([300, 200], [5, 1], 32, None, 1),        # T*G = 20: 256-key floor, 300 keys = 2 splits
-    ([256, 100], [5, 2], 32, None, 0),        # 256-key floor but nobody past 256 keys
-    ([400, 300], [1, 1], 32, (16, 64, 10**6), 1),  # sparse, below threshold: host bound 256
+    ([512, 300], [1, 1], 32, None, wl.BF16, 0),    # G = 4: 4 rows per KV head, 512-key splits
+    ([513, 300], [1, 1], 32, None, wl.BF16, 1),    # 513 keys: a second split
+    ([300, 200], [4, 1], 32, None, wl.BF16, 0),    # T*G = 16: still one tile, 512-key floor
+    ([352, 200], [5, 1], 32, None, wl.BF16, 0),    # T*G = 20 on bf16: 352-key floor
+    ([353, 200], [5, 1], 32, None, wl.BF16, 1),    # 353 keys: a second split
+    ([300, 200], [5, 1], 32, None, wl.I8, 1),      # int8 pool: 256-key floor, 300 keys = 2 splits
+    ([256, 100], [5, 2], 32, None, wl.I8, 0),      # 256-key floor but nobody past 256 keys
+    ([400, 300], [1, 1], 32, (16, 64, 10**6), wl.BF16, 1),  # sparse, below threshold: bound 256
 ]
 
 
@@ -167,9 +169,9 @@ REDUCE_CASES = [
 def test_reduce_launch_follows_split_floor(case):
     """The host launches the reduce only when some sequence can have a second split, by the
     same floor the kernels split with; every row still matches the oracle."""
-    ctx, ql, hq, sparse, expect = REDUCE_CASES[case]
-    announce(f"reduce launch case {case}: ctx={ctx} q_lens={ql} sparse={sparse}")
-    w = wl.make(f"reduce_case_{case}", seed=170 + case, dtype=wl.BF16, num_seqs_ctx=ctx,
+    ctx, ql, hq, sparse, dtype, expect = REDUCE_CASES[case]
+    announce(f"reduce launch case {case}: ctx={ctx} q_lens={ql} sparse={sparse} {dtype}")
+    w = wl.make(f"reduce_case_{case}", seed=170 + case, dtype=dtype, num_seqs_ctx=ctx,
                 q_lens=ql, num_q_heads=hq, num_kv_heads=8, head_dim=128)
     c = DeviceCase(w)
     c.append()
@@ -180,7 +182,7 @@ def test_reduce_launch_follows_split_floor(case):
     got = kb.kernel_times().get("attn_reduce", (0, 0.0))[0]
     assert got == expect, f"reduce launches {got}, expected {expect}"
     ref = c.oracle() if sparse is None else c.oracle_sparse(*sparse)
-    assert_close(out_f64(out), ref, wl.BF16, w.name, q_lens=w.q_lens)
+    assert_close(out_f64(out), ref, dtype, w.name, q_lens=w.q_lens)
 
 
 @pytest.mark.parametrize("dtype,bs", [(wl.BF16, 16), (wl.BF16, 64), (wl.F32, 16)])
