@@ -37,6 +37,7 @@ namespace kvp {
 namespace {
 
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ floatx16 mfma32(bf16x8 a, bf16x8 b, floatx16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -60,8 +61,13 @@ __device__ __forceinline__ void dma_tile(const void* gbase, uint32_t voff, uint3
   const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(g >> 32));
   const uint64_t gs = ((uint64_t)hi << 32) | (uint64_t)lo;
   const uint32_t ls = (uint32_t)__builtin_amdgcn_readfirstlane(lds_addr);
-  static_assert(NQ == 2 || NQ == 4, "pool tiles of 2 or 4 KiB");
-  if constexpr (NQ == 4)
+  static_assert(NQ == 1 || NQ == 2 || NQ == 4, "pool tiles of 1, 2 or 4 KiB");
+  if constexpr (NQ == 1)
+    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+                 :
+                 : "v"(voff), "s"(reinterpret_cast<const void*>(gs)), "s"(ls)
+                 : "memory", "m0");
+  else if constexpr (NQ == 4)
     asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1\n\t"
                  "global_load_lds_dwordx4 %0, %1 offset:1024\n\t"
                  "global_load_lds_dwordx4 %0, %1 offset:2048\n\t"
@@ -75,6 +81,21 @@ __device__ __forceinline__ void dma_tile(const void* gbase, uint32_t voff, uint3
                  :
                  : "v"(voff), "s"(reinterpret_cast<const void*>(gs)), "s"(ls)
                  : "memory", "m0");
+}
+
+// int8 pools: 64 dwords, lane l's from gbase + voff (voff per lane), into LDS at lds_addr + 4*l
+// (one global_load_lds_dword, issued like dma_tile).  Used for the 16 per-token scales of a pool
+// tile (voff = 4 * (lane % 16): four copies).
+__device__ __forceinline__ void dma_dwords(const void* gbase, uint32_t voff, uint32_t lds_addr) {
+  const uint64_t g = reinterpret_cast<uint64_t>(gbase);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)g);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(g >> 32));
+  const uint64_t gs = ((uint64_t)hi << 32) | (uint64_t)lo;
+  const uint32_t ls = (uint32_t)__builtin_amdgcn_readfirstlane(lds_addr);
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1"
+               :
+               : "v"(voff), "s"(reinterpret_cast<const void*>(gs)), "s"(ls)
+               : "memory", "m0");
 }
 
 template <typename P>
@@ -207,21 +228,31 @@ template <> struct PfSched<64> {
 };
 
 // Up to 12 waves per workgroup, 3 per SIMD: at most 168 registers per wave.
-template <int D>
+// I8: an int8 pool (codes and per-token fp32 scales), converted to bf16 in LDS (see the staging
+// notes below).
+template <int D, bool I8>
 __global__ __launch_bounds__(768) __attribute__((amdgpu_waves_per_eu(3)))
 void attn_prefill_mfma_kernel(AttnArgs a) {
   constexpr int KS = D / 16;          // 16-dim k-steps of the score product
   constexpr int MB = D / 32;          // 32-dim blocks of the output
   constexpr int TE = 16 * D;          // elements of one pool tile (K or V)
-  constexpr int TQ = TE * 2 / 1024;   // 1 KiB DMA pieces per pool tile
+  constexpr int TQ = TE * (I8 ? 1 : 2) / 1024;  // 1 KiB DMA pieces per pool tile
   constexpr int IDS = 1024;           // block ids of pool tiles held in LDS
   // One array per LDS stage ([K0..K3, V0..V3] each): with every access naming its array, the
   // compiler can tell the stage being computed from the ones the DMA is filling, and does not
-  // wait for those loads before reading.
+  // wait for those loads before reading.  bf16 pools: four bf16 stages.  int8 pools: three bf16
+  // stages plus three int8 stages (the codes of a 64-key tile and the 16 scales of each of its
+  // pool tiles, four times over: 64 floats); 154 KiB at D = 128.
   __shared__ __attribute__((aligned(16))) uint16_t lds0[8][TE];
   __shared__ __attribute__((aligned(16))) uint16_t lds1[8][TE];
   __shared__ __attribute__((aligned(16))) uint16_t lds2[8][TE];
-  __shared__ __attribute__((aligned(16))) uint16_t lds3[8][TE];
+  __shared__ __attribute__((aligned(16))) uint16_t lds3[I8 ? 1 : 8][I8 ? 8 : TE];
+  __shared__ __attribute__((aligned(16))) uint8_t q8a[I8 ? 8 : 1][I8 ? TE : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t q8b[I8 ? 8 : 1][I8 ? TE : 16];
+  __shared__ __attribute__((aligned(16))) uint8_t q8c[I8 ? 8 : 1][I8 ? TE : 16];
+  __shared__ __attribute__((aligned(16))) float sca[I8 ? 8 : 1][64];
+  __shared__ __attribute__((aligned(16))) float scb[I8 ? 8 : 1][64];
+  __shared__ __attribute__((aligned(16))) float scc[I8 ? 8 : 1][64];
   __shared__ __attribute__((aligned(16))) int s_ids[IDS];
 
   const int W = blockDim.x >> 6;
@@ -321,9 +352,17 @@ void attn_prefill_mfma_kernel(AttnArgs a) {
                          : !split ? wave
                          : (wave & 3) >= wrem ? (wave >> 2) * (4 - wrem) + (wave & 3) - wrem : -1;
   const uint32_t lane_off = 16u * lane;
-  const int my_pieces = issue_rank < 0 ? 0 : (8 - issue_rank + nissue - 1) / nissue * TQ;
+  // pool tiles a wave streams per 64-key tile (at most 2: nissue >= 4), and its DMA
+  // instructions per 64-key tile (int8: one more per pool tile, for its scales)
+  const int my_slots = issue_rank < 0 ? 0 : (8 - issue_rank + nissue - 1) / nissue;
+  const int my_pieces = my_slots * (TQ + (I8 ? 1 : 0));
   auto read_ids = [&](int j) -> i32x4 { return *reinterpret_cast<const i32x4*>(&s_ids[4 * j - ids0]); };
-  auto fetch = [&](int j, const i32x4& ids, uint16_t (&stage)[8][TE]) {
+  // int8 staging, per lane: byte offset of its scale (token lane % 16) in a pool tile's 16
+  // scales (the DMA offset of the scale loads)
+  const uint32_t sc_off = 4u * (lane & 15);
+  // Tile j into `stage` (bf16: a bf16 stage; int8: an int8 stage, the scales of pool tile slot s
+  // into scales[s]).
+  auto fetch = [&](int j, const i32x4& ids, auto&& stage, auto&& scales) {
     if (issue_rank < 0) return;  // wave-uniform
     int blk[4];
 #pragma unroll
@@ -333,15 +372,98 @@ void attn_prefill_mfma_kernel(AttnArgs a) {
       const int pt = min(4 * j + t, npt - 1);
       const int b = t == 0 ? blk[0] : t == 1 ? blk[1] : t == 2 ? blk[2] : blk[3];
       const size_t off = block_tile_offset(b, ((pt << 4) & bmask) >> 4, kvh, a.block_shift,
-                                           a.num_blocks, a.num_kv_heads, D) * 2;
-      dma_tile<TQ>((slot < 4 ? kbase : vbase) + off, lane_off, lds_address(stage[slot]));
+                                           a.num_blocks, a.num_kv_heads, D);  // elements
+      dma_tile<TQ>((slot < 4 ? kbase : vbase) + off * (I8 ? 1 : 2), lane_off, lds_address(stage[slot]));
+      if constexpr (I8)
+        dma_dwords((slot < 4 ? a.k_scale_layer : a.v_scale_layer) + off / D, sc_off,
+                   lds_address(&scales[slot][0]));
+    }
+  };
+  // int8 pools: 64-key tile jf from an int8 stage (published by a barrier) into the bf16 stage
+  // st.  Each value is code * scale rounded once to the nearest-even bf16 (computed as
+  // fma(code + 128, s, -128 s): the exact product, rounded once, as the fp32 product), and keys
+  // at or past the context get scale 0, so their K and V are exactly 0 (whatever the pool holds
+  // there).  The tile is cut into units of 16 codes per lane (K: the 16-byte rows lane + 64 m of
+  // a pool tile; V: token group pair m of a pool tile, D = 128; at D = 64 a pool tile is one
+  // unit), dealt round-robin to the waves, the half waves first (they carry half the matrix
+  // work), so that the conversion's vector work is spread over every SIMD and wave.  Per-lane
+  // offsets are derived from a lane id read afresh (volatile: not hoisted out of the tile loop),
+  // so they hold no registers through the rest of the step.
+  //   K [d/16][t][d%16] -> [d/8][t][d%8]: lane takes row lane + 64 m (token lane % 16, dims
+  //     16 (lane / 16 + 4 m) ..).
+  //   V [t/4][d%16][d/16][t%4] -> [d][t]: lane (dlo = lane % 16, r = lane / 16) takes dims
+  //     16 (dh0 + kk) + dlo, kk < 4, for the 4 tokens of group tg0 + m.
+  constexpr int UPS = D / 64;  // units per pool tile
+  const int conv_rank = half ? wave - F : (W - F) + wave;  // the waves' order for the deal
+  auto convert = [&](int jf, auto&& qs, auto&& scs, uint16_t (&st)[8][TE]) {
+    if constexpr (I8) {
+      uint32_t ln;
+      asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+      const uint32_t lsc = 4u * (ln & 15);
+      const int v_tg0 = D == 128 ? 2 * (int)(ln >> 5) : (int)(ln >> 4);
+      const int v_dh0 = D == 128 ? 4 * (int)((ln >> 4) & 1) : 0;
+      const uint32_t k_src = 16u * ln;
+      const uint32_t k_dst = 512u * (ln >> 4) + 16u * (ln & 15);
+      const uint32_t v_src = (uint32_t)(((v_tg0 * 16 + (int)(ln & 15)) * (D / 16) + v_dh0) * 4);
+      const uint32_t v_dst = (uint32_t)(((16 * v_dh0 + (int)(ln & 15)) * 16 + 4 * v_tg0) * 2);
+      for (int u = conv_rank; u < 8 * UPS; u += W) {  // wave-uniform
+        const int slot = u / UPS, m = u % UPS;
+        const char* src = reinterpret_cast<const char*>(qs[slot]);
+        const char* scl = reinterpret_cast<const char*>(scs[slot]);
+        char* dst = reinterpret_cast<char*>(st[slot]);
+        const int rem = L - (64 * jf + 16 * (slot & 3));  // keys of the pool tile in the context
+        if (slot < 4) {
+          const float sv = (int)(ln & 15) < rem ? *reinterpret_cast<const float*>(scl + lsc) : 0.f;
+          const float nb = -128.f * sv;
+          const u32x4 w = *reinterpret_cast<const u32x4*>(src + k_src + 1024 * m);
+          uint32_t r[8];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t x = w[e] ^ 0x80808080u;  // code + 128 in each byte
+            r[2 * e] = cvt_pk_bf16(__builtin_fmaf((float)(x & 0xffu), sv, nb),
+                                   __builtin_fmaf((float)((x >> 8) & 0xffu), sv, nb));
+            r[2 * e + 1] = cvt_pk_bf16(__builtin_fmaf((float)((x >> 16) & 0xffu), sv, nb),
+                                       __builtin_fmaf((float)(x >> 24), sv, nb));
+          }
+          // chunks 2c and 2c + 1 of the token (c = lane / 16 + 4 m): 16 tokens * 16 bytes apart
+          *reinterpret_cast<u32x4*>(dst + k_dst + 2048 * m) = u32x4{r[0], r[1], r[2], r[3]};
+          *reinterpret_cast<u32x4*>(dst + k_dst + 2048 * m + 256) = u32x4{r[4], r[5], r[6], r[7]};
+        } else {
+          const int tg = v_tg0 + m;
+          const u32x4 x = *reinterpret_cast<const u32x4*>(src + v_src + m * 16 * D / 4);
+          const floatx4 s4 = *reinterpret_cast<const floatx4*>(scl + 16 * tg);
+          float sv[4], nb[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            sv[e] = 4 * tg + e < rem ? s4[e] : 0.f;
+            nb[e] = -128.f * sv[e];
+          }
+#pragma unroll
+          for (int kk = 0; kk < 4; ++kk) {
+            const uint32_t xx = x[kk] ^ 0x80808080u;
+            const uint32_t r0 = cvt_pk_bf16(__builtin_fmaf((float)(xx & 0xffu), sv[0], nb[0]),
+                                            __builtin_fmaf((float)((xx >> 8) & 0xffu), sv[1], nb[1]));
+            const uint32_t r1 = cvt_pk_bf16(__builtin_fmaf((float)((xx >> 16) & 0xffu), sv[2], nb[2]),
+                                            __builtin_fmaf((float)(xx >> 24), sv[3], nb[3]));
+            // dim 16 (dh0 + kk) + dlo: 16 dims * 32 bytes apart; token group m: 8 bytes
+            *reinterpret_cast<u32x2*>(dst + v_dst + 512 * kk + 8 * m) = u32x2{r0, r1};
+          }
+        }
+      }
     }
   };
   // Three tiles in flight from the start (clamped: a short context re-reads its last tile, so
-  // every wave's count of outstanding pieces follows the same pattern).
-  fetch(jb, read_ids(jb), lds0);
-  fetch(min(jt0 + 1, jlast), read_ids(min(jt0 + 1, jlast)), lds1);
-  fetch(min(jt0 + 2, jlast), read_ids(min(jt0 + 2, jlast)), lds2);
+  // every wave's count of outstanding pieces follows the same pattern); int8 pools: a fourth
+  // goes into the first int8 stage once its codes are converted.
+  if constexpr (I8) {
+    fetch(jb, read_ids(jb), q8a, sca);
+    fetch(min(jt0 + 1, jlast), read_ids(min(jt0 + 1, jlast)), q8b, scb);
+    fetch(min(jt0 + 2, jlast), read_ids(min(jt0 + 2, jlast)), q8c, scc);
+  } else {
+    fetch(jb, read_ids(jb), lds0, sca);
+    fetch(min(jt0 + 1, jlast), read_ids(min(jt0 + 1, jlast)), lds1, sca);
+    fetch(min(jt0 + 2, jlast), read_ids(min(jt0 + 2, jlast)), lds2, sca);
+  }
 
   // ---- Q^T operands and per-row state ----------------------------------------------------
   // B operand of k-step k: lane (col, h) holds dims 16k + 8h .. +8 of the wave's row col.
@@ -381,9 +503,21 @@ void attn_prefill_mfma_kernel(AttnArgs a) {
   // V^T: dim col of the 32-dim block, tokens 8h .. +8 of the k-step's pool tile.
   const uint32_t v_lane = (uint32_t)((col * 16 + 8 * h) * 2);  // bytes
 
-  // Tiles 0 and 1 must have landed (at most this wave's pieces of tile 2 outstanding).
-  wait_vmcnt(my_pieces);
-  __syncthreads();
+  if constexpr (I8) {
+    // Tiles 0-2 (and Q) have landed and are published; tiles 0 and 1 are converted by every
+    // wave and published, then tile 3 streams into the first int8 stage (read by then).
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    barrier_no_fence();
+    convert(jb, q8a, sca, lds0);
+    convert(min(jt0 + 1, jlast), q8b, scb, lds1);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+    barrier_no_fence();
+    fetch(min(jt0 + 3, jlast), read_ids(min(jt0 + 3, jlast)), q8a, sca);
+  } else {
+    // Tiles 0 and 1 must have landed (at most this wave's pieces of tile 2 outstanding).
+    wait_vmcnt(my_pieces);
+    __syncthreads();
+  }
 
   // V slots of keys at or past the context (only in the last 64-key tile) may hold anything,
   // NaN included, and p = 0 times NaN is NaN: once that tile has landed, the workgroup zeroes
@@ -401,8 +535,10 @@ void attn_prefill_mfma_kernel(AttnArgs a) {
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this thread's LDS writes are done
     barrier_no_fence();
   };
-  zero_tail(lds0, jt0);
-  zero_tail(lds1, jt0 + 1);
+  if constexpr (!I8) {  // (int8 pools: the conversion zeroes them)
+    zero_tail(lds0, jt0);
+    zero_tail(lds1, jt0 + 1);
+  }
 
   // Attention of this wave's 32 rows against one 32-key block (pool tiles 2b, 2b+1 of the
   // stage).  `edge`: the block reaches past the wave's first row (causal diagonal) or past the
@@ -429,7 +565,9 @@ void attn_prefill_mfma_kernel(AttnArgs a) {
     if (edge) {
       // keys of this lane: kb + 16 (e / 8) + 8 h' + e % 8 (h' recomputed from the lane id here
       // rather than held in a register through the loop)
-      const int hh = (__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) >> 5) & 1;
+      uint32_t ln;
+      asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(ln));
+      const int hh = (int)((ln >> 5) & 1);
       const int lim = min(prow, L - 1) - kb - 8 * hh;  // e is visible iff 16 (e / 8) + e % 8 <= lim
 #pragma unroll
       for (int e = 0; e < 16; ++e)
@@ -534,22 +672,28 @@ void attn_prefill_mfma_kernel(AttnArgs a) {
     row_max(sa, k0, k0 + 31 > pw0 || k0 + 32 > L);
   }
 
-  // One 64-key tile j (stage `cur`): tile j+3 starts streaming into `nxt3` (free: its last
-  // reader, tile j-1, was done before the barrier that ended the previous step); the blocks of
-  // tile j are finished, their successors' score products reading `nxt1` (published a step
-  // ago); then tile j+2 (in `nxt2`, issued a step ago) is waited for and published.
+  // One 64-key tile j (stage `cur`).  bf16: tile j+3 starts streaming into `fst` (the fourth
+  // stage, free since its last reader, tile j-1, was done before the barrier that ended the
+  // previous step); the blocks of tile j are finished, their successors' score products reading
+  // `nxt1` (published a step ago); then tile j+2 (issued a step ago, in `nxt2`) is waited for
+  // and published.  int8: tile j+4 starts streaming into `fst` (the int8 stage of tile j+1,
+  // converted in the previous step); every wave converts its units of tile j+2 (its codes
+  // published by the barrier that ended the previous step) from `cst` into `nxt2` (last read as
+  // tile j-1); the blocks of tile j are finished as above; then the codes of tile j+3 (issued a
+  // step ago) are waited for, and the barrier publishes them with the bf16 tile j+2.
   auto step = [&](int j, uint16_t (&cur)[8][TE], uint16_t (&nxt1)[8][TE], uint16_t (&nxt2)[8][TE],
-                  uint16_t (&nxt3)[8][TE]) {
+                  auto&& fst, auto&& fsc, auto&& cst, auto&& csc) {
     // the ids of tile j+3; refill the id cache first when they lie past it (rare: only past
     // 16K keys; workgroup-uniform)
-    const int jf = min(j + 3, jlast);
+    const int jf = min(j + (I8 ? 4 : 3), jlast);
     if (4 * jf + 3 - ids0 >= IDS) {
       __syncthreads();
       ids0 = 4 * jf;
       load_ids(ids0);
       __syncthreads();
     }
-    fetch(jf, read_ids(jf), nxt3);
+    fetch(jf, read_ids(jf), fst, fsc);
+    if constexpr (I8) convert(min(j + 2, jlast), cst, csc, nxt2);
     // whole-block waves: blocks 2j and 2j+1; half waves: block 2j + parity, then the same parity
     // in tile j+1 (wave-uniform)
     if (!half) {
@@ -558,17 +702,34 @@ void attn_prefill_mfma_kernel(AttnArgs a) {
     }
     finish(2 * j + (half ? par : 1), cur, nxt1, half ? 2 : 1, sa, sb);
     sa = sb;
-    // tile j+2 has landed once at most this wave's pieces of tile j+3 are outstanding; every
-    // wave's share of it is visible after the barrier
-    wait_vmcnt(my_pieces);
-    barrier_no_fence();
-    zero_tail(nxt2, j + 2);
+    if constexpr (I8) {
+      // tile j+3's codes have landed once at most this wave's pieces of tile j+4 are
+      // outstanding; the conversion's writes are done (lgkmcnt(0))
+      wait_vmcnt(my_pieces);
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      barrier_no_fence();
+    } else {
+      // tile j+2 has landed once at most this wave's pieces of tile j+3 are outstanding; every
+      // wave's share of it is visible after the barrier
+      wait_vmcnt(my_pieces);
+      barrier_no_fence();
+      zero_tail(nxt2, j + 2);
+    }
   };
-  for (int j = jt0; j < jt1; j += 4) {
-    step(j, lds0, lds1, lds2, lds3);
-    if (j + 1 < jt1) step(j + 1, lds1, lds2, lds3, lds0);
-    if (j + 2 < jt1) step(j + 2, lds2, lds3, lds0, lds1);
-    if (j + 3 < jt1) step(j + 3, lds3, lds0, lds1, lds2);
+  if constexpr (I8) {
+    // three bf16 and three int8 stages: the pattern repeats every 3 tiles
+    for (int j = jt0; j < jt1; j += 3) {
+      step(j, lds0, lds1, lds2, q8b, scb, q8c, scc);
+      if (j + 1 < jt1) step(j + 1, lds1, lds2, lds0, q8c, scc, q8a, sca);
+      if (j + 2 < jt1) step(j + 2, lds2, lds0, lds1, q8a, sca, q8b, scb);
+    }
+  } else {
+    for (int j = jt0; j < jt1; j += 4) {
+      step(j, lds0, lds1, lds2, lds3, sca, sca, sca);
+      if (j + 1 < jt1) step(j + 1, lds1, lds2, lds3, lds0, sca, sca, sca);
+      if (j + 2 < jt1) step(j + 2, lds2, lds3, lds0, lds1, sca, sca, sca);
+      if (j + 3 < jt1) step(j + 3, lds3, lds0, lds1, lds2, sca, sca, sca);
+    }
   }
   // The last steps re-read the last tile into free stages: drain those loads before the stages
   // are reused below or the workgroup's LDS is released.
@@ -714,18 +875,27 @@ int prefill_ksplit(long long wgs, int num_cus, int max_ctx, bool deterministic) 
 }
 
 hipError_t launch_attn_prefill_mfma(const AttnArgs& a, int head_dim, int waves, long long wgs,
-                                    hipStream_t st) {
+                                    bool i8, hipStream_t st) {
   if (waves < 1 || waves > 12 || wgs < 0 || wgs > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  // int8 staging: at least 4 issuing waves, so that each streams at most 2 pool tiles
+  if (i8 && (waves < 4 || !a.k_scale_layer || !a.v_scale_layer)) return hipErrorInvalidConfiguration;
   // R row blocks with W/2 <= R <= W; at most 6 half pairs (their merge uses 3 stage arrays)
   if (2 * a.pf_rblk < waves || a.pf_rblk > waves || waves - a.pf_rblk > 6) return hipErrorInvalidConfiguration;
   if (wgs == 0) return hipSuccess;
   if (a.pf_ksplit < 1 || a.pf_ksplit > 8 || wgs * a.pf_ksplit > 0x7fffffffLL)
     return hipErrorInvalidConfiguration;
   const dim3 grid((unsigned)(wgs * a.pf_ksplit));
-  if (head_dim == 128)
-    attn_prefill_mfma_kernel<128><<<grid, 64 * waves, 0, st>>>(a);
-  else
-    attn_prefill_mfma_kernel<64><<<grid, 64 * waves, 0, st>>>(a);
+  if (i8) {
+    if (head_dim == 128)
+      attn_prefill_mfma_kernel<128, true><<<grid, 64 * waves, 0, st>>>(a);
+    else
+      attn_prefill_mfma_kernel<64, true><<<grid, 64 * waves, 0, st>>>(a);
+  } else {
+    if (head_dim == 128)
+      attn_prefill_mfma_kernel<128, false><<<grid, 64 * waves, 0, st>>>(a);
+    else
+      attn_prefill_mfma_kernel<64, false><<<grid, 64 * waves, 0, st>>>(a);
+  }
   return hipGetLastError();
 }
 

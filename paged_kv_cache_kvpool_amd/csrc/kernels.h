@@ -83,8 +83,10 @@ hipError_t launch_attn_vec(const AttnArgs& a, int elt_bytes, int head_dim, int r
 // `waves` (1..12) waves over a.pf_rblk 32-row blocks share LDS-staged K/V tiles; the workgroups, numbered sequence
 // by sequence (KV heads x row tiles of each prefill-class sequence), are found on the device
 // from q_lens.  `wgs`: grid size, at least the number of workgroups there are (extra ones exit).
+// int8_kv: the pool holds int8 codes with per-token scales, converted to bf16 in LDS (needs
+// waves >= 4): the path for int8 pools when the workspace has no room for a bf16 copy.
 hipError_t launch_attn_prefill_mfma(const AttnArgs& a, int head_dim, int waves, long long wgs,
-                                    hipStream_t st);
+                                    bool int8_kv, hipStream_t st);
 // Workgroups of the prefill kernel for prefill-class sequences of rows[i] = q_len * G rows each,
 // with rblk 32-row blocks per workgroup.
 long long prefill_wg_count(const int* rows, int n, int num_kv_heads, int rblk);
@@ -97,9 +99,10 @@ int prefill_ksplit(long long wgs, int num_cus, int max_ctx, bool deterministic);
 // SIMDs and the workgroups over the CUs.  whole_only: rblk = waves (no pairs).
 void prefill_plan(const int* rows, int n, int num_kv_heads, int num_cus, bool whole_only,
                   int* waves, int* rblk);
-// Prefill over an int8 pool: the prefill-class sequences' tiles dequantized to bf16 into a
-// workspace pool (max_seqs sequences of blocks_per_seq 16-token blocks) and its block table
-// [num_seqs][blocks_per_seq]; the grid covers max_seqs sequences of blocks_per_seq tiles.
+// Prefill over an int8 pool, when the workspace holds the copy: the prefill-class sequences'
+// tiles dequantized to bf16 into a workspace pool (max_seqs sequences of blocks_per_seq 16-token
+// blocks) and its block table [num_seqs][blocks_per_seq]; the grid covers max_seqs sequences
+// of blocks_per_seq tiles.
 struct DequantOut {
   uint16_t* k;
   uint16_t* v;

@@ -1,8 +1,9 @@
 // Prefill over an int8 pool: the K/V tiles of the prefill-class sequences (q_len > split_q_max)
 // are dequantized to bf16 (code times its token's scale, rounded to nearest even) into a
-// workspace pool that the bf16 prefill kernel then reads.  Prefill is bound by the matrix
-// cores and reads each key once per workgroup from LDS, so a converted copy costs one extra
-// pass over HBM, while converting inside its inner loop would cost VALU work it has none of.
+// workspace pool that the bf16 prefill kernel then reads.  The copy costs one extra pass over
+// HBM; the alternative, converting the codes in the prefill kernel's LDS stages (its int8
+// path, used when the workspace has no room for the copy), gives the same bits but adds vector
+// work that the prefill kernel cannot hide behind its matrix work, and measured slower.
 // (int8 KV storage: NInfer serving doc, "Server options", --kv-dtype int8; sparkinfer server
 // README, "Env", SPARKINFER_KV_INT8.)
 //

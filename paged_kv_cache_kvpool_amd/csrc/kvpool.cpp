@@ -55,6 +55,11 @@ bool env_flag(const char* name) {
   return v && *v && strcmp(v, "0") != 0;
 }
 
+bool env_is(const char* name, const char* value) {
+  const char* v = getenv(name);
+  return v && strcmp(v, value) == 0;
+}
+
 // Keys per split in split mode: 0 selects the per-sequence rule the kernels apply (about L/128
 // rounded up to 32 keys, within [split_floor, 2048]), KVATTN_SPLIT_TOKENS fixes a count for
 // tuning sweeps.  Neither
@@ -505,11 +510,14 @@ struct Plan {
   size_t pf_o_off, pf_ml_off;  // their partials in the workspace
   size_t o_bytes;     // partial outputs, rounded up to 256 bytes
   // int8 pools with prefill-class sequences: their tiles dequantized to a bf16 workspace pool
+  // first (the faster way), when the workspace holds it; else the prefill kernel converts the
+  // codes in LDS (bitwise the same results)
   int dq_seqs;        // prefill sequences it holds (exact or a bound)
   int dq_mpb;         // 16-token blocks per sequence (ceil(max_ctx_len / 16))
   size_t dq_off;      // byte offsets in the workspace: K pool, V pool, block table
   size_t dq_v_off, dq_tbl_off;
-  size_t bytes;
+  size_t bytes_lean;  // the workspace without the bf16 copy (= bytes when there is none)
+  size_t bytes;       // the workspace asked for
 };
 
 // The plan of one call.  With the host mirror of q_lens, the split-K rows, the prefill
@@ -567,10 +575,10 @@ Plan make_plan(const kvpool* p, int32_t num_q_heads, int32_t num_seqs, int32_t t
     // differently, so the bits follow the plan.
     kvp::prefill_plan(pf_rows.data(), (int)pf_rows.size(), p->num_kv_heads, p->num_cus,
                       env_flag("KVATTN_DETERMINISTIC"), &pl.waves, &pl.rblk);
-    // sweeps and tests: KVATTN_PREFILL_WAVES fixes W (then R = W unless KVATTN_PREFILL_RBLK
-    // fixes R within [W/2, W], at most 6 pairs)
+    // sweeps and tests: KVATTN_PREFILL_WAVES fixes W in [4, 12] (then R = W unless
+    // KVATTN_PREFILL_RBLK fixes R within [W/2, W], at most 6 pairs)
     if (const char* v = getenv("KVATTN_PREFILL_WAVES")) {
-      pl.waves = std::max(1, std::min(12, atoi(v)));
+      pl.waves = std::max(4, std::min(12, atoi(v)));
       pl.rblk = pl.waves;
       if (const char* r = getenv("KVATTN_PREFILL_RBLK"))
         pl.rblk = std::max(std::max((pl.waves + 1) / 2, pl.waves - 6), std::min(pl.waves, atoi(r)));
@@ -606,6 +614,7 @@ Plan make_plan(const kvpool* p, int32_t num_q_heads, int32_t num_seqs, int32_t t
     pl.pf_ml_off = pl.pf_o_off + (pslots * p->head_dim * 4 + 255) / 256 * 256;
     pl.bytes = pl.pf_ml_off + (pslots * 2 * 4 + 255) / 256 * 256;
   }
+  pl.bytes_lean = pl.bytes;
   if (p->dtype == KV_I8 && pl.prefill) {
     // [dequantized K][dequantized V][block table], each 256-byte aligned
     pl.dq_seqs = q_lens_host ? n_pf_exact
@@ -690,15 +699,20 @@ int forward_impl(kvpool_t* pool, int32_t layer, const void* q, void* out, int32_
     return fail(KV_ERANGE, "total_q * num_q_heads must stay below 2^31");
   if ((long long)num_seqs * pool->num_kv_heads * 8 * pl.max_splits >= (1ll << 30))
     return fail(KV_ERANGE, "too many work items (splits x KV heads x row tiles) in one call");
-  if (g_no_events && pl.bytes > workspace_bytes)
+  // int8 prefill: the bf16 copy when the workspace holds it (and KVATTN_INT8_PREFILL is not
+  // "lds"), else the conversion in LDS, which needs only bytes_lean
+  const bool dq = pl.bytes > pl.bytes_lean && workspace && workspace_bytes >= pl.bytes &&
+                  !env_is("KVATTN_INT8_PREFILL", "lds");
+  const size_t need = dq ? pl.bytes : pl.bytes_lean;
+  if (g_no_events && need > workspace_bytes)
     return fail(KV_ENOMEM,
                 "this call needs %zu bytes of scratch; the static buffer of the allocation-free "
                 "entry point holds %zu (call kvattn_forward with a workspace instead)",
-                pl.bytes, workspace_bytes);
-  if (pl.bytes) {
+                need, workspace_bytes);
+  if (need) {
     if (!workspace) return fail(KV_ENOMEM, "workspace of %zu bytes required", pl.bytes);
-    if (workspace_bytes < pl.bytes)
-      return fail(KV_ENOMEM, "workspace has %zu bytes, %zu required", workspace_bytes, pl.bytes);
+    if (workspace_bytes < need)
+      return fail(KV_ENOMEM, "workspace has %zu bytes, %zu required", workspace_bytes, need);
     if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
       return fail(KV_EINVAL, "workspace must be 256-byte aligned");
   }
@@ -809,26 +823,28 @@ int forward_impl(kvpool_t* pool, int32_t layer, const void* q, void* out, int32_
     }
     if (e == hipSuccess && pl.prefill) {
       kvp::AttnArgs ap = a;
-      if (i8) {
+      if (i8 && dq) {
         // dequantize the prefill sequences' tiles into the workspace pool, then run the bf16
         // kernel on it (16-token blocks, its own block table)
-        kvp::DequantOut dq;
-        dq.k = reinterpret_cast<uint16_t*>(ws + pl.dq_off);
-        dq.v = reinterpret_cast<uint16_t*>(ws + pl.dq_v_off);
-        dq.tables = reinterpret_cast<int32_t*>(ws + pl.dq_tbl_off);
-        dq.blocks_per_seq = pl.dq_mpb;
-        dq.max_seqs = pl.dq_seqs;
-        e = timed(K_DEQUANT, st, [&] { return kvp::launch_dequant_prefill(a, dq, pool->head_dim, st); });
-        ap.k_layer = dq.k;
-        ap.v_layer = dq.v;
-        ap.block_tables = dq.tables;
+        kvp::DequantOut o;
+        o.k = reinterpret_cast<uint16_t*>(ws + pl.dq_off);
+        o.v = reinterpret_cast<uint16_t*>(ws + pl.dq_v_off);
+        o.tables = reinterpret_cast<int32_t*>(ws + pl.dq_tbl_off);
+        o.blocks_per_seq = pl.dq_mpb;
+        o.max_seqs = pl.dq_seqs;
+        e = timed(K_DEQUANT, st, [&] { return kvp::launch_dequant_prefill(a, o, pool->head_dim, st); });
+        ap.k_layer = o.k;
+        ap.v_layer = o.v;
+        ap.block_tables = o.tables;
         ap.max_blocks_per_seq = pl.dq_mpb;
         ap.block_size = 16;
         ap.block_shift = 4;
         ap.num_blocks = std::max(1, pl.dq_seqs * pl.dq_mpb);
       }
+      // (int8 pools without the copy: the prefill kernel converts the codes in LDS)
+      const bool conv = i8 && !dq;
       if (e == hipSuccess)
-        e = timed(K_PREFILL_MFMA, st, [&] { return kvp::launch_attn_prefill_mfma(ap, pool->head_dim, pl.waves, pl.pf_wgs, st); });
+        e = timed(K_PREFILL_MFMA, st, [&] { return kvp::launch_attn_prefill_mfma(ap, pool->head_dim, pl.waves, pl.pf_wgs, conv, st); });
       if (e == hipSuccess && pl.pf_ks > 1)
         e = timed(K_REDUCE_PF, st, [&] { return kvp::launch_attn_reduce_prefill(ap, eb, pool->head_dim, st); });
     }

@@ -4,18 +4,23 @@ The append quantises bf16 rows into codes and per-(token, KV head) scales and is
 for bit (codes and scales, whole pool) with the oracle's quantising append; block copy moves
 codes and scales bit for bit.  Attention on an int8 pool is compared with the oracle run on the
 exactly dequantized K/V, at the bf16 bar (max-abs 2e-2, relative L2 5e-3): decode and
-verification read the codes directly, prefill reads a bf16 dequantized copy.
+verification read the codes directly; prefill reads a bf16 copy dequantized into the workspace
+when the workspace holds it, else converts the codes to bf16 in its LDS stages.  Either way it
+must give, bit for bit, the prefill kernel's output on a bf16 pool holding bf16(f32(code *
+scale)) of every element (test_int8_prefill_equals_bf16_of_dequantized).
 
 The pages report a GQA-fused int8 prefill attention whose results break down from 2048 prompt
 tokens up (sparkinfer server README, "Determinism", known defect); test_int8_prefill_lengths
 runs whole prompts of 1500 to 4000 tokens through the GQA-fused prefill kernel on an int8 pool.
 """
+import dataclasses
 import sys
 
 import numpy as np
 import pytest
 import torch
 
+from oracle import brute
 from oracle import quant as oq
 from paged_kv_cache_kvpool_amd import workloads as wl
 
@@ -24,6 +29,7 @@ pytestmark = pytest.mark.gpu
 if not torch.cuda.is_available():  # pragma: no cover
     pytest.skip("no GPU", allow_module_level=True)
 
+from paged_kv_cache_kvpool_amd import binding as kb  # noqa: E402
 from tests.gpu_util import DeviceCase, assert_close, out_f64  # noqa: E402
 
 
@@ -101,6 +107,92 @@ def test_int8_prefill_lengths(prompt):
     c.append()
     out = c.forward(mirror=True)
     torch.cuda.synchronize()
+    assert_close(out_f64(out), c.oracle(), wl.I8, w.name, q_lens=w.q_lens)
+
+
+def bf16_pool_of_dequantized(w, k8, v8, ks, vs):
+    """Raw bf16 K/V storage (8-dim K chunks) holding, for every element of the int8 pool
+    (k8, v8: raw codes; ks, vs: scales [layers][blocks][Hkv][B]), the nearest-even bf16 of the
+    float32 product code * scale; placed with the storage offset formulas of oracle.brute."""
+    geo = dict(num_kv_heads=w.num_kv_heads, block_size=w.block_size, head_dim=w.head_dim)
+    b, h, t, d = np.meshgrid(np.arange(w.num_blocks), np.arange(w.num_kv_heads),
+                             np.arange(w.block_size), np.arange(w.head_dim), indexing="ij")
+    src = (brute.k_offset_i8(b, h, t, d, **geo), brute.v_offset_i8(b, h, t, d, **geo))
+    dst = (brute.k_offset(b, h, t, d, x=8, **geo), brute.v_offset(b, h, t, d, **geo))
+    out = []
+    for raw, sc, si, di in ((k8, ks, src[0], dst[0]), (v8, vs, src[1], dst[1])):
+        pool = np.empty((w.num_layers, w.num_blocks * w.block_elems), dtype=np.uint16)
+        for layer in range(w.num_layers):
+            codes = raw[layer].reshape(-1).view(np.int8)[si].astype(np.float32)
+            with np.errstate(invalid="ignore"):  # NaN canary scales of unreferenced blocks
+                val = codes * sc[layer][b, h, t].astype(np.float32)  # one float32 rounding
+            pool[layer][di.reshape(-1)] = wl.rne_bf16_bits(val).reshape(-1)
+        out.append(pool.reshape(w.num_layers, w.num_blocks, w.block_elems))
+    return out
+
+
+@pytest.mark.parametrize("path", ["copy", "lds"])
+@pytest.mark.parametrize("hq,hkv,d,bs,ctx,ql", [
+    (40, 8, 128, 16, [700, 1100, 333], [300, 64, 333]),
+    (16, 2, 64, 64, [2100, 517], [129, 517]),
+    (8, 1, 128, 64, [4097], [200]),
+    (4, 1, 64, 16, [1500], [1500]),
+], ids=["H40x8_D128_B16", "H16x2_D64_B64", "H8x1_D128_B64_long", "H4x1_D64_prompt"])
+def test_int8_prefill_equals_bf16_of_dequantized(hq, hkv, d, bs, ctx, ql, path, monkeypatch):
+    """Both int8 prefill paths turn each code into bf16(f32(code * scale)) (keys past the
+    context zero) before the bf16 prefill arithmetic: "copy" into a workspace pool that the bf16
+    kernel reads, "lds" (KVATTN_INT8_PREFILL=lds, the path taken when the workspace has no room
+    for the copy) inside the kernel's LDS stages.  So the output equals, bit for bit, the bf16
+    kernel's on a bf16 pool holding those values (same rows, same plan: every sequence
+    prefill-class).  Exercises ragged last tiles, both head dims and block sizes, key ranges (few
+    workgroups) and whole prompts."""
+    if path == "lds":
+        monkeypatch.setenv("KVATTN_INT8_PREFILL", "lds")
+    else:
+        monkeypatch.delenv("KVATTN_INT8_PREFILL", raising=False)
+    announce(f"int8 prefill ({path}) == bf16 of dequantized Hq={hq} Hkv={hkv} D={d} B={bs} "
+             f"ctx={ctx} q={ql}")
+    w = wl.make(f"i8_eq_{hq}_{d}_{bs}", seed=191 + hq + d + bs + len(ctx), dtype=wl.I8,
+                num_seqs_ctx=ctx, q_lens=ql, num_q_heads=hq, num_kv_heads=hkv, head_dim=d,
+                block_size=bs)
+    assert all(q * (hq // hkv) > 128 for q in ql)  # prefill-class (more than 128 rows per KV head)
+    c = DeviceCase(w)
+    c.append()
+    out8 = c.forward(mirror=True)
+    torch.cuda.synchronize()
+    kb, vb = bf16_pool_of_dequantized(w, *c.host_pools())
+    wb = dataclasses.replace(w, name=w.name + "_bf16", dtype=wl.BF16, k_pool=kb, v_pool=vb,
+                             k_scales=None, v_scales=None, k_new=None, v_new=None)
+    monkeypatch.delenv("KVATTN_INT8_PREFILL", raising=False)
+    cb = DeviceCase(wb)
+    outb = cb.forward(mirror=True)
+    torch.cuda.synchronize()
+    a, r = bits(out8), bits(outb)
+    print(f"[parity] {w.name}: {int(np.count_nonzero(a != r))} of {a.size} outputs differ", flush=True)
+    assert np.array_equal(a, r)
+    assert_close(out_f64(out8), c.oracle(), wl.I8, w.name, q_lens=w.q_lens)
+
+
+def test_int8_prefill_short_workspace_takes_lds_path():
+    """A workspace smaller than kvattn_workspace_size asks (which counts the bf16 copy) but
+    large enough for the rest: the call runs, converting in LDS, with the same bits as with
+    the full workspace (mixed call: decode, verification and prefill rows)."""
+    announce("int8 prefill with a workspace short of the bf16 copy")
+    w = wl.make("i8_short_ws", seed=197, dtype=wl.I8, num_seqs_ctx=[3000, 700, 1000, 2600],
+                q_lens=[1, 4, 300, 129], num_q_heads=40, num_kv_heads=8, head_dim=128)
+    c = DeviceCase(w)
+    c.append()
+    full = c.forward(mirror=True)
+    need = kb.kvattn_workspace_size(c.pool.handle, w.num_q_heads, w.num_seqs, w.total_q,
+                                    int(w.ctx_lens.max()), int(w.q_lens.max()), w.q_lens)
+    short = need - 256  # no room for the copy (it holds at least 2 x 700 x 16 x D bytes)
+    ws = torch.empty(short, dtype=torch.uint8, device="cuda")
+    out = torch.full_like(c.q, float("nan"))
+    kb.kvattn_forward(c.pool.handle, w.layer, c.q, out, w.num_q_heads, w.scale, c.tables,
+                      c.tables.shape[1], c.ctx, c.ql, w.num_seqs, w.total_q,
+                      int(w.ctx_lens.max()), int(w.q_lens.max()), ws, short, q_lens_host=w.q_lens)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(out), bits(full))
     assert_close(out_f64(out), c.oracle(), wl.I8, w.name, q_lens=w.q_lens)
 
 

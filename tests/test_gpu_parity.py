@@ -142,26 +142,32 @@ def test_attention_prefill_shapes(q_len, dtype):
 
 @pytest.mark.parametrize("plan", ["4", "8", "10", "12", "12:10", "12:7", "8:5", "6:3", "5:3"])
 @pytest.mark.parametrize("head_dim", [128, 64])
-def test_attention_prefill_plans(plan, head_dim, monkeypatch):
+@pytest.mark.parametrize("dtype", [wl.BF16, wl.I8])
+def test_attention_prefill_plans(plan, head_dim, dtype, monkeypatch):
     """Prefill workgroups of W waves over R row blocks (forced through KVATTN_PREFILL_WAVES and
     KVATTN_PREFILL_RBLK; "W" alone means R = W): whole-block waves only, or with pairs of half
     waves that split a row block's keys by block parity and merge at the end.  Ragged sequences
-    leave partial row tiles and waves with no rows."""
+    leave partial row tiles and waves with no rows.  The plan also decides which waves stream
+    the tiles (half waves, the least loaded SIMDs' waves, or all) and in which order the waves
+    take the conversion units of an int8 pool, which runs here with the conversion in LDS
+    (KVATTN_INT8_PREFILL=lds; with the bf16 copy the kernel is the bf16 one)."""
+    if dtype == wl.I8:
+        monkeypatch.setenv("KVATTN_INT8_PREFILL", "lds")
     w, _, r = plan.partition(":")
     monkeypatch.setenv("KVATTN_PREFILL_WAVES", w)
     if r:
         monkeypatch.setenv("KVATTN_PREFILL_RBLK", r)
     else:
         monkeypatch.delenv("KVATTN_PREFILL_RBLK", raising=False)
-    announce(f"prefill plan {plan} D={head_dim}")
-    w = wl.make(f"prefill_plan_{plan.replace(':', 'r')}_{head_dim}", seed=61, dtype=wl.BF16,
+    announce(f"prefill plan {plan} D={head_dim} {dtype}")
+    w = wl.make(f"prefill_plan_{plan.replace(':', 'r')}_{head_dim}_{dtype}", seed=61, dtype=dtype,
                 num_seqs_ctx=[700, 450, 130, 1300], q_lens=[300, 450, 97, 64],
                 num_q_heads=10, num_kv_heads=2, head_dim=head_dim)
     c = DeviceCase(w)
     c.append()
     out = c.forward()
     torch.cuda.synchronize()
-    assert_close(out_f64(out), c.oracle(), wl.BF16, w.name, q_lens=w.q_lens)
+    assert_close(out_f64(out), c.oracle(), dtype, w.name, q_lens=w.q_lens)
 
 
 MIXED_CASES = [

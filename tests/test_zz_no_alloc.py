@@ -61,6 +61,31 @@ def test_noalloc_matches_workspace_call(mirror):
         run_pair(name, ctx, ql, mirror)
 
 
+def test_noalloc_int8_prefill_without_room_for_the_copy():
+    """An int8 prefill whose bf16 copy (about 147 MB here) exceeds the static buffer still runs
+    on the allocation-free entry point: the prefill kernel converts the codes in LDS, with the
+    same bits as kvattn_forward with a workspace that holds the copy; sampled rows against the
+    oracle."""
+    announce("noalloc int8 prefill, copy larger than the static buffer")
+    w = wl.make("noalloc_i8_long", seed=233, dtype=wl.I8, num_seqs_ctx=[36000], q_lens=[64],
+                num_q_heads=40, num_kv_heads=8, head_dim=128)
+    c = DeviceCase(w)
+    c.append()
+    torch.cuda.synchronize()
+    need = kb.kvattn_workspace_size(c.pool.handle, 40, 1, 64, 36000, 64, w.q_lens)
+    assert need > kb.KVATTN_NOALLOC_SCRATCH_BYTES
+    ref_ws = c.forward(mirror=True)
+    out = torch.full_like(c.q, float("nan"))
+    torch.cuda.synchronize()
+    c.pool.forward_noalloc(w.layer, c.q, c.tables, c.ctx, c.ql, 36000, 64, out, scale=w.scale,
+                           q_lens_host=w.q_lens)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits(out), bits(ref_ws))
+    rows = [0, 17, 40, 63]
+    ref = c.oracle()  # one sequence: the oracle over its 64 rows
+    assert_close(out_f64(out)[rows], ref[rows], wl.I8, w.name)
+
+
 def test_noalloc_refuses_oversize_call():
     """A call whose plan needs more than the static scratch is refused before any launch."""
     announce("noalloc oversize refusal")
