@@ -151,7 +151,11 @@ KVPOOL_API int kvpool_copy_blocks(kvpool_t *pool, const int32_t *src, const int3
 
 /* Workspace bytes kvattn_forward needs for these bounds (written to *bytes; may be 0).
  * q_lens_host: the optional host mirror of q_lens that kvattn_forward will get (NULL: sized for
- * any q_lens within the bounds). */
+ * any q_lens within the bounds).  On an int8 pool with prefill-class sequences this counts a
+ * bf16 copy of those sequences' keys and values (2 x ceil(max_ctx_len / 16) x num_kv_heads x 16
+ * x head_dim x 2 bytes per such sequence, plus its block table), which is the faster way; a
+ * smaller workspace without room for the copy is accepted, and the prefill kernel then converts
+ * the codes in LDS, with the same output bits. */
 KVPOOL_API int kvattn_workspace_size(const kvpool_t *pool, int32_t num_q_heads,
                                      int32_t num_seqs, int32_t total_q, int32_t max_ctx_len,
                                      int32_t max_q_len, const int32_t *q_lens_host,
@@ -191,8 +195,10 @@ KVPOOL_API int kvattn_workspace_size(const kvpool_t *pool, int32_t num_q_heads,
  *                    launched for a path no sequence takes; without it they are sized from the
  *                    bounds.  It must equal the device q_lens (checked under KVPOOL_VALIDATE=1).
  *   workspace        device scratch of at least kvattn_workspace_size() bytes (same bounds and
- *                    mirror), 256-byte aligned; contents on entry don't matter.  Calls that may
- *                    run at the same time (other streams) need workspaces of their own.
+ *                    mirror; int8 pools: less without room for the bf16 copy, see there),
+ *                    256-byte aligned; contents on entry don't matter.  Calls that may run at
+ *                    the same time (other streams) need workspaces of their own.  KV_ENOMEM
+ *                    names the bytes required when it is too small.
  * num_q_heads must be a multiple of the pool's num_kv_heads with at most 16 q-heads per KV
  * head. */
 KVPOOL_API int kvattn_forward(kvpool_t *pool, int32_t layer, const void *q, void *out,
@@ -211,8 +217,9 @@ KVPOOL_API int kvattn_forward(kvpool_t *pool, int32_t layer, const void *q, void
  * kvpool_profile enabled its launches are not timed) and makes no host synchronisation unless
  * KVPOOL_VALIDATE=1.  Arguments, outputs and bits: those of kvattn_forward with the same
  * arguments.  Errors: those of kvattn_forward; KV_ENOMEM when the call needs more scratch than
- * the buffer holds (kvattn_workspace_size with the same bounds tells how much; use
- * kvattn_forward then); KV_EDEVICE when the buffer's address could not be taken on the pool's
+ * the buffer holds (kvattn_workspace_size with the same bounds tells how much, less the bf16 copy
+ * for an int8 pool, which this entry point leaves out when it does not fit; use kvattn_forward
+ * then); KV_EDEVICE when the buffer's address could not be taken on the pool's
  * device.  Every call on one GPU shares that GPU's buffer, which keeps the last call's partial
  * results (no kernel needs it cleared on entry): calls ordered on one stream are safe, calls
  * that may overlap on one GPU (several streams or threads) race and must not be made. */
