@@ -18,12 +18,12 @@ namespace {
 constexpr int RT = 256;  // threads per workgroup
 }  // namespace
 
+// The merge of partial row r for q-head hh (one workgroup).
 template <typename E, int D>
-__global__ __launch_bounds__(256) void attn_reduce_kernel(AttnArgs a) {
+__device__ __forceinline__ void reduce_split_row(const AttnArgs& a, int r, int hh) {
   constexpr int DQ = D / 4;    // float4 columns
   constexpr int SG = RT / DQ;  // split groups
   const int tid = threadIdx.x;
-  const int r = blockIdx.x, hh = blockIdx.y;
   int s, i, q_start, L, T;
   if (!find_split_row(a, r, s, i, q_start, L, T)) return;
   int Lv, vs1, vshift;
@@ -100,6 +100,11 @@ __global__ __launch_bounds__(256) void attn_reduce_kernel(AttnArgs a) {
   }
 }
 
+template <typename E, int D>
+__global__ __launch_bounds__(256) void attn_reduce_kernel(AttnArgs a) {
+  reduce_split_row<E, D>(a, blockIdx.x, blockIdx.y);
+}
+
 // ---- prefill key ranges ----------------------------------------------------------------
 // Sequence s of query token grow (q_lens prefix sums, 64 sequences per step), the token's index
 // i in it and the sequence's lengths.  False past the last token.
@@ -138,11 +143,10 @@ __device__ __forceinline__ bool find_token(const AttnArgs& a, int grow, int& s, 
 // slice 256 y + t and loads its KR partials at once; tokens of split-K sequences leave at once.
 constexpr int kMaxKSplit = 8;
 template <typename E, int D, int KR>
-__global__ __launch_bounds__(256) void attn_reduce_prefill_kernel(AttnArgs a) {
+__device__ __forceinline__ void merge_prefill_token(const AttnArgs& a, int grow, int y) {
   constexpr int DQ = D / 4;
-  const int grow = blockIdx.x;
   const int Hq = a.num_q_heads;
-  const int u = blockIdx.y * RT + threadIdx.x;  // (q-head, 4-dim) slice
+  const int u = y * RT + threadIdx.x;  // (q-head, 4-dim) slice
   int s, i, L, T;
   if (!find_token(a, grow, s, i, L, T)) return;
   if (T <= a.split_q_max || i >= T) return;  // not a row the prefill kernel computed
@@ -182,25 +186,53 @@ __global__ __launch_bounds__(256) void attn_reduce_prefill_kernel(AttnArgs a) {
 }
 
 template <typename E, int D, int KR>
-hipError_t launch_reduce_pf(const AttnArgs& a, hipStream_t st) {
+__global__ __launch_bounds__(256) void attn_reduce_prefill_kernel(AttnArgs a) {
+  merge_prefill_token<E, D, KR>(a, blockIdx.x, blockIdx.y);
+}
+
+// Both merges in one launch (a call with split-K rows and prefill key ranges): workgroups
+// [0, part_rows * Hq) merge split-K rows as attn_reduce_kernel, the rest merge prefill tokens as
+// attn_reduce_prefill_kernel (block-uniform choice; the two sets touch disjoint rows of out).
+template <typename E, int D, int KR>
+__global__ __launch_bounds__(256) void attn_reduce_both_kernel(AttnArgs a, int pf_groups) {
+  const int nsplit = a.part_rows * a.num_q_heads;
+  const int b = blockIdx.x;
+  if (b < nsplit) {
+    reduce_split_row<E, D>(a, b / a.num_q_heads, b % a.num_q_heads);
+  } else {
+    const int c = b - nsplit;
+    merge_prefill_token<E, D, KR>(a, c / pf_groups, c % pf_groups);
+  }
+}
+
+template <typename E, int D, int KR>
+hipError_t launch_reduce_pf(const AttnArgs& a, bool both, hipStream_t st) {
   if constexpr (KR > kMaxKSplit) {
     return hipErrorInvalidConfiguration;
   } else if (a.pf_ksplit != KR) {
-    return launch_reduce_pf<E, D, KR + 1>(a, st);
+    return launch_reduce_pf<E, D, KR + 1>(a, both, st);
   } else {
-    const dim3 grid(a.total_q, (a.num_q_heads * (D / 4) + RT - 1) / RT);
-    attn_reduce_prefill_kernel<E, D, KR><<<grid, RT, 0, st>>>(a);
+    const int groups = (a.num_q_heads * (D / 4) + RT - 1) / RT;
+    if (both) {
+      const long long wgs = (long long)a.part_rows * a.num_q_heads + (long long)a.total_q * groups;
+      if (wgs > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+      attn_reduce_both_kernel<E, D, KR><<<(unsigned)wgs, RT, 0, st>>>(a, groups);
+    } else {
+      const dim3 grid(a.total_q, groups);
+      attn_reduce_prefill_kernel<E, D, KR><<<grid, RT, 0, st>>>(a);
+    }
     return hipGetLastError();
   }
 }
 
-hipError_t launch_attn_reduce_prefill(const AttnArgs& a, int elt_bytes, int head_dim,
+hipError_t launch_attn_reduce_prefill(const AttnArgs& a, int elt_bytes, int head_dim, bool both,
                                       hipStream_t st) {
-  if (a.pf_ksplit <= 1 || a.total_q <= 0) return hipSuccess;
+  if (a.pf_ksplit <= 1 || a.total_q <= 0) return both ? launch_attn_reduce(a, elt_bytes, head_dim, st) : hipSuccess;
   if (a.pf_ksplit > kMaxKSplit) return hipErrorInvalidConfiguration;
+  both = both && a.part_rows > 0;
   if (elt_bytes == 2)
-    return head_dim == 128 ? launch_reduce_pf<uint16_t, 128, 2>(a, st) : launch_reduce_pf<uint16_t, 64, 2>(a, st);
-  return head_dim == 128 ? launch_reduce_pf<float, 128, 2>(a, st) : launch_reduce_pf<float, 64, 2>(a, st);
+    return head_dim == 128 ? launch_reduce_pf<uint16_t, 128, 2>(a, both, st) : launch_reduce_pf<uint16_t, 64, 2>(a, both, st);
+  return head_dim == 128 ? launch_reduce_pf<float, 128, 2>(a, both, st) : launch_reduce_pf<float, 64, 2>(a, both, st);
 }
 
 hipError_t launch_attn_reduce(const AttnArgs& a, int elt_bytes, int head_dim, hipStream_t st) {

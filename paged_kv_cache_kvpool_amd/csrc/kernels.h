@@ -115,8 +115,10 @@ hipError_t launch_dequant_prefill(const AttnArgs& a, const DequantOut& o, int he
 // Cross-split merge of the split-K partials: one workgroup per (partial row, q-head).
 hipError_t launch_attn_reduce(const AttnArgs& a, int elt_bytes, int head_dim, hipStream_t st);
 // Merge of the prefill kernel's key-range partials (a.pf_ksplit > 1, at most 8): one workgroup
-// per query token.
-hipError_t launch_attn_reduce_prefill(const AttnArgs& a, int elt_bytes, int head_dim,
+// per (query token, group of 256 (q-head, 4-dim) slices).  both: the cross-split merge of the
+// split-K partials in the same launch (its workgroups first; the merges touch disjoint rows);
+// with no key ranges it is then launch_attn_reduce alone.
+hipError_t launch_attn_reduce_prefill(const AttnArgs& a, int elt_bytes, int head_dim, bool both,
                                       hipStream_t st);
 
 }  // namespace kvp

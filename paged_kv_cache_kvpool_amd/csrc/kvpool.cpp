@@ -845,8 +845,6 @@ int forward_impl(kvpool_t* pool, int32_t layer, const void* q, void* out, int32_
       const bool conv = i8 && !dq;
       if (e == hipSuccess)
         e = timed(K_PREFILL_MFMA, st, [&] { return kvp::launch_attn_prefill_mfma(ap, pool->head_dim, pl.waves, pl.pf_wgs, conv, st); });
-      if (e == hipSuccess && pl.pf_ks > 1)
-        e = timed(K_REDUCE_PF, st, [&] { return kvp::launch_attn_reduce_prefill(ap, eb, pool->head_dim, st); });
     }
   }
   if (e != hipSuccess) return fail(KV_EDEVICE, "attention launch: %s", hipGetErrorString(e));
@@ -856,10 +854,17 @@ int forward_impl(kvpool_t* pool, int32_t layer, const void* q, void* out, int32_
   const int min_split = pl.split > 0 ? pl.split
                                      : kvp::split_floor(pl.split_rows, sp.window > 0, i8);
   const bool need_reduce = pl.split_k && max_ctx_len > min_split;
-  if (need_reduce) {
+  // The prefill key-range merge, with the split-K merge in the same launch when both are needed
+  // (timed as the reduce then).  Both read only metadata and partials, so the original
+  // arguments serve (the prefill partials are in them).
+  const bool pf_merge = pl.prefill && pl.pf_ks > 1;
+  if (pf_merge)
+    e = timed(need_reduce ? K_REDUCE : K_REDUCE_PF, st, [&] {
+      return kvp::launch_attn_reduce_prefill(a, eb, pool->head_dim, need_reduce, st);
+    });
+  else if (need_reduce)
     e = timed(K_REDUCE, st, [&] { return kvp::launch_attn_reduce(a, eb, pool->head_dim, st); });
-    if (e != hipSuccess) return fail(KV_EDEVICE, "reduce launch: %s", hipGetErrorString(e));
-  }
+  if (e != hipSuccess) return fail(KV_EDEVICE, "reduce launch: %s", hipGetErrorString(e));
   return ok();
 }
 
