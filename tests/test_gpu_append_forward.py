@@ -1,9 +1,9 @@
 """GPU parity of kvattn_append_forward (append and attention in one call): the output and the
 whole pool after the call equal, bit for bit, those of kvpool_append followed by kvattn_forward
-on an identical second pool, and the output matches the oracle.  Split-K calls (decode,
-verification, many sequences, int8 pools, new tokens on both sides of a split boundary) append
-inside the split-K kernel; calls with prefill chunks, fp32 pools and the vector path fall back to
-the append kernel.  kvattn_append_forward_sparse is held to the same bar against kvpool_append
+on an identical second pool, and the output matches the oracle.  On bf16 pools the split-K
+kernel appends when every sequence takes it (decode, verification, many sequences, new tokens on
+both sides of a split boundary); calls with prefill chunks, int8 and fp32 pools and the vector
+path use the append kernel.  kvattn_append_forward_sparse is held to the same bar against kvpool_append
 followed by kvattn_forward_sparse (sequences below and above the sparse threshold, new tokens
 past the skipped keys, fixed splits that cut the window) and against the sparse oracle.
 """
@@ -41,6 +41,9 @@ CASES = {
     "mixed": dict(num_seqs_ctx=[3000, 700, 900, 5000], q_lens=[1, 4, 300, 1], num_q_heads=40,
                   num_kv_heads=8),
     "wide_rows": dict(num_seqs_ctx=[5000, 1300], q_lens=[8, 5], num_q_heads=64, num_kv_heads=8),
+    # three prefill sequences (two whole prompts) beside decode and verification, 64-token blocks
+    "mixed_prompts": dict(num_seqs_ctx=[1200, 64, 2049, 700, 33, 5000], q_lens=[1, 64, 129, 4, 33, 1],
+                          num_q_heads=32, num_kv_heads=8, block_size=64),
 }
 
 
@@ -64,7 +67,7 @@ def check(name, dtype, seed=601, mirror=True):
     assert_close(out_f64(got), b.oracle(), dtype, w.name, q_lens=w.q_lens)
 
 
-@pytest.mark.parametrize("name", ["decode", "verify", "many", "wide_rows", "mixed"])
+@pytest.mark.parametrize("name", ["decode", "verify", "many", "wide_rows", "mixed", "mixed_prompts"])
 @pytest.mark.parametrize("dtype", [wl.BF16, wl.I8])
 def test_append_forward(name, dtype):
     check(name, dtype)
@@ -73,6 +76,8 @@ def test_append_forward(name, dtype):
 def test_append_forward_without_mirror():
     check("verify", wl.BF16, mirror=False)
     check("decode", wl.I8, mirror=False)
+    check("mixed", wl.BF16, mirror=False)
+    check("mixed_prompts", wl.BF16, mirror=False)
 
 
 @pytest.mark.parametrize("split", ["256", "512"])
