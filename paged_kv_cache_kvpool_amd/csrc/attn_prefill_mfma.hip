@@ -271,19 +271,48 @@ void attn_prefill_mfma_kernel(AttnArgs a) {
   const int rb = half ? F + ((wave - F) >> 1) : wave;  // the wave's row block in the workgroup
   const int par = half ? ((wave - F) & 1) : 0;          // half waves: parity of their blocks
   const int NKR = a.pf_ksplit;  // key ranges per row tile
-  const int n_base = prefill_wg_total(a, R);  // row tiles of every (sequence, KV head)
-  const int n_wg = n_base * NKR;
-  if ((int)blockIdx.x >= n_wg) return;
-  // logical = key range * n_base + row tile: the row tiles of one key range of a (sequence, KV
-  // head) stay next to each other, on one XCD
-  const int logical = xcd_logical(blockIdx.x, n_wg);
-  // (wave-uniform values from divisions come out of vector registers: readfirstlane keeps them
-  // in scalar ones, as the register budget of three waves per SIMD needs)
-  const int kj = __builtin_amdgcn_readfirstlane(logical / n_base);
-  int s, kvh, rt, rts, q_start;
-  find_prefill_tile(a, logical - kj * n_base, R, s, kvh, rt, rts, q_start);
-  int L, T;
-  seq_lens(a, s, L, T);
+  // The workgroup's key range kj, sequence s, KV head, row tile rt (of rts), first query row and
+  // lengths.  logical = key range * n_base + row tile (n_base: row tiles of every (sequence, KV
+  // head)): the row tiles of one key range of a (sequence, KV head) stay next to each other, on
+  // one XCD.  (Wave-uniform values from divisions come out of vector registers: readfirstlane
+  // keeps them in scalar ones, as the register budget of three waves per SIMD needs.)
+  int kj, s, kvh, rt, rts, q_start, L, T;
+  if (a.num_seqs <= WAVE) {
+    // one read of the metadata (a sequence per lane) serves the count, the lookup and the
+    // lengths: no dependent re-reads before the block ids
+    int Lj = 0, Tj = 0, r = 0, q = 0;
+    if (lane < a.num_seqs) {
+      seq_lens(a, lane, Lj, Tj);
+      r = seq_row_tiles(a, Tj, R);
+      q = max(0, a.q_lens[lane]);
+    }
+    const int wg = r * a.num_kv_heads;
+    const int win = wave_incl_scan(wg);
+    const int qin = wave_incl_scan(q);
+    const int n_base = __builtin_amdgcn_readlane(win, WAVE - 1);
+    const int n_wg = n_base * NKR;
+    if ((int)blockIdx.x >= n_wg) return;
+    const int logical = xcd_logical(blockIdx.x, n_wg);
+    kj = __builtin_amdgcn_readfirstlane(logical / n_base);
+    const int nn = logical - kj * n_base;
+    const int k = __builtin_popcountll(__builtin_amdgcn_ballot_w64(win <= nn));
+    s = k;
+    rts = __builtin_amdgcn_readlane(r, k);
+    const int within = nn - (__builtin_amdgcn_readlane(win, k) - __builtin_amdgcn_readlane(wg, k));
+    kvh = __builtin_amdgcn_readfirstlane(within / rts);
+    rt = within - kvh * rts;
+    q_start = __builtin_amdgcn_readlane(qin, k) - __builtin_amdgcn_readlane(q, k);
+    L = __builtin_amdgcn_readlane(Lj, k);
+    T = __builtin_amdgcn_readlane(Tj, k);
+  } else {
+    const int n_base = prefill_wg_total(a, R);
+    const int n_wg = n_base * NKR;
+    if ((int)blockIdx.x >= n_wg) return;
+    const int logical = xcd_logical(blockIdx.x, n_wg);
+    kj = __builtin_amdgcn_readfirstlane(logical / n_base);
+    find_prefill_tile(a, logical - kj * n_base, R, s, kvh, rt, rts, q_start);
+    seq_lens(a, s, L, T);
+  }
   // wave-uniform: kept in scalar registers so the per-block edge tests stay on the SALU
   L = __builtin_amdgcn_readfirstlane(L);
   T = __builtin_amdgcn_readfirstlane(T);
