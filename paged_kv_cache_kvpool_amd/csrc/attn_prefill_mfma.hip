@@ -8,8 +8,11 @@
 // blocks of a (sequence, KV head) dealt to its workgroups strided.  K/V are
 // walked in tiles of 64 keys = 4 pool tiles, each streamed verbatim from the pool into LDS with
 // global_load_lds (no register staging; the pool's tile layout is the order the matrix cores
-// read) through 3 LDS stages: tiles j+1 and j+2 are in flight while tile j is computed; one
-// vmcnt wait and one barrier per tile.  Each 64-key tile is two 32-key blocks; per wave and
+// read) through a ring of 4 LDS stages: while tile j is computed, tile j+1 is ready, j+2 is
+// landing and j+3 is being issued; one vmcnt wait and one barrier per tile.  (int8 pools whose
+// bf16 copy does not fit the workspace: the codes and per-token scales stream into 3 int8
+// stages, 3 bf16 stages hold the converted tiles; see the staging code.)  Each 64-key tile is
+// two 32-key blocks; per wave and
 // block, on v_mfma_f32_32x32x16_bf16 (the 32x32 shape runs at twice the rate of 16x16x32 on
 // gfx950):
 //   S^T[key][row] = K . Q^T      D/16 MFMAs, K rows read from LDS in a key order (bits 2 and 3
