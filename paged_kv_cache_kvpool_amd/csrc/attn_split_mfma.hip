@@ -258,20 +258,22 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, const Item& it, bool
     return walk_tile_off<D>(a, kvh, tile0, ntile, it.vs1, it.vshift, ids0, ids1, tb, ti);
   };
   // Fused append (kvattn_append_forward): the new tokens whose keys fall in this item's range
-  // are written for its KV head (bit copies: the same bits as the append kernel) just before the loads of the first chunk that holds one, so the walk's
-  // earlier chunks never queue behind the stores.  The wave's later loads of those bytes see
-  // them without a wait: a wave's vector memory operations to one address are performed in
-  // order (the compiler relies on the same for any thread's store-then-load); the empty asm
-  // only keeps the compiler from moving loads above the stores.  Items of other row tiles of
-  // the same split write the same bytes.
-  // (bf16 pools only: in the int8 kernel at two waves per SIMD the code would cost registers
-  // the walk needs, and int8 calls append with the append kernel.)
+  // are written for its KV head (the same bits as the append kernel: bf16 rows copied, int8 rows
+  // quantised by append_row_i8) just before the loads of the first chunk that holds one, so
+  // the walk's earlier chunks never queue behind the stores.  The wave's later loads of those
+  // bytes see them without a wait: a wave's vector memory operations to one address are
+  // performed in order (the compiler relies on the same for any thread's store-then-load); the
+  // empty asm only keeps the compiler from moving loads above the stores.  Items of other row
+  // tiles of the same split write the same bytes.
+  // (int8 pools: 32-row tiles only; in the 16-row int8 kernel, at two waves per SIMD, the code
+  // would cost registers the walk needs, and such calls append with the append kernel.)
   // New tokens are the last T real positions; under sparsity they sit past the layout's gap
   // (the window always holds them), so their virtual positions are contiguous too.
   const int p_new = L - T;
   const int v_new = virt_key(p_new, it.vs1, it.vshift);  // virtual position of the first
   const int v_end = v_new + T;
-  const int c_new = (!I8 && NW == 1 && a.k_new != nullptr && nch > 0 && v_new < we && v_end > wb)
+  const int c_new = ((!I8 || NT == 2) && NW == 1 && a.k_new != nullptr && nch > 0 && v_new < we &&
+                     v_end > wb)
                         ? (max(v_new, wb) - wb) >> 5 : -1;  // wave-uniform
   auto append_new = [&]() {
     const uint16_t* kn = reinterpret_cast<const uint16_t*>(a.k_new);
@@ -291,13 +293,19 @@ __device__ __forceinline__ void run_item(const AttnArgs& a, const Item& it, bool
               *reinterpret_cast<const u32x4*>(kn + src + 8 * lane);
 #pragma unroll
         for (int d = lane; d < D; d += WAVE) vt[d * 16 + tt] = vn[src + d];  // V^T: dim d, slot tt
+      } else {
+        // int8 pools (32-row tiles): quantised and stored as the append kernel does
+        int8_t* kt = const_cast<int8_t*>(reinterpret_cast<const int8_t*>(a.k_layer)) + off;
+        int8_t* vt = const_cast<int8_t*>(reinterpret_cast<const int8_t*>(a.v_layer)) + off;
+        append_row_i8<D / 64>(kt, vt, const_cast<float*>(a.k_scale_layer) + off / D,
+                              const_cast<float*>(a.v_scale_layer) + off / D, kn + src, vn + src, tt);
       }
     }
     asm volatile("" ::: "memory");
   };
 
   auto load_chunk = [&](Chunk<D, I8>& c, int ci) {
-    if constexpr (!I8) {
+    if constexpr (!I8 || NT == 2) {
       if (ci == c_new) append_new();  // wave-uniform; once, before the chunk's own loads
     }
     const size_t o0 = tile_off(2 * ci), o1 = tile_off(2 * ci + 1);

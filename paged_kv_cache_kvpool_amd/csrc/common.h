@@ -355,8 +355,8 @@ __device__ __forceinline__ size_t block_tile_offset(int blk, int sub, int h, int
 //   V: [(t % 16) / 4][d % 16][d / 16][t % 4]         (the 4 keys of a dim group side by side)
 // One wave per (token, KV head) row: lane l holds dims E*l .. E*l + E - 1 (E = head_dim / 64),
 // the absolute max comes from a wave reduction, and codes are stored byte by byte (K) / to
-// their scattered V slots.  The append kernel and the split-K kernel's fused append both store
-// rows through append_row_i8, so their bits are the same.
+// their scattered V slots.  The append kernel and the 32-row split-K kernel's fused append both
+// store rows through append_row_i8, so their bits are the same.
 __device__ __forceinline__ float wave_max_f(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));

@@ -775,11 +775,16 @@ int forward_impl(kvpool_t* pool, int32_t layer, const void* q, void* out, int32_
   hipError_t e = hipSuccess;
   const bool vec = pool->dtype == KV_F32 || (pool->dtype == KV_BF16 && sp.window == 0 && !pl.prefill &&
                                               max_q_len == 1 && env_flag("KVATTN_DECODE_VEC"));
+  // Split-K sequences of at most 16 rows per KV head beside longer ones (host q_lens): two
+  // launches, 16- and 32-row tiles (see below).
+  const bool two_launches = pl.split_rows > 16 && pl.split_rows_min > 0 && pl.split_rows_min <= 16;
   if (k_new) {
-    // Append inside the split-K kernel when every sequence takes it on persistent waves (bf16
-    // pools); otherwise the append kernel runs first, as kvpool_append would.
-    const bool fuse = pool->dtype == KV_BF16 && !vec && !pl.prefill && pl.split_k &&
-                      (pl.split == 0 || pl.split <= 2048);
+    // Append inside the split-K kernel when every sequence takes it on persistent waves: bf16
+    // pools, and int8 pools whose sequences all run in 32-row tiles (one wave per SIMD, with
+    // registers to spare for the quantisation; at two waves per SIMD the 16-row int8 kernel has
+    // none).  Otherwise the append kernel runs first, as kvpool_append would.
+    const bool fuse = (pool->dtype == KV_BF16 || (i8 && pl.split_rows > 16 && !two_launches)) &&
+                      !vec && !pl.prefill && pl.split_k && (pl.split == 0 || pl.split <= 2048);
     if (fuse) {
       a.k_new = k_new;
       a.v_new = v_new;
@@ -814,9 +819,8 @@ int forward_impl(kvpool_t* pool, int32_t layer, const void* q, void* out, int32_
       // longer ones (verification), the short ones take the 16-row kernel, which runs twice the
       // waves, and the others the 32-row kernel, one launch after the other.  (One 32-row launch
       // for all would leave most of a decode item's tile empty.)  Timed as one stage.
-      const bool two = pl.split_rows > 16 && pl.split_rows_min > 0 && pl.split_rows_min <= 16;
       e = timed(K_SPLIT_MFMA, st, [&] {
-        if (!two) return split_launch(pl.split_rows, 0, INT32_MAX);
+        if (!two_launches) return split_launch(pl.split_rows, 0, INT32_MAX);
         hipError_t r = split_launch(16, 0, 16);
         return r == hipSuccess ? split_launch(pl.split_rows, 16, INT32_MAX) : r;
       });

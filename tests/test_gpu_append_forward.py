@@ -2,8 +2,9 @@
 whole pool after the call equal, bit for bit, those of kvpool_append followed by kvattn_forward
 on an identical second pool, and the output matches the oracle.  On bf16 pools the split-K
 kernel appends when every sequence takes it (decode, verification, many sequences, new tokens on
-both sides of a split boundary); calls with prefill chunks, int8 and fp32 pools and the vector
-path use the append kernel.  kvattn_append_forward_sparse is held to the same bar against kvpool_append
+both sides of a split boundary), on int8 pools when every sequence also runs in 32-row tiles
+(verification); calls with prefill chunks, 16-row int8 calls, fp32 pools and the vector path use
+the append kernel.  kvattn_append_forward_sparse is held to the same bar against kvpool_append
 followed by kvattn_forward_sparse (sequences below and above the sparse threshold, new tokens
 past the skipped keys, fixed splits that cut the window) and against the sparse oracle.
 """
@@ -80,13 +81,14 @@ def test_append_forward_without_mirror():
     check("mixed_prompts", wl.BF16, mirror=False)
 
 
+@pytest.mark.parametrize("dtype", [wl.BF16, wl.I8])
 @pytest.mark.parametrize("split", ["256", "512"])
-def test_new_tokens_across_a_split_boundary(split, monkeypatch):
+def test_new_tokens_across_a_split_boundary(split, dtype, monkeypatch):
     """Fixed splits put a verification's new tokens on both sides of a split boundary: each
     split's item writes its own."""
     monkeypatch.setenv("KVATTN_SPLIT_TOKENS", split)
-    announce(f"append_forward across a split boundary ({split})")
-    w = wl.make("af_boundary", seed=602, dtype=wl.BF16, num_seqs_ctx=[2 * int(split) + 2, 1026],
+    announce(f"append_forward across a split boundary ({split}, {dtype})")
+    w = wl.make("af_boundary", seed=602, dtype=dtype, num_seqs_ctx=[2 * int(split) + 2, 1026],
                 q_lens=[4, 4], num_q_heads=40, num_kv_heads=8, head_dim=128)
     a, b = DeviceCase(w), DeviceCase(w)
     a.append()
@@ -96,6 +98,39 @@ def test_new_tokens_across_a_split_boundary(split, monkeypatch):
     assert np.array_equal(raw(got), raw(ref))
     for x, y in zip(a.host_pools(), b.host_pools()):
         assert np.array_equal(np.asarray(x).view(np.uint8), np.asarray(y).view(np.uint8))
+
+
+@pytest.mark.parametrize("dtype,mirror", [(wl.I8, True), (wl.I8, False), (wl.BF16, True)])
+def test_verification_appends_in_the_split_kernel(dtype, mirror):
+    """Verification calls (1 + 3 drafts, 5 q-heads per KV head: 32-row tiles) append inside the
+    split-K kernel on bf16 and int8 pools alike: no append launch, and the bits of append +
+    forward.  A 16-row int8 call (decode) keeps the append kernel."""
+    from paged_kv_cache_kvpool_amd import binding as kb
+    announce(f"verification appends in the split kernel {dtype} mirror={mirror}")
+    w = wl.make(f"af_vfuse_{dtype}", seed=604, dtype=dtype, num_seqs_ctx=[32772, 2050, 700],
+                q_lens=[4, 4, 4], num_q_heads=40, num_kv_heads=8, head_dim=128)
+    a, b = DeviceCase(w), DeviceCase(w)
+    a.append()
+    ref = a.forward(mirror=mirror)
+    torch.cuda.synchronize()
+    kb.kvpool_profile(True)
+    got = b.append_forward(mirror=mirror)
+    torch.cuda.synchronize()
+    kb.kvpool_profile(False)
+    launched = kb.kernel_times()
+    assert "kv_append" not in launched, f"kernels {sorted(launched)}"
+    assert np.array_equal(raw(got), raw(ref))
+    for x, y in zip(a.host_pools(), b.host_pools()):
+        assert np.array_equal(np.asarray(x).view(np.uint8), np.asarray(y).view(np.uint8))
+    # a decode call on an int8 pool (16-row tiles) appends with the append kernel
+    wd = wl.make("af_vfuse_dec", seed=605, dtype=wl.I8, num_seqs_ctx=[3000, 700], q_lens=[1, 1],
+                 num_q_heads=32, num_kv_heads=8, head_dim=128)
+    d = DeviceCase(wd)
+    kb.kvpool_profile(True)
+    d.append_forward(mirror=mirror)
+    torch.cuda.synchronize()
+    kb.kvpool_profile(False)
+    assert "kv_append" in kb.kernel_times()
 
 
 def test_fp32_pool_falls_back():
