@@ -239,8 +239,10 @@ KVPOOL_API int kvattn_forward_noalloc(kvpool_t *pool, int32_t layer, const void 
  * of the two calls.  On a bf16 pool, when every sequence takes the split-K kernel (decode and
  * verification rows only, judged from q_lens_host when given, else from max_q_len), that
  * kernel writes each new token itself, in the work item whose keys hold it, before reading it:
- * one launch fewer per step.  Otherwise (int8 and fp32 pools, prefill chunks) the append
- * kernel runs first.  Arguments: those of both calls, with
+ * one launch fewer per step.  On an int8 pool the same holds when every sequence also has more
+ * than 16 query rows per KV head (verification: 32-row tiles), the kernel quantising the new
+ * rows as the append kernel does.  Otherwise (other int8 calls, fp32 pools, prefill chunks)
+ * the append kernel runs first.  Arguments: those of both calls, with
  * max_q_len bounding q_lens for both; each call's argument errors and (KVPOOL_VALIDATE)
  * metadata checks apply, and a nonzero return enqueues no work.  The workspace is
  * kvattn_workspace_size's. */
@@ -279,7 +281,8 @@ KVPOOL_API int kvattn_forward_sparse(kvpool_t *pool, int32_t layer, const void *
  * same serving loop as kvattn_append_forward).  The result, pool and output, is bit for bit that
  * of the two calls.  On a bf16 pool the split-K kernel writes each new token itself, in the work
  * item whose (sparse) key range holds it: new tokens are the last q_len positions, which every
- * row's window holds, so they always lie past the keys that sparsity skips.  On an int8 pool the
+ * row's window holds, so they always lie past the keys that sparsity skips.  On an int8 pool
+ * likewise when every sequence runs in 32-row tiles (more than 16 rows per KV head), else the
  * append kernel runs first.  Arguments and errors: those of both calls (the sparse parameter
  * checks come first); a nonzero return enqueues no work. */
 KVPOOL_API int kvattn_append_forward_sparse(kvpool_t *pool, int32_t layer, const void *k_new,
