@@ -7,7 +7,8 @@
 // only) in the same launch.
 //
 // Per 16-token tile the wave reads K and V with contiguous 1 KiB wave loads (16 bytes per
-// lane).  With the pool's tile layout, lane l of K load j holds dim chunk 4*j + l/16 of token
+// lane), their block ids read 64 tiles at a time; single-row waves stream the tiles through a
+// ring of register buffers (the loads of later tiles in flight while one is computed).  With the pool's tile layout, lane l of K load j holds dim chunk 4*j + l/16 of token
 // l%16, so each lane forms partial dot products over its chunks and two cross-row swaps
 // (v_permlane32_swap / v_permlane16_swap) finish them: every lane then holds the full score of
 // token l%16.  The tile max uses DPP within rows of 16 lanes.  For V (stored dims-major),
@@ -108,15 +109,47 @@ __global__ __launch_bounds__(64) void attn_vec_kernel(AttnArgs a) {
   const float c = a.scale_log2;
   const int tok0 = X * (lane % LPD);  // first token of this lane's V run
 
-  for (int t0 = kb; t0 < ke; t0 += TILE) {
-    const size_t toff =
-        tile_offset(tbl, t0, kvh, a.block_size, a.num_blocks, a.num_kv_heads, D);
-    u32x4 kw[NL], vw[NL];
+  // The split's tiles go through a ring of RN register buffers: the loads of tile i + RN - 1 are
+  // issued before tile i is computed, so RN - 1 tiles are in flight behind the one computed.
+  // Block ids come 64 tiles at a time (lane l: tile tb + l), read with readlane; tiles past the
+  // split's last re-read it (never computed).
+  // Single-row waves (no grouped heads) only: with more rows the registers q and o hold leave
+  // room for no ring without cutting the waves a SIMD runs at once, which large batches need
+  // more (bf16 decode of 4 rows per wave measured 130 -> 141 us with two buffers).  RN = 1: no
+  // lookahead (the block ids still come ahead, so a tile waits for one memory latency).
+  constexpr int RN = ROWS == 1 ? (NL <= 4 ? 4 : 2) : 1;
+  const int ntl = (ke - kb + TILE - 1) / TILE;
+  const int bshift = a.block_shift;
+  const int last_bi = (ke - 1) >> bshift;
+  int tb = 0;
+  auto load_ids = [&](int base) -> int {
+    return tbl[min((kb + TILE * (base + lane)) >> bshift, last_bi)];
+  };
+  int ids = load_ids(0);
+  struct VTile {
+    u32x4 k[NL], v[NL];
+  };
+  auto load_tile = [&](VTile& b, int ti) {
+    ti = min(ti, ntl - 1);
+    if (ti - tb >= WAVE) {  // wave-uniform: the next 64 tiles' block ids
+      tb = ti & ~(WAVE - 1);
+      ids = load_ids(tb);
+    }
+    const int blk = __builtin_amdgcn_readlane(ids, ti - tb);
+    const int t0 = kb + TILE * ti;
+    const size_t toff = block_tile_offset(blk, (t0 & (a.block_size - 1)) / TILE, kvh, bshift,
+                                          a.num_blocks, a.num_kv_heads, D);
 #pragma unroll
     for (int j = 0; j < NL; ++j) {
-      kw[j] = *reinterpret_cast<const u32x4*>(kl + toff + (size_t)(1024 * j + 16 * lane) / sizeof(E));
-      vw[j] = *reinterpret_cast<const u32x4*>(vl + toff + (size_t)(1024 * j + 16 * lane) / sizeof(E));
+      b.k[j] = *reinterpret_cast<const u32x4*>(kl + toff + (size_t)(1024 * j + 16 * lane) / sizeof(E));
+      b.v[j] = *reinterpret_cast<const u32x4*>(vl + toff + (size_t)(1024 * j + 16 * lane) / sizeof(E));
     }
+  };
+
+  auto compute = [&](VTile& b, int ti) {
+    const int t0 = kb + TILE * ti;
+    u32x4 (&kw)[NL] = b.k;
+    u32x4 (&vw)[NL] = b.v;
     const bool tail = t0 + TILE > ke;
     if (tail) {
       // V slots at or past ke may hold NaN: zero them (their p is 0).
@@ -160,12 +193,14 @@ __global__ __launch_bounds__(64) void attn_vec_kernel(AttnArgs a) {
       l_run[r] = l_run[r] * alpha[r] + pr;
       m_run[r] = m_new;
     }
-    __syncthreads();
+    // P goes to the lanes that hold each V run through LDS.  The workgroup is one wave, whose
+    // LDS operations are performed in order, so no barrier is needed between the last tile's
+    // reads, these writes and the reads below (a barrier would also wait for the ring's loads).
     if (g == 0) {
 #pragma unroll
       for (int r = 0; r < ROWS; ++r) sp_lds[r][n] = p[r];
     }
-    __syncthreads();
+    __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int r = 0; r < ROWS; ++r) {
       float pv[X];
@@ -185,7 +220,26 @@ __global__ __launch_bounds__(64) void attn_vec_kernel(AttnArgs a) {
         o[r][j] = acc;
       }
     }
+    __builtin_amdgcn_wave_barrier();
+  };
+
+  VTile rb[RN];
+#pragma unroll
+  for (int j = 0; j + 1 < RN; ++j) load_tile(rb[j], j);
+  for (int ti = 0; ti < ntl; ti += RN) {
+    bool done = false;
+#pragma unroll
+    for (int j = 0; j < RN; ++j) {
+      load_tile(rb[(j + RN - 1) % RN], ti + j + RN - 1);
+      compute(rb[j], ti + j);
+      if (ti + j + 1 >= ntl) {
+        done = true;
+        break;
+      }
+    }
+    if (done) break;
   }
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the ring's re-reads past the end
 
   // Each lane's l_run counts its own token (identical across the 4 row groups).
 #pragma unroll
