@@ -1,21 +1,24 @@
 // Split-K paged attention on the vector ALUs (fp32 and bf16 K/V).
 //
 // The fp32 path of every call, and an alternative bf16 decode path.  Same work split as the
-// matrix-core kernel: one wave per (row tile, split, KV head, sequence), partials merged by
-// the reduce kernel in fixed split order (no float atomics: sparkinfer server README,
+// matrix-core kernel: one workgroup per (row tile, split, KV head, sequence), partials merged
+// by the reduce kernel in fixed split order (no float atomics: sparkinfer server README,
 // "Determinism").  Sequences with more than split_q_max query tokens make one pass (split 0
-// only) in the same launch.
+// only) in the same launch.  A workgroup is one wave, except for single-row tiles (one q-head
+// per KV head, decode), where 4 waves take contiguous quarters of the split's tiles and merge
+// through LDS in wave order, so that a lone short decode is not one wave's walk.
 //
-// Per 16-token tile the wave reads K and V with contiguous 1 KiB wave loads (16 bytes per
-// lane), their block ids read 64 tiles at a time; single-row waves stream the tiles through a
-// ring of register buffers (the loads of later tiles in flight while one is computed).  With the pool's tile layout, lane l of K load j holds dim chunk 4*j + l/16 of token
-// l%16, so each lane forms partial dot products over its chunks and two cross-row swaps
-// (v_permlane32_swap / v_permlane16_swap) finish them: every lane then holds the full score of
-// token l%16.  The tile max uses DPP within rows of 16 lanes.  For V (stored dims-major),
-// lane l of load j holds X consecutive tokens of one dim, so the probabilities are exchanged
-// through LDS once per tile and each lane accumulates its dims; the few lanes that share a dim
-// are summed with DPP at the end of the split.  bf16 products use v_dot2_f32_bf16 on packed
-// pairs, with P rounded to bf16 (the same rounded P feeds numerator and denominator).
+// Per 16-token tile a wave reads K and V with contiguous 1 KiB wave loads (16 bytes per lane),
+// the tiles' block ids 64 at a time; single-row waves stream the tiles through a ring of
+// register buffers (the loads of later tiles in flight while one is computed).  With the pool's
+// tile layout, lane l of K load j holds dim chunk 4*j + l/16 of token l%16, so each lane forms
+// partial dot products over its chunks and two cross-row swaps (v_permlane32_swap /
+// v_permlane16_swap) finish them: every lane then holds the full score of token l%16.  The tile
+// max uses DPP within rows of 16 lanes.  For V (stored dims-major), lane l of load j holds X
+// consecutive tokens of one dim, so the probabilities are exchanged through LDS once per tile
+// and each lane accumulates its dims; the few lanes that share a dim are summed with DPP at the
+// end of the split.  bf16 products use v_dot2_f32_bf16 on packed pairs, with P rounded to bf16
+// (the same rounded P feeds numerator and denominator).
 #include "common.h"
 #include "kernels.h"
 
@@ -42,14 +45,22 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
 
 }  // namespace
 
+// Waves per workgroup: single-row waves (one query row per (sequence, KV head): no grouped
+// heads) split their split's tiles over 4 waves, merged through LDS in wave order, so that a
+// lone short decode is not one wave's walk; other instances run one wave per workgroup.
+template <int ROWS>
+constexpr int vec_waves() { return ROWS == 1 ? 4 : 1; }
+
 template <typename E, int D, int ROWS>
-__global__ __launch_bounds__(64) void attn_vec_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64 * vec_waves<ROWS>()) void attn_vec_kernel(AttnArgs a) {
   constexpr bool BF = sizeof(E) == 2;
   constexpr int X = VecTraits<E>::X;       // elements per 16 bytes
   constexpr int NL = TILE * D * (int)sizeof(E) / 1024;  // 16-byte loads per lane per tile
   constexpr int LPD = (int)sizeof(E);      // lanes sharing one V^T row (one dim)
   constexpr int QW = BF ? X / 2 : X;       // q words per lane per load slot
-  const int lane = threadIdx.x;
+  constexpr int NWV = vec_waves<ROWS>();
+  const int lane = threadIdx.x & (WAVE - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, g = lane >> 4;
   const int s = blockIdx.z, kvh = blockIdx.y;
   const int rt = blockIdx.x % a.row_tiles, sp = blockIdx.x / a.row_tiles;
@@ -102,7 +113,7 @@ __global__ __launch_bounds__(64) void attn_vec_kernel(AttnArgs a) {
     for (int j = 0; j < NL; ++j) o[r][j] = 0.f;
   }
 
-  __shared__ float sp_lds[ROWS][TILE];
+  __shared__ float sp_lds[NWV][ROWS][TILE];
   const int32_t* tbl = a.block_tables + (size_t)s * a.max_blocks_per_seq;
   const E* kl = reinterpret_cast<const E*>(a.k_layer);
   const E* vl = reinterpret_cast<const E*>(a.v_layer);
@@ -118,12 +129,16 @@ __global__ __launch_bounds__(64) void attn_vec_kernel(AttnArgs a) {
   // more (bf16 decode of 4 rows per wave measured 130 -> 141 us with two buffers).  RN = 1: no
   // lookahead (the block ids still come ahead, so a tile waits for one memory latency).
   constexpr int RN = ROWS == 1 ? (NL <= 4 ? 4 : 2) : 1;
-  const int ntl = (ke - kb + TILE - 1) / TILE;
+  // this wave's tiles of the split: [wt0, wt1) (a contiguous share; possibly none)
+  const int ntl_all = (ke - kb + TILE - 1) / TILE;
+  const int wq = (ntl_all + NWV - 1) / NWV;
+  const int wt0 = min(wave * wq, ntl_all);
+  const int ntl = min(ntl_all - wt0, wq);  // tiles of this wave, counted from wt0
   const int bshift = a.block_shift;
   const int last_bi = (ke - 1) >> bshift;
   int tb = 0;
   auto load_ids = [&](int base) -> int {
-    return tbl[min((kb + TILE * (base + lane)) >> bshift, last_bi)];
+    return tbl[min((kb + TILE * (wt0 + base + lane)) >> bshift, last_bi)];
   };
   int ids = load_ids(0);
   struct VTile {
@@ -136,7 +151,7 @@ __global__ __launch_bounds__(64) void attn_vec_kernel(AttnArgs a) {
       ids = load_ids(tb);
     }
     const int blk = __builtin_amdgcn_readlane(ids, ti - tb);
-    const int t0 = kb + TILE * ti;
+    const int t0 = kb + TILE * (wt0 + ti);
     const size_t toff = block_tile_offset(blk, (t0 & (a.block_size - 1)) / TILE, kvh, bshift,
                                           a.num_blocks, a.num_kv_heads, D);
 #pragma unroll
@@ -147,7 +162,7 @@ __global__ __launch_bounds__(64) void attn_vec_kernel(AttnArgs a) {
   };
 
   auto compute = [&](VTile& b, int ti) {
-    const int t0 = kb + TILE * ti;
+    const int t0 = kb + TILE * (wt0 + ti);
     u32x4 (&kw)[NL] = b.k;
     u32x4 (&vw)[NL] = b.v;
     const bool tail = t0 + TILE > ke;
@@ -193,19 +208,19 @@ __global__ __launch_bounds__(64) void attn_vec_kernel(AttnArgs a) {
       l_run[r] = l_run[r] * alpha[r] + pr;
       m_run[r] = m_new;
     }
-    // P goes to the lanes that hold each V run through LDS.  The workgroup is one wave, whose
-    // LDS operations are performed in order, so no barrier is needed between the last tile's
-    // reads, these writes and the reads below (a barrier would also wait for the ring's loads).
+    // P goes to the lanes that hold each V run through the wave's own LDS slice.  A wave's LDS
+    // operations are performed in order, so no barrier is needed between the last tile's reads,
+    // these writes and the reads below (a barrier would also wait for the ring's loads).
     if (g == 0) {
 #pragma unroll
-      for (int r = 0; r < ROWS; ++r) sp_lds[r][n] = p[r];
+      for (int r = 0; r < ROWS; ++r) sp_lds[wave][r][n] = p[r];
     }
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int r = 0; r < ROWS; ++r) {
       float pv[X];
 #pragma unroll
-      for (int e = 0; e < X; ++e) pv[e] = sp_lds[r][tok0 + e];
+      for (int e = 0; e < X; ++e) pv[e] = sp_lds[wave][r][tok0 + e];
 #pragma unroll
       for (int j = 0; j < NL; ++j) {
         float acc = o[r][j] * alpha[r];
@@ -224,8 +239,10 @@ __global__ __launch_bounds__(64) void attn_vec_kernel(AttnArgs a) {
   };
 
   VTile rb[RN];
+  if (ntl > 0) {  // wave-uniform
 #pragma unroll
-  for (int j = 0; j + 1 < RN; ++j) load_tile(rb[j], j);
+    for (int j = 0; j + 1 < RN; ++j) load_tile(rb[j], j);
+  }
   for (int ti = 0; ti < ntl; ti += RN) {
     bool done = false;
 #pragma unroll
@@ -242,9 +259,10 @@ __global__ __launch_bounds__(64) void attn_vec_kernel(AttnArgs a) {
   __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the ring's re-reads past the end
 
   // Each lane's l_run counts its own token (identical across the 4 row groups).
+  float lts[ROWS];
 #pragma unroll
   for (int r = 0; r < ROWS; ++r) {
-    const float lt = row_sum(l_run[r]);
+    lts[r] = row_sum(l_run[r]);
 #pragma unroll
     for (int j = 0; j < NL; ++j) {
       float v = o[r][j];
@@ -252,6 +270,43 @@ __global__ __launch_bounds__(64) void attn_vec_kernel(AttnArgs a) {
       if constexpr (LPD == 4) v += dpp<DPP_XOR2>(v);
       o[r][j] = v;
     }
+  }
+  if constexpr (NWV > 1) {
+    // The waves' (max, sum, O) merged in wave order by wave 0 (a wave without keys has max
+    // -inf and weighs 0), which then stores as a single wave would.
+    static_assert(ROWS == 1, "multi-wave workgroups hold one row");
+    __shared__ float s_m[NWV], s_l[NWV];
+    __shared__ float s_o[NWV][NL][WAVE];
+    if (lane == 0) {
+      s_m[wave] = m_run[0];
+      s_l[wave] = lts[0];
+    }
+#pragma unroll
+    for (int j = 0; j < NL; ++j) s_o[wave][j][lane] = o[0][j];
+    __syncthreads();
+    if (wave != 0) return;
+    float M = s_m[0];
+#pragma unroll
+    for (int w = 1; w < NWV; ++w) M = fmaxf(M, s_m[w]);
+    float lsum = 0.f, ov[NL];
+#pragma unroll
+    for (int j = 0; j < NL; ++j) ov[j] = 0.f;
+#pragma unroll
+    for (int w = 0; w < NWV; ++w) {
+      const float mw = s_m[w];
+      const float wt = mw == -INFINITY ? 0.f : fast_exp2((mw - M) * c);
+      lsum = __builtin_fmaf(wt, s_l[w], lsum);
+#pragma unroll
+      for (int j = 0; j < NL; ++j) ov[j] = __builtin_fmaf(wt, s_o[w][j][lane], ov[j]);
+    }
+    m_run[0] = M;
+    lts[0] = lsum;
+#pragma unroll
+    for (int j = 0; j < NL; ++j) o[0][j] = ov[j];
+  }
+#pragma unroll
+  for (int r = 0; r < ROWS; ++r) {
+    const float lt = lts[r];
     if (prow[r] < kb) continue;
     // Rows whose keys all lie in split 0 are finished here (the reduce skips them).
     if (prow[r] >= split) {
@@ -283,7 +338,7 @@ __global__ __launch_bounds__(64) void attn_vec_kernel(AttnArgs a) {
 
 template <typename E, int D>
 static void launch_rows(const AttnArgs& a, int rows, dim3 grid, hipStream_t st) {
-  if (rows <= 1) attn_vec_kernel<E, D, 1><<<grid, 64, 0, st>>>(a);
+  if (rows <= 1) attn_vec_kernel<E, D, 1><<<grid, 64 * vec_waves<1>(), 0, st>>>(a);
   else if (rows <= 2) attn_vec_kernel<E, D, 2><<<grid, 64, 0, st>>>(a);
   else if (rows <= 4) attn_vec_kernel<E, D, 4><<<grid, 64, 0, st>>>(a);
   else if (rows <= 5) attn_vec_kernel<E, D, 5><<<grid, 64, 0, st>>>(a);

@@ -213,6 +213,25 @@ def test_decode_vec_kernel_bf16(monkeypatch):
     assert_close(out_f64(out), c.oracle(), wl.BF16, w.name, q_lens=w.q_lens)
 
 
+@pytest.mark.parametrize("dtype,head_dim", [(wl.F32, 64), (wl.F32, 128), (wl.BF16, 128), (wl.BF16, 64)])
+def test_decode_vec_single_row_waves(dtype, head_dim, monkeypatch):
+    """One q-head per KV head (single-row waves: four waves share each split and merge in
+    LDS): contexts from 1 key (three waves without a tile) through 17 and 300 keys to several
+    splits (their partials merged by the reduce); bf16 through KVATTN_DECODE_VEC=1."""
+    if dtype == wl.BF16:
+        monkeypatch.setenv("KVATTN_DECODE_VEC", "1")
+    announce(f"single-row vec decode {dtype} d={head_dim}")
+    w = wl.make(f"vec_rows1_{dtype}_{head_dim}", seed=52, dtype=dtype,
+                num_seqs_ctx=[1, 17, 300, 513, 1030, 5000, 64, 2049], q_lens=[1] * 8,
+                num_q_heads=8, num_kv_heads=8, head_dim=head_dim)
+    c = DeviceCase(w)
+    c.append()
+    for mirror in (False, True):
+        out = c.forward(mirror=mirror)
+        torch.cuda.synchronize()
+        assert_close(out_f64(out), c.oracle(), dtype, w.name, q_lens=w.q_lens)
+
+
 # ---------------------------------------------------------------------------------------------
 # The five measured workloads at full size
 # ---------------------------------------------------------------------------------------------
