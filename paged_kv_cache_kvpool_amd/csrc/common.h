@@ -358,9 +358,8 @@ __device__ __forceinline__ size_t block_tile_offset(int blk, int sub, int h, int
 // their scattered V slots.  The append kernel and the 32-row split-K kernel's fused append both
 // store rows through append_row_i8, so their bits are the same.
 __device__ __forceinline__ float wave_max_f(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
+  // across the 4 rows of 16 lanes (permlane swaps), then within each row (DPP): no LDS trips
+  return row_max(xrow_max(v));
 }
 
 template <int E>
