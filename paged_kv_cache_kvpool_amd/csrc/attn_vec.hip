@@ -129,7 +129,7 @@ __global__ __launch_bounds__(64 * vec_waves<ROWS>()) void attn_vec_kernel(AttnAr
   // more (bf16 decode of 4 rows per wave measured 130 -> 141 us with two buffers).  RN = 1: no
   // lookahead (the block ids still come ahead, so a tile waits for one memory latency).
   constexpr int RN = ROWS == 1 ? (NL <= 4 ? 4 : 2) : 1;
-  // this wave's tiles of the split: [wt0, wt1) (a contiguous share; possibly none)
+  // this wave's tiles of the split: [wt0, wt0 + ntl) (a contiguous share; possibly none)
   const int ntl_all = (ke - kb + TILE - 1) / TILE;
   const int wq = (ntl_all + NWV - 1) / NWV;
   const int wt0 = min(wave * wq, ntl_all);
