@@ -845,59 +845,85 @@ long long prefill_wg_count(const int* rows, int n, int num_kv_heads, int rblk) {
   return wgs;
 }
 
+namespace {
+
+// Per 64-key tile cost of a workgroup of `w` waves over `r` row blocks, relative: waves w, w+4,
+// w+8 share a SIMD, a whole-block wave counts 1 and a half wave 1/2, and the tile time is a
+// fixed part plus the load of the busiest SIMD (measured on MI355X: about 1.0 + 0.45 x load
+// microseconds per 64-key tile); a busiest SIMD with a single wave cannot hide its own
+// latencies (measured 25-30% slower).
+double prefill_tile_cost(int w, int r) {
+  const int f = 2 * r - w;
+  double load[4] = {0, 0, 0, 0};
+  int nw[4] = {0, 0, 0, 0};
+  for (int i = 0; i < w; ++i) {
+    load[i & 3] += i < f ? 1.0 : 0.5;
+    ++nw[i & 3];
+  }
+  int bs = 0;
+  for (int k = 1; k < 4; ++k)
+    if (load[k] > load[bs] || (load[k] == load[bs] && nw[k] < nw[bs])) bs = k;
+  return (1.0 + 0.45 * load[bs]) * (nw[bs] <= 1 ? 1.3 : 1.0);
+}
+
+// Makespan of wgs workgroups cut into k key ranges each, over n 64-key tiles: one workgroup per
+// CU at a time (LDS-bound), rounds(k) = ceil(k wgs / CUs) rounds of workgroups over n/k tiles
+// plus their start and drain (about 8.5 tile times, measured), and the merge launch when k > 1
+// (about 7).
+double prefill_makespan(long long wgs, int k, double n, int num_cus, double tile) {
+  const long long rounds = (wgs * k + num_cus - 1) / num_cus;
+  return (double)rounds * (n / k + 8.5) * tile + (k > 1 ? 7.0 : 0.0);
+}
+
+int max_ksplit(int max_ctx) {
+  const int n = (max_ctx + 63) / 64;
+  return std::max(1, std::min(8, n / 4));  // ranges of at least 4 tiles
+}
+
+}  // namespace
+
 void prefill_plan(const int* rows, int n, int num_kv_heads, int num_cus, bool whole_only,
-                  int* waves, int* rblk) {
-  // Makespan model: one workgroup per CU at a time (LDS-bound), every workgroup streams all of
-  // its sequence's keys.  Per key tile a workgroup costs a fixed part (barrier, streaming) plus
-  // the load of its busiest SIMD: waves w, w+4, w+8 share a SIMD, a whole-block wave counts 1
-  // and a half wave 1/2 (measured on MI355X: about 1.0 + 0.45 x load microseconds per 64-key
-  // tile).  A busiest SIMD with a single wave cannot hide its own latencies (measured 25-30%
-  // slower).  Pick the (W, R), W/2 <= R <= W and at most 6 pairs, minimising rounds x tile cost,
-  // then the fewest workgroups, then the fewest waves.  whole_only: R = W (every row block one
-  // wave), the plans whose arithmetic per row block does not depend on (W, R).
-  int bw = 8, br = 8;
+                  int max_ctx, int* waves, int* rblk, int* ksplit) {
+  // The (W, R, k) of least makespan, W/2 <= R <= W with at most 6 pairs (R = W and k = 1 when
+  // whole_only), then the fewest workgroups, then the fewest waves.  The three are chosen
+  // together: a shape that is slower per tile but holds more row blocks per workgroup can
+  // still win once its row tiles are cut into key ranges that fill the CUs (a 512-token chunk
+  // over a 32K prefix, 40/8 heads: W = 8, R = 4 in 3 ranges 441 us; W = 12, R = 10 in 4 ranges
+  // 341 us).
+  const double nt = (double)((max_ctx + 63) / 64);
+  const int kmax = whole_only ? 1 : max_ksplit(max_ctx);
+  int bw = 8, br = 8, bk = 1;
   double best_cost = 1e300;
   for (int w = 4; w <= 12; ++w) {
     for (int r = whole_only ? w : std::max((w + 1) / 2, w - 6); r <= w; ++r) {
-      const int f = 2 * r - w;
-      double load[4] = {0, 0, 0, 0};
-      int nw[4] = {0, 0, 0, 0};
-      for (int i = 0; i < w; ++i) {
-        load[i & 3] += i < f ? 1.0 : 0.5;
-        ++nw[i & 3];
-      }
-      int bs = 0;
-      for (int k = 1; k < 4; ++k)
-        if (load[k] > load[bs] || (load[k] == load[bs] && nw[k] < nw[bs])) bs = k;
+      const double tile = prefill_tile_cost(w, r);
       const long long wgs = prefill_wg_count(rows, n, num_kv_heads, r);
-      const long long rounds = (wgs + num_cus - 1) / num_cus;
-      const double tile = (1.0 + 0.45 * load[bs]) * (nw[bs] <= 1 ? 1.3 : 1.0);
-      const double cost = (double)rounds * tile + 1e-4 * (double)wgs / num_cus + 1e-6 * w;
-      if (cost < best_cost) {
-        best_cost = cost;
-        bw = w;
-        br = r;
+      for (int k = 1; k <= kmax; ++k) {
+        const double cost = prefill_makespan(wgs, k, nt, num_cus, tile) +
+                            1e-4 * (double)(wgs * k) / num_cus + 1e-6 * w;
+        if (cost < best_cost) {
+          best_cost = cost;
+          bw = w;
+          br = r;
+          bk = k;
+        }
       }
     }
   }
   *waves = bw;
   *rblk = br;
+  *ksplit = bk;
 }
 
-int prefill_ksplit(long long wgs, int num_cus, int max_ctx, bool deterministic) {
-  // Cost in 64-key tile times (measured on MI355X: a workgroup over n tiles takes about n + 8.5
-  // of them, the 8.5 being its start and drain; the merge launch about 7): k ranges make
-  // rounds(k) = ceil(k wgs / CUs) rounds of workgroups over n/k tiles each.  A 512-token chunk
-  // over a 32K prefix (160 workgroups of 520 tiles) measured 598 us at k = 1, 442 us at k = 3;
-  // over a 4K prefix (72 tiles) k = 3 and k = 1 measured the same.
+int prefill_ksplit(long long wgs, int num_cus, int max_ctx, int waves, int rblk,
+                   bool deterministic) {
   if (deterministic || wgs <= 0 || num_cus <= 0) return 1;
-  const double n = (double)((max_ctx + 63) / 64);
-  const int kmax = std::max(1, std::min(8, (int)(n / 4)));
+  const double nt = (double)((max_ctx + 63) / 64);
+  const double tile = prefill_tile_cost(waves, rblk);
   int best_k = 1;
-  double best = n + 8.5;
-  for (int k = 2; k <= kmax; ++k) {
-    const long long rounds = (wgs * k + num_cus - 1) / num_cus;
-    const double cost = (double)rounds * (n / k + 8.5) + 7.0;
+  double best = prefill_makespan(wgs, 1, nt, num_cus, tile);
+  for (int k = 2; k <= max_ksplit(max_ctx); ++k) {
+    const double cost = prefill_makespan(wgs, k, nt, num_cus, tile);
     if (cost < best - 1e-9) {
       best = cost;
       best_k = k;

@@ -90,15 +90,17 @@ hipError_t launch_attn_prefill_mfma(const AttnArgs& a, int head_dim, int waves, 
 // Workgroups of the prefill kernel for prefill-class sequences of rows[i] = q_len * G rows each,
 // with rblk 32-row blocks per workgroup.
 long long prefill_wg_count(const int* rows, int n, int num_kv_heads, int rblk);
-// Key ranges per prefill row tile (1..8): more when the row tiles alone, wgs of them, leave
-// CUs idle; 1 in deterministic mode.  max_ctx: the longest context (ranges of whole 64-key
-// tiles, at least 4 each).
-int prefill_ksplit(long long wgs, int num_cus, int max_ctx, bool deterministic);
-// Workgroup shape for such a set of sequences: waves (4..12) and row blocks per workgroup
-// (waves/2 .. waves; the waves beyond 2*rblk - waves share a row block in pairs), balancing the
-// SIMDs and the workgroups over the CUs.  whole_only: rblk = waves (no pairs).
+// Key ranges per prefill row tile (1..8) for a given workgroup shape (waves, rblk): more when
+// the row tiles alone, wgs of them, leave CUs idle; 1 in deterministic mode.  max_ctx: the
+// longest context (ranges of whole 64-key tiles, at least 4 each).
+int prefill_ksplit(long long wgs, int num_cus, int max_ctx, int waves, int rblk,
+                   bool deterministic);
+// Workgroup shape and key ranges for such a set of sequences, chosen together for the least
+// modelled makespan: waves (4..12), row blocks per workgroup (waves/2 .. waves; the waves beyond
+// 2*rblk - waves share a row block in pairs) and key ranges per row tile (1..8).
+// whole_only: rblk = waves (no pairs) and one key range.
 void prefill_plan(const int* rows, int n, int num_kv_heads, int num_cus, bool whole_only,
-                  int* waves, int* rblk);
+                  int max_ctx, int* waves, int* rblk, int* ksplit);
 // Prefill over an int8 pool, when the workspace holds the copy: the prefill-class sequences'
 // tiles dequantized to bf16 into a workspace pool (max_seqs sequences of blocks_per_seq 16-token
 // blocks) and its block table [num_seqs][blocks_per_seq]; the grid covers max_seqs sequences

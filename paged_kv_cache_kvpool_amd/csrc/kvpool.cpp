@@ -566,6 +566,7 @@ Plan make_plan(const kvpool* p, int32_t num_q_heads, int32_t num_seqs, int32_t t
       pf_rows.assign(std::max(n, 1), max_q_len * G);
     }
   }
+  int pf_ks_plan = 1;
   if (pl.prefill) {
     // Deterministic mode (KVATTN_DETERMINISTIC=1): whole-block plans only.  A row block is then
     // always reduced by one wave over its keys in key order, whatever (W, R) the batch leads to,
@@ -573,8 +574,10 @@ Plan make_plan(const kvpool* p, int32_t num_q_heads, int32_t num_seqs, int32_t t
     // default a row block may also be split between a pair of half waves (even and odd key
     // blocks, merged at the end): faster when the batch is small, but the merge rounds
     // differently, so the bits follow the plan.
+    // The key ranges (below) are chosen with the shape, as part of one makespan model.
     kvp::prefill_plan(pf_rows.data(), (int)pf_rows.size(), p->num_kv_heads, p->num_cus,
-                      env_flag("KVATTN_DETERMINISTIC"), &pl.waves, &pl.rblk);
+                      env_flag("KVATTN_DETERMINISTIC"), max_ctx_len, &pl.waves, &pl.rblk,
+                      &pf_ks_plan);
     // sweeps and tests: KVATTN_PREFILL_WAVES fixes W in [4, 12] (then R = W unless
     // KVATTN_PREFILL_RBLK fixes R within [W/2, W], at most 6 pairs)
     if (const char* v = getenv("KVATTN_PREFILL_WAVES")) {
@@ -582,6 +585,7 @@ Plan make_plan(const kvpool* p, int32_t num_q_heads, int32_t num_seqs, int32_t t
       pl.rblk = pl.waves;
       if (const char* r = getenv("KVATTN_PREFILL_RBLK"))
         pl.rblk = std::max(std::max((pl.waves + 1) / 2, pl.waves - 6), std::min(pl.waves, atoi(r)));
+      pf_ks_plan = 0;  // the ranges for the forced shape, below
     }
     if (q_lens_host) {
       pl.pf_wgs = kvp::prefill_wg_count(pf_rows.data(), (int)pf_rows.size(), p->num_kv_heads, pl.rblk);
@@ -604,7 +608,9 @@ Plan make_plan(const kvpool* p, int32_t num_q_heads, int32_t num_seqs, int32_t t
   pl.pf_ks = 1;
   if (pl.prefill && p->dtype != KV_F32) {  // (fp32 pools run every sequence in attn_vec)
     const bool det = env_flag("KVATTN_DETERMINISTIC");
-    pl.pf_ks = kvp::prefill_ksplit(pl.pf_wgs, p->num_cus, max_ctx_len, det);
+    pl.pf_ks = pf_ks_plan > 0 ? pf_ks_plan
+                              : kvp::prefill_ksplit(pl.pf_wgs, p->num_cus, max_ctx_len, pl.waves,
+                                                    pl.rblk, det);
     if (const char* v = getenv("KVATTN_PREFILL_KSPLIT")) pl.pf_ks = std::max(1, std::min(8, atoi(v)));
     if (det) pl.pf_ks = 1;
   }
