@@ -22,6 +22,7 @@ namespace kvp {
 namespace {
 
 constexpr int kTiles = 4;  // 16-token tiles per workgroup
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // Prefill sequence, its index among the prefill-class sequences, KV head and tile group of flat
 // workgroup n, where sequence i holds Hkv * ceil(ceil(L / 16) / kTiles) workgroups.  False past
@@ -109,33 +110,50 @@ __global__ __launch_bounds__(256) void dequant_prefill_kernel(AttnArgs a, Dequan
       *reinterpret_cast<u32x4*>(kd + ((2 * c) * 16 + t) * 8) = u32x4{r[0], r[1], r[2], r[3]};
       *reinterpret_cast<u32x4*>(kd + ((2 * c + 1) * 16 + t) * 8) = u32x4{r[4], r[5], r[6], r[7]};
     }
-  } else if (tid < 2 * D) {
-    // V: dim d, its 16 tokens (4 groups of 4 codes) -> one bf16 row of 16 tokens
-    const int d = tid - D;
-    uint32_t x[kTiles][4];
-    floatx4 sv[kTiles][4];
+  }
+  // V: the tile's codes ([t/4][d%16][d/16][t%4], 16 D bytes) are read by D threads with one
+  // contiguous 16-byte load each, converted, and transposed through LDS into the bf16 rows
+  // [d][t] that the threads then store 32 bytes each (contiguous as well).  Thread j's 16 bytes
+  // are entries 4j .. 4j+3 of (token group tg, d%16, d/16), each the 4 tokens of group tg for one
+  // dim; all four share tg (D entries per group), so one float4 of scales serves them.
+  __shared__ __attribute__((aligned(16))) uint16_t vt_lds[kTiles][D * 16];
+  const int j = tid - D;
+  const bool vthr = tid >= D && tid < 2 * D;  // workgroup-uniform per wave (D is a multiple of 64)
+  if (vthr) {
+    u32x4 x[kTiles];
+    floatx4 s4[kTiles];
+    const int tg = (4 * j) / D;
 #pragma unroll
-    for (int u = 0; u < kTiles; ++u) {
-#pragma unroll
-      for (int tg = 0; tg < 4; ++tg) {
-        x[u][tg] = *reinterpret_cast<const uint32_t*>(v8 + src[u] + ((tg * 16 + (d & 15)) * (D / 16) + (d >> 4)) * 4);
-        sv[u][tg] = *reinterpret_cast<const floatx4*>(a.v_scale_layer + src[u] / D + 4 * tg);
-      }
+    for (int u = 0; u < kTiles; ++u) {  // every load first (tiles past nt repeat the last one)
+      x[u] = *reinterpret_cast<const u32x4*>(v8 + src[u] + 16 * j);
+      s4[u] = *reinterpret_cast<const floatx4*>(a.v_scale_layer + src[u] / D + 4 * tg);
     }
 #pragma unroll
     for (int u = 0; u < kTiles; ++u) {
-      if (u >= nt) break;
-      uint32_t r[8];
 #pragma unroll
-      for (int tg = 0; tg < 4; ++tg) {
-        const uint32_t xx = x[u][tg];
-        const floatx4 s4 = sv[u][tg];
-        r[2 * tg] = cvt_pk_bf16((float)(int8_t)(xx & 0xff) * s4[0], (float)(int8_t)((xx >> 8) & 0xff) * s4[1]);
-        r[2 * tg + 1] = cvt_pk_bf16((float)(int8_t)((xx >> 16) & 0xff) * s4[2], (float)(int8_t)(xx >> 24) * s4[3]);
+      for (int q = 0; q < 4; ++q) {
+        const int e = 4 * j + q;
+        const int d = 16 * (e % (D / 16)) + (e / (D / 16)) % 16;
+        const uint32_t xx = x[u][q];
+        const uint32_t r0 = cvt_pk_bf16((float)(int8_t)(xx & 0xff) * s4[u][0],
+                                        (float)(int8_t)((xx >> 8) & 0xff) * s4[u][1]);
+        const uint32_t r1 = cvt_pk_bf16((float)(int8_t)((xx >> 16) & 0xff) * s4[u][2],
+                                        (float)(int8_t)(xx >> 24) * s4[u][3]);
+        *reinterpret_cast<u32x2*>(&vt_lds[u][d * 16 + 4 * tg]) = u32x2{r0, r1};
       }
+    }
+  }
+  __syncthreads();
+  if (vthr) {
+    const int d = j;
+#pragma unroll
+    for (int u = 0; u < kTiles; ++u) {
+      if (u >= nt) break;
+      const u32x4 lo = *reinterpret_cast<const u32x4*>(&vt_lds[u][d * 16]);
+      const u32x4 hi = *reinterpret_cast<const u32x4*>(&vt_lds[u][d * 16 + 8]);
       uint16_t* vd = o.v + dst(u) + d * 16;
-      *reinterpret_cast<u32x4*>(vd) = u32x4{r[0], r[1], r[2], r[3]};
-      *reinterpret_cast<u32x4*>(vd + 8) = u32x4{r[4], r[5], r[6], r[7]};
+      *reinterpret_cast<u32x4*>(vd) = lo;
+      *reinterpret_cast<u32x4*>(vd + 8) = hi;
     }
   }
 }
