@@ -356,22 +356,25 @@ __device__ __forceinline__ size_t block_tile_offset(int blk, int sub, int h, int
 // One wave per (token, KV head) row: lane l holds dims E*l .. E*l + E - 1 (E = head_dim / 64),
 // the absolute max comes from a wave reduction, and codes are stored byte by byte (K) / to
 // their scattered V slots.  The append kernel and the 32-row split-K kernel's fused append both
-// store rows through append_row_i8, so their bits are the same.
+// store rows through store_row_i8, so their bits are the same.
 __device__ __forceinline__ float wave_max_f(float v) {
   // across the 4 rows of 16 lanes (permlane swaps), then within each row (DPP): no LDS trips
   return row_max(xrow_max(v));
 }
 
+// A row's E bf16 values of this lane (dims E*lane ..), as floats.
 template <int E>
-__device__ __forceinline__ void quantise_row(const uint16_t* src, float (&q)[E], float& scale) {
+__device__ __forceinline__ void load_row(const uint16_t* src, float (&x)[E]) {
   const int lane = threadIdx.x & (WAVE - 1);
-  float x[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) x[e] = __uint_as_float((uint32_t)src[E * lane + e] << 16);
+}
+
+template <int E>
+__device__ __forceinline__ void quantise_vals(const float (&x)[E], float (&q)[E], float& scale) {
   float m = 0.f;
 #pragma unroll
-  for (int e = 0; e < E; ++e) {
-    x[e] = __uint_as_float((uint32_t)src[E * lane + e] << 16);
-    m = fmaxf(m, fabsf(x[e]));
-  }
+  for (int e = 0; e < E; ++e) m = fmaxf(m, fabsf(x[e]));
   m = wave_max_f(m);
   scale = __fdiv_rn(m, 127.f);
 #pragma unroll
@@ -379,17 +382,17 @@ __device__ __forceinline__ void quantise_row(const uint16_t* src, float (&q)[E],
     q[e] = scale > 0.f ? fminf(fmaxf(rintf(__fdiv_rn(x[e], scale)), -127.f), 127.f) : 0.f;
 }
 
-// Quantises the bf16 rows krow / vrow (head_dim 64 E) of token slot tt of a 16-token tile and
-// stores codes and scales into the tile (kt, vt: the tile's codes; ks, vs: its 16 scales).
-// The whole wave takes part (wave reductions).
+// Quantises the K and V values kx / vx of one (token, KV head) row (head_dim 64 E, this lane's
+// dims) and stores the codes and scales at token slot tt of a 16-token tile (kt, vt: the tile's
+// codes; ks, vs: its 16 scales).  The whole wave takes part (wave reductions).
 template <int E>
-__device__ __forceinline__ void append_row_i8(int8_t* kt, int8_t* vt, float* ks, float* vs,
-                                              const uint16_t* krow, const uint16_t* vrow, int tt) {
+__device__ __forceinline__ void store_row_i8(int8_t* kt, int8_t* vt, float* ks, float* vs,
+                                             const float (&kx)[E], const float (&vx)[E], int tt) {
   constexpr int D = 64 * E;
   const int lane = threadIdx.x & (WAVE - 1);
   float qk[E], qv[E], sk, sv;
-  quantise_row<E>(krow, qk, sk);
-  quantise_row<E>(vrow, qv, sv);
+  quantise_vals<E>(kx, qk, sk);
+  quantise_vals<E>(vx, qv, sv);
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const int d = E * lane + e;
@@ -400,6 +403,16 @@ __device__ __forceinline__ void append_row_i8(int8_t* kt, int8_t* vt, float* ks,
     ks[tt] = sk;
     vs[tt] = sv;
   }
+}
+
+// The same from the bf16 rows krow / vrow in memory.
+template <int E>
+__device__ __forceinline__ void append_row_i8(int8_t* kt, int8_t* vt, float* ks, float* vs,
+                                              const uint16_t* krow, const uint16_t* vrow, int tt) {
+  float kx[E], vx[E];
+  load_row<E>(krow, kx);
+  load_row<E>(vrow, vx);
+  store_row_i8<E>(kt, vt, ks, vs, kx, vx, tt);
 }
 
 }  // namespace kvp

@@ -75,7 +75,7 @@ __global__ __launch_bounds__(256) void append_kernel(AppendArgs a) {
   }
 }
 
-// int8 pools: each new (token, KV head) row is quantised and stored by append_row_i8 (common.h),
+// int8 pools: each new (token, KV head) row is quantised and stored by store_row_i8 (common.h),
 // one wave per row of the workgroup's 16-token tile.
 template <int E>
 __global__ __launch_bounds__(256) void append_i8_kernel(AppendArgs a) {
@@ -100,12 +100,24 @@ __global__ __launch_bounds__(256) void append_i8_kernel(AppendArgs a) {
   float* vs = a.v_scale_layer + toff / D;
   const uint16_t* kn = reinterpret_cast<const uint16_t*>(a.k_new);
   const uint16_t* vn = reinterpret_cast<const uint16_t*>(a.v_new);
-  for (int p = lo + wave; p < hi; p += 4) {  // wave-uniform
+  // This wave's rows (positions lo + wave, + 4, ...: at most 4 of the tile's 16): every row's
+  // values are loaded before any is quantised, so the wave waits for memory once.
+  float kx[4][E], vx[4][E];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int p = lo + wave + 4 * i;
     const int row = q_start + (p - p0);
-    if (row >= a.total_q) continue;
-    const int tt = p - tile_start;
-    const size_t src = ((size_t)row * a.num_kv_heads + h) * D;
-    append_row_i8<E>(kt, vt, ks, vs, kn + src, vn + src, tt);
+    if (p < hi && row < a.total_q) {  // wave-uniform
+      const size_t src = ((size_t)row * a.num_kv_heads + h) * D;
+      load_row<E>(kn + src, kx[i]);
+      load_row<E>(vn + src, vx[i]);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int p = lo + wave + 4 * i;
+    const int row = q_start + (p - p0);
+    if (p < hi && row < a.total_q) store_row_i8<E>(kt, vt, ks, vs, kx[i], vx[i], p - tile_start);
   }
 }
 
