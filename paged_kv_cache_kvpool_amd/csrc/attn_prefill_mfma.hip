@@ -198,22 +198,30 @@ __device__ __forceinline__ void find_prefill_tile(const AttnArgs& a, int n, int 
 // Issue order of one finish (the softmax and P.V of a 32-key block beside the score product of
 // the next), as chunks of at most one MFMA each.  MFMA u < D/16 is k-step u of the next block's
 // score product; u = D/16 + (D/32) j + mb is k-step j of P.V for output dims 32mb .. +32, which
-// needs the P packs 4j .. 4j+3 (made two per chunk in chunks 0-7, so j = 0 may start at chunk
-// 4 and j = 1 at chunk 8).  -1: a chunk without MFMA.  Operand loads run two MFMAs ahead.
+// needs the P packs 4j .. 4j+3.  -1: a chunk without MFMA.  Operand loads run two MFMAs ahead.
+// The softmax of a score pair is two stages: exp2 (with its scale-and-subtract FMA) in one
+// chunk, the bf16 pack and the row-sum adds in a later one, so that no chunk's vector work waits
+// on the latency of its own exp2.
 template <int D> struct PfSched;
 template <> struct PfSched<128> {
   static constexpr int N = 16;
-  // MFMA of each chunk (all 16 chunks carry one): score k-steps 0-3, then P.V k-step 0 (u 8-11)
-  // interleaved with score k-steps 4-7, then P.V k-step 1 (u 12-15)
-  static constexpr int kOp[16] = {0, 1, 2, 3, 8, 4, 9, 5, 10, 6, 11, 7, 12, 13, 14, 15};
-  // exp2 pair (P pack) made in each chunk: packs 0-3 before P.V k-step 0 starts (chunk 4), packs
-  // 4-7 one every other chunk beside the MFMAs of chunks 4-11, before P.V k-step 1 (chunk 12)
-  static constexpr int kExp[16] = {0, 1, 2, 3, -1, 4, -1, 5, -1, 6, -1, 7, -1, -1, -1, -1};
+  // MFMA of each chunk (all 16 chunks carry one): score k-steps 0-4, then P.V k-step 0 (u 8-11)
+  // interleaved with score k-steps 5-7, then P.V k-step 1 (u 12-15)
+  static constexpr int kOp[16] = {0, 1, 2, 3, 4, 8, 5, 9, 6, 10, 7, 11, 12, 13, 14, 15};
+  // exp2 stage of each pair, and its pack stage a chunk later: packs 0-3 are made by chunk 4,
+  // before P.V k-step 0 starts (chunk 5); packs 4-7 by chunk 11, before P.V k-step 1 (chunk 12)
+  static constexpr int kExp[16] = {0, 1, 2, 3, 4, -1, 5, -1, 6, -1, 7, -1, -1, -1, -1, -1};
+  static constexpr int kPack[16] = {-1, 0, 1, 2, 3, 4, -1, 5, -1, 6, -1, 7, -1, -1, -1, -1};
   static constexpr int op(int ci) { return kOp[ci]; }
   static constexpr int exp_pair(int ci) { return kExp[ci]; }
+  static constexpr int pack_pair(int ci) { return kPack[ci]; }
   static constexpr int slot(int ci) { return ci; }
   static constexpr int next_load(int ci) { return ci + 2 < N ? ci + 2 : -1; }
   static constexpr int slot_of_load(int ci) { return ci; }
+  // part of the next block's lane-local row max made beside the last P.V MFMAs (its last score
+  // MFMA is issued in chunk 10, so its result is ready by then)
+  static constexpr int kMax[16] = {-1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, -1, 0, 1, 2};
+  static constexpr int max_part(int ci) { return kMax[ci]; }
 };
 template <> struct PfSched<64> {
   static constexpr int N = 10;
@@ -224,10 +232,13 @@ template <> struct PfSched<64> {
   static constexpr int kSlot[10] = {0, 1, 2, 3, 4, 5, 0, 0, 6, 7};
   static constexpr int op(int ci) { return kOp[ci]; }
   static constexpr int exp_pair(int ci) { return kExp[ci]; }
+  static constexpr int pack_pair(int ci) { return kExp[ci]; }  // both stages in one chunk
   static constexpr int slot(int ci) { return kSlot[ci]; }
   // the chunk whose operand the MFMA of chunk ci loads: the MFMA two places later
   static constexpr int next_load(int ci) { return kSlot[ci] + 2 < 8 ? kMf[kSlot[ci] + 2] : -1; }
   static constexpr int slot_of_load(int ci) { return kSlot[ci]; }
+  // the row max is made after the chunks
+  static constexpr int max_part(int) { return -1; }
 };
 
 // Up to 12 waves per workgroup, 3 per SIMD: at most 168 registers per wave.
@@ -589,11 +600,34 @@ void attn_prefill_mfma_kernel(AttnArgs a) {
     }
     return sc;
   };
+  // The row's max over a block's scores, in three parts that can go into separate chunks: the
+  // lane's scores 0-6, then 7-12, then 13-15 and the other half of the row (lanes l and l ^ 32
+  // hold the same row).  IEEE maximum (no NaN quieting needed: a masked score is -inf).
+  auto max_part = [&](const floatx16& sc, float& cm, int part) {
+    auto mx3 = [](float x, float y, float z) {
+      return __builtin_elementwise_maximum(__builtin_elementwise_maximum(x, y), z);
+    };
+    if (part == 0) {
+      cm = mx3(sc[0], sc[1], sc[2]);
+      cm = mx3(cm, sc[3], sc[4]);
+      cm = mx3(cm, sc[5], sc[6]);
+    } else if (part == 1) {
+      cm = mx3(cm, sc[7], sc[8]);
+      cm = mx3(cm, sc[9], sc[10]);
+      cm = mx3(cm, sc[11], sc[12]);
+    } else {
+      cm = mx3(cm, sc[13], sc[14]);
+      cm = __builtin_elementwise_maximum(cm, sc[15]);
+      float x, y;
+      swap32(cm, x, y);
+      cm = __builtin_elementwise_maximum(x, y);
+    }
+  };
   // Masks the scores of an edge block (past the wave's first row on the causal diagonal, or past
   // the context), then raises the running max where a row's max grew by more than 2^8 in exp2
-  // units (lazy: P stays <= 256 and the rescale is rare).  The max is IEEE maximum (no NaN
-  // quieting needed: a masked score is -inf, never NaN).
-  auto row_max = [&](floatx16& sc, int kb, bool edge) {
+  // units (lazy: P stays <= 256 and the rescale is rare).  `cmax`: the row's max over the
+  // unmasked scores when `have` (made beside the matrix work); an edge block makes it afresh.
+  auto row_max = [&](floatx16& sc, int kb, bool edge, float cmax, bool have) {
     if (edge) {
       // keys of this lane: kb + 16 (e / 8) + 8 h' + e % 8 (h' recomputed from the lane id here
       // rather than held in a register through the loop)
@@ -604,16 +638,12 @@ void attn_prefill_mfma_kernel(AttnArgs a) {
 #pragma unroll
       for (int e = 0; e < 16; ++e)
         if (16 * (e >> 3) + (e & 7) > lim) sc[e] = -INFINITY;
+      have = false;
     }
-    float cmax = __builtin_elementwise_maximum(__builtin_elementwise_maximum(sc[0], sc[1]), sc[2]);
-#pragma unroll
-    for (int e = 3; e < 15; e += 2)
-      cmax = __builtin_elementwise_maximum(__builtin_elementwise_maximum(cmax, sc[e]), sc[e + 1]);
-    cmax = __builtin_elementwise_maximum(cmax, sc[15]);
-    {
-      float x, y;
-      swap32(cmax, x, y);
-      cmax = __builtin_elementwise_maximum(x, y);
+    if (!have) {
+      max_part(sc, cmax, 0);
+      max_part(sc, cmax, 1);
+      max_part(sc, cmax, 2);
     }
     // true on a row's first key (msub = -inf); false for a row with no key yet (NaN)
     const float cm = cmax * c;
@@ -661,6 +691,8 @@ void attn_prefill_mfma_kernel(AttnArgs a) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) sn[e] = 0.f;
     uint32_t pk[8];
+    float cmax_n = 0.f;  // the next block's row max (unmasked), made in the last chunks
+    float e0 = 0.f, e1 = 0.f;  // exp2 results waiting for their pack stage
     __builtin_amdgcn_sched_barrier(0);
     // Chunks pinned in place: at most one MFMA, the operand load two MFMAs ahead, and at most one
     // exp2 pair of the softmax (the two scores' exp2, their bf16 pack and row sum), spread so
@@ -680,18 +712,29 @@ void attn_prefill_mfma_kernel(AttnArgs a) {
         const int nx = Sched::next_load(ci);
         if (nx >= 0) ops[Sched::slot_of_load(nx)] = load_op(Sched::op(nx));
       }
-      const int ep = Sched::exp_pair(ci);
+      const int mp = Sched::max_part(ci);
+      if (mp >= 0) max_part(sn, cmax_n, mp);
+      const int ep = Sched::exp_pair(ci), pp = Sched::pack_pair(ci);
+      float p0 = 0.f, p1 = 0.f;
       if (ep >= 0) {
-        const float p0 = fast_exp2(__builtin_fmaf(sc[2 * ep], c, nms));
-        const float p1 = fast_exp2(__builtin_fmaf(sc[2 * ep + 1], c, nms));
-        pk[ep] = cvt_pk_bf16(p0, p1);
+        p0 = fast_exp2(__builtin_fmaf(sc[2 * ep], c, nms));
+        p1 = fast_exp2(__builtin_fmaf(sc[2 * ep + 1], c, nms));
+      }
+      if (pp >= 0) {
+        // the pair's exp2 results: this chunk's, or the ones an earlier chunk left in e0, e1
+        const float x0 = pp == ep ? p0 : e0, x1 = pp == ep ? p1 : e1;
+        pk[pp] = cvt_pk_bf16(x0, x1);
         // row sum of the fp32 values (plain adds: the bf16 dot2 would take matrix-pipe slots)
-        l_lane += p0 + p1;
+        l_lane += x0 + x1;
+      }
+      if (ep >= 0 && pp != ep) {
+        e0 = p0;
+        e1 = p1;
       }
       __builtin_amdgcn_sched_barrier(0);
     }
     const int kn = 32 * (blk + stride);
-    if (kn < kew) row_max(sn, kn, kn + 31 > pw0 || kn + 32 > L);  // wave-uniform
+    if (kn < kew) row_max(sn, kn, kn + 31 > pw0 || kn + 32 > L, cmax_n, Sched::max_part(Sched::N - 1) >= 0);  // wave-uniform
   };
   // the wave's first block: the range's first, or its second for an odd half wave; whole-block
   // waves alternate their scores between sa and sb, half waves keep theirs in sa
@@ -701,7 +744,7 @@ void attn_prefill_mfma_kernel(AttnArgs a) {
   if (kew > 64 * jt0 + 32 * par) {
     sa = qk(lds0, par);
     const int k0 = 64 * jt0 + 32 * par;
-    row_max(sa, k0, k0 + 31 > pw0 || k0 + 32 > L);
+    row_max(sa, k0, k0 + 31 > pw0 || k0 + 32 > L, 0.f, false);
   }
 
   // One 64-key tile j (stage `cur`).  bf16: tile j+3 starts streaming into `fst` (the fourth
