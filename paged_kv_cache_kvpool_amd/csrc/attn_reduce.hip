@@ -147,21 +147,28 @@ __device__ __forceinline__ void merge_prefill_token(const AttnArgs& a, int grow,
   constexpr int DQ = D / 4;
   const int Hq = a.num_q_heads;
   const int u = y * RT + threadIdx.x;  // (q-head, 4-dim) slice
-  int s, i, L, T;
-  if (!find_token(a, grow, s, i, L, T)) return;
-  if (T <= a.split_q_max || i >= T) return;  // not a row the prefill kernel computed
-  if (u >= Hq * DQ) return;
-  const int hh = u / DQ, dq = u % DQ;
+  const bool slice = u < Hq * DQ;
+  const int hh = slice ? u / DQ : 0, dq = u % DQ;
+  // The token's partials are requested before its metadata (their slots depend on the token
+  // and slice alone, inside the buffer for every token < total_q), so the two reads overlap; a
+  // token the prefill kernel did not compute leaves them unused.  (Every lane stays for the
+  // token search, whose wave scans need the whole wave.)
   const size_t slot0 = ((size_t)grow * Hq + hh) * KR;
   const float2* pml = reinterpret_cast<const float2*>(a.pf_part_ml) + slot0;
   const floatx4* po = reinterpret_cast<const floatx4*>(a.pf_part_o) + slot0 * DQ + dq;
   float2 ml[KR];
   floatx4 ok[KR];
+  if (slice) {
 #pragma unroll
-  for (int k = 0; k < KR; ++k) {
-    ml[k] = pml[k];
-    ok[k] = po[(size_t)k * DQ];
+    for (int k = 0; k < KR; ++k) {
+      ml[k] = pml[k];
+      ok[k] = po[(size_t)k * DQ];
+    }
   }
+  int s, i, L, T;
+  if (!find_token(a, grow, s, i, L, T)) return;
+  if (T <= a.split_q_max || i >= T) return;  // not a row the prefill kernel computed
+  if (!slice) return;
   float M = -INFINITY;
 #pragma unroll
   for (int k = 0; k < KR; ++k) M = fmaxf(M, ml[k].x);
