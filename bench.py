@@ -499,7 +499,7 @@ def park_restore_cpu(pool, blocks, spare, budget_s=10.0):
                 sample=f"{n} of {blocks.size} blocks parked and restored ({t_used:.1f} s)")
 
 
-# The BASELINE configurations the default run measures: the headline (batched GQA decode) as
+# The benchmark configurations the default run measures: the headline (batched GQA decode) as
 # the top-level fields, every other configuration under "configs".  Targets: decode at >= 70% of
 # HBM peak, chunked prefill at >= 50% of bf16 MFMA peak; verification is reported against 70%;
 # the tiny fp32 decode is a latency row (microseconds).
@@ -707,7 +707,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=None, choices=sorted(WORKLOADS),
                     help="measure this workload alone (default: the headline batched GQA decode "
-                         "with every other BASELINE configuration under \"configs\")")
+                         "with every other benchmark configuration under \"configs\")")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=None,
                     help="seconds of oracle time per configuration (default 15 alone, 6 each in "
@@ -759,7 +759,7 @@ def main():
             "dtype": rec["dtype"], "data": "synthetic"}
     line.update({k: v for k, v in rec.items() if k not in line})
     if single:
-        # every other BASELINE configuration, measured in the same process the same way
+        # every other benchmark configuration, measured in the same process the same way
         configs = {}
         for name in DEFAULT_CONFIGS:
             r = run_workload(name, args, scratch, want_cpu, budget)
