@@ -370,8 +370,47 @@ void attn_prefill_mfma_kernel(AttnArgs a) {
   const int jb = __builtin_amdgcn_readfirstlane(min(jt0, ntiles - 1));
   const int jlast = __builtin_amdgcn_readfirstlane(max(min(jt1, ntiles) - 1, jb));
   int ids0 = 4 * jb;
-  load_ids(ids0);
-  __syncthreads();
+
+  // Q^T operands: the B operand of k-step k, lane (col, h) holding dims 16k + 8h .. +8 of the
+  // wave's row col.  Its loads go out right behind the first block-id loads (the ids are
+  // written to LDS only after both are in flight), so reading the workgroup's Q overlaps the id
+  // round trip.
+  const int Hq = a.num_q_heads;
+  const int r = rw0 + col;
+  const int qi = r / G;
+  const bool valid = r < rows && q_start + qi < a.total_q;
+  const int prow = valid ? L - T + qi : -1;  // the row's position (keys <= prow are visible)
+  // the row's index in q / out (recomputed for the store rather than held through the loop)
+  auto row_index = [&]() -> size_t { return valid ? (size_t)(q_start + qi) * Hq + kvh * G + r % G : 0; };
+  bf16x8 qb[KS];
+  {
+    constexpr int IDU = IDS / 256;  // ids per thread at most (at least 4 waves)
+    int idv[IDU];
+    // (loads unconditional, indices clamped, so that the waits before the LDS writes can count
+    // them: slot i >= IDS re-reads slot IDS - 1, an invalid row reads row 0 and drops it)
+#pragma unroll
+    for (int u = 0; u < IDU; ++u) {
+      const int i = min(tid + u * (int)blockDim.x, IDS - 1);
+      idv[u] = tbl[(min(ids0 + i, npt - 1) << 4) >> a.block_shift];
+    }
+    const size_t rh = row_index();
+    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + rh * D + 8 * h;
+#pragma unroll
+    for (int k = 0; k < KS; ++k) {
+      const u32x4 z = {0u, 0u, 0u, 0u};
+      const u32x4 v = *reinterpret_cast<const u32x4*>(qp + 16 * k);
+      qb[k] = __builtin_bit_cast(bf16x8, valid ? v : z);
+    }
+#pragma unroll
+    for (int u = 0; u < IDU; ++u) {
+      const int i = tid + u * (int)blockDim.x;
+      if (i < IDS) s_ids[i] = idv[u];
+    }
+  }
+  // the id writes are done before the barrier publishes them (no fence: the Q loads stay in
+  // flight)
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+  barrier_no_fence();
 
   // ---- K/V staging: the 8 pool tiles of a stage ([K0..K3, V0..V3] of a 64-key tile) are dealt
   // round-robin to the issuing waves, each streamed straight into LDS (global_load_lds: lane
@@ -508,25 +547,7 @@ void attn_prefill_mfma_kernel(AttnArgs a) {
     fetch(min(jt0 + 2, jlast), read_ids(min(jt0 + 2, jlast)), lds2, sca);
   }
 
-  // ---- Q^T operands and per-row state ----------------------------------------------------
-  // B operand of k-step k: lane (col, h) holds dims 16k + 8h .. +8 of the wave's row col.
-  const int Hq = a.num_q_heads;
-  const int r = rw0 + col;
-  const int qi = r / G;
-  const bool valid = r < rows && q_start + qi < a.total_q;
-  const int prow = valid ? L - T + qi : -1;  // the row's position (keys <= prow are visible)
-  // the row's index in q / out (recomputed for the store rather than held through the loop)
-  auto row_index = [&]() -> size_t { return valid ? (size_t)(q_start + qi) * Hq + kvh * G + r % G : 0; };
-  bf16x8 qb[KS];
-  {
-    const size_t rh = row_index();
-    const uint16_t* qp = reinterpret_cast<const uint16_t*>(a.q) + rh * D + 8 * h;
-#pragma unroll
-    for (int k = 0; k < KS; ++k) {
-      const u32x4 z = {0u, 0u, 0u, 0u};
-      qb[k] = __builtin_bit_cast(bf16x8, valid ? *reinterpret_cast<const u32x4*>(qp + 16 * k) : z);
-    }
-  }
+  // ---- per-row state (Q^T was loaded with the first block ids, above) ----------------------
   // msub: the running row max times c, in exp2 units (the same in both lanes of a row; -inf
   // until the row's first key); l_lane: this lane's share of the row sum; o: O^T, element e of
   // block mb = dim 32mb + 8(e/4) + 4h + e%4.
