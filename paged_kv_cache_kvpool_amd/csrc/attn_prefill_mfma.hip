@@ -421,16 +421,18 @@ void attn_prefill_mfma_kernel(AttnArgs a) {
   // and moved to scalar registers, where the addresses are computed; holding them in vector
   // registers across a step would cost registers the compute loop needs.
   typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
-  // The DMA issue goes to the waves with slack: the half waves when there are at least 4 of
-  // them beside whole-block waves (half the compute of the waves that set the tile time), else
-  // the waves of the least loaded SIMDs (waves are placed on the 4 SIMDs round-robin, so with
-  // W % 4 != 0 the SIMDs holding wave indices >= W % 4 mod 4 carry one wave less).  Fewer than 4
-  // such waves would make the issue itself the bottleneck: then all waves issue.
+  // The DMA issue goes to the waves with slack: with four or more half waves beside whole-block
+  // waves, to waves 0-3, the oldest wave of each SIMD (the issue arbiter favours the oldest
+  // wave, so these reach each tile's barrier first and wait there longest; the half waves, the
+  // youngest, come last), else to the waves of the least loaded SIMDs (waves are placed on the 4
+  // SIMDs round-robin, so with W % 4 != 0 the SIMDs holding wave indices >= W % 4 mod 4 carry
+  // one wave less).  Fewer than 4 such waves would make the issue itself the bottleneck: then
+  // all waves issue.
   const int wrem = W & 3;
   const bool by_half = F > 0 && W - F >= 4;
   const bool split = !by_half && wrem != 0 && (W >> 2) * (4 - wrem) >= 4;
-  const int nissue = by_half ? W - F : split ? (W >> 2) * (4 - wrem) : W;  // waves that issue DMA
-  const int issue_rank = by_half ? (half ? wave - F : -1)
+  const int nissue = by_half ? 4 : split ? (W >> 2) * (4 - wrem) : W;  // waves that issue DMA
+  const int issue_rank = by_half ? (wave < 4 ? wave : -1)
                          : !split ? wave
                          : (wave & 3) >= wrem ? (wave >> 2) * (4 - wrem) + (wave & 3) - wrem : -1;
   const uint32_t lane_off = 16u * lane;
