@@ -1000,9 +1000,10 @@ int prefill_ksplit(long long wgs, int num_cus, int max_ctx, int waves, int rblk,
 
 hipError_t launch_attn_prefill_mfma(const AttnArgs& a, int head_dim, int waves, long long wgs,
                                     bool i8, hipStream_t st) {
-  if (waves < 1 || waves > 12 || wgs < 0 || wgs > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  // int8 staging: at least 4 issuing waves, so that each streams at most 2 pool tiles
-  if (i8 && (waves < 4 || !a.k_scale_layer || !a.v_scale_layer)) return hipErrorInvalidConfiguration;
+  // at least 4 waves: the prologue's block-id loads cover the id cache with 256 threads, and
+  // the DMA issue deals a stage's 8 pool tiles to at least 4 waves
+  if (waves < 4 || waves > 12 || wgs < 0 || wgs > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  if (i8 && (!a.k_scale_layer || !a.v_scale_layer)) return hipErrorInvalidConfiguration;
   // R row blocks with W/2 <= R <= W; at most 6 half pairs (their merge uses 3 stage arrays)
   if (2 * a.pf_rblk < waves || a.pf_rblk > waves || waves - a.pf_rblk > 6) return hipErrorInvalidConfiguration;
   if (wgs == 0) return hipSuccess;

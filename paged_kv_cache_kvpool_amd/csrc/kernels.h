@@ -80,11 +80,11 @@ hipError_t launch_attn_split_mfma(const AttnArgs& a, int head_dim, int rows_per_
 hipError_t launch_attn_vec(const AttnArgs& a, int elt_bytes, int head_dim, int rows_per_tile,
                            int grid_x, hipStream_t st);
 // Prefill attention on the matrix cores (bf16) for the sequences with q_len > split_q_max:
-// `waves` (1..12) waves over a.pf_rblk 32-row blocks share LDS-staged K/V tiles; the workgroups, numbered sequence
+// `waves` (4..12) waves over a.pf_rblk 32-row blocks share LDS-staged K/V tiles; the workgroups, numbered sequence
 // by sequence (KV heads x row tiles of each prefill-class sequence), are found on the device
 // from q_lens.  `wgs`: grid size, at least the number of workgroups there are (extra ones exit).
-// int8_kv: the pool holds int8 codes with per-token scales, converted to bf16 in LDS (needs
-// waves >= 4): the path for int8 pools when the workspace has no room for a bf16 copy.
+// int8_kv: the pool holds int8 codes with per-token scales, converted to bf16 in LDS: the
+// path for int8 pools when the workspace has no room for a bf16 copy.
 hipError_t launch_attn_prefill_mfma(const AttnArgs& a, int head_dim, int waves, long long wgs,
                                     bool int8_kv, hipStream_t st);
 // Workgroups of the prefill kernel for prefill-class sequences of rows[i] = q_len * G rows each,
